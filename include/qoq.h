@@ -1,0 +1,180 @@
+/*
+ * qoq.h -- C ABI of libqoq, a QoQ W4A8 GEMM (QServe, arXiv 2405.04532) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ *   Y[M,N] = X[M,K] * W[N,K]^T
+ *
+ * X is FP16, quantized per token to INT8; W is held as UINT4 codes under
+ * progressive group quantization (per-channel INT8 in the protective range
+ * [-119,119], then groups of 128 with an integer scale and a UINT4 zero) or
+ * under plain per-channel UINT4; the GEMM unpacks the codes to INT8 in
+ * registers, accumulates INT8 x INT8 products in INT32 on the matrix cores and
+ * rescales once per output in FP32 before writing FP16.
+ *
+ * Passages defining each operation (page title, then section):
+ *   [EN]    "QServe: Low Bit Width Does Not Guarantee High Throughput", section 4
+ *           "Formalization and procedure": stage-1 and stage-2 equations and the
+ *           paragraph on the [-119,119] overflow margin, the integer scale and the
+ *           precomputed zero-point compensation; evaluation pseudocode steps 2, 4,
+ *           5 and 6 (progressive quantization, per-channel vs g128 choice, offline
+ *           pack reorder, register unpack feeding INT8 GEMM).
+ *   [SUM]   "QServe: W4A8KV4 Quantization and System Co-design for Efficient LLM
+ *           Serving" (research.elamur.ai), "Key points": FP16 per-channel scales,
+ *           range [-119,119], then group INT4; multiply first, subtract after.
+ *   [GUIDE] "QServe Guide: W4A8KV4 Quantization for LLM Serving", "Deep Dive" part 1
+ *           (per-token INT8 activations; one rescale by the two scales) and
+ *           "High-Throughput Native INT8 Tensor Core GEMMs" (INT32 accumulators).
+ *   [WIKI]  "QoQ / QServe — Quantification W4A8KV4", example configuration:
+ *           weight group size 128.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers, allocated and owned by the
+ *     caller. The library never allocates, frees or keeps them past the call.
+ *   - FP16 values are passed as raw binary16 bits (uint16_t); no HIP or PyTorch
+ *     header is needed to include this file.
+ *   - Every call validates its arguments on the host first. On a validation
+ *     error it returns a non-zero qoq_status, launches nothing and writes
+ *     nothing. Otherwise it enqueues its kernels on `stream` (a hipStream_t; NULL
+ *     is the default stream) and returns without synchronizing; a launch failure
+ *     is reported as QOQ_ERR_HIP. Faults inside a kernel surface at the caller's
+ *     next synchronization.
+ *   - Shapes: K is a multiple of 128 with 128 <= K <= 132096 (so that every
+ *     INT32 accumulator is exact: 132096 * 128 * 127 < 2^31); N is a multiple
+ *     of 16; M >= 0. M == 0 or N == 0 is an empty call that returns QOQ_OK.
+ *   - Every pointer is 16-byte aligned (QOQ_ERR_ALIGN otherwise).
+ *   - Inputs must be finite; results for NaN or infinite inputs are unspecified.
+ *   - Rounding: every "round" is round-half-to-even; scales are computed in IEEE
+ *     fp32 (correctly rounded division) and stored as FP16 (round to nearest
+ *     even), and the stored FP16 scale is the one used to quantize.
+ *   - There is no global mutable state: calls on different streams or threads
+ *     are independent.
+ */
+#ifndef QOQ_H_
+#define QOQ_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QOQ_ABI_VERSION 1
+#define QOQ_GROUP 128
+#define QOQ_MAX_K 132096
+
+typedef enum {
+    QOQ_MODE_G128 = 0,        /* progressive: INT8 [-119,119] per channel, then g128 UINT4 */
+    QOQ_MODE_PER_CHANNEL = 1  /* UINT4 per output channel, zero-point in the epilogue */
+} qoq_mode;
+
+typedef enum {
+    QOQ_OK = 0,
+    QOQ_ERR_NULL = 1,   /* a required pointer is NULL */
+    QOQ_ERR_SHAPE = 2,  /* M, N or K outside the limits above */
+    QOQ_ERR_ALIGN = 3,  /* a pointer is not 16-byte aligned */
+    QOQ_ERR_MODE = 4,   /* mode is neither QOQ_MODE_G128 nor QOQ_MODE_PER_CHANNEL */
+    QOQ_ERR_HIP = 5     /* the HIP runtime reported an error at launch */
+} qoq_status;
+
+/* QOQ_ABI_VERSION of the loaded library. */
+int qoq_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* qoq_status_str(int status);
+
+/*
+ * Weight quantization, offline ([EN] section 4, both equations; [SUM]).
+ *
+ *   w   [N,K] FP16 row-major, output channel n is row n (the nn.Linear layout).
+ *   q   [N,K] uint8, one UINT4 code (0..15) per byte.
+ *   s_c [N]   FP16 per-channel scale.
+ *   QOQ_MODE_G128, with G = K/128:
+ *     s_c[n] = f16(max_k |w[n,k]| / 119)
+ *     w8     = clip(round(w / s_c), -119, 119)               (stage 1)
+ *     per group g: mn = min(0, min w8), mx = max(0, max w8)
+ *     s_g[n,g] = max(1, ceil((mx - mn)/15))  (uint8, 1..16)  (stage 2)
+ *     z[n,g]   = round(-mn / s_g)            (uint8, 0..15)
+ *     q        = clip(round(w8 / s_g) + z, 0, 15)
+ *     so that (q - z) * s_g lies in [-127, 127] and W^ = s_c * s_g * (q - z).
+ *     s_g and z are [N,G] row-major.
+ *   QOQ_MODE_PER_CHANNEL (s_g must be NULL):
+ *     mn = min(0, min_k w), mx = max(0, max_k w), s_c = f16((mx - mn)/15),
+ *     z[n] = clip(round(-mn/s_c), 0, 15), q = clip(round(w/s_c) + z, 0, 15);
+ *     W^ = s_c * (q - z). z is [N].
+ *   A scale that is 0 (all-zero row, or one that rounds to 0 in FP16) gives
+ *   q = 0 and z = 0 for that row.
+ */
+qoq_status qoq_quantize_weights(int mode, const uint16_t* w, int64_t N, int64_t K,
+                                uint8_t* q, uint16_t* s_c, uint8_t* s_g, uint8_t* z,
+                                void* stream);
+
+/*
+ * Size in bytes of the packed weight blob, or -1 for an unsupported shape or
+ * mode. The blob is laid out for the gfx950 INT8 MFMA operand ([EN] pseudocode
+ * step 5: the codes are reordered offline so that the main loop does no
+ * address arithmetic beyond one 16-byte load per lane):
+ *
+ *   Codes: N*K/2 bytes at offset 0, in tiles of 16 output channels x 128 input
+ *   channels (one group), 1024 bytes each. Tile (t, g) = channels 16t..16t+15,
+ *   inputs 128g..128g+127, starts at byte (t*G + g)*1024. Write the position of
+ *   input k inside its group as k % 128 = 64*s + 16*j + i (s in 0..1, j in
+ *   0..3, i in 0..15) and c = n % 16. Then the code of (n, k) lives in
+ *     lane  = 16*j + c                 (the tile is 64 lanes x 16 bytes)
+ *     kappa = 16*s + i                 (the lane's code index, 0..31)
+ *     byte  = 16*lane + 4*(kappa/8) + (kappa % 4)
+ *     the low nibble when kappa % 8 < 4, else the high nibble.
+ *   So one 16-byte load by lane l brings, for channel c = l % 16, the 32 codes
+ *   that the MFMA k-steps s = 0 and 1 pair with activation bytes
+ *   128g + 64s + 16(l/16) + (0..15); (word & 0x0F0F0F0F) and
+ *   ((word >> 4) & 0x0F0F0F0F) of each 32-bit word give four codes in k order.
+ *
+ *   Parameters at offset N*K/2:
+ *     QOQ_MODE_G128: N rows of Gp = roundup(G, 16) bytes; byte g of row n is
+ *       ((s_g[n,g] - 1) << 4) | z[n,g]; padding bytes are 0.
+ *     QOQ_MODE_PER_CHANNEL: N bytes, z[n].
+ */
+int64_t qoq_packed_bytes(int mode, int64_t N, int64_t K);
+
+/* Pack canonical codes (q [N,K], s_g [N,G] or NULL, z) into `blob`
+ * (qoq_packed_bytes(mode, N, K) bytes). Needs N >= 16. */
+qoq_status qoq_pack_weights(int mode, const uint8_t* q, const uint8_t* s_g, const uint8_t* z,
+                            int64_t N, int64_t K, void* blob, void* stream);
+
+/* Inverse of qoq_pack_weights, for inspection and tests. */
+qoq_status qoq_unpack_weights(int mode, const void* blob, int64_t N, int64_t K,
+                              uint8_t* q, uint8_t* s_g, uint8_t* z, void* stream);
+
+/*
+ * Per-token INT8 activation quantization, every call ([GUIDE] Deep Dive part 1).
+ *
+ *   x      [M,K] FP16 row-major.
+ *   s_x[m] = f16(max_k |x[m,k]| / 127)                   (FP16, [M])
+ *   xq     = clamp(round(x / s_x), -128, 127)            (int8, [M,K])
+ *   rowsum[m] = sum_k xq[m,k]  (int32, [M]; may be NULL; required later by the
+ *             per-channel GEMM's zero-point compensation)
+ *   A scale of 0 gives xq = 0 for that row.
+ */
+qoq_status qoq_quantize_act(const uint16_t* x, int64_t M, int64_t K, int8_t* xq,
+                            uint16_t* s_x, int32_t* rowsum, void* stream);
+
+/*
+ * W4A8 GEMM with the FP16 epilogue ([EN] section 4 and pseudocode step 6;
+ * [GUIDE] "INT32 accumulators" and the one-time rescale).
+ *
+ *   xq [M,K] int8, s_x [M] FP16, rowsum [M] int32 (required in per-channel
+ *   mode, ignored in g128 mode), blob from qoq_pack_weights, s_c [N] FP16.
+ *   acc[m,n] = sum_k xq[m,k] * (q[n,k] - z) * s_g     (g128; exact INT32)
+ *            = sum_k xq[m,k] * (q[n,k] - z[n])        (per-channel; computed as
+ *              sum_k xq*q - z[n]*rowsum[m], exact)
+ *   y[m,n]   = f16( (f32(acc) * f32(s_x[m])) * f32(s_c[n]) )  (FP16 [M,N])
+ *   acc_out  [M,N] int32 receives acc when not NULL (slower; for inspection).
+ */
+qoq_status qoq_w4a8_gemm(int mode, const int8_t* xq, const uint16_t* s_x, const int32_t* rowsum,
+                         const void* blob, const uint16_t* s_c, int64_t M, int64_t N, int64_t K,
+                         uint16_t* y, int32_t* acc_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QOQ_H_ */

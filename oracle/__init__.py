@@ -1,0 +1,235 @@
+"""CPU oracle for the QoQ W4A8 GEMM path (QServe, arXiv 2405.04532).
+
+TEST INFRASTRUCTURE. Only the test suite, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package. The product path (the
+HIP library under ``quantized_gemm_qoq_amd``) never imports it, and the two share
+no code: the oracle is plain C in ``qoq_oracle.c``, loaded here through ctypes.
+
+Every function takes and returns numpy arrays. FP16 values travel as their raw
+binary16 bits (``uint16``). What each function computes, and the passage of the
+pages it follows, is stated beside it in ``qoq_oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+MODE_G128 = 0
+MODE_PER_CHANNEL = 1
+GROUP = 128
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "qoq_oracle.c")
+_LIB = os.path.join(_HERE, "libqoq_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, strict IEEE: no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+               "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
+               _SRC, "-o", tmp, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            lib = ctypes.CDLL(_LIB)
+            P = ctypes.c_void_p
+            I64 = ctypes.c_int64
+            I = ctypes.c_int
+            sigs = {
+                "orc_f16_to_f64": (ctypes.c_double, [ctypes.c_uint16]),
+                "orc_f32_to_f16": (ctypes.c_uint16, [ctypes.c_float]),
+                "orc_num_threads": (I, []),
+                "orc_quantize_act": (I, [P, I64, I64, P, P, P]),
+                "orc_quantize_weights_g128": (I, [P, I64, I64, P, P, P, P, P]),
+                "orc_quantize_weights_pc": (I, [P, I64, I64, P, P, P]),
+                "orc_dequantize_weights": (I, [I, P, P, P, P, I64, I64, P]),
+                "orc_packed_bytes": (I64, [I, I64, I64]),
+                "orc_pack": (I, [I, P, P, P, I64, I64, P]),
+                "orc_gemm": (I, [I, P, P, P, P, I64, I64, I64, P]),
+                "orc_gemm_points": (I, [I, P, P, P, P, I64, I64, I64, I64, P, P, P]),
+                "orc_epilogue": (I, [P, P, P, I64, I64, P]),
+                "orc_epilogue_points": (I, [P, P, P, I64, P, P, P]),
+                "orc_f32_to_f16_array": (None, [P, I64, P]),
+                "orc_f16_to_f64_array": (None, [P, I64, P]),
+            }
+            for name, (res, args) in sigs.items():
+                fn = getattr(lib, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = lib
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    a = np.asarray(a)
+    if a.dtype != dtype:
+        raise TypeError(f"expected {np.dtype(dtype)}, got {a.dtype}")
+    return np.ascontiguousarray(a)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise RuntimeError(f"oracle {what} failed with code {rc}")
+
+
+def num_threads() -> int:
+    return _load().orc_num_threads()
+
+
+def f32_to_f16_bits(values) -> np.ndarray:
+    """binary32 -> binary16 bits (RNE) through the oracle's own conversion."""
+    v = np.ascontiguousarray(np.asarray(values, dtype=np.float32).ravel())
+    out = np.empty(v.size, np.uint16)
+    _load().orc_f32_to_f16_array(_p(v), v.size, _p(out))
+    return out
+
+
+def f16_bits_to_f64(bits) -> np.ndarray:
+    """binary16 bits -> exact value, through the oracle's own decoding."""
+    b = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16).ravel())
+    out = np.empty(b.size, np.float64)
+    _load().orc_f16_to_f64_array(_p(b), b.size, _p(out))
+    return out
+
+
+def quantize_act(x_bits):
+    """Per-token INT8: returns (xq int8 [M,K], s_x uint16 [M], rowsum int32 [M])."""
+    x = _c(x_bits, np.uint16)
+    M, K = x.shape
+    xq = np.empty((M, K), np.int8)
+    s_x = np.empty(M, np.uint16)
+    rowsum = np.empty(M, np.int32)
+    _check(_load().orc_quantize_act(_p(x), M, K, _p(xq), _p(s_x), _p(rowsum)), "quantize_act")
+    return xq, s_x, rowsum
+
+
+def quantize_weights(mode, w_bits, want_w8=False):
+    """Progressive (g128) or per-channel W4 quantization.
+
+    Returns dict with s_c uint16 [N], q uint8 [N,K], z uint8 ([N,G] or [N]),
+    s_g uint8 [N,G] (g128 only) and, when asked, w8 int8 [N,K] (g128 only).
+    """
+    w = _c(w_bits, np.uint16)
+    N, K = w.shape
+    lib = _load()
+    s_c = np.empty(N, np.uint16)
+    q = np.empty((N, K), np.uint8)
+    if mode == MODE_G128:
+        G = K // GROUP
+        s_g = np.empty((N, G), np.uint8)
+        z = np.empty((N, G), np.uint8)
+        w8 = np.empty((N, K), np.int8) if want_w8 else None
+        _check(lib.orc_quantize_weights_g128(_p(w), N, K, _p(s_c), _p(q), _p(s_g), _p(z), _p(w8)),
+               "quantize_weights_g128")
+        out = {"s_c": s_c, "q": q, "s_g": s_g, "z": z}
+        if want_w8:
+            out["w8"] = w8
+        return out
+    if mode == MODE_PER_CHANNEL:
+        z = np.empty(N, np.uint8)
+        _check(lib.orc_quantize_weights_pc(_p(w), N, K, _p(s_c), _p(q), _p(z)),
+               "quantize_weights_pc")
+        return {"s_c": s_c, "q": q, "z": z, "s_g": None}
+    raise ValueError("bad mode")
+
+
+def dequantize_weights(mode, s_c, q, s_g, z):
+    q = _c(q, np.uint8)
+    N, K = q.shape
+    out = np.empty((N, K), np.float64)
+    sg = None if s_g is None else _c(s_g, np.uint8)
+    _check(_load().orc_dequantize_weights(mode, _p(_c(s_c, np.uint16)), _p(q), _p(sg),
+                                          _p(_c(z, np.uint8)), N, K, _p(out)),
+           "dequantize_weights")
+    return out
+
+
+def packed_bytes(mode, N, K) -> int:
+    return int(_load().orc_packed_bytes(mode, N, K))
+
+
+def pack(mode, q, s_g, z):
+    q = _c(q, np.uint8)
+    N, K = q.shape
+    nbytes = packed_bytes(mode, N, K)
+    if nbytes < 0:
+        raise ValueError("shape not packable")
+    blob = np.empty(nbytes, np.uint8)
+    sg = None if s_g is None else _c(s_g, np.uint8)
+    _check(_load().orc_pack(mode, _p(q), _p(sg), _p(_c(z, np.uint8)), N, K, _p(blob)), "pack")
+    return blob
+
+
+def gemm(mode, xq, q, s_g, z):
+    """Exact accumulator acc int32 [M,N]."""
+    xq = _c(xq, np.int8)
+    q = _c(q, np.uint8)
+    M, K = xq.shape
+    N = q.shape[0]
+    acc = np.empty((M, N), np.int32)
+    sg = None if s_g is None else _c(s_g, np.uint8)
+    _check(_load().orc_gemm(mode, _p(xq), _p(q), _p(sg), _p(_c(z, np.uint8)), M, N, K, _p(acc)),
+           "gemm")
+    return acc
+
+
+def gemm_points(mode, xq, q, s_g, z, ms, ns):
+    xq = _c(xq, np.int8)
+    q = _c(q, np.uint8)
+    M, K = xq.shape
+    N = q.shape[0]
+    ms = _c(np.asarray(ms, np.int64), np.int64)
+    ns = _c(np.asarray(ns, np.int64), np.int64)
+    acc = np.empty(len(ms), np.int32)
+    sg = None if s_g is None else _c(s_g, np.uint8)
+    _check(_load().orc_gemm_points(mode, _p(xq), _p(q), _p(sg), _p(_c(z, np.uint8)), M, N, K,
+                                   len(ms), _p(ms), _p(ns), _p(acc)), "gemm_points")
+    return acc
+
+
+def epilogue(acc, s_x, s_c):
+    """Y = acc * s_x * s_c in fp64 (exact), shape [M,N]."""
+    acc = _c(acc, np.int32)
+    M, N = acc.shape
+    y = np.empty((M, N), np.float64)
+    _check(_load().orc_epilogue(_p(acc), _p(_c(s_x, np.uint16)), _p(_c(s_c, np.uint16)), M, N,
+                                _p(y)), "epilogue")
+    return y
+
+
+def epilogue_points(acc, s_x, s_c, ms, ns):
+    acc = _c(acc, np.int32)
+    ms = _c(np.asarray(ms, np.int64), np.int64)
+    ns = _c(np.asarray(ns, np.int64), np.int64)
+    y = np.empty(len(ms), np.float64)
+    _check(_load().orc_epilogue_points(_p(acc), _p(_c(s_x, np.uint16)), _p(_c(s_c, np.uint16)),
+                                       len(ms), _p(ms), _p(ns), _p(y)), "epilogue_points")
+    return y
+
+
+def forward(mode, x_bits, w_bits):
+    """The whole path on the host: quantize both sides, contract, rescale."""
+    xq, s_x, rowsum = quantize_act(x_bits)
+    wq = quantize_weights(mode, w_bits)
+    acc = gemm(mode, xq, wq["q"], wq["s_g"], wq["z"])
+    y = epilogue(acc, s_x, wq["s_c"])
+    return {"xq": xq, "s_x": s_x, "rowsum": rowsum, "acc": acc, "y": y, **wq}

@@ -1,0 +1,451 @@
+/*
+ * qoq_oracle.c -- plain, slow, obviously correct CPU oracle for the QoQ W4A8
+ * GEMM path (QServe, arXiv 2405.04532).
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg load this library. It shares no source, header, table or
+ * helper with the GPU library; the two are written independently from the same
+ * description of the method and of the packed layout.
+ *
+ * Sources (page title, then the part of it that is followed):
+ *   [EN]  "QServe: Low Bit Width Does Not Guarantee High Throughput"
+ *         (English edition of the tabzhangjx.github.io blog post), section 4
+ *         "Formalization and procedure": the stage-1 equation (per-channel INT8
+ *         in the protective range [-119,119] with scale s_c = max|W_c|/119), the
+ *         stage-2 equation (group UINT4 codes q = clip(round(W8/s_cg) + z, 0, 15)
+ *         and reconstruction W^ = s_c * s_cg * (q - z)), and the paragraph after
+ *         it (integer scale, multiply then subtract a precomputed zero-point
+ *         compensation, no FP16 dequantisation in the main loop).
+ *   [ZH]  "QServe：低比特不等于高吞吐" (the same post in Chinese), section 4:
+ *         the same two equations.
+ *   [SUM] "QServe: W4A8KV4 Quantization and System Co-design for Efficient LLM
+ *         Serving" (research.elamur.ai summary), "Key points": per-channel FP16
+ *         scales, protective range [-119,119], then group INT4; multiply first,
+ *         subtract afterward.
+ *   [GUIDE] "QServe Guide: W4A8KV4 Quantization for LLM Serving" (aifetchly),
+ *         "Deep Dive" part 1: per-token symmetric INT8 activations,
+ *         X8 = clamp(round(X / dX), -128, 127) with dX = max|X| / 127, and the
+ *         output rescale Y = (sum_k X8 * W8) * (dX * dW) applied once; "High-
+ *         Throughput Native INT8 Tensor Core GEMMs": INT32 accumulation.
+ *         (That page's signed-INT4 weight format contradicts the other pages
+ *         and is not used.)
+ *   [WIKI] "QoQ / QServe — Quantification W4A8KV4" (brain.gartu.xyz), example
+ *         configuration: weight group size 128.
+ *
+ * Readings where the pages are silent (each is listed with its reason in the
+ * design notes of the repository):
+ *   R1  every "round" is round-half-to-even;
+ *   R2  scales are computed in IEEE fp32 (one rounding per operation), stored as
+ *       FP16 (round to nearest even), and the stored FP16 value is the one used
+ *       to quantize;
+ *   R3  group scale s_cg = max(1, ceil((mx - mn) / 15)), an integer;
+ *   R4  group zero z = round(-mn / s_cg), exact rational rounding;
+ *   R5  the group range always spans zero: mn = min(0, min W8), mx = max(0, max W8);
+ *   R6  a group is 128 consecutive input channels (K) of one output channel;
+ *   R7  per-channel mode: asymmetric UINT4 directly from FP16 with an FP16
+ *       scale s_c = (mx - mn)/15 and a UINT4 zero, the zero-point handled in
+ *       the epilogue;
+ *   R8  a zero scale (all-zero row, or a scale that rounds to 0 in FP16) gives
+ *       codes 0 and zero 0 (or Xq = 0);
+ *   R9  the GEMM accumulator is the exact integer sum; per-channel mode's
+ *       accumulator is sum_k Xq * (q - z);
+ *   R10 the output is acc * s_x * s_c; here it is computed in fp64, where it is
+ *       exact (31 + 11 + 11 significant bits <= 53).
+ *
+ * Inputs must be finite FP16 (passed as raw binary16 bits).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_OK 0
+#define ORC_ERR_SHAPE 1
+#define ORC_ERR_OVERFLOW 2
+#define ORC_ERR_MODE 3
+
+#define ORC_MODE_G128 0
+#define ORC_MODE_PER_CHANNEL 1
+
+#define GROUP 128
+
+/* ------------------------------------------------------------------------ */
+/* IEEE 754 binary16, written out from the format's definition.             */
+/* ------------------------------------------------------------------------ */
+
+/* Exact value of a binary16 bit pattern. */
+double orc_f16_to_f64(uint16_t h) {
+    int sign = h >> 15;
+    int e = (h >> 10) & 31;
+    int m = h & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24); /* subnormal: m * 2^-24 */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + m), e - 25); /* (1 + m/1024) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* Widening to fp32 is exact: every binary16 value is a binary32 value. */
+static float f16_to_f32(uint16_t h) { return (float)orc_f16_to_f64(h); }
+
+/* binary32 -> binary16, round to nearest, ties to even. */
+uint16_t orc_f32_to_f16(float f) {
+    uint16_t sign = signbit(f) ? 0x8000 : 0;
+    if (isnan(f)) return sign | 0x7e00;
+    if (isinf(f)) return sign | 0x7c00;
+    double a = fabs((double)f);
+    if (a < ldexp(1.0, -14)) {
+        /* Subnormal range: the grid spacing is 2^-24. A result of 1024 units is
+         * the smallest normal number, whose encoding is the same integer. */
+        double r = nearbyint(a * ldexp(1.0, 24));
+        return sign | (uint16_t)r;
+    }
+    int e;
+    (void)frexp(a, &e); /* a in [2^(e-1), 2^e) */
+    int E = e - 1;      /* unbiased exponent */
+    double r = nearbyint(ldexp(a, 10 - E)); /* 11-bit significand, RNE */
+    if (r == 2048.0) {
+        r = 1024.0;
+        E += 1;
+    }
+    if (E > 15) return sign | 0x7c00; /* overflow rounds to infinity */
+    return sign | (uint16_t)((E + 15) << 10) | (uint16_t)(r - 1024.0);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Small exact helpers.                                                      */
+/* ------------------------------------------------------------------------ */
+
+/* Round-half-to-even of the rational a / b, b > 0 (reading R1). */
+static int64_t rne_div(int64_t a, int64_t b) {
+    int64_t u = a < 0 ? -a : a;
+    int64_t t = u / b, r = u % b;
+    if (2 * r > b || (2 * r == b && (t & 1))) t += 1;
+    return a < 0 ? -t : t;
+}
+
+static int64_t clamp64(int64_t v, int64_t lo, int64_t hi) {
+    return v < lo ? lo : (v > hi ? hi : v);
+}
+
+/* Round-half-to-even of a finite float, as an integer (reading R1). */
+static int64_t rne_f32(float v) { return (int64_t)rintf(v); }
+
+int orc_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------------ */
+/* Activations: per-token symmetric INT8 ([GUIDE] Deep Dive part 1).         */
+/*   s_x[m]  = f16( max_k |X[m,k]| / 127 )          (fp32 division, R2)       */
+/*   Xq[m,k] = clamp( round(X[m,k] / s_x[m]), -128, 127 )                    */
+/*   rowsum[m] = sum_k Xq[m,k]   (needed by per-channel mode's epilogue)     */
+/* ------------------------------------------------------------------------ */
+int orc_quantize_act(const uint16_t* x, int64_t M, int64_t K, int8_t* xq,
+                     uint16_t* s_x, int32_t* rowsum) {
+    if (M < 0 || K < 1) return ORC_ERR_SHAPE;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t* row = x + m * K;
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float a = fabsf(f16_to_f32(row[k]));
+            if (a > amax) amax = a;
+        }
+        uint16_t s = orc_f32_to_f16(amax / 127.0f);
+        float sf = f16_to_f32(s);
+        int64_t sum = 0;
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t v = 0;
+            if (sf != 0.0f) v = clamp64(rne_f32(f16_to_f32(row[k]) / sf), -128, 127);
+            xq[m * K + k] = (int8_t)v;
+            sum += v;
+        }
+        s_x[m] = s;
+        if (rowsum) rowsum[m] = (int32_t)sum;
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Weights, progressive group quantization ([EN]/[ZH] section 4, [SUM]).     */
+/* Stage 1 (per output channel n):                                           */
+/*   s_c[n]   = f16( max_k |W[n,k]| / 119 )                                  */
+/*   W8[n,k]  = clip( round(W[n,k] / s_c[n]), -119, 119 )                    */
+/* Stage 2 (per group g of 128 consecutive k, R3-R6):                        */
+/*   mn = min(0, min W8), mx = max(0, max W8)                                */
+/*   s_g = max(1, ceil((mx - mn) / 15));  z = round(-mn / s_g)               */
+/*   q   = clip( round(W8 / s_g) + z, 0, 15 )                                */
+/* w8 (optional, may be NULL) receives the stage-1 INT8 values.              */
+/* ------------------------------------------------------------------------ */
+int orc_quantize_weights_g128(const uint16_t* w, int64_t N, int64_t K, uint16_t* s_c,
+                              uint8_t* q, uint8_t* s_g, uint8_t* z, int8_t* w8) {
+    if (N < 0 || K < GROUP || K % GROUP) return ORC_ERR_SHAPE;
+    const int64_t G = K / GROUP;
+#pragma omp parallel
+    {
+        int64_t* row8 = (int64_t*)malloc((size_t)K * sizeof(int64_t));
+#pragma omp for schedule(static)
+        for (int64_t n = 0; n < N; ++n) {
+            const uint16_t* row = w + n * K;
+            float amax = 0.0f;
+            for (int64_t k = 0; k < K; ++k) {
+                float a = fabsf(f16_to_f32(row[k]));
+                if (a > amax) amax = a;
+            }
+            uint16_t sc = orc_f32_to_f16(amax / 119.0f);
+            float scf = f16_to_f32(sc);
+            s_c[n] = sc;
+            for (int64_t k = 0; k < K; ++k) {
+                row8[k] = 0;
+                if (scf != 0.0f) row8[k] = clamp64(rne_f32(f16_to_f32(row[k]) / scf), -119, 119);
+                if (w8) w8[n * K + k] = (int8_t)row8[k];
+            }
+            for (int64_t g = 0; g < G; ++g) {
+                const int64_t* grp = row8 + g * GROUP;
+                int64_t mn = 0, mx = 0;
+                for (int i = 0; i < GROUP; ++i) {
+                    if (grp[i] < mn) mn = grp[i];
+                    if (grp[i] > mx) mx = grp[i];
+                }
+                int64_t sg = (mx - mn + 14) / 15; /* integer ceiling */
+                if (sg < 1) sg = 1;
+                int64_t zz = rne_div(-mn, sg);
+                s_g[n * G + g] = (uint8_t)sg;
+                z[n * G + g] = (uint8_t)zz;
+                for (int i = 0; i < GROUP; ++i)
+                    q[n * K + g * GROUP + i] = (uint8_t)clamp64(rne_div(grp[i], sg) + zz, 0, 15);
+            }
+        }
+        free(row8);
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Weights, per-channel W4 (reading R7).                                     */
+/*   mn = min(0, min_k W), mx = max(0, max_k W)                              */
+/*   s_c = f16( (mx - mn) / 15 );  z = clip( round(-mn / s_c), 0, 15 )       */
+/*   q   = clip( round(W / s_c) + z, 0, 15 )                                 */
+/* ------------------------------------------------------------------------ */
+int orc_quantize_weights_pc(const uint16_t* w, int64_t N, int64_t K, uint16_t* s_c,
+                            uint8_t* q, uint8_t* z) {
+    if (N < 0 || K < 1) return ORC_ERR_SHAPE;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        const uint16_t* row = w + n * K;
+        float mn = 0.0f, mx = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float v = f16_to_f32(row[k]);
+            if (v < mn) mn = v;
+            if (v > mx) mx = v;
+        }
+        uint16_t sc = orc_f32_to_f16((mx - mn) / 15.0f);
+        float scf = f16_to_f32(sc);
+        s_c[n] = sc;
+        int64_t zz = 0;
+        if (scf != 0.0f) zz = clamp64(rne_f32(-mn / scf), 0, 15);
+        z[n] = (uint8_t)zz;
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t v = 0;
+            if (scf != 0.0f) v = clamp64(rne_f32(f16_to_f32(row[k]) / scf) + zz, 0, 15);
+            q[n * K + k] = (uint8_t)v;
+        }
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Reconstruction ([EN] section 4, stage-2 equation): W^ = s_c * s_g * (q - z) */
+/* (per-channel mode: W^ = s_c * (q - z)). Exact in fp64.                    */
+/* ------------------------------------------------------------------------ */
+int orc_dequantize_weights(int mode, const uint16_t* s_c, const uint8_t* q, const uint8_t* s_g,
+                           const uint8_t* z, int64_t N, int64_t K, double* w_hat) {
+    if (mode != ORC_MODE_G128 && mode != ORC_MODE_PER_CHANNEL) return ORC_ERR_MODE;
+    if (mode == ORC_MODE_G128 && (K < GROUP || K % GROUP)) return ORC_ERR_SHAPE;
+    const int64_t G = K / GROUP;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        double sc = orc_f16_to_f64(s_c[n]);
+        for (int64_t k = 0; k < K; ++k) {
+            double v;
+            if (mode == ORC_MODE_G128)
+                v = sc * (double)s_g[n * G + k / GROUP] *
+                    (double)((int)q[n * K + k] - (int)z[n * G + k / GROUP]);
+            else
+                v = sc * (double)((int)q[n * K + k] - (int)z[n]);
+            w_hat[n * K + k] = v;
+        }
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Packed layout (the gfx950 MFMA operand order; the GPU packer implements   */
+/* the same written specification independently).                          */
+/*                                                                          */
+/* Codes: one 1024-byte tile per (t, g), t = n / 16, g = k / 128, at byte    */
+/* offset (t * G + g) * 1024. Within a tile, with c = n % 16 and the offset  */
+/* kk = k % 128 written as kk = 64 s + 16 j + i (s in 0..1, j in 0..3,       */
+/* i in 0..15):                                                              */
+/*   lane  = 16 j + c                (64 lanes x 16 bytes)                   */
+/*   kappa = 16 s + i                (0..31, the lane's code index)          */
+/*   byte  = 16 lane + 4 (kappa / 8) + (kappa % 4)                           */
+/*   nibble: low if (kappa % 8) < 4, else high.                              */
+/* Parameters follow the codes (offset N * K / 2):                           */
+/*   g128: N rows of Gp = roundup(G, 16) bytes; byte g of row n is           */
+/*         ((s_g - 1) << 4) | z, padding bytes are 0;                        */
+/*   per-channel: N bytes, byte n is z[n].                                   */
+/* ------------------------------------------------------------------------ */
+int64_t orc_packed_bytes(int mode, int64_t N, int64_t K) {
+    if (K < GROUP || K % GROUP || N < 16 || N % 16) return -1;
+    int64_t codes = N * K / 2;
+    if (mode == ORC_MODE_G128) {
+        int64_t G = K / GROUP, Gp = (G + 15) / 16 * 16;
+        return codes + N * Gp;
+    }
+    if (mode == ORC_MODE_PER_CHANNEL) return codes + N;
+    return -1;
+}
+
+int orc_pack(int mode, const uint8_t* q, const uint8_t* s_g, const uint8_t* z, int64_t N,
+             int64_t K, uint8_t* blob) {
+    int64_t total = orc_packed_bytes(mode, N, K);
+    if (total < 0) return ORC_ERR_SHAPE;
+    memset(blob, 0, (size_t)total);
+    const int64_t G = K / GROUP;
+    for (int64_t n = 0; n < N; ++n) {
+        int64_t t = n / 16, c = n % 16;
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t g = k / GROUP, kk = k % GROUP;
+            int64_t s = kk / 64, j = (kk % 64) / 16, i = kk % 16;
+            int64_t lane = 16 * j + c;
+            int64_t kappa = 16 * s + i;
+            int64_t off = (t * G + g) * 1024 + 16 * lane + 4 * (kappa / 8) + (kappa % 4);
+            int shift = (kappa % 8) < 4 ? 0 : 4;
+            blob[off] |= (uint8_t)((q[n * K + k] & 15) << shift);
+        }
+    }
+    uint8_t* params = blob + N * K / 2;
+    if (mode == ORC_MODE_G128) {
+        int64_t Gp = (G + 15) / 16 * 16;
+        for (int64_t n = 0; n < N; ++n)
+            for (int64_t g = 0; g < G; ++g)
+                params[n * Gp + g] =
+                    (uint8_t)(((s_g[n * G + g] - 1) << 4) | (z[n * G + g] & 15));
+    } else {
+        for (int64_t n = 0; n < N; ++n) params[n] = z[n];
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* GEMM: INT8 x INT8 with an exact integer accumulator ([GUIDE] "INT32       */
+/* accumulators"; [EN] section 4: the weight operand is the INT8 value       */
+/* W8^ = (q - z) * s_g of the stage-2 equation).                             */
+/*   g128:        acc[m,n] = sum_k Xq[m,k] * (q[n,k] - z[n,g]) * s_g[n,g]     */
+/*   per-channel: acc[m,n] = sum_k Xq[m,k] * (q[n,k] - z[n])                 */
+/* The sum is taken in int64; a value outside int32 is an error.            */
+/* ------------------------------------------------------------------------ */
+static void weight_row_int(int mode, const uint8_t* q, const uint8_t* s_g, const uint8_t* z,
+                           int64_t n, int64_t K, int64_t* out) {
+    const int64_t G = K / GROUP;
+    for (int64_t k = 0; k < K; ++k) {
+        if (mode == ORC_MODE_G128)
+            out[k] = ((int64_t)q[n * K + k] - z[n * G + k / GROUP]) * s_g[n * G + k / GROUP];
+        else
+            out[k] = (int64_t)q[n * K + k] - z[n];
+    }
+}
+
+int orc_gemm(int mode, const int8_t* xq, const uint8_t* q, const uint8_t* s_g, const uint8_t* z,
+             int64_t M, int64_t N, int64_t K, int32_t* acc) {
+    if (mode != ORC_MODE_G128 && mode != ORC_MODE_PER_CHANNEL) return ORC_ERR_MODE;
+    if (M < 0 || N < 0 || K < 1 || (mode == ORC_MODE_G128 && K % GROUP)) return ORC_ERR_SHAPE;
+    int overflow = 0;
+#pragma omp parallel
+    {
+        int64_t* wrow = (int64_t*)malloc((size_t)K * sizeof(int64_t));
+#pragma omp for schedule(static) reduction(| : overflow)
+        for (int64_t n = 0; n < N; ++n) {
+            weight_row_int(mode, q, s_g, z, n, K, wrow);
+            for (int64_t m = 0; m < M; ++m) {
+                const int8_t* xr = xq + m * K;
+                int64_t s = 0;
+                for (int64_t k = 0; k < K; ++k) s += (int64_t)xr[k] * wrow[k];
+                if (s > INT32_MAX || s < INT32_MIN) overflow = 1;
+                acc[m * N + n] = (int32_t)s;
+            }
+        }
+        free(wrow);
+    }
+    return overflow ? ORC_ERR_OVERFLOW : ORC_OK;
+}
+
+/* The same accumulator at P chosen (m, n) points, for shapes too large to
+ * contract whole on the host. */
+int orc_gemm_points(int mode, const int8_t* xq, const uint8_t* q, const uint8_t* s_g,
+                    const uint8_t* z, int64_t M, int64_t N, int64_t K, int64_t P,
+                    const int64_t* ms, const int64_t* ns, int32_t* acc) {
+    if (mode != ORC_MODE_G128 && mode != ORC_MODE_PER_CHANNEL) return ORC_ERR_MODE;
+    if (K < 1 || (mode == ORC_MODE_G128 && K % GROUP)) return ORC_ERR_SHAPE;
+    for (int64_t p = 0; p < P; ++p)
+        if (ms[p] < 0 || ms[p] >= M || ns[p] < 0 || ns[p] >= N) return ORC_ERR_SHAPE;
+    const int64_t G = K / GROUP;
+    int overflow = 0;
+#pragma omp parallel for schedule(static) reduction(| : overflow)
+    for (int64_t p = 0; p < P; ++p) {
+        int64_t m = ms[p], n = ns[p];
+        int64_t s = 0;
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t wv = mode == ORC_MODE_G128
+                             ? ((int64_t)q[n * K + k] - z[n * G + k / GROUP]) * s_g[n * G + k / GROUP]
+                             : (int64_t)q[n * K + k] - z[n];
+            s += (int64_t)xq[m * K + k] * wv;
+        }
+        if (s > INT32_MAX || s < INT32_MIN) overflow = 1;
+        acc[p] = (int32_t)s;
+    }
+    return overflow ? ORC_ERR_OVERFLOW : ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Epilogue ([GUIDE] Deep Dive part 1: the rescale by the activation scale    */
+/* and the weight scale, applied once): Y[m,n] = acc[m,n] * s_x[m] * s_c[n]. */
+/* Computed in fp64, where it is exact (R10); not rounded to FP16.           */
+/* ------------------------------------------------------------------------ */
+int orc_epilogue(const int32_t* acc, const uint16_t* s_x, const uint16_t* s_c, int64_t M,
+                 int64_t N, double* y) {
+    if (M < 0 || N < 0) return ORC_ERR_SHAPE;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            y[m * N + n] = (double)acc[m * N + n] * orc_f16_to_f64(s_x[m]) * orc_f16_to_f64(s_c[n]);
+    return ORC_OK;
+}
+
+int orc_epilogue_points(const int32_t* acc, const uint16_t* s_x, const uint16_t* s_c, int64_t P,
+                        const int64_t* ms, const int64_t* ns, double* y) {
+    for (int64_t p = 0; p < P; ++p)
+        y[p] = (double)acc[p] * orc_f16_to_f64(s_x[ms[p]]) * orc_f16_to_f64(s_c[ns[p]]);
+    return ORC_OK;
+}
+
+/* Array forms of the binary16 conversions, for tests over many values. */
+void orc_f32_to_f16_array(const float* in, int64_t n, uint16_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_f32_to_f16(in[i]);
+}
+
+void orc_f16_to_f64_array(const uint16_t* in, int64_t n, double* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_f16_to_f64(in[i]);
+}

@@ -1,0 +1,161 @@
+"""Pin the oracle to hand-worked examples of the pages' equations.
+
+Each fixture under tests/golden/ holds inputs whose scales are powers of two, so
+that every expected value was derived by hand (the derivations are in the
+fixtures). Several entries sit exactly on rounding ties, which pins
+round-half-to-even; the group examples pin the integer group scale, zero and
+code formulas of the stage-2 equation; the GEMM example pins the contraction
+and the one-time rescale.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _f16_bits(values):
+    return np.asarray(values, dtype=np.float16).view(np.uint16)
+
+
+def _act_inputs():
+    d = _load("act_quant.json")
+    K = d["K"]
+    x = np.zeros((len(d["rows"]), K), np.float16)
+    for r, row in enumerate(d["rows"]):
+        for k, v in row["nonzero"].items():
+            x[r, int(k)] = v
+    return d, x.view(np.uint16)
+
+
+def test_act_quant_golden():
+    d, x = _act_inputs()
+    xq, s_x, rowsum = oracle.quantize_act(x)
+    for r, row in enumerate(d["rows"]):
+        want = np.zeros(d["K"], np.int8)
+        for k, v in row["xq_nonzero"].items():
+            want[int(k)] = v
+        assert s_x[r] == row["s_x_bits"], (r, s_x[r])
+        np.testing.assert_array_equal(xq[r], want)
+        assert rowsum[r] == row["rowsum"]
+
+
+def _g128_inputs():
+    d = _load("weights_g128.json")
+    K = d["K"]
+    rows = []
+    for row in d["rows"]:
+        w8 = np.zeros(K, np.int64)
+        for k, v in row["w8_nonzero"].items():
+            w8[int(k)] = v
+        rows.append(w8.astype(np.float64) * 2.0 ** row["s_c_pow2"])
+    w = np.array(rows).astype(np.float16)
+    # The inputs are exact: w8 * 2^e with |w8| <= 119 fits an FP16 significand.
+    assert np.array_equal(w.astype(np.float64), np.array(rows))
+    return d, w.view(np.uint16)
+
+
+def test_weights_g128_golden():
+    d, w = _g128_inputs()
+    out = oracle.quantize_weights(oracle.MODE_G128, w, want_w8=True)
+    for r, row in enumerate(d["rows"]):
+        assert out["s_c"][r] == row["s_c_bits"]
+        w8 = np.zeros(d["K"], np.int8)
+        for k, v in row["w8_nonzero"].items():
+            w8[int(k)] = v
+        np.testing.assert_array_equal(out["w8"][r], w8)
+        for g, grp in enumerate(row["groups"]):
+            assert out["s_g"][r, g] == grp["s_g"], (r, g)
+            assert out["z"][r, g] == grp["z"], (r, g)
+            for k, v in grp["q_at"].items():
+                assert out["q"][r, int(k)] == v, (r, k)
+
+
+def _pc_inputs():
+    d = _load("weights_per_channel.json")
+    K = d["K"]
+    w = np.zeros((len(d["rows"]), K), np.uint16)
+    for r, row in enumerate(d["rows"]):
+        for k, v in row.get("w_nonzero", {}).items():
+            w[r, int(k)] = _f16_bits([v])[0]
+        for k, v in row.get("w_nonzero_bits", {}).items():
+            w[r, int(k)] = v
+    return d, w
+
+
+def test_weights_per_channel_golden():
+    d, w = _pc_inputs()
+    out = oracle.quantize_weights(oracle.MODE_PER_CHANNEL, w)
+    for r, row in enumerate(d["rows"]):
+        assert out["s_c"][r] == row["s_c_bits"], (r, out["s_c"][r])
+        assert out["z"][r] == row["z"]
+        for k, v in row["q_at"].items():
+            assert out["q"][r, int(k)] == v, (r, k)
+
+
+def _xq_from(nonzero_rows, K):
+    xq = np.zeros((len(nonzero_rows), K), np.int8)
+    for r, row in enumerate(nonzero_rows):
+        for k, v in row.items():
+            xq[r, int(k)] = v
+    return xq
+
+
+def test_gemm_g128_golden():
+    g = _load("gemm.json")["g128"]
+    _, w = _g128_inputs()
+    wq = oracle.quantize_weights(oracle.MODE_G128, w)
+    xq = _xq_from(g["xq_nonzero"], g["K"])
+    acc = oracle.gemm(oracle.MODE_G128, xq, wq["q"], wq["s_g"], wq["z"])
+    np.testing.assert_array_equal(acc, np.array(g["acc"], np.int32))
+    y = oracle.epilogue(acc, np.array(g["s_x_bits"], np.uint16), wq["s_c"])
+    np.testing.assert_array_equal(y, np.array(g["y"]))  # exact: powers of two
+
+
+def test_gemm_per_channel_golden():
+    g = _load("gemm.json")["per_channel"]
+    _, w = _pc_inputs()
+    wq = oracle.quantize_weights(oracle.MODE_PER_CHANNEL, w[:2])
+    xq = _xq_from(g["xq_nonzero"], g["K"])
+    acc = oracle.gemm(oracle.MODE_PER_CHANNEL, xq, wq["q"], None, wq["z"])
+    np.testing.assert_array_equal(acc, np.array(g["acc"], np.int32))
+    assert int(xq.astype(np.int64).sum()) == g["rowsum"][0]
+    y = oracle.epilogue(acc, np.array(g["s_x_bits"], np.uint16), wq["s_c"])
+    np.testing.assert_array_equal(y, np.array(g["y"]))
+
+
+def test_pack_layout_golden():
+    d = _load("pack_layout.json")
+    N, K = d["N"], d["K"]
+    q = np.zeros((N, K), np.uint8)
+    for n, k, v in d["q_nonzero"]:
+        q[n, k] = v
+    s_g = np.ones((N, K // 128), np.uint8)
+    z = np.zeros((N, K // 128), np.uint8)
+    for n, sg, zz in d["s_g_z_nonzero"]:
+        s_g[n, 0] = sg
+        z[n, 0] = zz
+    blob = oracle.pack(oracle.MODE_G128, q, s_g, z)
+    assert blob.size == d["total_bytes"] == oracle.packed_bytes(oracle.MODE_G128, N, K)
+    want = np.zeros(d["total_bytes"], np.uint8)
+    for off, v in d["bytes_nonzero"].items():
+        want[int(off)] = v
+    np.testing.assert_array_equal(blob, want)
+
+
+def test_per_channel_pack_size():
+    # codes N*K/2 plus one zero byte per channel
+    assert oracle.packed_bytes(oracle.MODE_PER_CHANNEL, 32, 256) == 32 * 128 + 32
+    # g128 params padded to 16 groups per row
+    assert oracle.packed_bytes(oracle.MODE_G128, 32, 128 * 17) == 32 * 64 * 17 + 32 * 32
+    assert oracle.packed_bytes(oracle.MODE_G128, 8, 128) == -1  # N must be a multiple of 16
+    assert oracle.packed_bytes(oracle.MODE_G128, 16, 100) == -1  # K must be a multiple of 128

@@ -1,0 +1,328 @@
+"""Pin the oracle to what the pages and the mathematics fix, beyond the
+hand-worked fixtures: exhaustive sweeps, error bounds, brute force on tiny
+inputs, a library contraction, special cases and the end-to-end approximation
+of the real product.
+
+Each check targets a plausible mistake: a wrong rounding mode or FP16 encoding
+(fp16 sweep), a floor instead of a ceiling or a sign error in the group zero
+(exhaustive stage-2 sweep), a dropped clip or a wrong range constant (headroom
+and stage-1 bounds), a transposed operand or a wrong scale (brute force,
+library matmul, end-to-end product).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from quantized_gemm_qoq_amd import workloads
+
+G128 = oracle.MODE_G128
+PC = oracle.MODE_PER_CHANNEL
+
+
+# ---------------------------------------------------------------- fp16 -----
+def test_f32_to_f16_matches_numpy_exhaustive_fp16_grid():
+    """Every binary16 value, every midpoint between neighbours (ties) and the
+    floats just either side of each midpoint round as numpy's RNE cast does."""
+    bits = np.arange(0, 0x7C00, dtype=np.uint32)  # all finite non-negative
+    vals = bits.astype(np.uint16).view(np.float16).astype(np.float32)
+    nxt = (bits + 1).astype(np.uint16).view(np.float16).astype(np.float32)
+    mids = ((vals.astype(np.float64) + nxt.astype(np.float64)) / 2).astype(np.float32)
+    up = np.nextafter(mids, np.float32(np.inf))
+    dn = np.nextafter(mids, np.float32(0))
+    cases = np.concatenate([vals, mids, up, dn])
+    cases = np.concatenate([cases, -cases])
+    with np.errstate(over="ignore"):
+        want = cases.astype(np.float16).view(np.uint16)
+    np.testing.assert_array_equal(oracle.f32_to_f16_bits(cases), want)
+
+
+def test_f32_to_f16_matches_numpy_random_bits():
+    rng = np.random.default_rng(7)
+    b = rng.integers(0, 2**32, size=2_000_000, dtype=np.uint64).astype(np.uint32)
+    f = b.view(np.float32)
+    f = f[np.isfinite(f)]
+    with np.errstate(over="ignore"):
+        want = f.astype(np.float16).view(np.uint16)
+    np.testing.assert_array_equal(oracle.f32_to_f16_bits(f), want)
+
+
+def test_f16_decode_matches_numpy():
+    bits = np.arange(0, 0x10000, dtype=np.uint32).astype(np.uint16)
+    finite = (bits & 0x7C00) != 0x7C00
+    got = oracle.f16_bits_to_f64(bits[finite])
+    np.testing.assert_array_equal(got, bits[finite].view(np.float16).astype(np.float64))
+
+
+# -------------------------------------------------------------- stage 2 ----
+def _stage2_sweep_rows():
+    """Rows whose groups realise every (mn, mx) with -119 <= mn <= 0 <= mx <= 119
+    and every integer w8 in [mn, mx]. Group 0 of each row holds +-119 so that
+    s_c = 2^-8 exactly and stage 1 is the identity on the integers."""
+    groups, meta = [], []
+    for mn in range(-119, 1):
+        for mx in range(0, 120):
+            vals = list(range(mn, mx + 1))
+            # 126 free slots per group besides mn and mx
+            for start in range(0, len(vals), 126):
+                chunk = vals[start:start + 126]
+                grp = np.zeros(128, np.int64)
+                grp[0], grp[1] = mn, mx
+                grp[2:2 + len(chunk)] = chunk
+                grp[2 + len(chunk):] = chunk[-1]
+                groups.append(grp)
+                meta.append((mn, mx))
+    per_row = 32
+    nrows = (len(groups) + per_row - 1) // per_row
+    anchor = np.zeros(128, np.int64)
+    anchor[0], anchor[1] = 119, -119
+    w8 = np.zeros((nrows, 128 * (per_row + 1)), np.int64)
+    for r in range(nrows):
+        w8[r, :128] = anchor
+    for i, grp in enumerate(groups):
+        r, c = divmod(i, per_row)
+        w8[r, 128 * (c + 1):128 * (c + 2)] = grp
+    # rows padded with zero groups: those groups are (0, 0)
+    return w8, meta, per_row
+
+
+def test_stage2_exhaustive_headroom_and_error_bound():
+    w8, meta, per_row = _stage2_sweep_rows()
+    w = (w8.astype(np.float64) * 2.0**-8).astype(np.float16)
+    assert np.array_equal(w.astype(np.float64), w8 * 2.0**-8)
+    out = oracle.quantize_weights(G128, w.view(np.uint16), want_w8=True)
+    assert np.all(out["s_c"] == 0x1C00)  # 2^-8
+    np.testing.assert_array_equal(out["w8"].astype(np.int64), w8)
+
+    q = out["q"].astype(np.int64)
+    s_g = out["s_g"].astype(np.int64)
+    z = out["z"].astype(np.int64)
+    N, K = q.shape
+    G = K // 128
+    sg_full = np.repeat(s_g, 128, axis=1)
+    z_full = np.repeat(z, 128, axis=1)
+    w8hat = (q - z_full) * sg_full
+
+    # Codes and zero in UINT4, integer scale in [1, 16].
+    assert q.min() >= 0 and q.max() <= 15
+    assert z.min() >= 0 and z.max() <= 15
+    assert s_g.min() >= 1 and s_g.max() <= 16
+    # The protective range keeps the unpacked INT8 value inside INT8: the pages'
+    # claim. The tight range is [-121, 121].
+    assert w8hat.min() >= -128 and w8hat.max() <= 127
+    assert w8hat.min() == -121 and w8hat.max() == 121
+    # Stage-2 error: the clip never binds, so every value is within s_g/2.
+    assert np.all(2 * np.abs(w8hat - w8) <= sg_full)
+
+    # The group scale is the smallest integer that covers the range in 15 steps:
+    # 15*s_g >= mx - mn and 15*(s_g - 1) < mx - mn (unless s_g = 1).
+    mn = np.minimum(0, w8.reshape(N, G, 128).min(axis=2))
+    mx = np.maximum(0, w8.reshape(N, G, 128).max(axis=2))
+    rng = mx - mn
+    assert np.all(15 * s_g >= rng)
+    assert np.all((s_g == 1) | (15 * (s_g - 1) < rng))
+    # The zero maps mn onto the code grid: |z*s_g + mn| <= s_g/2.
+    assert np.all(2 * np.abs(z * s_g + mn) <= s_g)
+
+    # Every (mn, mx) pair was realised.
+    seen = set(zip(mn[:, 1:].ravel().tolist(), mx[:, 1:].ravel().tolist()))
+    assert set(meta) <= seen
+
+
+def test_headroom_119_is_tight():
+    """With a protective range of 120 instead of 119 the same stage-2 formulas
+    overflow INT8: mn = -119, mx = 120, w8 = 120 gives s_g = 16, z = 7,
+    q = round(7.5) + 7 = 15 and (q - z) * s_g = 128 (pure arithmetic of the
+    stage-2 equation, independent of the oracle)."""
+    mn, mx, w = -119, 120, 120
+    sg = -(-(mx - mn) // 15)
+    z = round(-mn / sg)
+    qv = min(15, max(0, round(w / sg) + z))
+    assert (sg, z, qv) == (16, 7, 15)
+    assert (qv - z) * sg == 128
+
+
+# -------------------------------------------------------------- stage 1 ----
+@pytest.mark.parametrize("seed", [1, 2])
+def test_stage1_bounds_random(seed):
+    w = workloads.random_fp16((64, 1024), seed, 0.02)
+    w[3, 5] = 0.0
+    w[7] = 0.0  # an all-zero row
+    w[9, :] = 0.25  # a constant row
+    wb = w.numpy().view(np.uint16)
+    out = oracle.quantize_weights(G128, wb, want_w8=True)
+    wf = w.numpy().astype(np.float64)
+    s_c = oracle.f16_bits_to_f64(out["s_c"])
+    amax = np.abs(wf).max(axis=1)
+    # s_c is max|W|/119 rounded to FP16: within half an FP16 ulp (2^-11 relative).
+    nz = amax > 0
+    assert np.all(np.abs(s_c[nz] - amax[nz] / 119) <= (amax[nz] / 119) * 2.0**-11)
+    assert s_c[7] == 0 and np.all(out["q"][7] == 0) and np.all(out["z"][7] == 0)
+    w8 = out["w8"].astype(np.float64)
+    assert np.abs(w8).max() <= 119
+    ratio = wf[nz] / s_c[nz, None]
+    # Round to nearest: within 1/2 (plus the fp32 division's rounding), no clip binds.
+    assert np.all(np.abs(w8[nz] - ratio) <= 0.5 + 1e-4)
+    # The largest magnitude of each row maps to +-119.
+    arg = np.abs(wf).argmax(axis=1)
+    assert np.all(np.abs(w8[np.arange(64)[nz], arg[nz]]) == 119)
+    # A constant row: every element is the row max.
+    assert np.all(w8[9] == 119)
+
+
+def test_reconstruction_bound_g128_and_per_channel():
+    x16 = workloads.random_fp16((48, 1024), 11, 0.02)
+    x16[5, 100] = 0.9  # an outlier in one row
+    wb = x16.numpy().view(np.uint16)
+    wf = x16.numpy().astype(np.float64)
+    out = oracle.quantize_weights(G128, wb)
+    what = oracle.dequantize_weights(G128, out["s_c"], out["q"], out["s_g"], out["z"])
+    s_c = oracle.f16_bits_to_f64(out["s_c"])[:, None]
+    sg = np.repeat(out["s_g"].astype(np.float64), 128, axis=1)
+    # |W^ - W| <= s_c * (1/2 + s_g/2): stage-1 rounding plus stage-2 rounding.
+    assert np.all(np.abs(what - wf) <= s_c * (0.5 + 1e-4 + sg / 2))
+    rel_g = np.linalg.norm(what - wf) / np.linalg.norm(wf)
+
+    pc = oracle.quantize_weights(PC, wb)
+    what_pc = oracle.dequantize_weights(PC, pc["s_c"], pc["q"], None, pc["z"])
+    s_pc = oracle.f16_bits_to_f64(pc["s_c"])[:, None]
+    assert np.all(np.abs(what_pc - wf) <= s_pc * 0.51)
+    rel_pc = np.linalg.norm(what_pc - wf) / np.linalg.norm(wf)
+    # Group quantization is finer than one range per row.
+    assert rel_g < rel_pc < 0.5
+
+
+# ----------------------------------------------------------- activations ---
+def test_act_quant_bounds_random():
+    x = workloads.random_fp16((40, 2048), 5, 1.0)
+    x[0] = 0.0
+    x[1, 7] = -30.0
+    x[2, :] = -1.5
+    xb = x.numpy().view(np.uint16)
+    xq, s_x, rowsum = oracle.quantize_act(xb)
+    xf = x.numpy().astype(np.float64)
+    s = oracle.f16_bits_to_f64(s_x)
+    assert s[0] == 0 and np.all(xq[0] == 0) and rowsum[0] == 0
+    nz = s > 0
+    err = np.abs(xq[nz].astype(np.float64) * s[nz, None] - xf[nz])
+    assert np.all(err <= s[nz, None] * (0.5 + 1e-4))
+    assert np.abs(xq.astype(np.int64)).max() <= 127
+    arg = np.abs(xf).argmax(axis=1)
+    assert np.all(np.abs(xq[np.arange(40)[nz], arg[nz]]) == 127)
+    assert xq[1, 7] == -127
+    assert np.all(xq[2] == -127)
+    np.testing.assert_array_equal(rowsum, xq.astype(np.int64).sum(axis=1))
+
+
+def test_act_scale_underflow_gives_zero_codes():
+    # max|X| = 2^-24 (the smallest FP16 subnormal): max/127 rounds to 0 in FP16.
+    x = np.zeros((1, 128), np.uint16)
+    x[0, 3] = 0x0001
+    xq, s_x, rowsum = oracle.quantize_act(x)
+    assert s_x[0] == 0 and np.all(xq == 0) and rowsum[0] == 0
+
+
+# ------------------------------------------------------------------ GEMM ---
+def _brute(mode, xq, q, s_g, z):
+    M, K = xq.shape
+    N = q.shape[0]
+    acc = np.zeros((M, N), np.int64)
+    for m in range(M):
+        for n in range(N):
+            s = 0
+            for k in range(K):
+                if mode == G128:
+                    wv = (int(q[n, k]) - int(z[n, k // 128])) * int(s_g[n, k // 128])
+                else:
+                    wv = int(q[n, k]) - int(z[n])
+                s += int(xq[m, k]) * wv
+            acc[m, n] = s
+    return acc
+
+
+@pytest.mark.parametrize("mode", [G128, PC])
+@pytest.mark.parametrize("shape", [(1, 128, 3), (5, 256, 7), (16, 512, 16)])
+def test_gemm_brute_force_tiny(mode, shape):
+    M, K, N = shape
+    x = workloads.random_fp16((M, K), 100 + K, 1.0).numpy().view(np.uint16)
+    w = workloads.random_fp16((N, K), 200 + K, 0.02).numpy().view(np.uint16)
+    xq, s_x, rowsum = oracle.quantize_act(x)
+    wq = oracle.quantize_weights(mode, w)
+    acc = oracle.gemm(mode, xq, wq["q"], wq["s_g"], wq["z"])
+    np.testing.assert_array_equal(acc, _brute(mode, xq, wq["q"], wq["s_g"], wq["z"]))
+    ms = np.repeat(np.arange(M), N)
+    ns = np.tile(np.arange(N), M)
+    pts = oracle.gemm_points(mode, xq, wq["q"], wq["s_g"], wq["z"], ms, ns)
+    np.testing.assert_array_equal(pts, acc.ravel())
+
+
+@pytest.mark.parametrize("mode", [G128, PC])
+def test_gemm_matches_library_matmul(mode):
+    M, K, N = 37, 1024, 96
+    x = workloads.random_fp16((M, K), 31, 1.0).numpy().view(np.uint16)
+    w = workloads.random_fp16((N, K), 32, 0.02).numpy().view(np.uint16)
+    xq, s_x, rowsum = oracle.quantize_act(x)
+    wq = oracle.quantize_weights(mode, w)
+    q = wq["q"].astype(np.int64)
+    if mode == G128:
+        w8 = (q - np.repeat(wq["z"], 128, 1)) * np.repeat(wq["s_g"], 128, 1)
+    else:
+        w8 = q - wq["z"].astype(np.int64)[:, None]
+    want = np.matmul(xq.astype(np.int64), w8.T)
+    acc = oracle.gemm(mode, xq, wq["q"], wq["s_g"], wq["z"])
+    np.testing.assert_array_equal(acc, want)
+    if mode == PC:
+        # The epilogue form the GPU uses: sum xq*q - z*rowsum.
+        factored = np.matmul(xq.astype(np.int64), q.T) - np.outer(rowsum, wq["z"].astype(np.int64))
+        np.testing.assert_array_equal(acc, factored)
+
+
+def test_gemm_int32_range_at_max_k():
+    """At K = 132096 the largest reachable products stay inside INT32, and the
+    oracle refuses a sum that would not (|xq| = 128 with |W8^| = 128 is outside
+    what the quantizers emit)."""
+    K = 132096
+    xq = np.full((1, K), -127, np.int8)
+    q = np.zeros((16, K), np.uint8)
+    s_g = np.full((16, K // 128), 11, np.uint8)
+    z = np.full((16, K // 128), 11, np.uint8)  # (0 - 11) * 11 = -121, the tight extreme
+    acc = oracle.gemm(G128, xq, q, s_g, z)
+    assert np.all(acc == K * 127 * 121)
+    xq[:] = -128
+    s_g[:] = 16
+    z[:] = 8  # (0 - 8) * 16 = -128: K * 128 * 128 > 2^31 - 1
+    with pytest.raises(RuntimeError):
+        oracle.gemm(G128, xq, q, s_g, z)
+
+
+def test_epilogue_is_exact_product():
+    acc = np.array([[2**30 + 1, -(2**30) - 3]], np.int32)
+    s_x = np.array([0x3BFF], np.uint16)  # 1 - 2^-11
+    s_c = np.array([0x3BFF, 0x0001], np.uint16)
+    y = oracle.epilogue(acc, s_x, s_c)
+    a = 1 - 2.0**-11
+    assert y[0, 0] == (2**30 + 1) * a * a  # exactly representable in fp64
+    assert y[0, 1] == -(2**30 + 3) * a * 2.0**-24
+
+
+@pytest.mark.parametrize("mode", [G128, PC])
+def test_end_to_end_approximates_real_product(mode):
+    """Y approximates X W^T: a transposed operand, a missing scale or a wrong
+    sign would not."""
+    layer = workloads.WORKLOADS["tiny"].layers[0]
+    x16, w16 = workloads.generate(layer)
+    res = oracle.forward(mode, x16.numpy().view(np.uint16), w16.numpy().view(np.uint16))
+    ref = x16.numpy().astype(np.float64) @ w16.numpy().astype(np.float64).T
+    rel = np.linalg.norm(res["y"] - ref) / np.linalg.norm(ref)
+    assert rel < 0.15, rel
+    cos = (res["y"] * ref).sum() / np.linalg.norm(res["y"]) / np.linalg.norm(ref)
+    assert cos > 0.99
+
+
+def test_zero_inputs_give_zero_output():
+    x = np.zeros((3, 256), np.uint16)
+    w = workloads.random_fp16((16, 256), 3, 0.02).numpy().view(np.uint16)
+    for mode in (G128, PC):
+        res = oracle.forward(mode, x, w)
+        assert np.all(res["y"] == 0) and np.all(res["acc"] == 0)
+        res = oracle.forward(mode, w[:2], np.zeros((16, 256), np.uint16))
+        assert np.all(res["y"] == 0)
