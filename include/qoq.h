@@ -73,7 +73,8 @@ typedef enum {
     QOQ_ERR_SHAPE = 2,  /* M, N or K outside the limits above */
     QOQ_ERR_ALIGN = 3,  /* a pointer is not 16-byte aligned */
     QOQ_ERR_MODE = 4,   /* mode is neither QOQ_MODE_G128 nor QOQ_MODE_PER_CHANNEL */
-    QOQ_ERR_HIP = 5     /* the HIP runtime reported an error at launch */
+    QOQ_ERR_HIP = 5,    /* the HIP runtime reported an error at launch */
+    QOQ_ERR_WORKSPACE = 6 /* workspace given but smaller than qoq_gemm_workspace_bytes() */
 } qoq_status;
 
 /* QOQ_ABI_VERSION of the loaded library. */
@@ -149,29 +150,56 @@ qoq_status qoq_unpack_weights(int mode, const void* blob, int64_t N, int64_t K,
  *
  *   x      [M,K] FP16 row-major.
  *   s_x[m] = f16(max_k |x[m,k]| / 127)                   (FP16, [M])
- *   xq     = clamp(round(x / s_x), -128, 127)            (int8, [M,K])
+ *   xq     = clamp(round(x / s_x), -128, 127)            (int8, packed, below)
  *   rowsum[m] = sum_k xq[m,k]  (int32, [M]; may be NULL; required later by the
  *             per-channel GEMM's zero-point compensation)
  *   A scale of 0 gives xq = 0 for that row.
+ *
+ * xq is written in the order the gfx950 INT8 MFMA consumes its A operand, so
+ * that every operand load of the GEMM is one coalesced 1 KB read (the same
+ * idea as the offline weight reorder, applied to the per-call activations).
+ * qoq_act_bytes(M, K) bytes, Mp = roundup(M, 16) rows (rows M..Mp-1 are 0):
+ *   tile (g, u) = rows 16u..16u+15, inputs 128g..128g+127, 2048 bytes at
+ *   offset (g * Mp/16 + u) * 2048; with k % 128 = 64*s + 16*j + i and
+ *   r = m % 16, the byte of (m, k) is at 1024*s + 16*(16*j + r) + i.
  */
+int64_t qoq_act_bytes(int64_t M, int64_t K);
+
 qoq_status qoq_quantize_act(const uint16_t* x, int64_t M, int64_t K, int8_t* xq,
                             uint16_t* s_x, int32_t* rowsum, void* stream);
+
+/*
+ * Workspace bytes that qoq_w4a8_gemm can use for this shape (0 if its plan
+ * needs none), or -1 for an unsupported shape or mode. With the workspace,
+ * decode-sized M may split K across workgroups (partial INT32 sums, added
+ * exactly); without it, the library picks a plan that needs none.
+ */
+int64_t qoq_gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K);
 
 /*
  * W4A8 GEMM with the FP16 epilogue ([EN] section 4 and pseudocode step 6;
  * [GUIDE] "INT32 accumulators" and the one-time rescale).
  *
- *   xq [M,K] int8, s_x [M] FP16, rowsum [M] int32 (required in per-channel
- *   mode, ignored in g128 mode), blob from qoq_pack_weights, s_c [N] FP16.
+ *   xq packed INT8 activations from qoq_quantize_act, s_x [M] FP16, rowsum
+ *   [M] int32 (required in per-channel mode, ignored in g128 mode), blob from
+ *   qoq_pack_weights, s_c [N] FP16.
  *   acc[m,n] = sum_k xq[m,k] * (q[n,k] - z) * s_g     (g128; exact INT32)
  *            = sum_k xq[m,k] * (q[n,k] - z[n])        (per-channel; computed as
  *              sum_k xq*q - z[n]*rowsum[m], exact)
  *   y[m,n]   = f16( (f32(acc) * f32(s_x[m])) * f32(s_c[n]) )  (FP16 [M,N])
- *   acc_out  [M,N] int32 receives acc when not NULL (slower; for inspection).
+ *   acc_out  [M,N] int32 receives acc when not NULL (for inspection).
+ *
+ *   workspace: NULL, or device memory of workspace_bytes >=
+ *   qoq_gemm_workspace_bytes(mode, M, N, K) that was zero-filled before its
+ *   first use. The library leaves it ready for the next call (its counters back
+ *   at zero), so one zero-fill at allocation suffices. Calls that overlap in
+ *   time (e.g. on different streams) must not share a workspace. A workspace
+ *   that is too small gives QOQ_ERR_WORKSPACE.
  */
 qoq_status qoq_w4a8_gemm(int mode, const int8_t* xq, const uint16_t* s_x, const int32_t* rowsum,
                          const void* blob, const uint16_t* s_c, int64_t M, int64_t N, int64_t K,
-                         uint16_t* y, int32_t* acc_out, void* stream);
+                         uint16_t* y, int32_t* acc_out, void* workspace, int64_t workspace_bytes,
+                         void* stream);
 
 #ifdef __cplusplus
 }

@@ -65,6 +65,8 @@ def _load():
                 "orc_epilogue": (I, [P, P, P, I64, I64, P]),
                 "orc_epilogue_points": (I, [P, P, P, I64, P, P, P]),
                 "orc_f32_to_f16_array": (None, [P, I64, P]),
+                "orc_act_bytes": (I64, [I64, I64]),
+                "orc_pack_act": (I, [P, I64, I64, P]),
                 "orc_f16_to_f64_array": (None, [P, I64, P]),
             }
             for name, (res, args) in sigs.items():
@@ -120,6 +122,22 @@ def quantize_act(x_bits):
     rowsum = np.empty(M, np.int32)
     _check(_load().orc_quantize_act(_p(x), M, K, _p(xq), _p(s_x), _p(rowsum)), "quantize_act")
     return xq, s_x, rowsum
+
+
+def act_bytes(M, K) -> int:
+    return int(_load().orc_act_bytes(M, K))
+
+
+def pack_act(xq):
+    """Row-major INT8 activations [M,K] -> the packed tile order (flat int8)."""
+    xq = _c(xq, np.int8)
+    M, K = xq.shape
+    n = act_bytes(M, K)
+    if n < 0:
+        raise ValueError("shape not packable")
+    out = np.empty(n, np.int8)
+    _check(_load().orc_pack_act(_p(xq), M, K, _p(out)), "pack_act")
+    return out
 
 
 def quantize_weights(mode, w_bits, want_w8=False):

@@ -350,6 +350,35 @@ int orc_pack(int mode, const uint8_t* q, const uint8_t* s_g, const uint8_t* z, i
 }
 
 /* ------------------------------------------------------------------------ */
+/* Packed activations (the GPU quantizer's output order; written here from    */
+/* the same written specification, independently of the GPU code).          */
+/* Mp = roundup(M, 16) rows; rows M..Mp-1 are zero. Tile (g, u) = rows        */
+/* 16u..16u+15, inputs 128g..128g+127, 2048 bytes at (g * Mp/16 + u) * 2048. */
+/* With k % 128 = 64 s + 16 j + i and r = m % 16, the byte of (m, k) is at    */
+/* 1024 s + 16 (16 j + r) + i within the tile.                               */
+/* ------------------------------------------------------------------------ */
+int64_t orc_act_bytes(int64_t M, int64_t K) {
+    if (M < 0 || K < GROUP || K % GROUP) return -1;
+    return (M + 15) / 16 * 16 * K;
+}
+
+int orc_pack_act(const int8_t* xq, int64_t M, int64_t K, int8_t* out) {
+    int64_t total = orc_act_bytes(M, K);
+    if (total < 0) return ORC_ERR_SHAPE;
+    memset(out, 0, (size_t)total);
+    const int64_t U = (M + 15) / 16;
+    for (int64_t m = 0; m < M; ++m) {
+        const int64_t u = m / 16, r = m % 16;
+        for (int64_t k = 0; k < K; ++k) {
+            const int64_t g = k / GROUP, kk = k % GROUP;
+            const int64_t s = kk / 64, j = (kk % 64) / 16, i = kk % 16;
+            out[(g * U + u) * 2048 + 1024 * s + 16 * (16 * j + r) + i] = xq[m * K + k];
+        }
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* GEMM: INT8 x INT8 with an exact integer accumulator ([GUIDE] "INT32       */
 /* accumulators"; [EN] section 4: the weight operand is the INT8 value       */
 /* W8^ = (q - z) * s_g of the stage-2 equation).                             */

@@ -1,0 +1,304 @@
+"""QoQ W4A8 GEMM for AMD Instinct MI355X (gfx950).
+
+Python binding of ``libqoq.so`` (the C ABI declared in ``include/qoq.h``). The
+functions carry the C names and do argument marshalling only: every step of
+the path runs in the library's HIP kernels. PyTorch provides the device memory
+(tensors, whose ``data_ptr`` is passed) and the stream (the current stream of
+the tensors' device). There is no fallback: if the library cannot be loaded,
+or a call fails, a ``QoQError`` is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Tuple
+
+import torch
+
+MODE_G128 = 0
+MODE_PER_CHANNEL = 1
+GROUP = 128
+MAX_K = 132096
+MODES = {"g128": MODE_G128, "per_channel": MODE_PER_CHANNEL}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqoq.so")
+
+# Every entry point that include/qoq.h declares.
+EXPORTED = (
+    "qoq_abi_version",
+    "qoq_status_str",
+    "qoq_quantize_weights",
+    "qoq_packed_bytes",
+    "qoq_pack_weights",
+    "qoq_unpack_weights",
+    "qoq_act_bytes",
+    "qoq_quantize_act",
+    "qoq_gemm_workspace_bytes",
+    "qoq_w4a8_gemm",
+)
+
+
+class QoQError(RuntimeError):
+    pass
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load_library():
+    """Load libqoq.so (building it first if it has never been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            from . import build
+
+            build.build()
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+        sigs = {
+            "qoq_abi_version": (I, []),
+            "qoq_status_str": (ctypes.c_char_p, [I]),
+            "qoq_quantize_weights": (I, [I, P, I64, I64, P, P, P, P, P]),
+            "qoq_packed_bytes": (I64, [I, I64, I64]),
+            "qoq_pack_weights": (I, [I, P, P, P, I64, I64, P, P]),
+            "qoq_unpack_weights": (I, [I, P, I64, I64, P, P, P, P]),
+            "qoq_act_bytes": (I64, [I64, I64]),
+            "qoq_quantize_act": (I, [P, I64, I64, P, P, P, P]),
+            "qoq_gemm_workspace_bytes": (I64, [I, I64, I64, I64]),
+            "qoq_w4a8_gemm": (I, [I, P, P, P, P, P, I64, I64, I64, P, P, P, I64, P]),
+        }
+        for name, (res, args) in sigs.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+        return lib
+
+
+def _mode(mode) -> int:
+    if isinstance(mode, str):
+        return MODES[mode]
+    return int(mode)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t: torch.Tensor, dtype, name: str, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise QoQError(f"{name} must live in GPU memory (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise QoQError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise QoQError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _check(status: int, name: str):
+    if status != 0:
+        msg = load_library().qoq_status_str(status).decode()
+        raise QoQError(f"{name}: {msg} (status {status})")
+
+
+def qoq_abi_version() -> int:
+    return int(load_library().qoq_abi_version())
+
+
+def qoq_status_str(status: int) -> str:
+    return load_library().qoq_status_str(int(status)).decode()
+
+
+def qoq_packed_bytes(mode, N: int, K: int) -> int:
+    return int(load_library().qoq_packed_bytes(_mode(mode), int(N), int(K)))
+
+
+def qoq_quantize_weights(mode, w: torch.Tensor, q=None, s_c=None, s_g=None, z=None):
+    """W [N,K] fp16 -> (q uint8 [N,K], s_c fp16 [N], s_g uint8 [N,K/128] | None, z uint8)."""
+    mode = _mode(mode)
+    _need(w, torch.float16, "w")
+    N, K = w.shape
+    dev = w.device
+    q = q if q is not None else torch.empty((N, K), dtype=torch.uint8, device=dev)
+    s_c = s_c if s_c is not None else torch.empty((N,), dtype=torch.float16, device=dev)
+    if mode == MODE_G128:
+        G = K // GROUP
+        s_g = s_g if s_g is not None else torch.empty((N, G), dtype=torch.uint8, device=dev)
+        z = z if z is not None else torch.empty((N, G), dtype=torch.uint8, device=dev)
+        _need(s_g, torch.uint8, "s_g", (N, G))
+        _need(z, torch.uint8, "z", (N, G))
+    else:
+        s_g = None
+        z = z if z is not None else torch.empty((N,), dtype=torch.uint8, device=dev)
+        _need(z, torch.uint8, "z", (N,))
+    _need(q, torch.uint8, "q", (N, K))
+    _need(s_c, torch.float16, "s_c", (N,))
+    st = load_library().qoq_quantize_weights(mode, _ptr(w), N, K, _ptr(q), _ptr(s_c), _ptr(s_g),
+                                             _ptr(z), _stream(w))
+    _check(st, "qoq_quantize_weights")
+    return q, s_c, s_g, z
+
+
+def qoq_pack_weights(mode, q: torch.Tensor, s_g: Optional[torch.Tensor], z: torch.Tensor,
+                     blob: Optional[torch.Tensor] = None) -> torch.Tensor:
+    mode = _mode(mode)
+    _need(q, torch.uint8, "q")
+    N, K = q.shape
+    nbytes = qoq_packed_bytes(mode, N, K)
+    if nbytes < 0:
+        raise QoQError(f"qoq_pack_weights: unsupported shape N={N} K={K}")
+    blob = blob if blob is not None else torch.empty((nbytes,), dtype=torch.uint8, device=q.device)
+    _need(blob, torch.uint8, "blob", (nbytes,))
+    _need(z, torch.uint8, "z")
+    if s_g is not None:
+        _need(s_g, torch.uint8, "s_g")
+    st = load_library().qoq_pack_weights(mode, _ptr(q), _ptr(s_g), _ptr(z), N, K, _ptr(blob),
+                                         _stream(q))
+    _check(st, "qoq_pack_weights")
+    return blob
+
+
+def qoq_unpack_weights(mode, blob: torch.Tensor, N: int, K: int):
+    mode = _mode(mode)
+    _need(blob, torch.uint8, "blob")
+    dev = blob.device
+    q = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    if mode == MODE_G128:
+        s_g = torch.empty((N, K // GROUP), dtype=torch.uint8, device=dev)
+        z = torch.empty((N, K // GROUP), dtype=torch.uint8, device=dev)
+    else:
+        s_g = None
+        z = torch.empty((N,), dtype=torch.uint8, device=dev)
+    st = load_library().qoq_unpack_weights(mode, _ptr(blob), N, K, _ptr(q), _ptr(s_g), _ptr(z),
+                                           _stream(blob))
+    _check(st, "qoq_unpack_weights")
+    return q, s_g, z
+
+
+def qoq_act_bytes(M: int, K: int) -> int:
+    return int(load_library().qoq_act_bytes(int(M), int(K)))
+
+
+def qoq_quantize_act(x: torch.Tensor, xq=None, s_x=None, rowsum=None, want_rowsum: bool = True):
+    """X [M,K] fp16 -> (xq, s_x fp16 [M], rowsum int32 [M] | None).
+
+    xq is a flat int8 tensor of qoq_act_bytes(M, K) bytes in the packed tile
+    order the GEMM reads (the layout is written out in include/qoq.h)."""
+    _need(x, torch.float16, "x")
+    M, K = x.shape
+    dev = x.device
+    nbytes = qoq_act_bytes(M, K)
+    if nbytes < 0:
+        raise QoQError(f"qoq_quantize_act: unsupported shape M={M} K={K}")
+    xq = xq if xq is not None else torch.empty((nbytes,), dtype=torch.int8, device=dev)
+    s_x = s_x if s_x is not None else torch.empty((M,), dtype=torch.float16, device=dev)
+    if rowsum is None and want_rowsum:
+        rowsum = torch.empty((M,), dtype=torch.int32, device=dev)
+    _need(xq, torch.int8, "xq", (nbytes,))
+    _need(s_x, torch.float16, "s_x", (M,))
+    if rowsum is not None:
+        _need(rowsum, torch.int32, "rowsum", (M,))
+    st = load_library().qoq_quantize_act(_ptr(x), M, K, _ptr(xq), _ptr(s_x), _ptr(rowsum),
+                                         _stream(x))
+    _check(st, "qoq_quantize_act")
+    return xq, s_x, rowsum
+
+
+def qoq_gemm_workspace_bytes(mode, M: int, N: int, K: int) -> int:
+    return int(load_library().qoq_gemm_workspace_bytes(_mode(mode), int(M), int(N), int(K)))
+
+
+_workspaces = {}
+
+
+def gemm_workspace(mode, M: int, N: int, K: int, device) -> Optional[torch.Tensor]:
+    """A zero-filled workspace for this device, grown when a shape needs more.
+
+    One workspace per device is shared by every call that does not bring its
+    own, so calls issued concurrently on different streams must pass their own
+    (the library re-arms the workspace at the end of each call)."""
+    need = qoq_gemm_workspace_bytes(mode, M, N, K)
+    if need <= 0:
+        return None
+    dev = torch.device(device)
+    key = (dev.type, dev.index if dev.index is not None else torch.cuda.current_device())
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.zeros((max(need, 1 << 20),), dtype=torch.uint8, device=dev)
+        _workspaces[key] = ws
+    return ws
+
+
+def qoq_w4a8_gemm(mode, xq: torch.Tensor, s_x: torch.Tensor, rowsum: Optional[torch.Tensor],
+                  blob: torch.Tensor, s_c: torch.Tensor, N: int, y=None, acc_out=None,
+                  workspace="auto", K: Optional[int] = None):
+    """Y [M,N] fp16 = rescale(sum_k xq * unpack(blob)); acc_out (int32 [M,N]) optional.
+
+    xq: packed activations from qoq_quantize_act (M is the length of s_x).
+    workspace: "auto" (the device's shared workspace), None (a plan that needs
+    none) or a zero-initialised uint8 tensor of qoq_gemm_workspace_bytes()."""
+    mode = _mode(mode)
+    _need(xq, torch.int8, "xq")
+    _need(s_x, torch.float16, "s_x")
+    M = s_x.numel()
+    dev = xq.device
+    mp = (M + 15) // 16 * 16
+    if K is None:
+        if mp == 0:
+            raise QoQError("qoq_w4a8_gemm: K must be given when M == 0")
+        K = xq.numel() // mp
+    if xq.numel() != mp * K:
+        raise QoQError(f"xq has {xq.numel()} bytes, expected {mp} x {K}")
+    _need(s_c, torch.float16, "s_c", (N,))
+    _need(blob, torch.uint8, "blob")
+    if rowsum is not None:
+        _need(rowsum, torch.int32, "rowsum", (M,))
+    y = y if y is not None else torch.empty((M, N), dtype=torch.float16, device=dev)
+    _need(y, torch.float16, "y", (M, N))
+    if acc_out is not None:
+        _need(acc_out, torch.int32, "acc_out", (M, N))
+    nbytes = qoq_packed_bytes(mode, N, K)
+    if M and N and blob.numel() != nbytes:
+        raise QoQError(f"blob has {blob.numel()} bytes, expected {nbytes}")
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a tensor")
+        workspace = gemm_workspace(mode, M, N, K, dev) if M and N else None
+    ws_bytes = 0
+    if workspace is not None:
+        _need(workspace, torch.uint8, "workspace")
+        ws_bytes = workspace.numel()
+    st = load_library().qoq_w4a8_gemm(mode, _ptr(xq), _ptr(s_x), _ptr(rowsum), _ptr(blob),
+                                      _ptr(s_c), M, N, K, _ptr(y), _ptr(acc_out), _ptr(workspace),
+                                      ws_bytes, _stream(xq))
+    _check(st, "qoq_w4a8_gemm")
+    return y
+
+
+class PackedWeight:
+    """A weight matrix quantized and packed once (offline), kept resident."""
+
+    def __init__(self, mode, w: torch.Tensor):
+        self.mode = _mode(mode)
+        self.N, self.K = w.shape
+        q, self.s_c, s_g, z = qoq_quantize_weights(self.mode, w)
+        self.blob = qoq_pack_weights(self.mode, q, s_g, z)
+
+    def forward(self, x: torch.Tensor, y=None) -> torch.Tensor:
+        """Per-call path: per-token INT8 quantization of x, then the W4A8 GEMM."""
+        xq, s_x, rowsum = qoq_quantize_act(x, want_rowsum=self.mode == MODE_PER_CHANNEL)
+        return qoq_w4a8_gemm(self.mode, xq, s_x, rowsum, self.blob, self.s_c, self.N, y=y,
+                             K=self.K)

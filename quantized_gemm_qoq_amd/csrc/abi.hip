@@ -1,0 +1,142 @@
+// abi.hip -- the C ABI of libqoq (declared and documented in include/qoq.h):
+// argument validation, then one enqueue on the caller's stream.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qoq.h"
+#include "qoq_launch.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_mode(int mode) { return mode == QOQ_MODE_G128 || mode == QOQ_MODE_PER_CHANNEL; }
+
+bool valid_k(int64_t K) { return K >= QOQ_GROUP && K <= QOQ_MAX_K && K % QOQ_GROUP == 0; }
+
+// Clears any stale runtime error, runs the enqueue, then reports whether the
+// launches were accepted.
+template <typename F>
+qoq_status launch_checked(F&& f) {
+    (void)hipGetLastError();
+    f();
+    return hipGetLastError() == hipSuccess ? QOQ_OK : QOQ_ERR_HIP;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int qoq_abi_version(void) { return QOQ_ABI_VERSION; }
+
+const char* qoq_status_str(int status) {
+    switch (status) {
+        case QOQ_OK: return "ok";
+        case QOQ_ERR_NULL: return "a required pointer is NULL";
+        case QOQ_ERR_SHAPE: return "shape outside the supported limits";
+        case QOQ_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case QOQ_ERR_MODE: return "unknown quantization mode";
+        case QOQ_ERR_HIP: return "HIP runtime error at launch";
+        case QOQ_ERR_WORKSPACE: return "workspace smaller than qoq_gemm_workspace_bytes()";
+        default: return "unknown status";
+    }
+}
+
+qoq_status qoq_quantize_weights(int mode, const uint16_t* w, int64_t N, int64_t K, uint8_t* q,
+                                uint16_t* s_c, uint8_t* s_g, uint8_t* z, void* stream) {
+    if (!valid_mode(mode)) return QOQ_ERR_MODE;
+    if (N < 0 || N % 16 || !valid_k(K)) return QOQ_ERR_SHAPE;
+    if (N == 0) return QOQ_OK;
+    if (!w || !q || !s_c || !z) return QOQ_ERR_NULL;
+    if (mode == QOQ_MODE_G128 && !s_g) return QOQ_ERR_NULL;
+    if (!aligned16(w) || !aligned16(q) || !aligned16(s_c) || !aligned16(z) ||
+        (mode == QOQ_MODE_G128 && !aligned16(s_g)))
+        return QOQ_ERR_ALIGN;
+    return launch_checked([&] {
+        qoq::launch_quantize_weights(mode, w, N, K, q, s_c, s_g, z, as_stream(stream));
+    });
+}
+
+int64_t qoq_packed_bytes(int mode, int64_t N, int64_t K) {
+    if (!valid_mode(mode) || N < 16 || N % 16 || !valid_k(K)) return -1;
+    return qoq::packed_bytes(mode, N, K);
+}
+
+qoq_status qoq_pack_weights(int mode, const uint8_t* q, const uint8_t* s_g, const uint8_t* z,
+                            int64_t N, int64_t K, void* blob, void* stream) {
+    if (!valid_mode(mode)) return QOQ_ERR_MODE;
+    if (N < 16 || N % 16 || !valid_k(K)) return QOQ_ERR_SHAPE;
+    if (!q || !z || !blob) return QOQ_ERR_NULL;
+    if (mode == QOQ_MODE_G128 && !s_g) return QOQ_ERR_NULL;
+    if (!aligned16(q) || !aligned16(z) || !aligned16(blob) ||
+        (mode == QOQ_MODE_G128 && !aligned16(s_g)))
+        return QOQ_ERR_ALIGN;
+    return launch_checked([&] {
+        qoq::launch_pack(mode, q, s_g, z, N, K, static_cast<uint8_t*>(blob), as_stream(stream));
+    });
+}
+
+qoq_status qoq_unpack_weights(int mode, const void* blob, int64_t N, int64_t K, uint8_t* q,
+                              uint8_t* s_g, uint8_t* z, void* stream) {
+    if (!valid_mode(mode)) return QOQ_ERR_MODE;
+    if (N < 16 || N % 16 || !valid_k(K)) return QOQ_ERR_SHAPE;
+    if (!blob || !q || !z) return QOQ_ERR_NULL;
+    if (mode == QOQ_MODE_G128 && !s_g) return QOQ_ERR_NULL;
+    if (!aligned16(blob) || !aligned16(q) || !aligned16(z) ||
+        (mode == QOQ_MODE_G128 && !aligned16(s_g)))
+        return QOQ_ERR_ALIGN;
+    return launch_checked([&] {
+        qoq::launch_unpack(mode, static_cast<const uint8_t*>(blob), N, K, q, s_g, z,
+                           as_stream(stream));
+    });
+}
+
+int64_t qoq_act_bytes(int64_t M, int64_t K) {
+    if (M < 0 || M > INT32_MAX - 15 || !valid_k(K)) return -1;
+    return (M + 15) / 16 * 16 * K;
+}
+
+qoq_status qoq_quantize_act(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, uint16_t* s_x,
+                            int32_t* rowsum, void* stream) {
+    if (M < 0 || M > INT32_MAX - 15 || !valid_k(K)) return QOQ_ERR_SHAPE;
+    if (M == 0) return QOQ_OK;
+    if (!x || !xq || !s_x) return QOQ_ERR_NULL;
+    if (!aligned16(x) || !aligned16(xq) || !aligned16(s_x) || (rowsum && !aligned16(rowsum)))
+        return QOQ_ERR_ALIGN;
+    return launch_checked(
+        [&] { qoq::launch_quantize_act(x, M, K, xq, s_x, rowsum, as_stream(stream)); });
+}
+
+int64_t qoq_gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K) {
+    if (!valid_mode(mode) || M < 0 || M > INT32_MAX || N < 0 || N % 16 || N > INT32_MAX ||
+        !valid_k(K))
+        return -1;
+    if (M == 0 || N == 0) return 0;
+    return qoq::gemm_workspace_bytes(mode, M, N, K);
+}
+
+qoq_status qoq_w4a8_gemm(int mode, const int8_t* xq, const uint16_t* s_x, const int32_t* rowsum,
+                         const void* blob, const uint16_t* s_c, int64_t M, int64_t N, int64_t K,
+                         uint16_t* y, int32_t* acc_out, void* workspace, int64_t workspace_bytes,
+                         void* stream) {
+    if (!valid_mode(mode)) return QOQ_ERR_MODE;
+    if (M < 0 || M > INT32_MAX - 15 || N < 0 || N % 16 || N > INT32_MAX || !valid_k(K))
+        return QOQ_ERR_SHAPE;
+    if (M == 0 || N == 0) return QOQ_OK;
+    if (!xq || !s_x || !blob || !s_c || !y) return QOQ_ERR_NULL;
+    if (mode == QOQ_MODE_PER_CHANNEL && !rowsum) return QOQ_ERR_NULL;
+    if (!aligned16(xq) || !aligned16(s_x) || !aligned16(blob) || !aligned16(s_c) ||
+        !aligned16(y) || (rowsum && !aligned16(rowsum)) || (acc_out && !aligned16(acc_out)) ||
+        (workspace && !aligned16(workspace)))
+        return QOQ_ERR_ALIGN;
+    if (workspace && workspace_bytes < qoq::gemm_workspace_bytes(mode, M, N, K))
+        return QOQ_ERR_WORKSPACE;
+    return launch_checked([&] {
+        qoq::launch_gemm(mode, xq, s_x, rowsum, static_cast<const uint8_t*>(blob), s_c, M, N, K, y,
+                         acc_out, workspace, as_stream(stream));
+    });
+}
+
+}  // extern "C"

@@ -1,0 +1,462 @@
+// gemm.hip -- W4A8 GEMM on the gfx950 INT8 matrix cores.
+//
+//   acc[m,n] = sum_k xq[m,k] * W8^[n,k]   (exact INT32)
+//   y[m,n]   = f16((f32(acc) * s_x[m]) * s_c[n])
+//
+// W8^ is unpacked in registers from the packed UINT4 codes: g128 mode by
+// multiplying with the group's integer scale and subtracting the precomputed
+// zero-point compensation ("QServe: Low Bit Width Does Not Guarantee High
+// Throughput", section 4, the paragraph on the [-119,119] margin); per-channel
+// mode feeds the codes themselves and subtracts z[n] * rowsum[m] in the
+// epilogue. The rescale by the per-token and per-channel scales happens once,
+// after the integer sum ("QServe Guide: W4A8KV4 Quantization for LLM Serving",
+// Deep Dive part 1).
+//
+// Matrix-core mapping (v_mfma_i32_16x16x64_i8): A = activations (16 rows m),
+// B = weights (16 channels n). For both operands lane l holds row/channel
+// l % 16 and bytes 16*(l/16) .. +15 of the 64-wide k slice; the accumulator
+// lane l holds rows 4*(l/16) + 0..3 of channel l % 16.
+#include <cmath>
+
+#include "qoq_device.hpp"
+#include "qoq_launch.hpp"
+
+namespace qoq {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWavesPerBlock = kThreads / kWave;
+
+// Epilogue for one lane's four accumulator rows of one channel.
+template <bool kG128>
+__device__ __forceinline__ void store_outputs(int32x4 a, int m_first, int n, int M, int N,
+                                              const uint16_t* __restrict__ s_x,
+                                              const int32_t* __restrict__ rowsum, float sc,
+                                              int zpc, uint16_t* __restrict__ y,
+                                              int32_t* __restrict__ acc_out) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int m = m_first + v;
+        if (m < M) {
+            int r = a[v];
+            if (!kG128) r -= zpc * rowsum[m];
+            const size_t o = (size_t)m * N + n;
+            if (acc_out) acc_out[o] = r;
+            float v = ((float)r * h2f(s_x[m])) * sc;
+            // The contract rounds the product to fp32, then to FP16. Without this
+            // barrier the backend folds the last multiply and the conversion into
+            // one mixed-precision FMA that rounds only once.
+            asm("" : "+v"(v));
+            y[o] = f2h(v);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Reference kernel: each wave owns one 16-channel tile and 64 rows, and streams
+// the whole K. Used where no tuned kernel applies.
+template <bool kG128>
+__global__ __launch_bounds__(kThreads) void k_gemm_simple(
+    const int8_t* __restrict__ xq, const uint16_t* __restrict__ s_x,
+    const int32_t* __restrict__ rowsum, const uint8_t* __restrict__ blob,
+    const uint16_t* __restrict__ s_c, int M, int N, int K, uint16_t* __restrict__ y,
+    int32_t* __restrict__ acc_out) {
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
+    const int t = blockIdx.x * kWavesPerBlock + wave;
+    if (t * 16 >= N) return;
+    const int m0 = blockIdx.y * 64;
+    const int G = K / kGroup;
+    const int Gp = (G + 15) / 16 * 16;
+    const int U = (M + 15) / 16;  // activation tiles of 16 rows
+    const int c = lane % 16;
+    const int j = lane / 16;
+    const int n = t * 16 + c;
+    const uint4* tiles = reinterpret_cast<const uint4*>(blob) + (size_t)t * G * kWave + lane;
+    const uint8_t* params = blob + (size_t)N * K / 2;
+    const int32x4* act = reinterpret_cast<const int32x4*>(xq) + lane;
+
+    int32x4 acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = int32x4{0, 0, 0, 0};
+
+    for (int g = 0; g < G; ++g) {
+        const uint4 p = tiles[(size_t)g * kWave];
+        GroupConst gc{0u, 0u};
+        if (kG128) gc = group_const(params[(size_t)n * Gp + g]);
+        int32x4 b0, b1;
+        unpack_lane<kG128>(p, gc, b0, b1);
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            const int u = m0 / 16 + mb;
+            if (u < U) {
+                const int32x4* src = act + ((size_t)g * U + u) * 128;
+                acc[mb] = mfma16x16x64(src[0], b0, acc[mb]);
+                acc[mb] = mfma16x16x64(src[64], b1, acc[mb]);
+            }
+        }
+    }
+
+    const float sc = h2f(s_c[n]);
+    const int zpc = kG128 ? 0 : (int)params[n];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+        store_outputs<kG128>(acc[mb], m0 + 16 * mb + 4 * j, n, M, N, s_x, rowsum, sc, zpc, y,
+                             acc_out);
+}
+
+// ---------------------------------------------------------------------------
+// Decode kernel (M <= 64): weight streaming at HBM rate.
+//
+// A workgroup of 4 waves owns NT n-tiles (16*NT channels) and the k-range of
+// split s (of S). Its waves split that range into 4 contiguous parts; each
+// wave keeps all 16*MB rows and its NT tiles in registers, so an activation
+// fragment is reused NT times and a weight fragment MB times. Vector loads
+// complete in issue order on gfx9, so activations and weights ride one FIFO:
+// both are prefetched D groups ahead into a register ring. At the end the four
+// waves' partial sums are added through LDS; with S > 1 every workgroup also
+// writes its partial tile to the workspace and the last of the S workgroups of
+// an n-block (found with an atomic counter) adds the others and runs the
+// epilogue, then re-arms the counter for the next call. INT32 addition is
+// exact and associative, so the result does not depend on the order.
+template <bool kG128, int MB, int NT, int D, int W>
+__global__ __launch_bounds__(W * 64) void k_gemm_decode(
+    const int8_t* __restrict__ xq, const uint16_t* __restrict__ s_x,
+    const int32_t* __restrict__ rowsum, const uint8_t* __restrict__ blob,
+    const uint16_t* __restrict__ s_c, int M, int N, int K, int S, uint16_t* __restrict__ y,
+    int32_t* __restrict__ acc_out, int32x4* __restrict__ ws, unsigned* __restrict__ counters) {
+    __shared__ int32x4 red[W][NT * MB][kWave];
+    __shared__ unsigned ticket;
+
+    const int lane = threadIdx.x % kWave;
+    // The wave index is uniform across the wave: keep everything derived from it
+    // in scalar registers so that loop control stays scalar.
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int nb = blockIdx.x / S;
+    const int s = blockIdx.x - nb * S;
+    const int G = K / kGroup;
+    const int Gp = (G + 15) / 16 * 16;
+    const int tiles = N / 16;
+    const int c = lane % 16;
+    const int j = lane / 16;
+
+    // k-range of this workgroup, then of this wave (contiguous).
+    const int wg0 = (int)((int64_t)G * s / S);
+    const int wg1 = (int)((int64_t)G * (s + 1) / S);
+    const int g0 = wg0 + (wg1 - wg0) * wave / W;
+    const int g1 = wg0 + (wg1 - wg0) * (wave + 1) / W;
+    const int count = g1 - g0;
+    const int last = max(count - 1, 0);
+
+    // Weight tile pointers (clamped for the ragged n tail: the data of an
+    // out-of-range tile is never stored) and per-lane parameter rows.
+    const uint4* bptr[NT];
+    const uint8_t* pptr[NT];
+    const uint8_t* params = blob + (size_t)N * K / 2;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        const int t = min(nb * NT + i, tiles - 1);
+        bptr[i] = reinterpret_cast<const uint4*>(blob) + ((size_t)t * G + min(g0, G - 1)) * kWave +
+                  lane;
+        pptr[i] = params + (size_t)(16 * t + c) * Gp + min(g0, G - 1);
+    }
+    // Activation tiles (packed 16-row tiles; a tile index past the last one is
+    // clamped: it feeds only accumulator rows that are never stored).
+    const int U = (M + 15) / 16;
+    const int32x4* aptr[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+        aptr[mb] = reinterpret_cast<const int32x4*>(xq) +
+                   ((size_t)min(g0, G - 1) * U + min(mb, U - 1)) * 128 + lane;
+
+    int32x4 acc[NT][MB];
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[i][mb] = int32x4{0, 0, 0, 0};
+
+    // The wave walks its k-range in chunks of D groups. All loads of a chunk
+    // are issued together into registers that belong to that chunk, then
+    // consumed in order, so every wait on the in-order load counter is static
+    // and nothing is in flight across the loop's back edge; the latency between
+    // chunks is hidden by the other waves resident on the compute unit. Group
+    // indices past the wave's range are clamped (those loads re-read the last
+    // group and their products are skipped).
+    for (int base = 0; base < count; base += D) {
+        uint4 rb[D][NT];
+        uint32_t rp[D][NT];
+        int32x4 ra[D][MB][2];
+#pragma unroll
+        for (int q = 0; q < D; ++q) {
+            const int gi = min(base + q, last);
+#pragma unroll
+            for (int i = 0; i < NT; ++i) {
+                rb[q][i] = bptr[i][(size_t)gi * kWave];
+                if (kG128) rp[q][i] = pptr[i][gi];
+            }
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const int32x4* src = aptr[mb] + (size_t)gi * U * 128;
+                ra[q][mb][0] = src[0];
+                ra[q][mb][1] = src[64];
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < D; ++q) {
+            if (base + q < count) {
+                int32x4 b[NT][2];
+#pragma unroll
+                for (int i = 0; i < NT; ++i) {
+                    GroupConst gc{0u, 0u};
+                    if (kG128) gc = group_const(rp[q][i]);
+                    unpack_lane<kG128>(rb[q][i], gc, b[i][0], b[i][1]);
+                }
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int i = 0; i < NT; ++i)
+#pragma unroll
+                        for (int mb = 0; mb < MB; ++mb)
+                            acc[i][mb] = mfma16x16x64(ra[q][mb][ks], b[i][ks], acc[i][mb]);
+            }
+        }
+    }
+
+    // Add the waves' partial sums: wave w finishes the (tile, m-block) pairs
+    // p = w, w + W, ...
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) red[wave][i * MB + mb][lane] = acc[i][mb];
+    __syncthreads();
+    constexpr int kPairs = NT * MB;
+    constexpr int kOwn = (kPairs + W - 1) / W;
+    int32x4 part[kOwn];
+#pragma unroll
+    for (int o = 0; o < kOwn; ++o) {
+        const int p = wave + o * W;
+        part[o] = int32x4{0, 0, 0, 0};
+        if (p < kPairs) {
+#pragma unroll
+            for (int w = 0; w < W; ++w) part[o] += red[w][p][lane];
+        }
+    }
+
+    if (S > 1) {
+        // Publish this workgroup's partial tile, then take a ticket. Only one
+        // thread fences at device scope: the barrier has already made every
+        // thread's stores reach the shared cache, and the one release writes
+        // them back; only the last workgroup's one acquire follows.
+        int32x4* mine = ws + ((size_t)blockIdx.x * kPairs) * kWave + lane;
+#pragma unroll
+        for (int o = 0; o < kOwn; ++o) {
+            const int p = wave + o * W;
+            if (p < kPairs) mine[(size_t)p * kWave] = part[o];
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (threadIdx.x == 0)
+            ticket = __hip_atomic_fetch_add(&counters[nb], 1u, __ATOMIC_ACQ_REL,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (ticket != (unsigned)(S - 1)) return;
+        for (int s2 = 0; s2 < S; ++s2) {
+            if (s2 == s) continue;
+            const int32x4* other = ws + ((size_t)(nb * S + s2) * kPairs) * kWave + lane;
+#pragma unroll
+            for (int o = 0; o < kOwn; ++o) {
+                const int p = wave + o * W;
+                if (p < kPairs)
+                    part[o] += __builtin_nontemporal_load(&other[(size_t)p * kWave]);
+            }
+        }
+        if (threadIdx.x == 0) counters[nb] = 0u;
+    }
+
+    const uint8_t* pc_z = params;  // per-channel zero bytes
+#pragma unroll
+    for (int o = 0; o < kOwn; ++o) {
+        const int p = wave + o * W;
+        if (p < kPairs) {
+            const int i = p / MB, mb = p % MB;
+            const int t = nb * NT + i;
+            if (t < tiles) {
+                const int n = 16 * t + c;
+                const int zpc = kG128 ? 0 : (int)pc_z[n];
+                store_outputs<kG128>(part[o], 16 * mb + 4 * j, n, M, N, s_x, rowsum,
+                                     h2f(s_c[n]), zpc, y, acc_out);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Plans.
+
+constexpr int kCUs = 256;
+
+struct Plan {
+    int kind = 0;  // 0: simple, 1: decode
+    int mb = 0, nt = 0, s = 1, d = 1, w = 4;
+    int64_t nblk = 0;
+    int64_t ws_bytes = 0;
+};
+
+#ifdef QOQ_TUNING
+int g_force_nt = 0, g_force_s = 0, g_force_d = 0, g_force_w = 0;
+#endif
+
+// Workspace layout: a fixed region of kMaxCounters arrival counters at offset
+// 0 (every plan leaves the counters it used at zero, and no plan writes
+// partial sums there, so plans of different shapes can share a workspace),
+// then the partial tiles.
+constexpr int64_t kMaxCounters = 16384;
+constexpr int64_t kCounterBytes = kMaxCounters * 4;
+
+int64_t decode_ws_bytes(int mb, int nt, int s, int64_t nblk) {
+    if (s <= 1) return 0;
+    const int64_t partial = nblk * s * (int64_t)nt * mb * kWave * 16;  // int32x4 per lane
+    return kCounterBytes + partial;
+}
+
+// The (MB, NT, W) combinations that are instantiated.
+constexpr bool decode_shape_ok(int mb, int nt, int w) {
+    return nt * mb <= 24 && !(mb == 2 && nt == 12) && w * nt * mb <= 96;
+}
+
+// Decode plan. Measured on MI355X over the Llama-3-8B and Qwen1.5-72B decode
+// layers: the workgroup count should cover most compute units, and more
+// channels per workgroup cut the activation bytes each one re-reads, but past
+// three 16-channel tiles the register cost lowers occupancy; eight waves per
+// workgroup and one group per load chunk keep the most loads in flight.
+// Splitting K across workgroups never paid for its partial sums and fences on
+// these shapes, so the plan keeps the whole K in one workgroup (the split
+// machinery stays available to plans that are given a workspace).
+Plan plan_gemm(int64_t M, int64_t N, int64_t K, bool /*have_ws*/) {
+    Plan p;
+    if (M > 64) return p;
+    p.kind = 1;
+    p.mb = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+    const int64_t tiles = N / 16;
+    static const int nts[] = {3, 2, 1};
+    p.nt = 1;
+    for (int nt : nts) {
+        if ((tiles + nt - 1) / nt >= kCUs * 2 / 3) {
+            p.nt = nt;
+            break;
+        }
+    }
+    p.s = 1;
+    p.d = 1;
+    p.w = decode_shape_ok(p.mb, p.nt, 8) ? 8 : 4;
+#ifdef QOQ_TUNING
+    if (g_force_nt) p.nt = g_force_nt;
+    if (g_force_s) p.s = g_force_s;
+    if (g_force_d) p.d = g_force_d;
+    if (g_force_w) p.w = g_force_w;
+#endif
+    (void)K;
+    p.nblk = (tiles + p.nt - 1) / p.nt;
+    p.ws_bytes = decode_ws_bytes(p.mb, p.nt, p.s, p.nblk);
+    return p;
+}
+
+struct DecodeArgs {
+    const int8_t* xq;
+    const uint16_t* s_x;
+    const int32_t* rowsum;
+    const uint8_t* blob;
+    const uint16_t* s_c;
+    int M, N, K;
+    uint16_t* y;
+    int32_t* acc_out;
+    void* ws;
+    hipStream_t stream;
+};
+
+template <bool kG128, int MB, int NT, int D, int W>
+void launch_decode_t(const Plan& p, const DecodeArgs& a) {
+    unsigned* counters = reinterpret_cast<unsigned*>(a.ws);
+    int32x4* partial =
+        a.ws ? reinterpret_cast<int32x4*>(static_cast<char*>(a.ws) + kCounterBytes) : nullptr;
+    hipLaunchKernelGGL((k_gemm_decode<kG128, MB, NT, D, W>), dim3((unsigned)(p.nblk * p.s)),
+                       dim3(W * 64), 0, a.stream, a.xq, a.s_x, a.rowsum, a.blob, a.s_c, a.M, a.N,
+                       a.K, p.s, a.y, a.acc_out, partial, counters);
+}
+
+template <bool kG128, int MB, int NT>
+void launch_decode_dw(const Plan& p, const DecodeArgs& a) {
+    if (p.w == 8) {
+        if constexpr (decode_shape_ok(MB, NT, 8)) {
+            if (p.d == 2) launch_decode_t<kG128, MB, NT, 2, 8>(p, a);
+            else launch_decode_t<kG128, MB, NT, 1, 8>(p, a);
+            return;
+        }
+    }
+    if (p.d == 2) launch_decode_t<kG128, MB, NT, 2, 4>(p, a);
+    else launch_decode_t<kG128, MB, NT, 1, 4>(p, a);
+}
+
+template <bool kG128, int MB>
+void launch_decode_nt(const Plan& p, const DecodeArgs& a) {
+#define QOQ_NT_CASE(NTV)                                                 \
+    case NTV:                                                            \
+        if constexpr (decode_shape_ok(MB, NTV, 4)) launch_decode_dw<kG128, MB, NTV>(p, a); \
+        break;
+    switch (p.nt) {
+        QOQ_NT_CASE(1)
+        QOQ_NT_CASE(2)
+        QOQ_NT_CASE(3)
+        QOQ_NT_CASE(4)
+        QOQ_NT_CASE(6)
+        QOQ_NT_CASE(8)
+        QOQ_NT_CASE(12)
+        default: break;
+    }
+#undef QOQ_NT_CASE
+}
+
+template <bool kG128>
+void launch_decode(const Plan& p, const DecodeArgs& a) {
+    if (p.mb == 1) launch_decode_nt<kG128, 1>(p, a);
+    else if (p.mb == 2) launch_decode_nt<kG128, 2>(p, a);
+    else launch_decode_nt<kG128, 4>(p, a);
+}
+
+}  // namespace
+
+int64_t gemm_workspace_bytes(int /*mode*/, int64_t M, int64_t N, int64_t K) {
+    return plan_gemm(M, N, K, true).ws_bytes;
+}
+
+void launch_gemm(int mode, const int8_t* xq, const uint16_t* s_x, const int32_t* rowsum,
+                 const uint8_t* blob, const uint16_t* s_c, int64_t M, int64_t N, int64_t K,
+                 uint16_t* y, int32_t* acc_out, void* ws, hipStream_t stream) {
+    const Plan p = plan_gemm(M, N, K, ws != nullptr);
+    if (p.kind == 1) {
+        const DecodeArgs a{xq, s_x, rowsum, blob, s_c, (int)M, (int)N, (int)K, y, acc_out, ws, stream};
+        if (mode == 0)
+            launch_decode<true>(p, a);
+        else
+            launch_decode<false>(p, a);
+        return;
+    }
+    const dim3 grid((unsigned)((N / 16 + 3) / 4), (unsigned)((M + 63) / 64));
+    if (mode == 0)
+        hipLaunchKernelGGL(k_gemm_simple<true>, grid, dim3(kThreads), 0, stream, xq, s_x, rowsum,
+                           blob, s_c, (int)M, (int)N, (int)K, y, acc_out);
+    else
+        hipLaunchKernelGGL(k_gemm_simple<false>, grid, dim3(kThreads), 0, stream, xq, s_x, rowsum,
+                           blob, s_c, (int)M, (int)N, (int)K, y, acc_out);
+}
+
+#ifdef QOQ_TUNING
+extern "C" void qoq_tuning_force_decode(int nt, int s, int d, int w) {
+    g_force_nt = nt;
+    g_force_s = s;
+    g_force_d = d;
+    g_force_w = w;
+}
+#endif
+
+}  // namespace qoq

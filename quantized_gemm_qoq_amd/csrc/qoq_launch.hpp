@@ -1,0 +1,33 @@
+// qoq_launch.hpp -- host-side launchers of the libqoq kernels. Arguments are
+// validated by the C ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qoq {
+
+void launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, uint16_t* s_x,
+                         int32_t* rowsum, hipStream_t stream);
+
+void launch_quantize_weights(int mode, const uint16_t* w, int64_t N, int64_t K, uint8_t* q,
+                             uint16_t* s_c, uint8_t* s_g, uint8_t* z, hipStream_t stream);
+
+int64_t packed_bytes(int mode, int64_t N, int64_t K);
+
+void launch_pack(int mode, const uint8_t* q, const uint8_t* s_g, const uint8_t* z, int64_t N,
+                 int64_t K, uint8_t* blob, hipStream_t stream);
+
+void launch_unpack(int mode, const uint8_t* blob, int64_t N, int64_t K, uint8_t* q, uint8_t* s_g,
+                   uint8_t* z, hipStream_t stream);
+
+// Workspace bytes the GEMM plan for this shape can use (0: none).
+int64_t gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K);
+
+// ws: NULL (a plan without cross-workgroup reduction is used) or at least
+// gemm_workspace_bytes() of zero-initialised device memory.
+void launch_gemm(int mode, const int8_t* xq, const uint16_t* s_x, const int32_t* rowsum,
+                 const uint8_t* blob, const uint16_t* s_c, int64_t M, int64_t N, int64_t K,
+                 uint16_t* y, int32_t* acc_out, void* ws, hipStream_t stream);
+
+}  // namespace qoq

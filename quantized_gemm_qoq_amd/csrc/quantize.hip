@@ -1,0 +1,247 @@
+// quantize.hip -- per-token INT8 activation quantization and the offline
+// weight quantizers (progressive g128 and per-channel UINT4), for gfx950.
+//
+// Method: QServe / QoQ (arXiv 2405.04532).
+//   Activations: "QServe Guide: W4A8KV4 Quantization for LLM Serving", Deep Dive
+//   part 1 -- per-token symmetric INT8 with scale max|X|/127.
+//   Weights: "QServe: Low Bit Width Does Not Guarantee High Throughput",
+//   section 4 -- stage 1 (per-channel INT8 in [-119, 119], scale max|W|/119)
+//   and stage 2 (groups of 128 inputs, integer scale, UINT4 zero and codes).
+// Rounding follows the library contract in qoq.h: round half to even, scales
+// computed in IEEE fp32 with correctly rounded division, stored as FP16, and
+// the stored FP16 scale is the one used to quantize.
+#include "qoq_device.hpp"
+#include "qoq_launch.hpp"
+
+namespace qoq {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+
+template <typename T, typename Op>
+__device__ __forceinline__ T block_reduce(T v, T* smem, Op wave_op) {
+    v = wave_op(v);
+    const int wave = threadIdx.x / kWave;
+    if ((threadIdx.x % kWave) == 0) smem[wave] = v;
+    __syncthreads();
+    T r = smem[0];
+#pragma unroll
+    for (int i = 1; i < kWaves; ++i) r = wave_op.combine(r, smem[i]);
+    __syncthreads();
+    return r;
+}
+
+struct MaxU {
+    __device__ unsigned operator()(unsigned v) const { return wave_max_u(v); }
+    __device__ unsigned combine(unsigned a, unsigned b) const { return max(a, b); }
+};
+struct SumI {
+    __device__ int operator()(int v) const { return wave_sum_i(v); }
+    __device__ int combine(int a, int b) const { return a + b; }
+};
+struct MaxF {
+    __device__ float operator()(float v) const { return wave_max_f(v); }
+    __device__ float combine(float a, float b) const { return fmaxf(a, b); }
+};
+struct MinF {
+    __device__ float operator()(float v) const { return wave_min_f(v); }
+    __device__ float combine(float a, float b) const { return fminf(a, b); }
+};
+
+// Quantize one FP16 value with the row's FP16 scale (given as float, non-zero).
+__device__ __forceinline__ int quant_act1(uint32_t hbits, float sf) {
+    const float r = rintf(h2f(hbits) / sf);
+    return (int)fminf(fmaxf(r, -128.0f), 127.0f);
+}
+
+// One workgroup per token row (the grid covers the padded rows too, which are
+// written as zeros). Pass 1 takes the row's largest magnitude on the FP16 bit
+// patterns; pass 2 re-reads the row (an L2 hit) and writes each run of 16
+// codes to its 16-byte slot of the packed tile order.
+__global__ __launch_bounds__(kThreads) void k_quantize_act(const uint16_t* __restrict__ x, int M,
+                                                           int K, int8_t* __restrict__ xq,
+                                                           uint16_t* __restrict__ s_x,
+                                                           int32_t* __restrict__ rowsum) {
+    __shared__ unsigned red_u[kWaves];
+    __shared__ int red_i[kWaves];
+    const int m = blockIdx.x;
+    const int U = gridDim.x / 16;  // grid = Mp rows
+    const int u = m / 16, r = m % 16;
+    const int nchunk = K / 16;
+    uint4* out = reinterpret_cast<uint4*>(xq);
+    // 16-byte slot of chunk c (inputs 16c .. 16c+15) of this row.
+    auto slot = [&](int c) {
+        const int g = c / 8, s = (c / 4) % 2, j = c % 4;
+        return ((size_t)g * U + u) * 128 + 64 * s + 16 * j + r;
+    };
+    if (m >= M) {
+        for (int c = threadIdx.x; c < nchunk; c += kThreads) out[slot(c)] = make_uint4(0, 0, 0, 0);
+        return;
+    }
+    const uint4* row = reinterpret_cast<const uint4*>(x + (size_t)m * K);
+    const int nvec = K / 8;
+
+    unsigned amax = 0;
+    for (int i = threadIdx.x; i < nvec; i += kThreads) {
+        const uint4 v = row[i];
+        amax = max(amax, max(max(absmax_bits2(v.x), absmax_bits2(v.y)),
+                             max(absmax_bits2(v.z), absmax_bits2(v.w))));
+    }
+    amax = block_reduce(amax, red_u, MaxU{});
+    const uint16_t sbits = f2h(h2f(amax) / 127.0f);
+    const float sf = h2f(sbits);
+
+    int sum = 0;
+    for (int c = threadIdx.x; c < nchunk; c += kThreads) {
+        uint4 o = make_uint4(0, 0, 0, 0);
+        if (sf != 0.0f) {
+            const uint4 v0 = row[2 * c], v1 = row[2 * c + 1];
+            const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+            uint32_t packed[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const uint32_t hb = (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu);
+                const int q = quant_act1(hb, sf);
+                sum += q;
+                packed[e >> 2] |= (uint32_t)(q & 0xFF) << (8 * (e & 3));
+            }
+            o = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+        }
+        out[slot(c)] = o;
+    }
+    if (rowsum) sum = block_reduce(sum, red_i, SumI{});
+    if (threadIdx.x == 0) {
+        s_x[m] = sbits;
+        if (rowsum) rowsum[m] = sum;
+    }
+}
+
+// Progressive group quantization, one workgroup per output channel.
+// Stage 1 needs the row's largest magnitude; stage 2 runs one wave per group
+// of 128, two inputs per lane.
+__global__ __launch_bounds__(kThreads) void k_quantize_weights_g128(
+    const uint16_t* __restrict__ w, int K, uint8_t* __restrict__ q, uint16_t* __restrict__ s_c,
+    uint8_t* __restrict__ s_g, uint8_t* __restrict__ zp) {
+    __shared__ unsigned red_u[kWaves];
+    const size_t n = blockIdx.x;
+    const uint16_t* row = w + n * (size_t)K;
+    const uint4* rowv = reinterpret_cast<const uint4*>(row);
+    const int nvec = K / 8;
+    const int G = K / kGroup;
+
+    unsigned amax = 0;
+    for (int i = threadIdx.x; i < nvec; i += kThreads) {
+        const uint4 v = rowv[i];
+        amax = max(amax, max(max(absmax_bits2(v.x), absmax_bits2(v.y)),
+                             max(absmax_bits2(v.z), absmax_bits2(v.w))));
+    }
+    amax = block_reduce(amax, red_u, MaxU{});
+    const uint16_t scbits = f2h(h2f(amax) / 119.0f);
+    const float scf = h2f(scbits);
+    if (threadIdx.x == 0) s_c[n] = scbits;
+
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
+    for (int g = wave; g < G; g += kWaves) {
+        const uint32_t pair = reinterpret_cast<const uint32_t*>(row + g * kGroup)[lane];
+        int w8[2] = {0, 0};
+        if (scf != 0.0f) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const float r = rintf(h2f(e ? pair >> 16 : pair & 0xFFFFu) / scf);
+                w8[e] = (int)fminf(fmaxf(r, -119.0f), 119.0f);
+            }
+        }
+        const int mn = wave_min_i(min(0, min(w8[0], w8[1])));
+        const int mx = wave_max_i(max(0, max(w8[0], w8[1])));
+        const int sg = max(1, (mx - mn + 14) / 15);
+        // Quotients of small integers: the fp32 division is exact at ties and
+        // cannot cross a half-integer otherwise, so rintf rounds the rational.
+        const float sgf = (float)sg;
+        const int zz = (int)rintf((float)(-mn) / sgf);
+        uint32_t codes = 0;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int c = min(15, max(0, (int)rintf((float)w8[e] / sgf) + zz));
+            codes |= (uint32_t)c << (8 * e);
+        }
+        reinterpret_cast<uint16_t*>(q + n * (size_t)K + g * kGroup)[lane] = (uint16_t)codes;
+        if (lane == 0) {
+            s_g[n * (size_t)G + g] = (uint8_t)sg;
+            zp[n * (size_t)G + g] = (uint8_t)zz;
+        }
+    }
+}
+
+// Per-channel UINT4: one asymmetric range per output channel, spanning zero.
+__global__ __launch_bounds__(kThreads) void k_quantize_weights_pc(
+    const uint16_t* __restrict__ w, int K, uint8_t* __restrict__ q, uint16_t* __restrict__ s_c,
+    uint8_t* __restrict__ zp) {
+    __shared__ float red_f[kWaves];
+    const size_t n = blockIdx.x;
+    const uint4* rowv = reinterpret_cast<const uint4*>(w + n * (size_t)K);
+    const int nvec = K / 8;
+
+    float mn = 0.0f, mx = 0.0f;
+    for (int i = threadIdx.x; i < nvec; i += kThreads) {
+        const uint4 v = rowv[i];
+        const uint32_t ws[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float f = h2f((e & 1) ? (ws[e >> 1] >> 16) : (ws[e >> 1] & 0xFFFFu));
+            mn = fminf(mn, f);
+            mx = fmaxf(mx, f);
+        }
+    }
+    mn = block_reduce(mn, red_f, MinF{});
+    mx = block_reduce(mx, red_f, MaxF{});
+    const float range = mx - mn;
+    const uint16_t scbits = f2h(range / 15.0f);
+    const float scf = h2f(scbits);
+    int zz = 0;
+    if (scf != 0.0f) zz = (int)fminf(fmaxf(rintf(-mn / scf), 0.0f), 15.0f);
+    if (threadIdx.x == 0) {
+        s_c[n] = scbits;
+        zp[n] = (uint8_t)zz;
+    }
+
+    uint2* out = reinterpret_cast<uint2*>(q + n * (size_t)K);
+    for (int i = threadIdx.x; i < nvec; i += kThreads) {
+        uint2 o = {0u, 0u};
+        if (scf != 0.0f) {
+            const uint4 v = rowv[i];
+            const uint32_t ws[4] = {v.x, v.y, v.z, v.w};
+            uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float f = h2f((e & 1) ? (ws[e >> 1] >> 16) : (ws[e >> 1] & 0xFFFFu));
+                const int c = min(15, max(0, (int)rintf(f / scf) + zz));
+                packed[e >> 2] |= (uint32_t)c << (8 * (e & 3));
+            }
+            o = make_uint2(packed[0], packed[1]);
+        }
+        out[i] = o;
+    }
+}
+
+}  // namespace
+
+void launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, uint16_t* s_x,
+                         int32_t* rowsum, hipStream_t stream) {
+    const unsigned mp = (unsigned)((M + 15) / 16 * 16);
+    hipLaunchKernelGGL(k_quantize_act, dim3(mp), dim3(kThreads), 0, stream, x, (int)M, (int)K, xq,
+                       s_x, rowsum);
+}
+
+void launch_quantize_weights(int mode, const uint16_t* w, int64_t N, int64_t K, uint8_t* q,
+                             uint16_t* s_c, uint8_t* s_g, uint8_t* z, hipStream_t stream) {
+    if (mode == 0)
+        hipLaunchKernelGGL(k_quantize_weights_g128, dim3((unsigned)N), dim3(kThreads), 0, stream, w,
+                           (int)K, q, s_c, s_g, z);
+    else
+        hipLaunchKernelGGL(k_quantize_weights_pc, dim3((unsigned)N), dim3(kThreads), 0, stream, w,
+                           (int)K, q, s_c, z);
+}
+
+}  // namespace qoq

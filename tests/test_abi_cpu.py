@@ -1,0 +1,136 @@
+"""Host-only checks of the C ABI: the library loads, exports every entry point
+that include/qoq.h declares, and rejects invalid arguments before launching
+anything (no call here reaches a kernel, so no GPU is needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_gemm_qoq_amd as qoq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qoq.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_MODE, ERR_HIP, ERR_WORKSPACE = range(7)
+A = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: every call below fails validation
+U = ctypes.c_void_p(0x10004)  # misaligned
+NUL = None
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qoq_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return qoq.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    decl = declared_functions()
+    assert decl == sorted(qoq.EXPORTED)
+    for name in decl:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    hdr = open(HEADER).read()
+    ver = int(re.search(r"#define QOQ_ABI_VERSION (\d+)", hdr).group(1))
+    assert lib.qoq_abi_version() == ver == qoq.qoq_abi_version()
+    for s in range(7):
+        assert lib.qoq_status_str(s) and lib.qoq_status_str(s) != b"unknown status"
+    assert lib.qoq_status_str(99) == b"unknown status"
+
+
+def test_packed_bytes(lib):
+    assert lib.qoq_packed_bytes(0, 16, 128) == 16 * 64 + 16 * 16
+    assert lib.qoq_packed_bytes(1, 16, 128) == 16 * 64 + 16
+    assert lib.qoq_packed_bytes(0, 6144, 4096) == 6144 * 2048 + 6144 * 32
+    assert lib.qoq_packed_bytes(0, 15, 128) == -1
+    assert lib.qoq_packed_bytes(0, 16, 129) == -1
+    assert lib.qoq_packed_bytes(0, 16, 132096 + 128) == -1
+    assert lib.qoq_packed_bytes(2, 16, 128) == -1
+
+
+def test_act_bytes(lib):
+    assert lib.qoq_act_bytes(1, 128) == 16 * 128
+    assert lib.qoq_act_bytes(16, 256) == 16 * 256
+    assert lib.qoq_act_bytes(17, 256) == 32 * 256
+    assert lib.qoq_act_bytes(0, 128) == 0
+    assert lib.qoq_act_bytes(4, 100) == -1
+
+
+def test_quantize_act_validation(lib):
+    f = lib.qoq_quantize_act
+    assert f(A, 0, 128, A, A, A, NUL) == OK  # empty: nothing launched
+    assert f(NUL, 0, 128, NUL, NUL, NUL, NUL) == OK
+    assert f(A, -1, 128, A, A, A, NUL) == ERR_SHAPE
+    assert f(A, 4, 100, A, A, A, NUL) == ERR_SHAPE
+    assert f(A, 4, 0, A, A, A, NUL) == ERR_SHAPE
+    assert f(A, 4, 132096 + 128, A, A, A, NUL) == ERR_SHAPE
+    assert f(NUL, 4, 128, A, A, A, NUL) == ERR_NULL
+    assert f(A, 4, 128, NUL, A, A, NUL) == ERR_NULL
+    assert f(A, 4, 128, A, NUL, A, NUL) == ERR_NULL
+    assert f(U, 4, 128, A, A, A, NUL) == ERR_ALIGN
+    assert f(A, 4, 128, A, A, U, NUL) == ERR_ALIGN
+
+
+def test_quantize_weights_validation(lib):
+    f = lib.qoq_quantize_weights
+    assert f(2, A, 16, 128, A, A, A, A, NUL) == ERR_MODE
+    assert f(0, A, 0, 128, NUL, NUL, NUL, NUL, NUL) == OK
+    assert f(0, A, 15, 128, A, A, A, A, NUL) == ERR_SHAPE
+    assert f(0, A, 16, 64, A, A, A, A, NUL) == ERR_SHAPE
+    assert f(0, A, 16, 128, A, A, NUL, A, NUL) == ERR_NULL  # g128 needs s_g
+    assert f(1, A, 16, 128, A, A, NUL, NUL, NUL) == ERR_NULL  # z always needed
+    assert f(0, U, 16, 128, A, A, A, A, NUL) == ERR_ALIGN
+
+
+def test_pack_unpack_validation(lib):
+    p = lib.qoq_pack_weights
+    u = lib.qoq_unpack_weights
+    assert p(3, A, A, A, 16, 128, A, NUL) == ERR_MODE
+    assert p(0, A, A, A, 0, 128, A, NUL) == ERR_SHAPE  # a blob needs at least one tile
+    assert p(0, A, A, A, 24, 128, A, NUL) == ERR_SHAPE
+    assert p(0, A, NUL, A, 16, 128, A, NUL) == ERR_NULL
+    assert p(0, A, A, A, 16, 128, NUL, NUL) == ERR_NULL
+    assert p(0, A, A, A, 16, 128, U, NUL) == ERR_ALIGN
+    assert u(0, A, 16, 130, A, A, A, NUL) == ERR_SHAPE
+    assert u(1, A, 16, 128, NUL, NUL, A, NUL) == ERR_NULL
+    assert u(1, U, 16, 128, A, NUL, A, NUL) == ERR_ALIGN
+
+
+def test_gemm_validation(lib):
+    f = lib.qoq_w4a8_gemm
+    def args(mode=0, xq=A, sx=A, rs=A, blob=A, sc=A, M=8, N=16, K=128, y=A, acc=NUL, ws=NUL,
+             wsb=0):
+        return f(mode, xq, sx, rs, blob, sc, M, N, K, y, acc, ws, wsb, NUL)
+    assert args(mode=5) == ERR_MODE
+    assert args(M=0) == OK
+    assert args(N=0) == OK
+    assert args(M=-2) == ERR_SHAPE
+    assert args(N=8) == ERR_SHAPE
+    assert args(K=256 + 64) == ERR_SHAPE
+    assert args(K=132096 + 128) == ERR_SHAPE
+    assert args(xq=NUL) == ERR_NULL
+    assert args(y=NUL) == ERR_NULL
+    assert args(mode=1, rs=NUL) == ERR_NULL  # per-channel needs the row sums
+    assert args(blob=U) == ERR_ALIGN
+    assert args(acc=U) == ERR_ALIGN
+    assert args(ws=U, wsb=1 << 20) == ERR_ALIGN
+    need = lib.qoq_gemm_workspace_bytes(0, 64, 6144, 4096)
+    assert need >= 0
+    if need > 0:
+        assert args(M=64, N=6144, K=4096, ws=A, wsb=need - 1) == ERR_WORKSPACE
+
+
+def test_workspace_bytes(lib):
+    f = lib.qoq_gemm_workspace_bytes
+    assert f(2, 8, 16, 128) == -1
+    assert f(0, 8, 15, 128) == -1
+    assert f(0, 0, 16, 128) == 0
+    assert f(0, 8, 16, 128) >= 0
+    assert f(0, 64, 6144, 4096) % 16 == 0

@@ -74,10 +74,13 @@ def _operand_bytes(words):
 
 
 def emulate_gemm(mode, xq, blob, rowsum, N, K):
-    """Emulate the kernel's operand assembly over the packed blob:
-    lane l of an MFMA 16x16x64 step holds row/column l % 16 and bytes
-    16*(l // 16) .. +15 of the 64-wide k slice, for both operands."""
+    """Emulate the kernel's operand assembly over the packed blob and the
+    packed activations: lane l of an MFMA 16x16x64 step holds row/column
+    l % 16 and bytes 16*(l // 16) .. +15 of the 64-wide k slice, for both
+    operands; the A operand of tile (g, u), k-step s is the 1 KB at
+    (g * Mp/16 + u) * 2048 + 1024 * s of the packed activations."""
     M = xq.shape[0]
+    apk = oracle.pack_act(xq)
     G = K // 128
     T = N // 16
     words = np.ascontiguousarray(blob[: N * K // 2]).view(np.uint32).reshape(T, G, 64, 4)
@@ -106,10 +109,12 @@ def emulate_gemm(mode, xq, blob, rowsum, N, K):
                 b = _operand_bytes(ops).astype(np.int64)  # [64 lanes, 16]
                 k0 = 128 * g + 64 * s
                 for mb in range(Mp // 16):
-                    # A operand: lane l holds row 16*mb + l%16, bytes k0 + 16*(l//16) + 0..15
+                    off = (g * (Mp // 16) + mb) * 2048 + 1024 * s
+                    a = apk[off:off + 1024].reshape(64, 16).astype(np.int64)
+                    # the same operand read from the row-major values directly
                     rows = 16 * mb + c
-                    a = np.stack([xpad[rows[l], k0 + 16 * j[l]: k0 + 16 * j[l] + 16] for l in range(64)])
-                    a = a.astype(np.int64)
+                    a_rm = np.stack([xpad[rows[l], k0 + 16 * j[l]: k0 + 16 * j[l] + 16] for l in range(64)])
+                    np.testing.assert_array_equal(a, a_rm)
                     # D[i][jj] = sum over lane groups jg and bytes of A[i + 16 jg] * B[jj + 16 jg]
                     d = np.zeros((16, 16), np.int64)
                     for jg in range(4):

@@ -159,3 +159,19 @@ def test_per_channel_pack_size():
     assert oracle.packed_bytes(oracle.MODE_G128, 32, 128 * 17) == 32 * 64 * 17 + 32 * 32
     assert oracle.packed_bytes(oracle.MODE_G128, 8, 128) == -1  # N must be a multiple of 16
     assert oracle.packed_bytes(oracle.MODE_G128, 16, 100) == -1  # K must be a multiple of 128
+
+
+def test_pack_act_layout_hand_worked():
+    """Packed activations (layout in include/qoq.h): with M = 17 (two row tiles,
+    Mp = 32) and K = 256 (two groups), value (m, k) goes to
+    (g * 2 + u) * 2048 + 1024 * s + 16 * (16 * j + r) + i."""
+    xq = np.zeros((17, 256), np.int8)
+    xq[0, 0] = 1     # g0 u0 s0 j0 r0 i0 -> 0
+    xq[5, 77] = 2    # 77 = 64 + 13: s1 j0 i13; r5 -> 1024 + 80 + 13 = 1117
+    xq[16, 130] = 3  # u1 r0, k 130: g1, kk 2 -> s0 j0 i2 -> (1*2 + 1)*2048 + 2 = 6146
+    xq[15, 127] = -4  # u0 r15, kk 127: s1 j3 i15 -> 1024 + 16*(48 + 15) + 15 = 2047
+    p = oracle.pack_act(xq)
+    assert p.size == 32 * 256
+    want = np.zeros(32 * 256, np.int8)
+    want[0], want[1117], want[6146], want[2047] = 1, 2, 3, -4
+    np.testing.assert_array_equal(p, want)
