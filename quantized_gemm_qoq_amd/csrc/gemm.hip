@@ -81,7 +81,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_simple(
     for (int i = 0; i < 4; ++i) acc[i] = int32x4{0, 0, 0, 0};
 
     for (int g = 0; g < G; ++g) {
-        const uint4 p = tiles[(size_t)g * kWave];
+        const u32x4 p = reinterpret_cast<const u32x4*>(tiles)[(size_t)g * kWave];
         GroupConst gc{0u, 0u};
         if (kG128) gc = group_const(params[(size_t)n * Gp + g]);
         int32x4 b0, b1;
@@ -150,13 +150,13 @@ __global__ __launch_bounds__(W * 64) void k_gemm_decode(
 
     // Weight tile pointers (clamped for the ragged n tail: the data of an
     // out-of-range tile is never stored) and per-lane parameter rows.
-    const uint4* bptr[NT];
+    const u32x4* bptr[NT];
     const uint8_t* pptr[NT];
     const uint8_t* params = blob + (size_t)N * K / 2;
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
         const int t = min(nb * NT + i, tiles - 1);
-        bptr[i] = reinterpret_cast<const uint4*>(blob) + ((size_t)t * G + min(g0, G - 1)) * kWave +
+        bptr[i] = reinterpret_cast<const u32x4*>(blob) + ((size_t)t * G + min(g0, G - 1)) * kWave +
                   lane;
         pptr[i] = params + (size_t)(16 * t + c) * Gp + min(g0, G - 1);
     }
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(W * 64) void k_gemm_decode(
     // indices past the wave's range are clamped (those loads re-read the last
     // group and their products are skipped).
     for (int base = 0; base < count; base += D) {
-        uint4 rb[D][NT];
+        u32x4 rb[D][NT];
         uint32_t rp[D][NT];
         int32x4 ra[D][MB][2];
 #pragma unroll
@@ -291,13 +291,205 @@ __global__ __launch_bounds__(W * 64) void k_gemm_decode(
 }
 
 // ---------------------------------------------------------------------------
+// Tiled kernel (M > 64): matrix-core bound.
+//
+// A workgroup of WM x WN waves computes a BM x BN block of Y; wave (wm, wn)
+// owns TM x TN 16x16 tiles. Per k-step (one group of 128 inputs):
+//   - the block's activations for the group are one contiguous run of BM/16
+//     packed 2 KB tiles; the workgroup copies them into one of two LDS buffers
+//     with coalesced 16-byte loads, and each wave reads its A operands back
+//     with one conflict-free 16-byte LDS read per lane (lane order is memory
+//     order in the packed layout);
+//   - each wave loads its TN packed weight tiles straight into registers (one
+//     16-byte load per lane per tile) and unpacks them there;
+//   - the loads for step g+1 are issued before the matrix-core work of step g,
+//     and one barrier per step swaps the LDS buffers.
+// Blocks are renumbered so that each XCD (blocks are dealt to the 8 XCDs
+// round-robin) works through a contiguous, grouped part of the block grid and
+// its L2 sees the same activation rows and weight columns many times.
+// Per-step pieces of the tiled kernel, force-inlined with arrays passed by
+// reference so that every operand stays in registers.
+template <int N>
+__device__ __forceinline__ void tile_load_a(u32x4 (&stage)[N], const u32x4* __restrict__ act,
+                                            const int (&a_src)[N], size_t aoff) {
+#pragma unroll
+    for (int v = 0; v < N; ++v) stage[v] = act[aoff + a_src[v]];
+}
+
+template <int N, int kThr>
+__device__ __forceinline__ void tile_store_a(u32x4* buf, const u32x4 (&stage)[N]) {
+#pragma unroll
+    for (int v = 0; v < N; ++v) buf[threadIdx.x + v * kThr] = stage[v];
+}
+
+template <bool kG128, int TN>
+__device__ __forceinline__ void tile_load_b(u32x4 (&bq)[TN], uint32_t (&pq)[TN],
+                                            const u32x4* const (&bptr)[TN],
+                                            const uint8_t* const (&pptr)[TN], int g) {
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+        bq[i] = bptr[i][(size_t)g * kWave];
+        if (kG128) pq[i] = pptr[i][g];
+    }
+}
+
+// One k-step: unpack this wave's TN weight tiles, read its TM activation
+// tiles from LDS (lw: the wave's first tile, lane offset applied) and issue
+// TM x TN x 2 matrix-core operations.
+template <bool kG128, int TM, int TN>
+__device__ __forceinline__ void tile_compute(int32x4 (&acc)[TM][TN], const u32x4* lw,
+                                             const u32x4 (&bq)[TN], const uint32_t (&pq)[TN]) {
+    int32x4 b[TN][2];
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+        GroupConst gc{0u, 0u};
+        if (kG128) gc = group_const(pq[i]);
+        unpack_lane<kG128>(bq[i], gc, b[i][0], b[i][1]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int a = 0; a < TM; ++a) {
+            const int32x4 af = __builtin_bit_cast(int32x4, lw[a * 128 + ks * 64]);
+#pragma unroll
+            for (int i = 0; i < TN; ++i) acc[a][i] = mfma16x16x64(af, b[i][ks], acc[a][i]);
+        }
+    }
+}
+
+template <bool kG128, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64) void k_gemm_tile(
+    const int8_t* __restrict__ xq, const uint16_t* __restrict__ s_x,
+    const int32_t* __restrict__ rowsum, const uint8_t* __restrict__ blob,
+    const uint16_t* __restrict__ s_c, int M, int N, int K, uint16_t* __restrict__ y,
+    int32_t* __restrict__ acc_out) {
+    constexpr int kThr = WM * WN * 64;
+    constexpr int TM = BM / WM / 16;
+    constexpr int TN = BN / WN / 16;
+    constexpr int kAVec = BM * 128 / 16;       // 16-byte vectors of A per group
+    constexpr int kAPerThr = kAVec / kThr;     // per thread
+    static_assert(kAVec % kThr == 0, "A staging must divide evenly");
+    // Two separately declared buffers, each named by fixed code (no run-time
+    // buffer index).
+    __shared__ u32x4 lds_a0[kAVec];
+    __shared__ u32x4 lds_a1[kAVec];
+
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int wm = wave / WN, wn = wave % WN;
+    const int c = lane % 16, j = lane / 16;
+    const int G = K / kGroup;
+    const int Gp = (G + 15) / 16 * 16;
+    const int U = (M + 15) / 16;
+    const int tiles = N / 16;
+    const int grid_m = (M + BM - 1) / BM, grid_n = (N + BN - 1) / BN;
+
+    // Block renumbering: contiguous range per XCD, then groups of 4 block rows.
+    int pid = blockIdx.x;
+    const int nblocks = grid_m * grid_n;
+    if (nblocks % 8 == 0) pid = (pid % 8) * (nblocks / 8) + pid / 8;
+    constexpr int kGroupM = 4;
+    const int per_group = kGroupM * grid_n;
+    const int first_m = (pid / per_group) * kGroupM;
+    const int gsz = min(grid_m - first_m, kGroupM);
+    const int bm = first_m + (pid % per_group) % gsz;
+    const int bn = (pid % per_group) / gsz;
+
+    // A staging: vector i of the block's run goes to LDS slot i; thread t
+    // moves vectors t, t + kThr, ...
+    const int u0 = bm * (BM / 16);
+    int a_src[kAPerThr];
+#pragma unroll
+    for (int v = 0; v < kAPerThr; ++v) {
+        const int idx = threadIdx.x + v * kThr;
+        const int u = min(u0 + idx / 128, U - 1);      // clamp past the last row tile
+        a_src[v] = u * 128 + idx % 128;
+    }
+    const u32x4* act = reinterpret_cast<const u32x4*>(xq);
+    const size_t a_stride = (size_t)U * 128;  // vectors per group
+
+    // Weight tiles of this wave (clamped for the ragged n tail).
+    const u32x4* bptr[TN];
+    const uint8_t* pptr[TN];
+    const uint8_t* params = blob + (size_t)N * K / 2;
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+        const int t = min(bn * (BN / 16) + wn * TN + i, tiles - 1);
+        bptr[i] = reinterpret_cast<const u32x4*>(blob) + (size_t)t * G * kWave + lane;
+        pptr[i] = params + (size_t)(16 * t + c) * Gp;
+    }
+
+    int32x4 acc[TM][TN];
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TN; ++b) acc[a][b] = int32x4{0, 0, 0, 0};
+
+    u32x4 stage[kAPerThr];
+    u32x4 b0q[TN], b1q[TN];
+    uint32_t p0q[TN], p1q[TN];
+    const u32x4* lw0 = lds_a0 + (size_t)(wm * TM) * 128 + lane;
+    const u32x4* lw1 = lds_a1 + (size_t)(wm * TM) * 128 + lane;
+
+    // Prologue: group 0 in buffer 0, group 1 in flight to the staging
+    // registers, weights of group 0 in flight.
+    tile_load_a(stage, act, a_src, 0);
+    tile_store_a<kAPerThr, kThr>(lds_a0, stage);
+    tile_load_a(stage, act, a_src, (size_t)min(1, G - 1) * a_stride);
+    tile_load_b<kG128, TN>(b0q, p0q, bptr, pptr, 0);
+    __syncthreads();
+
+    // Step h: publish the staged activations of group h+1 into the idle
+    // buffer, issue the loads of group h+2 (activations) and h+1 (weights),
+    // then run step h on the other buffer. Each load is first used a full step
+    // later, so it is neither sunk to its use nor waited for early. Two steps
+    // per iteration give each access a fixed buffer and register set. Group
+    // indices are clamped at the end (the extra loads are never used).
+    for (int h = 0; h < G; h += 2) {
+        tile_store_a<kAPerThr, kThr>(lds_a1, stage);
+        tile_load_a(stage, act, a_src, (size_t)min(h + 2, G - 1) * a_stride);
+        tile_load_b<kG128, TN>(b1q, p1q, bptr, pptr, min(h + 1, G - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        tile_compute<kG128, TM, TN>(acc, lw0, b0q, p0q);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        if (h + 1 < G) {
+            tile_store_a<kAPerThr, kThr>(lds_a0, stage);
+            tile_load_a(stage, act, a_src, (size_t)min(h + 3, G - 1) * a_stride);
+            tile_load_b<kG128, TN>(b0q, p0q, bptr, pptr, min(h + 2, G - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            tile_compute<kG128, TM, TN>(acc, lw1, b1q, p1q);
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+        }
+    }
+
+    // Epilogue.
+    const uint8_t* pc_z = params;
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+        const int t = bn * (BN / 16) + wn * TN + i;
+        if (t >= tiles) continue;
+        const int n = 16 * t + c;
+        const float sc = h2f(s_c[n]);
+        const int zpc = kG128 ? 0 : (int)pc_z[n];
+#pragma unroll
+        for (int a = 0; a < TM; ++a) {
+            const int m_first = bm * BM + (wm * TM + a) * 16 + 4 * j;
+            store_outputs<kG128>(acc[a][i], m_first, n, M, N, s_x, rowsum, sc, zpc, y, acc_out);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Plans.
 
 constexpr int kCUs = 256;
 
 struct Plan {
-    int kind = 0;  // 0: simple, 1: decode
+    int kind = 0;  // 0: simple, 1: decode, 2: tiled
     int mb = 0, nt = 0, s = 1, d = 1, w = 4;
+    int bm = 0, bn = 0;
     int64_t nblk = 0;
     int64_t ws_bytes = 0;
 };
@@ -332,9 +524,27 @@ constexpr bool decode_shape_ok(int mb, int nt, int w) {
 // Splitting K across workgroups never paid for its partial sums and fences on
 // these shapes, so the plan keeps the whole K in one workgroup (the split
 // machinery stays available to plans that are given a workspace).
+#ifdef QOQ_TUNING
+int g_force_bm = 0, g_force_bn = 0;
+#endif
+
 Plan plan_gemm(int64_t M, int64_t N, int64_t K, bool /*have_ws*/) {
     Plan p;
-    if (M > 64) return p;
+    if (M > 64) {
+        p.kind = 2;
+        // Largest block whose grid still covers the compute units.
+        const int64_t gm256 = (M + 255) / 256, gm128 = (M + 127) / 128;
+        const int64_t gn256 = (N + 255) / 256, gn128 = (N + 127) / 128;
+        if (gm256 * gn256 >= kCUs) { p.bm = 256; p.bn = 256; }
+        else if (gm128 * gn256 >= kCUs) { p.bm = 128; p.bn = 256; }
+        else { p.bm = 128; p.bn = 128; }
+        (void)gn128;
+#ifdef QOQ_TUNING
+        if (g_force_bm) p.bm = g_force_bm;
+        if (g_force_bn) p.bn = g_force_bn;
+#endif
+        return p;
+    }
     p.kind = 1;
     p.mb = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
     const int64_t tiles = N / 16;
@@ -425,6 +635,22 @@ void launch_decode(const Plan& p, const DecodeArgs& a) {
 
 }  // namespace
 
+template <bool kG128, int BM, int BN, int WM, int WN>
+void launch_tile_t(const DecodeArgs& a) {
+    const unsigned blocks = (unsigned)(((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN));
+    hipLaunchKernelGGL((k_gemm_tile<kG128, BM, BN, WM, WN>), dim3(blocks), dim3(WM * WN * 64), 0,
+                       a.stream, a.xq, a.s_x, a.rowsum, a.blob, a.s_c, a.M, a.N, a.K, a.y,
+                       a.acc_out);
+}
+
+template <bool kG128>
+void launch_tile(const Plan& p, const DecodeArgs& a) {
+    if (p.bm == 256 && p.bn == 256) launch_tile_t<kG128, 256, 256, 2, 4>(a);
+    else if (p.bm == 128 && p.bn == 256) launch_tile_t<kG128, 128, 256, 2, 4>(a);
+    else if (p.bm == 256 && p.bn == 128) launch_tile_t<kG128, 256, 128, 4, 2>(a);
+    else launch_tile_t<kG128, 128, 128, 2, 2>(a);
+}
+
 int64_t gemm_workspace_bytes(int /*mode*/, int64_t M, int64_t N, int64_t K) {
     return plan_gemm(M, N, K, true).ws_bytes;
 }
@@ -433,12 +659,19 @@ void launch_gemm(int mode, const int8_t* xq, const uint16_t* s_x, const int32_t*
                  const uint8_t* blob, const uint16_t* s_c, int64_t M, int64_t N, int64_t K,
                  uint16_t* y, int32_t* acc_out, void* ws, hipStream_t stream) {
     const Plan p = plan_gemm(M, N, K, ws != nullptr);
+    const DecodeArgs a{xq, s_x, rowsum, blob, s_c, (int)M, (int)N, (int)K, y, acc_out, ws, stream};
     if (p.kind == 1) {
-        const DecodeArgs a{xq, s_x, rowsum, blob, s_c, (int)M, (int)N, (int)K, y, acc_out, ws, stream};
         if (mode == 0)
             launch_decode<true>(p, a);
         else
             launch_decode<false>(p, a);
+        return;
+    }
+    if (p.kind == 2) {
+        if (mode == 0)
+            launch_tile<true>(p, a);
+        else
+            launch_tile<false>(p, a);
         return;
     }
     const dim3 grid((unsigned)((N / 16 + 3) / 4), (unsigned)((M + 63) / 64));
@@ -451,6 +684,10 @@ void launch_gemm(int mode, const int8_t* xq, const uint16_t* s_x, const int32_t*
 }
 
 #ifdef QOQ_TUNING
+extern "C" void qoq_tuning_force_tile(int bm, int bn) {
+    g_force_bm = bm;
+    g_force_bn = bn;
+}
 extern "C" void qoq_tuning_force_decode(int nt, int s, int d, int w) {
     g_force_nt = nt;
     g_force_s = s;

@@ -9,6 +9,7 @@
 namespace qoq {
 
 typedef int int32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
@@ -90,7 +91,7 @@ __device__ __forceinline__ uint32_t unpack4_g128(uint32_t codes, GroupConst gc) 
 // Packed 16 bytes of one lane (32 codes) -> the two MFMA B operands (k-steps
 // s = 0 and 1) of 16 INT8 values each, in the byte order of the A operand.
 template <bool kG128>
-__device__ __forceinline__ void unpack_lane(uint4 p, GroupConst gc, int32x4& b0, int32x4& b1) {
+__device__ __forceinline__ void unpack_lane(u32x4 p, GroupConst gc, int32x4& b0, int32x4& b1) {
     uint32_t a0 = p.x & 0x0F0F0F0Fu, a1 = (p.x >> 4) & 0x0F0F0F0Fu;
     uint32_t a2 = p.y & 0x0F0F0F0Fu, a3 = (p.y >> 4) & 0x0F0F0F0Fu;
     uint32_t c0 = p.z & 0x0F0F0F0Fu, c1 = (p.z >> 4) & 0x0F0F0F0Fu;
