@@ -47,6 +47,15 @@ def parse_args(argv=None):
                    help="target host time of the oracle's CPU-baseline sample (0: skip)")
     p.add_argument("--kernel-launches", type=int, default=400,
                    help="launches per kernel in the per-kernel timing pass")
+    p.add_argument("--layer", default=None,
+                   help="layer of a multi-layer workload to time (default: the workload's only layer)")
+    p.add_argument("--profile-launches", type=int, default=0,
+                   help="instead of timing: launch each kernel of one step this many times on "
+                        "cold caches, then a 256 MiB copy as many times (for counter runs)")
+    p.add_argument("--pmc-summary", nargs="+", default=None, metavar="DIR",
+                   help="instead of timing: read rocprofv3 counter CSVs (FETCH_SIZE run, "
+                        "WRITE_SIZE run) of a --profile-launches run and write the traffic "
+                        "summary for this workload under profiles/")
     return p.parse_args(argv)
 
 
@@ -68,6 +77,100 @@ def act_bytes(M: int, K: int) -> int:
     return 2 * M * K + M * K + 2 * M + 4 * M
 
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+# Sources whose kernels the traffic figures describe; a stored figure is used
+# only while these files are unchanged.
+KERNEL_SOURCES = ("quantized_gemm_qoq_amd/csrc/gemm.hip", "quantized_gemm_qoq_amd/csrc/qoq_device.hpp",
+                  "quantized_gemm_qoq_amd/csrc/quantize.hip")
+CALIBRATION_MIB = 256
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_path(workload: str, layer: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}_{layer}.json")
+
+
+def stored_traffic(workload: str, layer: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None if there is none or the kernels changed since it was taken."""
+    path = traffic_path(workload, layer)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    k = d.get("kernels", {}).get(kernel)
+    return None if k is None else k["hbm_bytes"]
+
+
+def pmc_summary(args, wl, layer) -> int:
+    """Turn the counter CSVs of a --profile-launches run into the per-launch HBM
+    traffic of each kernel, calibrated by the copy: FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch) are each scaled so that the copy of CALIBRATION_MIB reads
+    and writes exactly that many bytes."""
+    import csv
+    import glob
+    import statistics
+
+    vals = {}
+    for d in args.pmc_summary:
+        for f in glob.glob(os.path.join(d, "**", "*_counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    name = r["Kernel_Name"]
+                    if "k_gemm" in name:
+                        mode = "g128" if ("<true" in name or "ILb1E" in name) else "per_channel"
+                        key = "w4a8_gemm_" + mode
+                    elif "k_quantize_act" in name:
+                        key = "quantize_act"
+                    elif "copyBuffer" in name:
+                        key = "copy"
+                    else:
+                        continue
+                    vals.setdefault((key, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    med = {k: statistics.median(v) for k, v in vals.items()}
+    cal = CALIBRATION_MIB * 1024.0
+    fs = cal / med[("copy", "FETCH_SIZE")]
+    ws = cal / med[("copy", "WRITE_SIZE")]
+    out = {"workload": wl.name, "layer": layer.name, "M": layer.M, "K": layer.K, "N": layer.N,
+           "source_hash": kernel_source_hash(), "source_files": list(KERNEL_SOURCES),
+           "calibration": {"copy_MiB": CALIBRATION_MIB,
+                           "FETCH_SIZE_KiB": med[("copy", "FETCH_SIZE")],
+                           "WRITE_SIZE_KiB": med[("copy", "WRITE_SIZE")],
+                           "fetch_scale": round(fs, 4), "write_scale": round(ws, 4)},
+           "commands": [
+               f"rocprofv3 --kernel-trace --pmc FETCH_SIZE --output-format csv -d <dir1> -- "
+               f"python3 bench.py --workload {wl.name} --layer {layer.name} --profile-launches 3",
+               f"rocprofv3 --kernel-trace --pmc WRITE_SIZE --output-format csv -d <dir2> -- "
+               f"python3 bench.py --workload {wl.name} --layer {layer.name} --profile-launches 3",
+               f"python3 bench.py --workload {wl.name} --layer {layer.name} --pmc-summary <dir1> <dir2>"],
+           "kernels": {}}
+    for key in sorted({k for k, _ in med if k != "copy"}):
+        fk, wk = med.get((key, "FETCH_SIZE")), med.get((key, "WRITE_SIZE"))
+        if fk is None or wk is None:
+            continue
+        fb, wb = fk * 1024 * fs, wk * 1024 * ws
+        out["kernels"][key] = {"FETCH_SIZE_KiB": fk, "WRITE_SIZE_KiB": wk,
+                               "hbm_read_bytes": round(fb), "hbm_write_bytes": round(wb),
+                               "hbm_bytes": round(fb + wb)}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(traffic_path(wl.name, layer.name), "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out["kernels"]))
+    return 0
+
+
 def main(argv=None) -> int:
     args = parse_args(argv)
     if args.gpus != 1:
@@ -78,23 +181,31 @@ def main(argv=None) -> int:
         print("bench.py: --steps must be >= 1", file=sys.stderr)
         return 2
 
+    from quantized_gemm_qoq_amd import workloads
+
+    wl = workloads.WORKLOADS[args.workload]
+    if args.layer is None and len(wl.layers) != 1:
+        layer_list = ", ".join(l.name for l in wl.layers)
+        print(f"bench.py: workload {wl.name} has several layers ({layer_list}); "
+              "name one with --layer", file=sys.stderr)
+        return 2
+    layers = [l for l in wl.layers if args.layer in (None, l.name)]
+    if not layers:
+        print(f"bench.py: no layer {args.layer} in workload {wl.name}", file=sys.stderr)
+        return 2
+    layer = layers[0]
+    if args.pmc_summary:
+        return pmc_summary(args, wl, layer)
+
     import torch
 
     import quantized_gemm_qoq_amd as qoq
-    from quantized_gemm_qoq_amd import workloads
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 3
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    wl = workloads.WORKLOADS[args.workload]
-    if len(wl.layers) != 1:
-        layer_list = ", ".join(l.name for l in wl.layers)
-        print(f"bench.py: workload {wl.name} has several layers ({layer_list}); "
-              "the benchmark times single-layer workloads", file=sys.stderr)
-        return 2
-    layer = wl.layers[0]
     M, N, K = layer.M, layer.N, layer.K
     modes = [qoq.MODES[m] for m in wl.modes]
 
@@ -113,6 +224,9 @@ def main(argv=None) -> int:
         offline[wl.modes[modes.index(mode)]] = round((time.perf_counter() - t0) * 1e3, 3)
         packed[mode] = (blob, s_c)
         del q, s_g, z
+
+    if args.profile_launches > 0:
+        return profile_launches(args, qoq, torch, dev, x_dev, packed, modes, M, N, K)
 
     # ---- rotating buffer sets
     per_set = 2 * M * K + M * K + 8 * M
@@ -172,7 +286,19 @@ def main(argv=None) -> int:
 
     step_bytes = act_bytes(M, K) + sum(gemm_bytes(m, M, N, K) for m in modes)
     step_ops = sum(2 * M * N * K for _ in modes)
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    # Decode M is bound by HBM (bytes), large M by the matrix cores (ops); the
+    # ridge of 5.0 POPS over 8 TB/s sits near M = 160 for these shapes.
+    bound = "hbm" if M <= 162 else "mfma"
+    if bound == "hbm":
+        metric = ("W4A8 GEMM HBM GB/s (decode M) on the per-call path: per-token INT8 "
+                  "quantization + W4A8 GEMM")
+        unit = "GB/s"
+        value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    else:
+        metric = ("W4A8 GEMM TOPS (large M) on the per-call path: per-token INT8 "
+                  "quantization + W4A8 GEMM")
+        unit = "TOPS"
+        value = step_ops / (ms_per_step * 1e-3) / 1e12
 
     # ---- per-kernel timing: HIP events on the stream the kernels run on,
     # bracketing graph replays of back-to-back launches of one kernel over the
@@ -212,26 +338,25 @@ def main(argv=None) -> int:
     dominant = max((k for k in kernels if k.startswith("w4a8_gemm")),
                    key=lambda k: kernels[k]["avg_us"])
     dk = kernels[dominant]
-    bound = "hbm" if M <= 162 else "mfma"
+    traffic = stored_traffic(wl.name, layer.name, dominant)
     if bound == "hbm":
         roofline = {"bound": "hbm", "achieved": dk["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(dk["GB/s"] / HBM_PEAK_GBS, 4), "traffic": None,
-                    "kernel": dominant}
+                    "frac": round(dk["GB/s"] / HBM_PEAK_GBS, 4), "traffic": traffic,
+                    "kernel": dominant, "algorithmic_bytes": dk["bytes"]}
     else:
         roofline = {"bound": "mfma", "achieved": dk["TOPS"], "peak": INT8_PEAK_TOPS,
                     "unit": "TOPS", "frac": round(dk["TOPS"] / INT8_PEAK_TOPS, 4),
-                    "traffic": None, "kernel": dominant}
+                    "traffic": traffic, "kernel": dominant, "algorithmic_bytes": dk["bytes"]}
 
     # ---- CPU baseline: the oracle on the host cores, same step, bounded sample
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = cpu_baseline(layer, modes, sets[0], step_bytes, args.cpu_seconds)
+        cpu = cpu_baseline(layer, modes, sets[0], bound, args.cpu_seconds)
 
     out = {
-        "metric": "W4A8 GEMM HBM GB/s (decode M) on the per-call path: per-token INT8 "
-                  "quantization + W4A8 GEMM",
-        "value": round(value, 1),
-        "unit": "GB/s",
+        "metric": metric,
+        "value": round(value, 2 if bound == "mfma" else 1),
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -240,8 +365,9 @@ def main(argv=None) -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int8 x uint4 -> int32 (fp16 in/out)",
-        "data": "synthetic (seeded N(0,0.02) weights with 0.5% x10 input channels, N(0,1) activations)",
-        "config": {"workload": wl.name, "description": wl.description, "M": M, "K": K, "N": N,
+        "data": describe_data(layer),
+        "config": {"workload": wl.name, "layer": layer.name, "description": wl.description,
+                   "M": M, "K": K, "N": N,
                    "modes": list(wl.modes), "parallelism": "single GPU",
                    "rotating_copies": R, "graph_replay": True},
         "step_bytes": step_bytes,
@@ -255,10 +381,50 @@ def main(argv=None) -> int:
     return 0
 
 
-def cpu_baseline(layer, modes, s, step_bytes, seconds):
-    """Time the oracle (the plain C reference, as it stands) on the host over
-    whole steps of the same workload until `seconds` have passed (at least one
-    step), and spot-check the GPU's last outputs of this buffer set against it."""
+def describe_data(layer) -> str:
+    w = f"W ~ N(0,{layer.w_sigma})"
+    if layer.w_outliers:
+        w += f" with {layer.w_outliers} input channels x{layer.w_outlier_scale:g}"
+    x = "X ~ N(0,1)" if layer.x_kind == "normal" else "X = SiLU(A)*B, A,B ~ N(0,1)"
+    if layer.x_outliers:
+        x += f" with {layer.x_outliers} channels x{layer.x_outlier_scale:g}"
+    return f"synthetic, seeded ({layer.seed}): {w}, {x}; FP16"
+
+
+def profile_launches(args, qoq, torch, dev, x_dev, packed, modes, M, N, K) -> int:
+    """Launch every kernel of one step `--profile-launches` times, each on cold
+    caches (a 512 MiB fill in between evicts the L2s and the Infinity Cache),
+    then the calibration copy of CALIBRATION_MIB as many times. Nothing is
+    timed: this is the program that counter runs profile."""
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    xq = torch.empty((qoq.qoq_act_bytes(M, K),), dtype=torch.int8, device=dev)
+    s_x = torch.empty((M,), dtype=torch.float16, device=dev)
+    rowsum = torch.empty((M,), dtype=torch.int32, device=dev)
+    y = torch.empty((M, N), dtype=torch.float16, device=dev)
+    for i in range(args.profile_launches):
+        flush.fill_(i & 0xFF)
+        qoq.qoq_quantize_act(x_dev, xq, s_x, rowsum)
+        for mode in modes:
+            blob, s_c = packed[mode]
+            flush.fill_(i & 0xFF)
+            qoq.qoq_w4a8_gemm(mode, xq, s_x, rowsum if mode == qoq.MODE_PER_CHANNEL else None,
+                              blob, s_c, N, y=y)
+    src = torch.full((CALIBRATION_MIB << 20,), 1, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for i in range(args.profile_launches):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_launches": args.profile_launches, "M": M, "N": N, "K": K,
+                      "modes": [int(m) for m in modes], "calibration_MiB": CALIBRATION_MIB}))
+    return 0
+
+
+def cpu_baseline(layer, modes, s, bound, seconds):
+    """Time the oracle (the plain C reference, as it stands) on the host cores
+    over the same step on the first `rows` token rows of the workload, with
+    `rows` chosen so that the sample takes about `seconds` (all M rows where
+    that fits), and spot-check the GPU's outputs of this buffer set against it.
+    The rate is the sample's own algorithmic bytes (or ops) over its time."""
     import numpy as np
     import torch
 
@@ -266,34 +432,51 @@ def cpu_baseline(layer, modes, s, step_bytes, seconds):
     from quantized_gemm_qoq_amd import workloads
 
     x16, w16 = workloads.generate(layer)
-    xb = x16.numpy().view(np.uint16)
+    M, N, K = layer.M, layer.N, layer.K
+    xb_all = x16.numpy().view(np.uint16)
     wb = w16.numpy().view(np.uint16)
-    prepared = {}
-    for mode in modes:
-        wq = oracle.quantize_weights(mode, wb)
-        prepared[mode] = wq
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        xq, s_x, rowsum = oracle.quantize_act(xb)
+    prepared = {mode: oracle.quantize_weights(mode, wb) for mode in modes}
+
+    def one_step(rows):
+        xq, s_x, _ = oracle.quantize_act(np.ascontiguousarray(xb_all[:rows]))
         ys = {}
         for mode in modes:
             wq = prepared[mode]
             acc = oracle.gemm(mode, xq, wq["q"], wq["s_g"], wq["z"])
             ys[mode] = oracle.epilogue(acc, s_x, wq["s_c"])
+        return ys
+
+    # Size the sample: one probe step on a few rows gives the cost per row.
+    probe = min(M, 4)
+    t0 = time.perf_counter()
+    one_step(probe)
+    per_row = (time.perf_counter() - t0) / probe
+    rows = int(max(1, min(M, seconds / 2 / max(per_row, 1e-9))))
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        ys = one_step(rows)
         reps += 1
         if time.perf_counter() - t0 >= seconds:
             break
     dt = (time.perf_counter() - t0) / reps
     ok = True
     for mode in modes:
-        yg = s[("y", mode)].cpu().view(torch.int16).numpy().view(np.float16).astype(np.float64)
+        yg = s[("y", mode)][:rows].cpu().view(torch.int16).numpy().view(np.float16).astype(np.float64)
         ok &= bool(np.abs(yg - ys[mode]).max() <= 1e-3 * np.abs(ys[mode]).max())
-    return {"value": round(step_bytes / dt / 1e9, 3), "unit": "GB/s",
+    if bound == "hbm":
+        work = act_bytes(rows, K) + sum(gemm_bytes(m, rows, N, K) for m in modes)
+        value, unit = work / dt / 1e9, "GB/s"
+    else:
+        work = sum(2 * rows * N * K for _ in modes)
+        value, unit = work / dt / 1e12, "TOPS"
+    return {"value": round(value, 4), "unit": unit,
             "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{reps} whole step(s) of the same workload (per-token quantization + "
-                      f"{len(modes)} GEMM(s) + epilogue), {dt * 1e3:.1f} ms each",
-            "ms_per_step": round(dt * 1e3, 2),
+            "sample": f"{reps} step(s) on the first {rows} of {M} token rows (per-token "
+                      f"quantization + {len(modes)} GEMM(s) + epilogue over all N={N} "
+                      f"channels), {dt * 1e3:.1f} ms each; rate = the sample's algorithmic "
+                      f"{'bytes' if bound == 'hbm' else 'ops'} over its time",
+            "ms_per_sample_step": round(dt * 1e3, 2),
             "gpu_matches_oracle": ok}
 
 

@@ -358,7 +358,7 @@ __device__ __forceinline__ void tile_compute(int32x4 (&acc)[TM][TN], const u32x4
 }
 
 template <bool kG128, int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(WM * WN * 64) void k_gemm_tile(
+__global__ __launch_bounds__(WM * WN * 64, 2) void k_gemm_tile(
     const int8_t* __restrict__ xq, const uint16_t* __restrict__ s_x,
     const int32_t* __restrict__ rowsum, const uint8_t* __restrict__ blob,
     const uint16_t* __restrict__ s_c, int M, int N, int K, uint16_t* __restrict__ y,
@@ -443,26 +443,29 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_tile(
     // buffer, issue the loads of group h+2 (activations) and h+1 (weights),
     // then run step h on the other buffer. Each load is first used a full step
     // later, so it is neither sunk to its use nor waited for early. Two steps
-    // per iteration give each access a fixed buffer and register set. Group
-    // indices are clamped at the end (the extra loads are never used).
-    for (int h = 0; h < G; h += 2) {
+    // per iteration give each access a fixed buffer and register set; both
+    // halves are unconditional (a branch around the second half would let the
+    // compiler sink the first half's weight loads into it), and an odd group
+    // count finishes with one more step on buffer 0. Group indices of the
+    // look-ahead loads are clamped at the end (those loads are never used).
+    int h = 0;
+    for (; h + 1 < G; h += 2) {
         tile_store_a<kAPerThr, kThr>(lds_a1, stage);
         tile_load_a(stage, act, a_src, (size_t)min(h + 2, G - 1) * a_stride);
-        tile_load_b<kG128, TN>(b1q, p1q, bptr, pptr, min(h + 1, G - 1));
+        tile_load_b<kG128, TN>(b1q, p1q, bptr, pptr, h + 1);
         __builtin_amdgcn_sched_barrier(0);
         tile_compute<kG128, TM, TN>(acc, lw0, b0q, p0q);
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
-        if (h + 1 < G) {
-            tile_store_a<kAPerThr, kThr>(lds_a0, stage);
-            tile_load_a(stage, act, a_src, (size_t)min(h + 3, G - 1) * a_stride);
-            tile_load_b<kG128, TN>(b0q, p0q, bptr, pptr, min(h + 2, G - 1));
-            __builtin_amdgcn_sched_barrier(0);
-            tile_compute<kG128, TM, TN>(acc, lw1, b1q, p1q);
-            __builtin_amdgcn_sched_barrier(0);
-            __syncthreads();
-        }
+        tile_store_a<kAPerThr, kThr>(lds_a0, stage);
+        tile_load_a(stage, act, a_src, (size_t)min(h + 3, G - 1) * a_stride);
+        tile_load_b<kG128, TN>(b0q, p0q, bptr, pptr, min(h + 2, G - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        tile_compute<kG128, TM, TN>(acc, lw1, b1q, p1q);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
     }
+    if (h < G) tile_compute<kG128, TM, TN>(acc, lw0, b0q, p0q);
 
     // Epilogue.
     const uint8_t* pc_z = params;
@@ -482,12 +485,230 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_tile(
 }
 
 // ---------------------------------------------------------------------------
+// Wide-wave tiled kernel (M > 64). The waves of a workgroup sit side by side
+// in N and each one spans all BM rows of the block (TM = BM/16 row tiles, TN
+// channel tiles), so each weight tile is loaded and unpacked by exactly one
+// wave and feeds TM x 2 matrix-core operations per group: the unpack work per
+// operation falls with BM, which is what keeps the vector ALU off the critical
+// path at the gfx950 INT8 matrix-core rate. With BM = 256 the accumulators take
+// 256 registers per lane (one wave per SIMD, accumulators in the AccVGPRs).
+//   - Activations: one contiguous run of BM/16 packed 2 KB tiles per group,
+//     staged through registers into one of two LDS buffers.
+//   - Weights: one 16-byte buffer load per lane per tile straight into
+//     registers; group parameter bytes map to the packed-multiply constants
+//     through a 256-entry LDS table.
+//   - Every address is a per-lane 32-bit offset fixed at the start plus a
+//     wave-uniform per-group offset (buffer loads), so the loop does no
+//     address arithmetic.
+// The plan selects this kernel only when every byte offset fits in 32 bits.
+constexpr int kBufferConfig = 0x00020000;  // gfx9 buffer resource word 3: 32-bit dwords
+
+template <int N>
+__device__ __forceinline__ void wide_load_a(u32x4 (&stage)[N], __amdgpu_buffer_rsrc_t ra,
+                                            const uint32_t (&a_off)[N], uint32_t soff) {
+#pragma unroll
+    for (int v = 0; v < N; ++v)
+        stage[v] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)a_off[v], (int)soff, 0);
+}
+
+template <bool kG128, int TN>
+__device__ __forceinline__ void wide_load_b(u32x4 (&bq)[TN], uint32_t (&pq)[TN],
+                                            __amdgpu_buffer_rsrc_t rb, __amdgpu_buffer_rsrc_t rp,
+                                            const uint32_t (&b_off)[TN],
+                                            const uint32_t (&p_off)[TN], int g) {
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+        bq[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)b_off[i], g * 1024, 0);
+        if (kG128) pq[i] = __builtin_amdgcn_raw_buffer_load_b8(rp, (int)p_off[i], g, 0);
+    }
+}
+
+// One group on one wave: unpack the TN weight tiles (both k-steps) and run the
+// TM x TN x 2 matrix-core operations, reading each activation tile from LDS
+// just ahead of its use. The group pattern at the end asks the scheduler to
+// interleave the k-step-1 unpack and the LDS reads with the k-step-0
+// matrix-core operations.
+template <bool kG128, int TM, int TN>
+__device__ __forceinline__ void wide_compute(int32x4 (&acc)[TM][TN], const u32x4* lw,
+                                             const u32x4 (&bq)[TN], const uint32_t (&pq)[TN],
+                                             const uint32_t* lut) {
+    uint32_t gw[TN];
+#pragma unroll
+    for (int i = 0; i < TN; ++i) gw[i] = kG128 ? lut[pq[i] & 0xFFu] : 0u;
+    int32x4 b0[TN], b1[TN];
+#pragma unroll
+    for (int i = 0; i < TN; ++i) b0[i] = unpack_half<kG128, 0>(bq[i], gw[i]);
+#pragma unroll
+    for (int i = 0; i < TN; ++i) b1[i] = unpack_half<kG128, 1>(bq[i], gw[i]);
+#pragma unroll
+    for (int a = 0; a < TM; ++a) {
+        const int32x4 af = __builtin_bit_cast(int32x4, lw[a * 128]);
+#pragma unroll
+        for (int i = 0; i < TN; ++i) acc[a][i] = mfma16x16x64(af, b0[i], acc[a][i]);
+    }
+#pragma unroll
+    for (int a = 0; a < TM; ++a) {
+        const int32x4 af = __builtin_bit_cast(int32x4, lw[a * 128 + 64]);
+#pragma unroll
+        for (int i = 0; i < TN; ++i) acc[a][i] = mfma16x16x64(af, b1[i], acc[a][i]);
+    }
+    // Scheduling pattern (masks: 0x2 VALU, 0x8 MFMA, 0x100 LDS read).
+    constexpr int kUnpackHalf = (kG128 ? 14 : 6) * TN;  // VALU per k-step unpack
+    constexpr int kValuPerRow = (kUnpackHalf + TM - 1) / TM;
+    if (kG128) {
+        __builtin_amdgcn_sched_group_barrier(0x002, TN, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, TN, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x002, kUnpackHalf, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int a = 0; a < TM; ++a) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kValuPerRow, 0);
+    }
+#pragma unroll
+    for (int a = 0; a < TM; ++a) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);
+    }
+}
+
+template <bool kG128, int BM, int BN, int WN>
+__global__ __launch_bounds__(WN * 64, 2) void k_gemm_wide(
+    const int8_t* __restrict__ xq, const uint16_t* __restrict__ s_x,
+    const int32_t* __restrict__ rowsum, const uint8_t* __restrict__ blob,
+    const uint16_t* __restrict__ s_c, int M, int N, int K, uint16_t* __restrict__ y,
+    int32_t* __restrict__ acc_out) {
+    constexpr int kThr = WN * 64;
+    constexpr int TM = BM / 16;
+    constexpr int TN = BN / WN / 16;
+    constexpr int kAVec = BM * 128 / 16;   // 16-byte vectors of A per group
+    constexpr int kAPerThr = kAVec / kThr;
+    static_assert(kAVec % kThr == 0, "A staging must divide evenly");
+    __shared__ u32x4 lds_a0[kAVec];
+    __shared__ u32x4 lds_a1[kAVec];
+    __shared__ uint32_t lut[256];
+
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int c = lane % 16, j = lane / 16;
+    const int G = K / kGroup;
+    const int Gp = (G + 15) / 16 * 16;
+    const int U = (M + 15) / 16;
+    const int tiles = N / 16;
+    const int grid_m = (M + BM - 1) / BM, grid_n = (N + BN - 1) / BN;
+
+    // Block renumbering: contiguous range per XCD, then groups of 4 block rows.
+    int pid = blockIdx.x;
+    const int nblocks = grid_m * grid_n;
+    if (nblocks % 8 == 0) pid = (pid % 8) * (nblocks / 8) + pid / 8;
+    constexpr int kGroupM = 4;
+    const int per_group = kGroupM * grid_n;
+    const int first_m = (pid / per_group) * kGroupM;
+    const int gsz = min(grid_m - first_m, kGroupM);
+    const int bm = first_m + (pid % per_group) % gsz;
+    const int bn = (pid % per_group) / gsz;
+
+    if (kG128)
+        for (int i = threadIdx.x; i < 256; i += kThr) lut[i] = group_word((uint32_t)i);
+
+    const size_t code_bytes = (size_t)N * K / 2;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)xq, (short)0, (int)((uint32_t)G * (uint32_t)U * 2048u), kBufferConfig);
+    const __amdgpu_buffer_rsrc_t rb =
+        __builtin_amdgcn_make_buffer_rsrc((void*)blob, (short)0, (int)(uint32_t)code_bytes, kBufferConfig);
+    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(blob + code_bytes), (short)0, (int)(uint32_t)(kG128 ? N * Gp : N), kBufferConfig);
+
+    // Activation vector idx = threadIdx.x + v * kThr of the block's run goes to
+    // LDS slot idx (row tiles past the last one are clamped; their rows are
+    // never stored).
+    const int u0 = bm * (BM / 16);
+    uint32_t a_off[kAPerThr];
+#pragma unroll
+    for (int v = 0; v < kAPerThr; ++v) {
+        const int idx = threadIdx.x + v * kThr;
+        const int u = min(u0 + idx / 128, U - 1);
+        a_off[v] = (uint32_t)(u * 128 + idx % 128) * 16u;
+    }
+    const uint32_t a_step = (uint32_t)U * 2048u;  // bytes per group
+
+    // Weight tiles of this wave (clamped for the ragged n tail).
+    uint32_t b_off[TN], p_off[TN];
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+        const int t = min(bn * (BN / 16) + wave * TN + i, tiles - 1);
+        b_off[i] = ((uint32_t)t * (uint32_t)G * 64u + (uint32_t)lane) * 16u;
+        p_off[i] = (uint32_t)(16 * t + c) * (uint32_t)Gp;
+    }
+
+    int32x4 acc[TM][TN];
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TN; ++b) acc[a][b] = int32x4{0, 0, 0, 0};
+
+    u32x4 stage[kAPerThr];
+    u32x4 b0q[TN], b1q[TN];
+    uint32_t p0q[TN], p1q[TN];
+    const u32x4* lw0 = lds_a0 + lane;
+    const u32x4* lw1 = lds_a1 + lane;
+
+    // Prologue: group 0 in buffer 0, group 1 in flight to the staging
+    // registers, weights of group 0 in flight.
+    wide_load_a(stage, ra, a_off, 0u);
+    tile_store_a<kAPerThr, kThr>(lds_a0, stage);
+    wide_load_a(stage, ra, a_off, (uint32_t)min(1, G - 1) * a_step);
+    wide_load_b<kG128, TN>(b0q, p0q, rb, rp, b_off, p_off, 0);
+    __syncthreads();
+
+    // Same two-buffer pipeline as the 16-row-wave kernel above: in step h the
+    // staged activations of group h+1 go to the idle buffer, the loads of
+    // groups h+2 (activations) and h+1 (weights) are issued, then group h runs.
+    int h = 0;
+    for (; h + 1 < G; h += 2) {
+        tile_store_a<kAPerThr, kThr>(lds_a1, stage);
+        wide_load_a(stage, ra, a_off, (uint32_t)min(h + 2, G - 1) * a_step);
+        wide_load_b<kG128, TN>(b1q, p1q, rb, rp, b_off, p_off, h + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        wide_compute<kG128, TM, TN>(acc, lw0, b0q, p0q, lut);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        tile_store_a<kAPerThr, kThr>(lds_a0, stage);
+        wide_load_a(stage, ra, a_off, (uint32_t)min(h + 3, G - 1) * a_step);
+        wide_load_b<kG128, TN>(b0q, p0q, rb, rp, b_off, p_off, min(h + 2, G - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        wide_compute<kG128, TM, TN>(acc, lw1, b1q, p1q, lut);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+    }
+    if (h < G) wide_compute<kG128, TM, TN>(acc, lw0, b0q, p0q, lut);
+
+    // Epilogue.
+    const uint8_t* pc_z = blob + code_bytes;
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+        const int t = bn * (BN / 16) + wave * TN + i;
+        if (t >= tiles) continue;
+        const int n = 16 * t + c;
+        const float sc = h2f(s_c[n]);
+        const int zpc = kG128 ? 0 : (int)pc_z[n];
+#pragma unroll
+        for (int a = 0; a < TM; ++a) {
+            const int m_first = bm * BM + a * 16 + 4 * j;
+            store_outputs<kG128>(acc[a][i], m_first, n, M, N, s_x, rowsum, sc, zpc, y, acc_out);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Plans.
 
 constexpr int kCUs = 256;
 
 struct Plan {
-    int kind = 0;  // 0: simple, 1: decode, 2: tiled
+    int kind = 0;  // 0: simple, 1: decode, 2: tiled (16-row waves), 3: tiled (wide waves)
     int mb = 0, nt = 0, s = 1, d = 1, w = 4;
     int bm = 0, bn = 0;
     int64_t nblk = 0;
@@ -525,23 +746,39 @@ constexpr bool decode_shape_ok(int mb, int nt, int w) {
 // these shapes, so the plan keeps the whole K in one workgroup (the split
 // machinery stays available to plans that are given a workspace).
 #ifdef QOQ_TUNING
-int g_force_bm = 0, g_force_bn = 0;
+int g_force_bm = 0, g_force_bn = 0, g_force_kind = 0;
 #endif
+
+// Every byte offset the buffer-load kernel forms must fit in 32 bits.
+bool fits_buffer_offsets(int64_t M, int64_t N, int64_t K) {
+    const int64_t G = K / kGroup, U = (M + 15) / 16, Gp = (G + 15) / 16 * 16;
+    return G * U * 2048 < (int64_t(1) << 32) && N * K / 2 < (int64_t(1) << 32) &&
+           N * Gp < (int64_t(1) << 32);
+}
 
 Plan plan_gemm(int64_t M, int64_t N, int64_t K, bool /*have_ws*/) {
     Plan p;
     if (M > 64) {
-        p.kind = 2;
-        // Largest block whose grid still covers the compute units.
-        const int64_t gm256 = (M + 255) / 256, gm128 = (M + 127) / 128;
-        const int64_t gn256 = (N + 255) / 256, gn128 = (N + 127) / 128;
-        if (gm256 * gn256 >= kCUs) { p.bm = 256; p.bn = 256; }
-        else if (gm128 * gn256 >= kCUs) { p.bm = 128; p.bn = 256; }
-        else { p.bm = 128; p.bn = 128; }
-        (void)gn128;
+        // Measured on MI355X over the Llama-3-8B and Qwen1.5-72B layers: from
+        // M = 512 up the wide-wave kernel with 128 x 256 blocks is fastest in
+        // both modes; below that, fewer than two blocks per compute unit are
+        // available and the 16-row-wave kernel with 128 x 256 blocks (or
+        // 128 x 128 when even those are too few) does better.
+        const int64_t gm128 = (M + 127) / 128;
+        const int64_t gn256 = (N + 255) / 256;
+        if (M >= 512 && fits_buffer_offsets(M, N, K)) {
+            p.kind = 3;
+            p.bm = 128;
+            p.bn = 256;
+        } else {
+            p.kind = 2;
+            p.bm = 128;
+            p.bn = gm128 * gn256 >= kCUs / 2 ? 256 : 128;
+        }
 #ifdef QOQ_TUNING
         if (g_force_bm) p.bm = g_force_bm;
         if (g_force_bn) p.bn = g_force_bn;
+        if (g_force_kind) p.kind = g_force_kind > 0 ? g_force_kind : 0;
 #endif
         return p;
     }
@@ -598,6 +835,9 @@ template <bool kG128, int MB, int NT>
 void launch_decode_dw(const Plan& p, const DecodeArgs& a) {
     if (p.w == 8) {
         if constexpr (decode_shape_ok(MB, NT, 8)) {
+#ifdef QOQ_TUNING
+            if (p.d == 4) { launch_decode_t<kG128, MB, NT, 4, 8>(p, a); return; }
+#endif
             if (p.d == 2) launch_decode_t<kG128, MB, NT, 2, 8>(p, a);
             else launch_decode_t<kG128, MB, NT, 1, 8>(p, a);
             return;
@@ -643,11 +883,20 @@ void launch_tile_t(const DecodeArgs& a) {
                        a.acc_out);
 }
 
+template <bool kG128, int BM, int BN, int WN>
+void launch_wide_t(const DecodeArgs& a) {
+    const unsigned blocks = (unsigned)(((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN));
+    hipLaunchKernelGGL((k_gemm_wide<kG128, BM, BN, WN>), dim3(blocks), dim3(WN * 64), 0, a.stream,
+                       a.xq, a.s_x, a.rowsum, a.blob, a.s_c, a.M, a.N, a.K, a.y, a.acc_out);
+}
+
 template <bool kG128>
 void launch_tile(const Plan& p, const DecodeArgs& a) {
-    if (p.bm == 256 && p.bn == 256) launch_tile_t<kG128, 256, 256, 2, 4>(a);
-    else if (p.bm == 128 && p.bn == 256) launch_tile_t<kG128, 128, 256, 2, 4>(a);
-    else if (p.bm == 256 && p.bn == 128) launch_tile_t<kG128, 256, 128, 4, 2>(a);
+    if (p.kind == 3) {
+        launch_wide_t<kG128, 128, 256, 4>(a);
+        return;
+    }
+    if (p.bn == 256) launch_tile_t<kG128, 128, 256, 2, 4>(a);
     else launch_tile_t<kG128, 128, 128, 2, 2>(a);
 }
 
@@ -667,7 +916,7 @@ void launch_gemm(int mode, const int8_t* xq, const uint16_t* s_x, const int32_t*
             launch_decode<false>(p, a);
         return;
     }
-    if (p.kind == 2) {
+    if (p.kind == 2 || p.kind == 3) {
         if (mode == 0)
             launch_tile<true>(p, a);
         else
@@ -684,9 +933,10 @@ void launch_gemm(int mode, const int8_t* xq, const uint16_t* s_x, const int32_t*
 }
 
 #ifdef QOQ_TUNING
-extern "C" void qoq_tuning_force_tile(int bm, int bn) {
+extern "C" void qoq_tuning_force_tile(int bm, int bn, int kind) {
     g_force_bm = bm;
     g_force_bn = bn;
+    g_force_kind = kind;
 }
 extern "C" void qoq_tuning_force_decode(int nt, int s, int d, int w) {
     g_force_nt = nt;

@@ -88,6 +88,37 @@ __device__ __forceinline__ uint32_t unpack4_g128(uint32_t codes, GroupConst gc) 
     return r ^ 0x80808080u;
 }
 
+// The same unpack with both constants in one 32-bit group word: s_g in the low
+// half and C in the high half. The packed multiply-add reads the scale from
+// the low half and the addend from the high half for both result halves
+// (op_sel / op_sel_hi), so no per-step duplication of the constants is needed.
+__device__ __forceinline__ uint32_t group_word(uint32_t pbyte) {
+    const uint32_t sg = (pbyte >> 4) + 1u;
+    const uint32_t zs = (pbyte & 15u) * sg;
+    const uint32_t c16 = ((128u - zs) * 257u) & 0xFFFFu;
+    return sg | (c16 << 16);
+}
+__device__ __forceinline__ uint32_t unpack4_g128w(uint32_t codes, uint32_t gw) {
+    uint32_t r;
+    asm("v_pk_mad_u16 %0, %1, %2, %2 op_sel:[0,0,1] op_sel_hi:[1,0,1]"
+        : "=v"(r)
+        : "v"(codes), "v"(gw));
+    return r ^ 0x80808080u;
+}
+
+// One k-step (KS = 0 or 1) of a lane's 32 packed codes -> one MFMA B operand.
+template <bool kG128, int KS>
+__device__ __forceinline__ int32x4 unpack_half(u32x4 p, uint32_t gw) {
+    const uint32_t w0 = KS ? p.z : p.x, w1 = KS ? p.w : p.y;
+    uint32_t a0 = w0 & 0x0F0F0F0Fu, a1 = (w0 >> 4) & 0x0F0F0F0Fu;
+    uint32_t a2 = w1 & 0x0F0F0F0Fu, a3 = (w1 >> 4) & 0x0F0F0F0Fu;
+    if (kG128) {
+        a0 = unpack4_g128w(a0, gw); a1 = unpack4_g128w(a1, gw);
+        a2 = unpack4_g128w(a2, gw); a3 = unpack4_g128w(a3, gw);
+    }
+    return int32x4{(int)a0, (int)a1, (int)a2, (int)a3};
+}
+
 // Packed 16 bytes of one lane (32 codes) -> the two MFMA B operands (k-steps
 // s = 0 and 1) of 16 INT8 values each, in the byte order of the A operand.
 template <bool kG128>

@@ -112,7 +112,7 @@ def test_pack_and_unpack(mode, N, K):
 # ------------------------------------------------------------------- GEMM --
 GEMM_SHAPES = [
     (1, 16, 128), (8, 256, 512), (17, 48, 384), (64, 96, 1152), (100, 160, 256),
-    (129, 32, 640), (257, 80, 128), (512, 512, 1024), (3, 16, 132096),
+    (129, 32, 640), (257, 80, 128), (512, 512, 1024), (520, 272, 640), (3, 16, 132096),
 ]
 
 
