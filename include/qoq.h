@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define QOQ_ABI_VERSION 1
+#define QOQ_ABI_VERSION 2
 #define QOQ_GROUP 128
 #define QOQ_MAX_K 132096
 
@@ -130,8 +130,9 @@ qoq_status qoq_quantize_weights(int mode, const uint16_t* w, int64_t N, int64_t 
  *   ((word >> 4) & 0x0F0F0F0F) of each 32-bit word give four codes in k order.
  *
  *   Parameters at offset N*K/2:
- *     QOQ_MODE_G128: N rows of Gp = roundup(G, 16) bytes; byte g of row n is
- *       ((s_g[n,g] - 1) << 4) | z[n,g]; padding bytes are 0.
+ *     QOQ_MODE_G128: N*G bytes, 16 per (tile t, group g) at (t*G + g)*16, so
+ *       that the 16 channels of a tile's group sit in one 16-byte run; byte c
+ *       of the run is ((s_g[16t+c,g] - 1) << 4) | z[16t+c,g].
  *     QOQ_MODE_PER_CHANNEL: N bytes, z[n].
  */
 int64_t qoq_packed_bytes(int mode, int64_t N, int64_t K);
@@ -169,10 +170,10 @@ qoq_status qoq_quantize_act(const uint16_t* x, int64_t M, int64_t K, int8_t* xq,
                             uint16_t* s_x, int32_t* rowsum, void* stream);
 
 /*
- * Workspace bytes that qoq_w4a8_gemm can use for this shape (0 if its plan
- * needs none), or -1 for an unsupported shape or mode. With the workspace,
- * decode-sized M may split K across workgroups (partial INT32 sums, added
- * exactly); without it, the library picks a plan that needs none.
+ * Scratch bytes that qoq_w4a8_gemm needs for this shape, or -1 for an
+ * unsupported shape or mode. Every current plan keeps all partial sums inside
+ * one workgroup, so this is 0; the workspace arguments exist so that a plan
+ * with a cross-workgroup reduction can be added without changing the ABI.
  */
 int64_t qoq_gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K);
 
@@ -189,12 +190,10 @@ int64_t qoq_gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K);
  *   y[m,n]   = f16( (f32(acc) * f32(s_x[m])) * f32(s_c[n]) )  (FP16 [M,N])
  *   acc_out  [M,N] int32 receives acc when not NULL (for inspection).
  *
- *   workspace: NULL, or device memory of workspace_bytes >=
- *   qoq_gemm_workspace_bytes(mode, M, N, K) that was zero-filled before its
- *   first use. The library leaves it ready for the next call (its counters back
- *   at zero), so one zero-fill at allocation suffices. Calls that overlap in
- *   time (e.g. on different streams) must not share a workspace. A workspace
- *   that is too small gives QOQ_ERR_WORKSPACE.
+ *   workspace: NULL, or device memory of workspace_bytes bytes. A workspace
+ *   smaller than qoq_gemm_workspace_bytes(mode, M, N, K) gives
+ *   QOQ_ERR_WORKSPACE; with the current plans none is needed and a given one
+ *   is not touched.
  */
 qoq_status qoq_w4a8_gemm(int mode, const int8_t* xq, const uint16_t* s_x, const int32_t* rowsum,
                          const void* blob, const uint16_t* s_c, int64_t M, int64_t N, int64_t K,

@@ -303,17 +303,14 @@ int orc_dequantize_weights(int mode, const uint16_t* s_c, const uint8_t* q, cons
 /*   byte  = 16 lane + 4 (kappa / 8) + (kappa % 4)                           */
 /*   nibble: low if (kappa % 8) < 4, else high.                              */
 /* Parameters follow the codes (offset N * K / 2):                           */
-/*   g128: N rows of Gp = roundup(G, 16) bytes; byte g of row n is           */
-/*         ((s_g - 1) << 4) | z, padding bytes are 0;                        */
+/*   g128: 16 bytes per (t, g) at (t * G + g) * 16, byte c of which is       */
+/*         ((s_g - 1) << 4) | z of channel 16 t + c in group g;              */
 /*   per-channel: N bytes, byte n is z[n].                                   */
 /* ------------------------------------------------------------------------ */
 int64_t orc_packed_bytes(int mode, int64_t N, int64_t K) {
     if (K < GROUP || K % GROUP || N < 16 || N % 16) return -1;
     int64_t codes = N * K / 2;
-    if (mode == ORC_MODE_G128) {
-        int64_t G = K / GROUP, Gp = (G + 15) / 16 * 16;
-        return codes + N * Gp;
-    }
+    if (mode == ORC_MODE_G128) return codes + N * (K / GROUP);
     if (mode == ORC_MODE_PER_CHANNEL) return codes + N;
     return -1;
 }
@@ -338,10 +335,9 @@ int orc_pack(int mode, const uint8_t* q, const uint8_t* s_g, const uint8_t* z, i
     }
     uint8_t* params = blob + N * K / 2;
     if (mode == ORC_MODE_G128) {
-        int64_t Gp = (G + 15) / 16 * 16;
         for (int64_t n = 0; n < N; ++n)
             for (int64_t g = 0; g < G; ++g)
-                params[n * Gp + g] =
+                params[((n / 16) * G + g) * 16 + n % 16] =
                     (uint8_t)(((s_g[n * G + g] - 1) << 4) | (z[n * G + g] & 15));
     } else {
         for (int64_t n = 0; n < N; ++n) params[n] = z[n];

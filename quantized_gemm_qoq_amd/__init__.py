@@ -225,11 +225,11 @@ _workspaces = {}
 
 
 def gemm_workspace(mode, M: int, N: int, K: int, device) -> Optional[torch.Tensor]:
-    """A zero-filled workspace for this device, grown when a shape needs more.
+    """The device's shared zero-filled workspace when the plan for this shape
+    needs scratch memory, else None (no current plan needs any).
 
     One workspace per device is shared by every call that does not bring its
-    own, so calls issued concurrently on different streams must pass their own
-    (the library re-arms the workspace at the end of each call)."""
+    own, so calls issued concurrently on different streams must pass their own."""
     need = qoq_gemm_workspace_bytes(mode, M, N, K)
     if need <= 0:
         return None

@@ -67,7 +67,6 @@ __global__ __launch_bounds__(kThreads) void k_gemm_simple(
     if (t * 16 >= N) return;
     const int m0 = blockIdx.y * 64;
     const int G = K / kGroup;
-    const int Gp = (G + 15) / 16 * 16;
     const int U = (M + 15) / 16;  // activation tiles of 16 rows
     const int c = lane % 16;
     const int j = lane / 16;
@@ -83,7 +82,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_simple(
     for (int g = 0; g < G; ++g) {
         const u32x4 p = reinterpret_cast<const u32x4*>(tiles)[(size_t)g * kWave];
         GroupConst gc{0u, 0u};
-        if (kG128) gc = group_const(params[(size_t)n * Gp + g]);
+        if (kG128) gc = group_const(params[((size_t)t * G + g) * 16 + c]);
         int32x4 b0, b1;
         unpack_lane<kG128>(p, gc, b0, b1);
 #pragma unroll
@@ -103,191 +102,6 @@ __global__ __launch_bounds__(kThreads) void k_gemm_simple(
     for (int mb = 0; mb < 4; ++mb)
         store_outputs<kG128>(acc[mb], m0 + 16 * mb + 4 * j, n, M, N, s_x, rowsum, sc, zpc, y,
                              acc_out);
-}
-
-// ---------------------------------------------------------------------------
-// Decode kernel (M <= 64): weight streaming at HBM rate.
-//
-// A workgroup of 4 waves owns NT n-tiles (16*NT channels) and the k-range of
-// split s (of S). Its waves split that range into 4 contiguous parts; each
-// wave keeps all 16*MB rows and its NT tiles in registers, so an activation
-// fragment is reused NT times and a weight fragment MB times. Vector loads
-// complete in issue order on gfx9, so activations and weights ride one FIFO:
-// both are prefetched D groups ahead into a register ring. At the end the four
-// waves' partial sums are added through LDS; with S > 1 every workgroup also
-// writes its partial tile to the workspace and the last of the S workgroups of
-// an n-block (found with an atomic counter) adds the others and runs the
-// epilogue, then re-arms the counter for the next call. INT32 addition is
-// exact and associative, so the result does not depend on the order.
-template <bool kG128, int MB, int NT, int D, int W>
-__global__ __launch_bounds__(W * 64) void k_gemm_decode(
-    const int8_t* __restrict__ xq, const uint16_t* __restrict__ s_x,
-    const int32_t* __restrict__ rowsum, const uint8_t* __restrict__ blob,
-    const uint16_t* __restrict__ s_c, int M, int N, int K, int S, uint16_t* __restrict__ y,
-    int32_t* __restrict__ acc_out, int32x4* __restrict__ ws, unsigned* __restrict__ counters) {
-    __shared__ int32x4 red[W][NT * MB][kWave];
-    __shared__ unsigned ticket;
-
-    const int lane = threadIdx.x % kWave;
-    // The wave index is uniform across the wave: keep everything derived from it
-    // in scalar registers so that loop control stays scalar.
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int nb = blockIdx.x / S;
-    const int s = blockIdx.x - nb * S;
-    const int G = K / kGroup;
-    const int Gp = (G + 15) / 16 * 16;
-    const int tiles = N / 16;
-    const int c = lane % 16;
-    const int j = lane / 16;
-
-    // k-range of this workgroup, then of this wave (contiguous).
-    const int wg0 = (int)((int64_t)G * s / S);
-    const int wg1 = (int)((int64_t)G * (s + 1) / S);
-    const int g0 = wg0 + (wg1 - wg0) * wave / W;
-    const int g1 = wg0 + (wg1 - wg0) * (wave + 1) / W;
-    const int count = g1 - g0;
-    const int last = max(count - 1, 0);
-
-    // Weight tile pointers (clamped for the ragged n tail: the data of an
-    // out-of-range tile is never stored) and per-lane parameter rows.
-    const u32x4* bptr[NT];
-    const uint8_t* pptr[NT];
-    const uint8_t* params = blob + (size_t)N * K / 2;
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-        const int t = min(nb * NT + i, tiles - 1);
-        bptr[i] = reinterpret_cast<const u32x4*>(blob) + ((size_t)t * G + min(g0, G - 1)) * kWave +
-                  lane;
-        pptr[i] = params + (size_t)(16 * t + c) * Gp + min(g0, G - 1);
-    }
-    // Activation tiles (packed 16-row tiles; a tile index past the last one is
-    // clamped: it feeds only accumulator rows that are never stored).
-    const int U = (M + 15) / 16;
-    const int32x4* aptr[MB];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-        aptr[mb] = reinterpret_cast<const int32x4*>(xq) +
-                   ((size_t)min(g0, G - 1) * U + min(mb, U - 1)) * 128 + lane;
-
-    int32x4 acc[NT][MB];
-#pragma unroll
-    for (int i = 0; i < NT; ++i)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[i][mb] = int32x4{0, 0, 0, 0};
-
-    // The wave walks its k-range in chunks of D groups. All loads of a chunk
-    // are issued together into registers that belong to that chunk, then
-    // consumed in order, so every wait on the in-order load counter is static
-    // and nothing is in flight across the loop's back edge; the latency between
-    // chunks is hidden by the other waves resident on the compute unit. Group
-    // indices past the wave's range are clamped (those loads re-read the last
-    // group and their products are skipped).
-    for (int base = 0; base < count; base += D) {
-        u32x4 rb[D][NT];
-        uint32_t rp[D][NT];
-        int32x4 ra[D][MB][2];
-#pragma unroll
-        for (int q = 0; q < D; ++q) {
-            const int gi = min(base + q, last);
-#pragma unroll
-            for (int i = 0; i < NT; ++i) {
-                rb[q][i] = bptr[i][(size_t)gi * kWave];
-                if (kG128) rp[q][i] = pptr[i][gi];
-            }
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                const int32x4* src = aptr[mb] + (size_t)gi * U * 128;
-                ra[q][mb][0] = src[0];
-                ra[q][mb][1] = src[64];
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < D; ++q) {
-            if (base + q < count) {
-                int32x4 b[NT][2];
-#pragma unroll
-                for (int i = 0; i < NT; ++i) {
-                    GroupConst gc{0u, 0u};
-                    if (kG128) gc = group_const(rp[q][i]);
-                    unpack_lane<kG128>(rb[q][i], gc, b[i][0], b[i][1]);
-                }
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                    for (int i = 0; i < NT; ++i)
-#pragma unroll
-                        for (int mb = 0; mb < MB; ++mb)
-                            acc[i][mb] = mfma16x16x64(ra[q][mb][ks], b[i][ks], acc[i][mb]);
-            }
-        }
-    }
-
-    // Add the waves' partial sums: wave w finishes the (tile, m-block) pairs
-    // p = w, w + W, ...
-#pragma unroll
-    for (int i = 0; i < NT; ++i)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) red[wave][i * MB + mb][lane] = acc[i][mb];
-    __syncthreads();
-    constexpr int kPairs = NT * MB;
-    constexpr int kOwn = (kPairs + W - 1) / W;
-    int32x4 part[kOwn];
-#pragma unroll
-    for (int o = 0; o < kOwn; ++o) {
-        const int p = wave + o * W;
-        part[o] = int32x4{0, 0, 0, 0};
-        if (p < kPairs) {
-#pragma unroll
-            for (int w = 0; w < W; ++w) part[o] += red[w][p][lane];
-        }
-    }
-
-    if (S > 1) {
-        // Publish this workgroup's partial tile, then take a ticket. Only one
-        // thread fences at device scope: the barrier has already made every
-        // thread's stores reach the shared cache, and the one release writes
-        // them back; only the last workgroup's one acquire follows.
-        int32x4* mine = ws + ((size_t)blockIdx.x * kPairs) * kWave + lane;
-#pragma unroll
-        for (int o = 0; o < kOwn; ++o) {
-            const int p = wave + o * W;
-            if (p < kPairs) mine[(size_t)p * kWave] = part[o];
-        }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (threadIdx.x == 0)
-            ticket = __hip_atomic_fetch_add(&counters[nb], 1u, __ATOMIC_ACQ_REL,
-                                            __HIP_MEMORY_SCOPE_AGENT);
-        __syncthreads();
-        if (ticket != (unsigned)(S - 1)) return;
-        for (int s2 = 0; s2 < S; ++s2) {
-            if (s2 == s) continue;
-            const int32x4* other = ws + ((size_t)(nb * S + s2) * kPairs) * kWave + lane;
-#pragma unroll
-            for (int o = 0; o < kOwn; ++o) {
-                const int p = wave + o * W;
-                if (p < kPairs)
-                    part[o] += __builtin_nontemporal_load(&other[(size_t)p * kWave]);
-            }
-        }
-        if (threadIdx.x == 0) counters[nb] = 0u;
-    }
-
-    const uint8_t* pc_z = params;  // per-channel zero bytes
-#pragma unroll
-    for (int o = 0; o < kOwn; ++o) {
-        const int p = wave + o * W;
-        if (p < kPairs) {
-            const int i = p / MB, mb = p % MB;
-            const int t = nb * NT + i;
-            if (t < tiles) {
-                const int n = 16 * t + c;
-                const int zpc = kG128 ? 0 : (int)pc_z[n];
-                store_outputs<kG128>(part[o], 16 * mb + 4 * j, n, M, N, s_x, rowsum,
-                                     h2f(s_c[n]), zpc, y, acc_out);
-            }
-        }
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -329,7 +143,7 @@ __device__ __forceinline__ void tile_load_b(u32x4 (&bq)[TN], uint32_t (&pq)[TN],
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
         bq[i] = bptr[i][(size_t)g * kWave];
-        if (kG128) pq[i] = pptr[i][g];
+        if (kG128) pq[i] = pptr[i][(size_t)g * 16];
     }
 }
 
@@ -379,7 +193,6 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void k_gemm_tile(
     const int wm = wave / WN, wn = wave % WN;
     const int c = lane % 16, j = lane / 16;
     const int G = K / kGroup;
-    const int Gp = (G + 15) / 16 * 16;
     const int U = (M + 15) / 16;
     const int tiles = N / 16;
     const int grid_m = (M + BM - 1) / BM, grid_n = (N + BN - 1) / BN;
@@ -416,7 +229,7 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void k_gemm_tile(
     for (int i = 0; i < TN; ++i) {
         const int t = min(bn * (BN / 16) + wn * TN + i, tiles - 1);
         bptr[i] = reinterpret_cast<const u32x4*>(blob) + (size_t)t * G * kWave + lane;
-        pptr[i] = params + (size_t)(16 * t + c) * Gp;
+        pptr[i] = params + (size_t)t * G * 16 + c;
     }
 
     int32x4 acc[TM][TN];
@@ -519,7 +332,7 @@ __device__ __forceinline__ void wide_load_b(u32x4 (&bq)[TN], uint32_t (&pq)[TN],
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
         bq[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)b_off[i], g * 1024, 0);
-        if (kG128) pq[i] = __builtin_amdgcn_raw_buffer_load_b8(rp, (int)p_off[i], g, 0);
+        if (kG128) pq[i] = __builtin_amdgcn_raw_buffer_load_b8(rp, (int)p_off[i], g * 16, 0);
     }
 }
 
@@ -594,7 +407,6 @@ __global__ __launch_bounds__(WN * 64, 2) void k_gemm_wide(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int c = lane % 16, j = lane / 16;
     const int G = K / kGroup;
-    const int Gp = (G + 15) / 16 * 16;
     const int U = (M + 15) / 16;
     const int tiles = N / 16;
     const int grid_m = (M + BM - 1) / BM, grid_n = (N + BN - 1) / BN;
@@ -619,7 +431,7 @@ __global__ __launch_bounds__(WN * 64, 2) void k_gemm_wide(
     const __amdgpu_buffer_rsrc_t rb =
         __builtin_amdgcn_make_buffer_rsrc((void*)blob, (short)0, (int)(uint32_t)code_bytes, kBufferConfig);
     const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(blob + code_bytes), (short)0, (int)(uint32_t)(kG128 ? N * Gp : N), kBufferConfig);
+        (void*)(blob + code_bytes), (short)0, (int)(uint32_t)(kG128 ? N * G : N), kBufferConfig);
 
     // Activation vector idx = threadIdx.x + v * kThr of the block's run goes to
     // LDS slot idx (row tiles past the last one are clamped; their rows are
@@ -640,7 +452,7 @@ __global__ __launch_bounds__(WN * 64, 2) void k_gemm_wide(
     for (int i = 0; i < TN; ++i) {
         const int t = min(bn * (BN / 16) + wave * TN + i, tiles - 1);
         b_off[i] = ((uint32_t)t * (uint32_t)G * 64u + (uint32_t)lane) * 16u;
-        p_off[i] = (uint32_t)(16 * t + c) * (uint32_t)Gp;
+        p_off[i] = (uint32_t)t * (uint32_t)G * 16u + (uint32_t)c;
     }
 
     int32x4 acc[TM][TN];
@@ -703,112 +515,252 @@ __global__ __launch_bounds__(WN * 64, 2) void k_gemm_wide(
 }
 
 // ---------------------------------------------------------------------------
+// Pipelined decode kernel (M <= 64): weight streaming at HBM rate.
+//
+// A workgroup of W waves owns NT 16-channel tiles and the whole K; wave w takes
+// the contiguous groups [G*w/W, G*(w+1)/W) and keeps all 16*MB rows and its NT
+// tiles in registers, so an activation fragment is reused NT times and a
+// weight fragment MB times. The loads run R groups ahead through a ring of R
+// register sets: the loop body is unrolled R times so that every set has a
+// fixed name, every load and every matrix-core step is unconditional (a load
+// guarded by a branch would be sunk to its use by the compiler), and every
+// wait on the in-order load counter is static. A prefetch past the wave's last
+// group gets an out-of-range buffer offset: the load returns zeros without a
+// memory request and is never consumed. Groups left over when the count is not
+// a multiple of R run one at a time after the pipelined part. The waves' sums
+// are added with LDS integer atomics (exact and order-free), then each wave
+// runs the epilogue for a share of the (tile, row block) pairs.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+template <bool kG128, int MB, int NT>
+__device__ __forceinline__ void stream_load(u32x4 (&bq)[NT], uint32_t (&pq)[NT],
+                                            int32x4 (&aq)[MB][2], __amdgpu_buffer_rsrc_t rb,
+                                            __amdgpu_buffer_rsrc_t rp, __amdgpu_buffer_rsrc_t ra,
+                                            const uint32_t (&b_off)[NT],
+                                            const uint32_t (&p_off)[NT],
+                                            const uint32_t (&a_off)[MB], int gi, bool valid,
+                                            uint32_t a_step) {
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        const uint32_t ob = valid ? b_off[i] + (uint32_t)gi * 1024u : kOutOfRange;
+        bq[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)ob, 0, 0);
+        if (kG128) {
+            const uint32_t op = valid ? p_off[i] + (uint32_t)gi * 16u : kOutOfRange;
+            pq[i] = __builtin_amdgcn_raw_buffer_load_b8(rp, (int)op, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const uint32_t oa = valid ? a_off[mb] + (uint32_t)gi * a_step : kOutOfRange;
+        aq[mb][0] = __builtin_bit_cast(int32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, (int)oa, 0, 0));
+        aq[mb][1] =
+            __builtin_bit_cast(int32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, (int)oa, 1024, 0));
+    }
+}
+
+template <bool kG128, int MB, int NT>
+__device__ __forceinline__ void stream_compute(int32x4 (&acc)[NT][MB], const u32x4 (&bq)[NT],
+                                               const uint32_t (&pq)[NT],
+                                               const int32x4 (&aq)[MB][2], const uint32_t* lut) {
+    uint32_t gw[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) gw[i] = kG128 ? lut[pq[i] & 0xFFu] : 0u;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        const int32x4 b0 = unpack_half<kG128, 0>(bq[i], gw[i]);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[i][mb] = mfma16x16x64(aq[mb][0], b0, acc[i][mb]);
+        const int32x4 b1 = unpack_half<kG128, 1>(bq[i], gw[i]);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[i][mb] = mfma16x16x64(aq[mb][1], b1, acc[i][mb]);
+    }
+}
+
+template <bool kG128, int MB, int NT, int R, int W>
+__global__ __launch_bounds__(W * 64) void k_gemm_stream(
+    const int8_t* __restrict__ xq, const uint16_t* __restrict__ s_x,
+    const int32_t* __restrict__ rowsum, const uint8_t* __restrict__ blob,
+    const uint16_t* __restrict__ s_c, int M, int N, int K, uint16_t* __restrict__ y,
+    int32_t* __restrict__ acc_out) {
+    constexpr int kPairs = NT * MB;
+    constexpr int kThr = W * 64;
+    // red[(p * 4 + v) * 64 + lane]: row v of pair p in lane order (conflict-free).
+    __shared__ int32_t red[kPairs * 4 * kWave];
+    __shared__ uint32_t lut[256];
+
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int nb = blockIdx.x;
+    const int G = K / kGroup;
+    const int tiles = N / 16;
+    const int U = (M + 15) / 16;
+    const int c = lane % 16, j = lane / 16;
+
+    for (int i = threadIdx.x; i < kPairs * 4 * kWave; i += kThr) red[i] = 0;
+    if (kG128)
+        for (int i = threadIdx.x; i < 256; i += kThr) lut[i] = group_word((uint32_t)i);
+    __syncthreads();
+
+    const int g0 = G * wave / W;
+    const int count = G * (wave + 1) / W - g0;
+
+    const size_t code_bytes = (size_t)N * K / 2;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)xq, (short)0, (int)((uint32_t)G * (uint32_t)U * 2048u), kBufferConfig);
+    const __amdgpu_buffer_rsrc_t rb =
+        __builtin_amdgcn_make_buffer_rsrc((void*)blob, (short)0, (int)(uint32_t)code_bytes, kBufferConfig);
+    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(blob + code_bytes), (short)0, (int)(uint32_t)(kG128 ? N * G : N), kBufferConfig);
+
+    // Per-lane byte offsets of this wave's first group; out-of-range tiles and
+    // row blocks are clamped (their results are never stored).
+    uint32_t b_off[NT], p_off[NT], a_off[MB];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        const int t = min(nb * NT + i, tiles - 1);
+        b_off[i] = ((uint32_t)t * (uint32_t)G + (uint32_t)g0) * 1024u + (uint32_t)lane * 16u;
+        p_off[i] = ((uint32_t)t * (uint32_t)G + (uint32_t)g0) * 16u + (uint32_t)c;
+    }
+    const uint32_t a_step = (uint32_t)U * 2048u;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+        a_off[mb] = (uint32_t)g0 * a_step + (uint32_t)min(mb, U - 1) * 2048u + (uint32_t)lane * 16u;
+
+    int32x4 acc[NT][MB];
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[i][mb] = int32x4{0, 0, 0, 0};
+
+    u32x4 bq[R][NT];
+    uint32_t pq[R][NT];
+    int32x4 aq[R][MB][2];
+    const int main_count = count / R * R;
+#pragma unroll
+    for (int r = 0; r < R - 1; ++r)
+        stream_load<kG128, MB, NT>(bq[r], pq[r], aq[r], rb, rp, ra, b_off, p_off, a_off, r,
+                                   r < main_count, a_step);
+    for (int h = 0; h < main_count; h += R) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int nxt = h + r + R - 1;
+            stream_load<kG128, MB, NT>(bq[(r + R - 1) % R], pq[(r + R - 1) % R],
+                                       aq[(r + R - 1) % R], rb, rp, ra, b_off, p_off, a_off, nxt,
+                                       nxt < main_count, a_step);
+            stream_compute<kG128, MB, NT>(acc, bq[r], pq[r], aq[r], lut);
+        }
+    }
+    for (int h = main_count; h < count; ++h) {
+        stream_load<kG128, MB, NT>(bq[0], pq[0], aq[0], rb, rp, ra, b_off, p_off, a_off, h, true,
+                                   a_step);
+        stream_compute<kG128, MB, NT>(acc, bq[0], pq[0], aq[0], lut);
+    }
+
+    // Sum the waves' partial tiles in LDS.
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                atomicAdd(&red[((i * MB + mb) * 4 + v) * kWave + lane], acc[i][mb][v]);
+    __syncthreads();
+
+    const uint8_t* pc_z = blob + code_bytes;
+    for (int p = wave; p < kPairs; p += W) {
+        const int i = p / MB, mb = p % MB;
+        const int t = nb * NT + i;
+        if (t >= tiles) continue;
+        const int n = 16 * t + c;
+        int32x4 a;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) a[v] = red[(p * 4 + v) * kWave + lane];
+        const int zpc = kG128 ? 0 : (int)pc_z[n];
+        store_outputs<kG128>(a, 16 * mb + 4 * j, n, M, N, s_x, rowsum, h2f(s_c[n]), zpc, y,
+                             acc_out);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Plans.
 
 constexpr int kCUs = 256;
 
+enum Kind { kSimple = 0, kTile = 2, kWide = 3, kStream = 4 };
+
 struct Plan {
-    int kind = 0;  // 0: simple, 1: decode, 2: tiled (16-row waves), 3: tiled (wide waves)
-    int mb = 0, nt = 0, s = 1, d = 1, w = 4;
-    int bm = 0, bn = 0;
+    int kind = kSimple;
+    int mb = 0, nt = 0, r = 2, w = 8;  // stream kernel: row blocks, tiles, ring depth, waves
+    int bn = 256;                      // 16-row-wave tiled kernel: 128 x bn blocks
     int64_t nblk = 0;
-    int64_t ws_bytes = 0;
 };
 
 #ifdef QOQ_TUNING
-int g_force_nt = 0, g_force_s = 0, g_force_d = 0, g_force_w = 0;
+int g_force_kind = 0, g_force_nt = 0, g_force_r = 0, g_force_w = 0, g_force_bn = 0;
 #endif
 
-// Workspace layout: a fixed region of kMaxCounters arrival counters at offset
-// 0 (every plan leaves the counters it used at zero, and no plan writes
-// partial sums there, so plans of different shapes can share a workspace),
-// then the partial tiles.
-constexpr int64_t kMaxCounters = 16384;
-constexpr int64_t kCounterBytes = kMaxCounters * 4;
-
-int64_t decode_ws_bytes(int mb, int nt, int s, int64_t nblk) {
-    if (s <= 1) return 0;
-    const int64_t partial = nblk * s * (int64_t)nt * mb * kWave * 16;  // int32x4 per lane
-    return kCounterBytes + partial;
-}
-
-// The (MB, NT, W) combinations that are instantiated.
-constexpr bool decode_shape_ok(int mb, int nt, int w) {
-    return nt * mb <= 24 && !(mb == 2 && nt == 12) && w * nt * mb <= 96;
-}
-
-// Decode plan. Measured on MI355X over the Llama-3-8B and Qwen1.5-72B decode
-// layers: the workgroup count should cover most compute units, and more
-// channels per workgroup cut the activation bytes each one re-reads, but past
-// three 16-channel tiles the register cost lowers occupancy; eight waves per
-// workgroup and one group per load chunk keep the most loads in flight.
-// Splitting K across workgroups never paid for its partial sums and fences on
-// these shapes, so the plan keeps the whole K in one workgroup (the split
-// machinery stays available to plans that are given a workspace).
-#ifdef QOQ_TUNING
-int g_force_bm = 0, g_force_bn = 0, g_force_kind = 0;
-#endif
-
-// Every byte offset the buffer-load kernel forms must fit in 32 bits.
+// The buffer-load kernels form 32-bit byte offsets, and mark prefetches past
+// the end with offset 2^31: every real offset must stay below that.
 bool fits_buffer_offsets(int64_t M, int64_t N, int64_t K) {
-    const int64_t G = K / kGroup, U = (M + 15) / 16, Gp = (G + 15) / 16 * 16;
-    return G * U * 2048 < (int64_t(1) << 32) && N * K / 2 < (int64_t(1) << 32) &&
-           N * Gp < (int64_t(1) << 32);
+    const int64_t G = K / kGroup, U = (M + 15) / 16;
+    return G * U * 2048 < (int64_t(1) << 31) && N * K / 2 < (int64_t(1) << 31) &&
+           N * G < (int64_t(1) << 31);
 }
 
-Plan plan_gemm(int64_t M, int64_t N, int64_t K, bool /*have_ws*/) {
+// Measured on MI355X over the Llama-3-8B and Qwen1.5-72B layers:
+//   M <= 64: the streaming kernel; three 16-channel tiles per workgroup once
+//     that still leaves two workgroups per compute unit, else two; for 16 rows
+//     a two-deep ring and 8 waves, for 17..64 rows 16 waves that each load one
+//     group at a time (the activation bytes then dominate, and more waves with
+//     fewer groups each beat a deeper ring, which would not fit the registers
+//     of 16 waves).
+//   M >= 512: the wide-wave tiled kernel with 128 x 256 blocks.
+//   64 < M < 512: fewer than two 128 x 256 blocks per compute unit exist; the
+//     16-row-wave tiled kernel with 128 x 256 blocks, or 128 x 128 when even
+//     those are too few.
+// Shapes whose offsets do not fit the buffer-load kernels take the reference
+// kernel (M <= 64) or the 16-row-wave tiled kernel (M > 64).
+Plan plan_gemm(int64_t M, int64_t N, int64_t K) {
     Plan p;
-    if (M > 64) {
-        // Measured on MI355X over the Llama-3-8B and Qwen1.5-72B layers: from
-        // M = 512 up the wide-wave kernel with 128 x 256 blocks is fastest in
-        // both modes; below that, fewer than two blocks per compute unit are
-        // available and the 16-row-wave kernel with 128 x 256 blocks (or
-        // 128 x 128 when even those are too few) does better.
-        const int64_t gm128 = (M + 127) / 128;
-        const int64_t gn256 = (N + 255) / 256;
-        if (M >= 512 && fits_buffer_offsets(M, N, K)) {
-            p.kind = 3;
-            p.bm = 128;
-            p.bn = 256;
-        } else {
-            p.kind = 2;
-            p.bm = 128;
-            p.bn = gm128 * gn256 >= kCUs / 2 ? 256 : 128;
-        }
-#ifdef QOQ_TUNING
-        if (g_force_bm) p.bm = g_force_bm;
-        if (g_force_bn) p.bn = g_force_bn;
-        if (g_force_kind) p.kind = g_force_kind > 0 ? g_force_kind : 0;
-#endif
-        return p;
-    }
-    p.kind = 1;
-    p.mb = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
     const int64_t tiles = N / 16;
-    static const int nts[] = {3, 2, 1};
-    p.nt = 1;
-    for (int nt : nts) {
-        if ((tiles + nt - 1) / nt >= kCUs * 2 / 3) {
-            p.nt = nt;
-            break;
+    const bool fits = fits_buffer_offsets(M, N, K);
+    if (M <= 64) {
+        if (fits) {
+            p.kind = kStream;
+            p.mb = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+            p.nt = (tiles + 2) / 3 >= 2 * kCUs ? 3 : 2;
+            if (p.mb == 1) {
+                p.r = 2;
+                p.w = 8;
+            } else {
+                p.r = 1;
+                p.w = 16;
+            }
         }
+    } else if (M >= 512 && fits) {
+        p.kind = kWide;
+    } else {
+        p.kind = kTile;
+        const int64_t gm128 = (M + 127) / 128, gn256 = (N + 255) / 256;
+        p.bn = gm128 * gn256 >= kCUs / 2 ? 256 : 128;
     }
-    p.s = 1;
-    p.d = 1;
-    p.w = decode_shape_ok(p.mb, p.nt, 8) ? 8 : 4;
 #ifdef QOQ_TUNING
+    if (g_force_kind) {
+        p.kind = g_force_kind < 0 ? kSimple : g_force_kind;
+        if (p.kind == kStream && p.mb == 0) p.mb = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+        if (p.kind == kStream && (M > 64 || !fits)) p.kind = kSimple;
+        if (p.kind == kWide && !fits) p.kind = kTile;
+    }
     if (g_force_nt) p.nt = g_force_nt;
-    if (g_force_s) p.s = g_force_s;
-    if (g_force_d) p.d = g_force_d;
+    if (g_force_r) p.r = g_force_r;
     if (g_force_w) p.w = g_force_w;
+    if (g_force_bn) p.bn = g_force_bn;
 #endif
-    (void)K;
-    p.nblk = (tiles + p.nt - 1) / p.nt;
-    p.ws_bytes = decode_ws_bytes(p.mb, p.nt, p.s, p.nblk);
+    if (p.kind == kStream) p.nblk = (tiles + p.nt - 1) / p.nt;
     return p;
 }
 
-struct DecodeArgs {
+struct GemmArgs {
     const int8_t* xq;
     const uint16_t* s_x;
     const int32_t* rowsum;
@@ -817,66 +769,47 @@ struct DecodeArgs {
     int M, N, K;
     uint16_t* y;
     int32_t* acc_out;
-    void* ws;
     hipStream_t stream;
 };
 
-template <bool kG128, int MB, int NT, int D, int W>
-void launch_decode_t(const Plan& p, const DecodeArgs& a) {
-    unsigned* counters = reinterpret_cast<unsigned*>(a.ws);
-    int32x4* partial =
-        a.ws ? reinterpret_cast<int32x4*>(static_cast<char*>(a.ws) + kCounterBytes) : nullptr;
-    hipLaunchKernelGGL((k_gemm_decode<kG128, MB, NT, D, W>), dim3((unsigned)(p.nblk * p.s)),
-                       dim3(W * 64), 0, a.stream, a.xq, a.s_x, a.rowsum, a.blob, a.s_c, a.M, a.N,
-                       a.K, p.s, a.y, a.acc_out, partial, counters);
+template <bool kG128, int MB, int NT, int R, int W>
+void launch_stream_t(const Plan& p, const GemmArgs& a) {
+    hipLaunchKernelGGL((k_gemm_stream<kG128, MB, NT, R, W>), dim3((unsigned)p.nblk), dim3(W * 64),
+                       0, a.stream, a.xq, a.s_x, a.rowsum, a.blob, a.s_c, a.M, a.N, a.K, a.y,
+                       a.acc_out);
 }
 
 template <bool kG128, int MB, int NT>
-void launch_decode_dw(const Plan& p, const DecodeArgs& a) {
-    if (p.w == 8) {
-        if constexpr (decode_shape_ok(MB, NT, 8)) {
+void launch_stream_rw(const Plan& p, const GemmArgs& a) {
 #ifdef QOQ_TUNING
-            if (p.d == 4) { launch_decode_t<kG128, MB, NT, 4, 8>(p, a); return; }
+    if (p.r == 4 && p.w == 4) { launch_stream_t<kG128, MB, NT, 4, 4>(p, a); return; }
+    if (p.r == 2 && p.w == 4) { launch_stream_t<kG128, MB, NT, 2, 4>(p, a); return; }
+    if (p.r == 4 && p.w == 8) { launch_stream_t<kG128, MB, NT, 4, 8>(p, a); return; }
+    if (p.r == 2 && p.w == 16) { launch_stream_t<kG128, MB, NT, 2, 16>(p, a); return; }
+    if (p.r == 1 && p.w == 8) { launch_stream_t<kG128, MB, NT, 1, 8>(p, a); return; }
 #endif
-            if (p.d == 2) launch_decode_t<kG128, MB, NT, 2, 8>(p, a);
-            else launch_decode_t<kG128, MB, NT, 1, 8>(p, a);
-            return;
-        }
-    }
-    if (p.d == 2) launch_decode_t<kG128, MB, NT, 2, 4>(p, a);
-    else launch_decode_t<kG128, MB, NT, 1, 4>(p, a);
+    if (p.r == 1) launch_stream_t<kG128, MB, NT, 1, 16>(p, a);
+    else launch_stream_t<kG128, MB, NT, 2, 8>(p, a);
 }
 
 template <bool kG128, int MB>
-void launch_decode_nt(const Plan& p, const DecodeArgs& a) {
-#define QOQ_NT_CASE(NTV)                                                 \
-    case NTV:                                                            \
-        if constexpr (decode_shape_ok(MB, NTV, 4)) launch_decode_dw<kG128, MB, NTV>(p, a); \
-        break;
-    switch (p.nt) {
-        QOQ_NT_CASE(1)
-        QOQ_NT_CASE(2)
-        QOQ_NT_CASE(3)
-        QOQ_NT_CASE(4)
-        QOQ_NT_CASE(6)
-        QOQ_NT_CASE(8)
-        QOQ_NT_CASE(12)
-        default: break;
-    }
-#undef QOQ_NT_CASE
+void launch_stream_nt(const Plan& p, const GemmArgs& a) {
+#ifdef QOQ_TUNING
+    if (p.nt == 1) { launch_stream_rw<kG128, MB, 1>(p, a); return; }
+#endif
+    if (p.nt == 3) launch_stream_rw<kG128, MB, 3>(p, a);
+    else launch_stream_rw<kG128, MB, 2>(p, a);
 }
 
 template <bool kG128>
-void launch_decode(const Plan& p, const DecodeArgs& a) {
-    if (p.mb == 1) launch_decode_nt<kG128, 1>(p, a);
-    else if (p.mb == 2) launch_decode_nt<kG128, 2>(p, a);
-    else launch_decode_nt<kG128, 4>(p, a);
+void launch_stream(const Plan& p, const GemmArgs& a) {
+    if (p.mb == 1) launch_stream_nt<kG128, 1>(p, a);
+    else if (p.mb == 2) launch_stream_nt<kG128, 2>(p, a);
+    else launch_stream_nt<kG128, 4>(p, a);
 }
 
-}  // namespace
-
 template <bool kG128, int BM, int BN, int WM, int WN>
-void launch_tile_t(const DecodeArgs& a) {
+void launch_tile_t(const GemmArgs& a) {
     const unsigned blocks = (unsigned)(((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN));
     hipLaunchKernelGGL((k_gemm_tile<kG128, BM, BN, WM, WN>), dim3(blocks), dim3(WM * WN * 64), 0,
                        a.stream, a.xq, a.s_x, a.rowsum, a.blob, a.s_c, a.M, a.N, a.K, a.y,
@@ -884,65 +817,65 @@ void launch_tile_t(const DecodeArgs& a) {
 }
 
 template <bool kG128, int BM, int BN, int WN>
-void launch_wide_t(const DecodeArgs& a) {
+void launch_wide_t(const GemmArgs& a) {
     const unsigned blocks = (unsigned)(((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN));
     hipLaunchKernelGGL((k_gemm_wide<kG128, BM, BN, WN>), dim3(blocks), dim3(WN * 64), 0, a.stream,
                        a.xq, a.s_x, a.rowsum, a.blob, a.s_c, a.M, a.N, a.K, a.y, a.acc_out);
 }
 
 template <bool kG128>
-void launch_tile(const Plan& p, const DecodeArgs& a) {
-    if (p.kind == 3) {
-        launch_wide_t<kG128, 128, 256, 4>(a);
-        return;
-    }
-    if (p.bn == 256) launch_tile_t<kG128, 128, 256, 2, 4>(a);
-    else launch_tile_t<kG128, 128, 128, 2, 2>(a);
+void launch_simple(const GemmArgs& a) {
+    const dim3 grid((unsigned)((a.N / 16 + 3) / 4), (unsigned)((a.M + 63) / 64));
+    hipLaunchKernelGGL(k_gemm_simple<kG128>, grid, dim3(kThreads), 0, a.stream, a.xq, a.s_x,
+                       a.rowsum, a.blob, a.s_c, a.M, a.N, a.K, a.y, a.acc_out);
 }
 
-int64_t gemm_workspace_bytes(int /*mode*/, int64_t M, int64_t N, int64_t K) {
-    return plan_gemm(M, N, K, true).ws_bytes;
+template <bool kG128>
+void launch_plan(const Plan& p, const GemmArgs& a) {
+    switch (p.kind) {
+        case kStream:
+            launch_stream<kG128>(p, a);
+            break;
+        case kWide:
+            launch_wide_t<kG128, 128, 256, 4>(a);
+            break;
+        case kTile:
+            if (p.bn == 256) launch_tile_t<kG128, 128, 256, 2, 4>(a);
+            else launch_tile_t<kG128, 128, 128, 2, 2>(a);
+            break;
+        default:
+            launch_simple<kG128>(a);
+            break;
+    }
+}
+
+}  // namespace
+
+// No current plan needs scratch memory.
+int64_t gemm_workspace_bytes(int /*mode*/, int64_t /*M*/, int64_t /*N*/, int64_t /*K*/) {
+    return 0;
 }
 
 void launch_gemm(int mode, const int8_t* xq, const uint16_t* s_x, const int32_t* rowsum,
                  const uint8_t* blob, const uint16_t* s_c, int64_t M, int64_t N, int64_t K,
-                 uint16_t* y, int32_t* acc_out, void* ws, hipStream_t stream) {
-    const Plan p = plan_gemm(M, N, K, ws != nullptr);
-    const DecodeArgs a{xq, s_x, rowsum, blob, s_c, (int)M, (int)N, (int)K, y, acc_out, ws, stream};
-    if (p.kind == 1) {
-        if (mode == 0)
-            launch_decode<true>(p, a);
-        else
-            launch_decode<false>(p, a);
-        return;
-    }
-    if (p.kind == 2 || p.kind == 3) {
-        if (mode == 0)
-            launch_tile<true>(p, a);
-        else
-            launch_tile<false>(p, a);
-        return;
-    }
-    const dim3 grid((unsigned)((N / 16 + 3) / 4), (unsigned)((M + 63) / 64));
+                 uint16_t* y, int32_t* acc_out, void* /*ws*/, hipStream_t stream) {
+    const Plan p = plan_gemm(M, N, K);
+    const GemmArgs a{xq, s_x, rowsum, blob, s_c, (int)M, (int)N, (int)K, y, acc_out, stream};
     if (mode == 0)
-        hipLaunchKernelGGL(k_gemm_simple<true>, grid, dim3(kThreads), 0, stream, xq, s_x, rowsum,
-                           blob, s_c, (int)M, (int)N, (int)K, y, acc_out);
+        launch_plan<true>(p, a);
     else
-        hipLaunchKernelGGL(k_gemm_simple<false>, grid, dim3(kThreads), 0, stream, xq, s_x, rowsum,
-                           blob, s_c, (int)M, (int)N, (int)K, y, acc_out);
+        launch_plan<false>(p, a);
 }
 
 #ifdef QOQ_TUNING
-extern "C" void qoq_tuning_force_tile(int bm, int bn, int kind) {
-    g_force_bm = bm;
-    g_force_bn = bn;
+// Plan overrides for measurement builds: kind (-1 reference, 2 tiled, 3 wide,
+// 4 streaming; 0 keeps the plan), then the kind's own parameters (0 keeps).
+extern "C" void qoq_tuning_force(int kind, int nt, int r, int w, int bn) {
     g_force_kind = kind;
-}
-extern "C" void qoq_tuning_force_decode(int nt, int s, int d, int w) {
     g_force_nt = nt;
-    g_force_s = s;
-    g_force_d = d;
+    g_force_r = r;
     g_force_w = w;
+    g_force_bn = bn;
 }
 #endif
 

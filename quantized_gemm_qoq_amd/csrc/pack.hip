@@ -71,29 +71,29 @@ __global__ __launch_bounds__(kThreads) void k_unpack_codes(const uint8_t* __rest
     *reinterpret_cast<uint4*>(dst + 64) = s1;
 }
 
-// g128 parameters: N rows of Gp bytes, ((s_g - 1) << 4) | z, zero padding.
+// g128 parameters: 16 bytes per (tile t, group g) at (t * G + g) * 16, byte c
+// of which is ((s_g - 1) << 4) | z of channel 16 t + c. One thread per byte.
 __global__ __launch_bounds__(kThreads) void k_pack_params_g128(const uint8_t* __restrict__ s_g,
                                                                const uint8_t* __restrict__ z,
-                                                               int64_t N, int G, int Gp,
+                                                               int64_t N, int G,
                                                                uint8_t* __restrict__ params) {
     const int64_t tid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (tid >= N * Gp) return;
-    const int64_t n = tid / Gp;
-    const int g = (int)(tid % Gp);
-    uint8_t b = 0;
-    if (g < G) b = (uint8_t)(((s_g[n * G + g] - 1) << 4) | (z[n * G + g] & 15));
-    params[tid] = b;
+    if (tid >= N * G) return;
+    const int64_t t = tid / (16 * (int64_t)G);
+    const int64_t rem = tid % (16 * (int64_t)G);
+    const int64_t g = rem / 16, n = 16 * t + rem % 16;
+    params[tid] = (uint8_t)(((s_g[n * G + g] - 1) << 4) | (z[n * G + g] & 15));
 }
 
 __global__ __launch_bounds__(kThreads) void k_unpack_params_g128(const uint8_t* __restrict__ params,
-                                                                 int64_t N, int G, int Gp,
+                                                                 int64_t N, int G,
                                                                  uint8_t* __restrict__ s_g,
                                                                  uint8_t* __restrict__ z) {
     const int64_t tid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (tid >= N * G) return;
     const int64_t n = tid / G;
-    const int g = (int)(tid % G);
-    const uint8_t b = params[n * Gp + g];
+    const int64_t g = tid % G;
+    const uint8_t b = params[((n / 16) * G + g) * 16 + n % 16];
     s_g[tid] = (uint8_t)((b >> 4) + 1);
     z[tid] = (uint8_t)(b & 15);
 }
@@ -110,10 +110,7 @@ unsigned blocks_for(int64_t threads) { return (unsigned)((threads + kThreads - 1
 
 int64_t packed_bytes(int mode, int64_t N, int64_t K) {
     const int64_t codes = N * K / 2;
-    if (mode == 0) {
-        const int64_t G = K / kGroup, Gp = (G + 15) / 16 * 16;
-        return codes + N * Gp;
-    }
+    if (mode == 0) return codes + N * (K / kGroup);
     return codes + N;
 }
 
@@ -125,9 +122,8 @@ void launch_pack(int mode, const uint8_t* q, const uint8_t* s_g, const uint8_t* 
                        (int)K, blob);
     uint8_t* params = blob + N * K / 2;
     if (mode == 0) {
-        const int Gp = (G + 15) / 16 * 16;
-        hipLaunchKernelGGL(k_pack_params_g128, dim3(blocks_for(N * Gp)), dim3(kThreads), 0, stream,
-                           s_g, z, N, G, Gp, params);
+        hipLaunchKernelGGL(k_pack_params_g128, dim3(blocks_for(N * G)), dim3(kThreads), 0, stream,
+                           s_g, z, N, G, params);
     } else {
         hipLaunchKernelGGL(k_copy_bytes, dim3(blocks_for(N)), dim3(kThreads), 0, stream, z, N,
                            params);
@@ -142,9 +138,8 @@ void launch_unpack(int mode, const uint8_t* blob, int64_t N, int64_t K, uint8_t*
                        (int)K, q);
     const uint8_t* params = blob + N * K / 2;
     if (mode == 0) {
-        const int Gp = (G + 15) / 16 * 16;
         hipLaunchKernelGGL(k_unpack_params_g128, dim3(blocks_for(N * G)), dim3(kThreads), 0, stream,
-                           params, N, G, Gp, s_g, z);
+                           params, N, G, s_g, z);
     } else {
         hipLaunchKernelGGL(k_copy_bytes, dim3(blocks_for(N)), dim3(kThreads), 0, stream, params, N,
                            z);

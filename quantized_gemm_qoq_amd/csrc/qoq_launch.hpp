@@ -24,8 +24,7 @@ void launch_unpack(int mode, const uint8_t* blob, int64_t N, int64_t K, uint8_t*
 // Workspace bytes the GEMM plan for this shape can use (0: none).
 int64_t gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K);
 
-// ws: NULL (a plan without cross-workgroup reduction is used) or at least
-// gemm_workspace_bytes() of zero-initialised device memory.
+// ws: scratch of gemm_workspace_bytes() (currently always 0, so unused).
 void launch_gemm(int mode, const int8_t* xq, const uint16_t* s_x, const int32_t* rowsum,
                  const uint8_t* blob, const uint16_t* s_c, int64_t M, int64_t N, int64_t K,
                  uint16_t* y, int32_t* acc_out, void* ws, hipStream_t stream);

@@ -46,9 +46,10 @@ def test_version_and_status_strings(lib):
 
 
 def test_packed_bytes(lib):
-    assert lib.qoq_packed_bytes(0, 16, 128) == 16 * 64 + 16 * 16
+    assert lib.qoq_packed_bytes(0, 16, 128) == 16 * 64 + 16
     assert lib.qoq_packed_bytes(1, 16, 128) == 16 * 64 + 16
     assert lib.qoq_packed_bytes(0, 6144, 4096) == 6144 * 2048 + 6144 * 32
+    assert lib.qoq_packed_bytes(0, 32, 128 * 17) == 32 * 64 * 17 + 32 * 17
     assert lib.qoq_packed_bytes(0, 15, 128) == -1
     assert lib.qoq_packed_bytes(0, 16, 129) == -1
     assert lib.qoq_packed_bytes(0, 16, 132096 + 128) == -1

@@ -85,7 +85,6 @@ def emulate_gemm(mode, xq, blob, rowsum, N, K):
     T = N // 16
     words = np.ascontiguousarray(blob[: N * K // 2]).view(np.uint32).reshape(T, G, 64, 4)
     params = blob[N * K // 2:]
-    Gp = (G + 15) // 16 * 16
     Mp = (M + 15) // 16 * 16
     xpad = np.zeros((Mp, K), np.int8)
     xpad[:M] = xq
@@ -98,7 +97,8 @@ def emulate_gemm(mode, xq, blob, rowsum, N, K):
         for g in range(G):
             w = words[t, g]  # [64, 4]
             if mode == G128:
-                p = params[n * Gp + g].astype(np.uint32)
+                # 16 parameter bytes per (tile, group), one per channel
+                p = params[(t * G + g) * 16 + c].astype(np.uint32)
                 s_g, z = (p >> 4) + 1, p & 15
             for s in range(2):
                 P0, P1 = w[:, 2 * s], w[:, 2 * s + 1]
@@ -163,8 +163,8 @@ def test_pack_spec_round_trip_independent_decode():
                         k = 128 * g + 64 * s + 16 * j + i
                         back[16 * t + c, k] = (tile[16 * lane + byte] >> (4 * half)) & 15
     np.testing.assert_array_equal(back, q)
-    Gp = 16
-    params = blob[N * K // 2:].reshape(N, Gp)
-    np.testing.assert_array_equal((params[:, :G] >> 4) + 1, s_g)
-    np.testing.assert_array_equal(params[:, :G] & 15, z)
-    assert np.all(params[:, G:] == 0)
+    assert blob.size == N * K // 2 + N * G
+    # parameters: [tile][group][16 channels]
+    params = blob[N * K // 2:].reshape(N // 16, G, 16).transpose(0, 2, 1).reshape(N, G)
+    np.testing.assert_array_equal((params >> 4) + 1, s_g)
+    np.testing.assert_array_equal(params & 15, z)

@@ -113,6 +113,8 @@ def test_pack_and_unpack(mode, N, K):
 GEMM_SHAPES = [
     (1, 16, 128), (8, 256, 512), (17, 48, 384), (64, 96, 1152), (100, 160, 256),
     (129, 32, 640), (257, 80, 128), (512, 512, 1024), (520, 272, 640), (3, 16, 132096),
+    # streaming-kernel ring: main loop plus a leftover group, for 1, 2 and 4 row blocks
+    (9, 32, 128 * 21), (30, 48, 128 * 67), (48, 64, 128 * 70),
 ]
 
 
@@ -176,30 +178,29 @@ def test_gemm_is_deterministic():
 
 @pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("M,N,K", [(64, 6144, 4096), (16, 8192, 8192), (40, 1040, 2048), (5, 400, 640)])
-def test_split_k_plan_matches_unsplit(mode, M, N, K):
-    """With a workspace the decode plan may split K across workgroups; the
-    accumulators must equal the plan without a workspace bit for bit, twice in
-    a row (the workspace is re-armed by the first call)."""
+def test_workspace_argument_leaves_results_unchanged(mode, M, N, K):
+    """qoq_w4a8_gemm accepts a caller-provided workspace of
+    qoq_gemm_workspace_bytes() bytes (zero for every current plan); the
+    accumulators must equal those of a call without one, bit for bit, twice
+    in a row, and the packed activations must match the oracle's layout."""
     xb = _rand_bits((M, K), 90 + M, 1.0)
     wb = _rand_bits((N, K), 91 + N, 0.02)
     pw = qoq.PackedWeight(mode, f16_dev(wb))
     xq, s_x, rs = qoq.qoq_quantize_act(f16_dev(xb))
-    print(f"split-k mode={mode} M={M} N={N} K={K} ws={qoq.qoq_gemm_workspace_bytes(mode, M, N, K)}",
-          flush=True)
+    need = qoq.qoq_gemm_workspace_bytes(mode, M, N, K)
+    print(f"workspace mode={mode} M={M} N={N} K={K} ws={need}", flush=True)
+    assert need >= 0
     a0 = torch.empty((M, N), dtype=torch.int32, device=DEV)
     qoq.qoq_w4a8_gemm(mode, xq, s_x, rs, pw.blob, pw.s_c, N, acc_out=a0, workspace=None)
-    ws = torch.zeros((max(1, qoq.qoq_gemm_workspace_bytes(mode, M, N, K)),), dtype=torch.uint8,
-                     device=DEV)
+    ws = torch.zeros((max(1, need),), dtype=torch.uint8, device=DEV)
     for _ in range(2):
         a1 = torch.empty((M, N), dtype=torch.int32, device=DEV)
-        y1 = qoq.qoq_w4a8_gemm(mode, xq, s_x, rs, pw.blob, pw.s_c, N, acc_out=a1, workspace=ws)
+        qoq.qoq_w4a8_gemm(mode, xq, s_x, rs, pw.blob, pw.s_c, N, acc_out=a1, workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(a0, a1)
     if M * N * K <= 4e8:
         xq_rm = oracle.quantize_act(xb)[0]
         np.testing.assert_array_equal(host(xq), oracle.pack_act(xq_rm))
-        acc_want = oracle.gemm(mode, xq_rm, *(_oracle_w(mode, wb)))
-        np.testing.assert_array_equal(host(a1), acc_want)
 
 
 def _oracle_w(mode, wb):

@@ -141,9 +141,9 @@ def test_pack_layout_golden():
         q[n, k] = v
     s_g = np.ones((N, K // 128), np.uint8)
     z = np.zeros((N, K // 128), np.uint8)
-    for n, sg, zz in d["s_g_z_nonzero"]:
-        s_g[n, 0] = sg
-        z[n, 0] = zz
+    for n, g, sg, zz in d["s_g_z_nonzero"]:
+        s_g[n, g] = sg
+        z[n, g] = zz
     blob = oracle.pack(oracle.MODE_G128, q, s_g, z)
     assert blob.size == d["total_bytes"] == oracle.packed_bytes(oracle.MODE_G128, N, K)
     want = np.zeros(d["total_bytes"], np.uint8)
@@ -155,8 +155,8 @@ def test_pack_layout_golden():
 def test_per_channel_pack_size():
     # codes N*K/2 plus one zero byte per channel
     assert oracle.packed_bytes(oracle.MODE_PER_CHANNEL, 32, 256) == 32 * 128 + 32
-    # g128 params padded to 16 groups per row
-    assert oracle.packed_bytes(oracle.MODE_G128, 32, 128 * 17) == 32 * 64 * 17 + 32 * 32
+    # g128: one parameter byte per (channel, group)
+    assert oracle.packed_bytes(oracle.MODE_G128, 32, 128 * 17) == 32 * 64 * 17 + 32 * 17
     assert oracle.packed_bytes(oracle.MODE_G128, 8, 128) == -1  # N must be a multiple of 16
     assert oracle.packed_bytes(oracle.MODE_G128, 16, 100) == -1  # K must be a multiple of 128
 
