@@ -392,7 +392,7 @@ __global__ __launch_bounds__(WN * 64, 2) void k_gemm_wide(
     const int8_t* __restrict__ xq, const uint16_t* __restrict__ s_x,
     const int32_t* __restrict__ rowsum, const uint8_t* __restrict__ blob,
     const uint16_t* __restrict__ s_c, int M, int N, int K, uint16_t* __restrict__ y,
-    int32_t* __restrict__ acc_out) {
+    int32_t* __restrict__ acc_out, int group_m) {
     constexpr int kThr = WN * 64;
     constexpr int TM = BM / 16;
     constexpr int TN = BN / WN / 16;
@@ -411,14 +411,14 @@ __global__ __launch_bounds__(WN * 64, 2) void k_gemm_wide(
     const int tiles = N / 16;
     const int grid_m = (M + BM - 1) / BM, grid_n = (N + BN - 1) / BN;
 
-    // Block renumbering: contiguous range per XCD, then groups of 4 block rows.
+    // Block renumbering: contiguous range per XCD, then groups of group_m block
+    // rows.
     int pid = blockIdx.x;
     const int nblocks = grid_m * grid_n;
     if (nblocks % 8 == 0) pid = (pid % 8) * (nblocks / 8) + pid / 8;
-    constexpr int kGroupM = 4;
-    const int per_group = kGroupM * grid_n;
-    const int first_m = (pid / per_group) * kGroupM;
-    const int gsz = min(grid_m - first_m, kGroupM);
+    const int per_group = group_m * grid_n;
+    const int first_m = (pid / per_group) * group_m;
+    const int gsz = min(grid_m - first_m, group_m);
     const int bm = first_m + (pid % per_group) % gsz;
     const int bn = (pid % per_group) / gsz;
 
@@ -475,24 +475,29 @@ __global__ __launch_bounds__(WN * 64, 2) void k_gemm_wide(
     wide_load_b<kG128, TN>(b0q, p0q, rb, rp, b_off, p_off, 0);
     __syncthreads();
 
-    // Same two-buffer pipeline as the 16-row-wave kernel above: in step h the
-    // staged activations of group h+1 go to the idle buffer, the loads of
-    // groups h+2 (activations) and h+1 (weights) are issued, then group h runs.
+    // Step h: issue the weight loads of group h+1, run group h, then publish
+    // the staged activations of group h+1 into the idle buffer and issue the
+    // activation loads of group h+2. The wait for the staged activations thus
+    // falls after the step's matrix-core operations are issued, and every load
+    // has a whole step to arrive. Two steps per iteration give each buffer and
+    // register set a fixed name; both halves are unconditional (a branch would
+    // let the compiler sink loads to their use), and an odd group count ends
+    // with one more step. Look-ahead group indices are clamped at the end.
     int h = 0;
     for (; h + 1 < G; h += 2) {
-        tile_store_a<kAPerThr, kThr>(lds_a1, stage);
-        wide_load_a(stage, ra, a_off, (uint32_t)min(h + 2, G - 1) * a_step);
         wide_load_b<kG128, TN>(b1q, p1q, rb, rp, b_off, p_off, h + 1);
         __builtin_amdgcn_sched_barrier(0);
         wide_compute<kG128, TM, TN>(acc, lw0, b0q, p0q, lut);
         __builtin_amdgcn_sched_barrier(0);
+        tile_store_a<kAPerThr, kThr>(lds_a1, stage);
+        wide_load_a(stage, ra, a_off, (uint32_t)min(h + 2, G - 1) * a_step);
         __syncthreads();
-        tile_store_a<kAPerThr, kThr>(lds_a0, stage);
-        wide_load_a(stage, ra, a_off, (uint32_t)min(h + 3, G - 1) * a_step);
         wide_load_b<kG128, TN>(b0q, p0q, rb, rp, b_off, p_off, min(h + 2, G - 1));
         __builtin_amdgcn_sched_barrier(0);
         wide_compute<kG128, TM, TN>(acc, lw1, b1q, p1q, lut);
         __builtin_amdgcn_sched_barrier(0);
+        tile_store_a<kAPerThr, kThr>(lds_a0, stage);
+        wide_load_a(stage, ra, a_off, (uint32_t)min(h + 3, G - 1) * a_step);
         __syncthreads();
     }
     if (h < G) wide_compute<kG128, TM, TN>(acc, lw0, b0q, p0q, lut);
@@ -692,11 +697,12 @@ struct Plan {
     int kind = kSimple;
     int mb = 0, nt = 0, r = 2, w = 8;  // stream kernel: row blocks, tiles, ring depth, waves
     int bn = 256;                      // 16-row-wave tiled kernel: 128 x bn blocks
+    int group_m = 4;                   // wide kernel: block rows per XCD raster group
     int64_t nblk = 0;
 };
 
 #ifdef QOQ_TUNING
-int g_force_kind = 0, g_force_nt = 0, g_force_r = 0, g_force_w = 0, g_force_bn = 0;
+int g_force_kind = 0, g_force_nt = 0, g_force_r = 0, g_force_w = 0, g_force_bn = 0, g_force_gm = 0;
 #endif
 
 // The buffer-load kernels form 32-bit byte offsets, and mark prefetches past
@@ -755,6 +761,7 @@ Plan plan_gemm(int64_t M, int64_t N, int64_t K) {
     if (g_force_r) p.r = g_force_r;
     if (g_force_w) p.w = g_force_w;
     if (g_force_bn) p.bn = g_force_bn;
+    if (g_force_gm) p.group_m = g_force_gm;
 #endif
     if (p.kind == kStream) p.nblk = (tiles + p.nt - 1) / p.nt;
     return p;
@@ -770,6 +777,7 @@ struct GemmArgs {
     uint16_t* y;
     int32_t* acc_out;
     hipStream_t stream;
+    int group_m;
 };
 
 template <bool kG128, int MB, int NT, int R, int W>
@@ -820,7 +828,8 @@ template <bool kG128, int BM, int BN, int WN>
 void launch_wide_t(const GemmArgs& a) {
     const unsigned blocks = (unsigned)(((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN));
     hipLaunchKernelGGL((k_gemm_wide<kG128, BM, BN, WN>), dim3(blocks), dim3(WN * 64), 0, a.stream,
-                       a.xq, a.s_x, a.rowsum, a.blob, a.s_c, a.M, a.N, a.K, a.y, a.acc_out);
+                       a.xq, a.s_x, a.rowsum, a.blob, a.s_c, a.M, a.N, a.K, a.y, a.acc_out,
+                       a.group_m);
 }
 
 template <bool kG128>
@@ -860,7 +869,8 @@ void launch_gemm(int mode, const int8_t* xq, const uint16_t* s_x, const int32_t*
                  const uint8_t* blob, const uint16_t* s_c, int64_t M, int64_t N, int64_t K,
                  uint16_t* y, int32_t* acc_out, void* /*ws*/, hipStream_t stream) {
     const Plan p = plan_gemm(M, N, K);
-    const GemmArgs a{xq, s_x, rowsum, blob, s_c, (int)M, (int)N, (int)K, y, acc_out, stream};
+    const GemmArgs a{xq,     s_x, rowsum, blob, s_c, (int)M, (int)N, (int)K,
+                     y,      acc_out, stream, p.group_m};
     if (mode == 0)
         launch_plan<true>(p, a);
     else
@@ -870,7 +880,9 @@ void launch_gemm(int mode, const int8_t* xq, const uint16_t* s_x, const int32_t*
 #ifdef QOQ_TUNING
 // Plan overrides for measurement builds: kind (-1 reference, 2 tiled, 3 wide,
 // 4 streaming; 0 keeps the plan), then the kind's own parameters (0 keeps).
-extern "C" void qoq_tuning_force(int kind, int nt, int r, int w, int bn) {
+// gm: block rows per XCD raster group of the wide kernel.
+extern "C" void qoq_tuning_force(int kind, int nt, int r, int w, int bn, int gm) {
+    g_force_gm = gm;
     g_force_kind = kind;
     g_force_nt = nt;
     g_force_r = r;
