@@ -117,6 +117,80 @@ __global__ __launch_bounds__(kThreads) void k_quantize_act(const uint16_t* __res
     }
 }
 
+// The same quantization with the row held in registers (CH runs of 16 inputs
+// per thread): one read of the row instead of two. Used for
+// K <= 16 * kThreads * CH.
+template <int CH>
+__global__ __launch_bounds__(kThreads) void k_quantize_act_reg(const uint16_t* __restrict__ x,
+                                                               int M, int K,
+                                                               int8_t* __restrict__ xq,
+                                                               uint16_t* __restrict__ s_x,
+                                                               int32_t* __restrict__ rowsum) {
+    __shared__ unsigned red_u[kWaves];
+    __shared__ int red_i[kWaves];
+    const int m = blockIdx.x;
+    const int U = gridDim.x / 16;  // grid = Mp rows
+    const int u = m / 16, r = m % 16;
+    const int nchunk = K / 16;
+    u32x4* out = reinterpret_cast<u32x4*>(xq);
+    // 16-byte slot of chunk c (inputs 16c .. 16c+15) of this row.
+    auto slot = [&](int c) {
+        const int g = c / 8, s = (c / 4) % 2, j = c % 4;
+        return ((size_t)g * U + u) * 128 + 64 * s + 16 * j + r;
+    };
+    if (m >= M) {
+        for (int c = threadIdx.x; c < nchunk; c += kThreads) out[slot(c)] = u32x4{0u, 0u, 0u, 0u};
+        return;
+    }
+    const u32x4* row = reinterpret_cast<const u32x4*>(x + (size_t)m * K);
+    u32x4 v0[CH], v1[CH];
+    unsigned amax = 0;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int c = threadIdx.x + kThreads * i;
+        v0[i] = u32x4{0u, 0u, 0u, 0u};
+        v1[i] = u32x4{0u, 0u, 0u, 0u};
+        if (c < nchunk) {
+            v0[i] = row[2 * c];
+            v1[i] = row[2 * c + 1];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            amax = max(amax, max(absmax_bits2(v0[i][e]), absmax_bits2(v1[i][e])));
+    }
+    amax = block_reduce(amax, red_u, MaxU{});
+    const uint16_t sbits = f2h(h2f(amax) / 127.0f);
+    const float sf = h2f(sbits);
+
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int c = threadIdx.x + kThreads * i;
+        if (c < nchunk) {
+            u32x4 o = u32x4{0u, 0u, 0u, 0u};
+            if (sf != 0.0f) {
+                const uint32_t w[8] = {v0[i][0], v0[i][1], v0[i][2], v0[i][3],
+                                       v1[i][0], v1[i][1], v1[i][2], v1[i][3]};
+                uint32_t packed[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const uint32_t hb = (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu);
+                    const int q = quant_act1(hb, sf);
+                    sum += q;
+                    packed[e >> 2] |= (uint32_t)(q & 0xFF) << (8 * (e & 3));
+                }
+                o = u32x4{packed[0], packed[1], packed[2], packed[3]};
+            }
+            out[slot(c)] = o;
+        }
+    }
+    if (rowsum) sum = block_reduce(sum, red_i, SumI{});
+    if (threadIdx.x == 0) {
+        s_x[m] = sbits;
+        if (rowsum) rowsum[m] = sum;
+    }
+}
+
 // Progressive group quantization, one workgroup per output channel.
 // Stage 1 needs the row's largest magnitude; stage 2 runs one wave per group
 // of 128, two inputs per lane.
@@ -230,8 +304,18 @@ __global__ __launch_bounds__(kThreads) void k_quantize_weights_pc(
 void launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, uint16_t* s_x,
                          int32_t* rowsum, hipStream_t stream) {
     const unsigned mp = (unsigned)((M + 15) / 16 * 16);
-    hipLaunchKernelGGL(k_quantize_act, dim3(mp), dim3(kThreads), 0, stream, x, (int)M, (int)K, xq,
-                       s_x, rowsum);
+    const int64_t runs = K / 16;  // 16-input runs per row
+#define QOQ_REG(CHV)                                                                          \
+    hipLaunchKernelGGL(k_quantize_act_reg<CHV>, dim3(mp), dim3(kThreads), 0, stream, x, (int)M, \
+                       (int)K, xq, s_x, rowsum)
+    if (runs <= kThreads) QOQ_REG(1);
+    else if (runs <= 2 * kThreads) QOQ_REG(2);
+    else if (runs <= 4 * kThreads) QOQ_REG(4);
+    else if (runs <= 8 * kThreads) QOQ_REG(8);
+    else
+        hipLaunchKernelGGL(k_quantize_act, dim3(mp), dim3(kThreads), 0, stream, x, (int)M, (int)K,
+                           xq, s_x, rowsum);
+#undef QOQ_REG
 }
 
 void launch_quantize_weights(int mode, const uint16_t* w, int64_t N, int64_t K, uint8_t* q,

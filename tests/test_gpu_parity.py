@@ -50,7 +50,11 @@ def _special_rows(x_bits):
 
 
 # ------------------------------------------------------------ activations --
-@pytest.mark.parametrize("M,K", [(1, 128), (7, 384), (64, 4096), (300, 1152), (3, 132096)])
+# K covers each register-resident row size (up to 4096, 8192, 16384 and 32768
+# inputs per row, ragged within them), the first size above them, and the
+# largest K.
+@pytest.mark.parametrize("M,K", [(1, 128), (7, 384), (64, 4096), (300, 1152), (5, 8192),
+                                 (4, 14336), (3, 24576), (2, 32768 + 128), (3, 132096)])
 def test_quantize_act(M, K):
     xb = _special_rows(_rand_bits((M, K), 10 + M, 1.0))
     print(f"quantize_act M={M} K={K}", flush=True)
