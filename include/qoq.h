@@ -170,10 +170,11 @@ qoq_status qoq_quantize_act(const uint16_t* x, int64_t M, int64_t K, int8_t* xq,
                             uint16_t* s_x, int32_t* rowsum, void* stream);
 
 /*
- * Scratch bytes that qoq_w4a8_gemm needs for this shape, or -1 for an
- * unsupported shape or mode. Every current plan keeps all partial sums inside
- * one workgroup, so this is 0; the workspace arguments exist so that a plan
- * with a cross-workgroup reduction can be added without changing the ABI.
+ * Workspace bytes that qoq_w4a8_gemm uses for this shape when it is given a
+ * workspace (0 if its plan needs none), or -1 for an unsupported shape or
+ * mode. For M > 64 with too few output blocks to cover the compute units, the
+ * plan splits K into S ranges whose exact INT32 partial sums (S*M*N*4 bytes)
+ * are added by a second kernel; without a workspace the unsplit plan runs.
  */
 int64_t qoq_gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K);
 
@@ -190,10 +191,11 @@ int64_t qoq_gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K);
  *   y[m,n]   = f16( (f32(acc) * f32(s_x[m])) * f32(s_c[n]) )  (FP16 [M,N])
  *   acc_out  [M,N] int32 receives acc when not NULL (for inspection).
  *
- *   workspace: NULL, or device memory of workspace_bytes bytes. A workspace
- *   smaller than qoq_gemm_workspace_bytes(mode, M, N, K) gives
- *   QOQ_ERR_WORKSPACE; with the current plans none is needed and a given one
- *   is not touched.
+ *   workspace: NULL, or device memory of workspace_bytes bytes, used for
+ *   split-K partial sums (no initialisation needed; its contents are
+ *   overwritten). A workspace smaller than qoq_gemm_workspace_bytes(mode, M,
+ *   N, K) gives QOQ_ERR_WORKSPACE. Calls that overlap in time (e.g. on
+ *   different streams) must not share a workspace.
  */
 qoq_status qoq_w4a8_gemm(int mode, const int8_t* xq, const uint16_t* s_x, const int32_t* rowsum,
                          const void* blob, const uint16_t* s_c, int64_t M, int64_t N, int64_t K,

@@ -225,8 +225,8 @@ _workspaces = {}
 
 
 def gemm_workspace(mode, M: int, N: int, K: int, device) -> Optional[torch.Tensor]:
-    """The device's shared zero-filled workspace when the plan for this shape
-    needs scratch memory, else None (no current plan needs any).
+    """The device's shared workspace when the plan for this shape uses one
+    (split-K partial sums), else None.
 
     One workspace per device is shared by every call that does not bring its
     own, so calls issued concurrently on different streams must pass their own."""

@@ -16,6 +16,7 @@
 // B = weights (16 channels n). For both operands lane l holds row/channel
 // l % 16 and bytes 16*(l/16) .. +15 of the 64-wide k slice; the accumulator
 // lane l holds rows 4*(l/16) + 0..3 of channel l % 16.
+#include <algorithm>
 #include <cmath>
 
 #include "qoq_device.hpp"
@@ -26,6 +27,16 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / kWave;
+
+// FP16 output of one accumulator: (f32(acc) * s_x) * s_c, each product rounded
+// to fp32, then the result rounded to FP16.
+__device__ __forceinline__ uint16_t output_value(int r, float sx, float sc) {
+    float v = ((float)r * sx) * sc;
+    // Without this barrier the backend folds the last multiply and the
+    // conversion into one mixed-precision FMA that rounds only once.
+    asm("" : "+v"(v));
+    return f2h(v);
+}
 
 // Epilogue for one lane's four accumulator rows of one channel.
 template <bool kG128>
@@ -42,12 +53,7 @@ __device__ __forceinline__ void store_outputs(int32x4 a, int m_first, int n, int
             if (!kG128) r -= zpc * rowsum[m];
             const size_t o = (size_t)m * N + n;
             if (acc_out) acc_out[o] = r;
-            float v = ((float)r * h2f(s_x[m])) * sc;
-            // The contract rounds the product to fp32, then to FP16. Without this
-            // barrier the backend folds the last multiply and the conversion into
-            // one mixed-precision FMA that rounds only once.
-            asm("" : "+v"(v));
-            y[o] = f2h(v);
+            y[o] = output_value(r, h2f(s_x[m]), sc);
         }
     }
 }
@@ -176,7 +182,7 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void k_gemm_tile(
     const int8_t* __restrict__ xq, const uint16_t* __restrict__ s_x,
     const int32_t* __restrict__ rowsum, const uint8_t* __restrict__ blob,
     const uint16_t* __restrict__ s_c, int M, int N, int K, uint16_t* __restrict__ y,
-    int32_t* __restrict__ acc_out) {
+    int32_t* __restrict__ acc_out, int S, int32_t* __restrict__ part) {
     constexpr int kThr = WM * WN * 64;
     constexpr int TM = BM / WM / 16;
     constexpr int TN = BN / WN / 16;
@@ -197,9 +203,15 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void k_gemm_tile(
     const int tiles = N / 16;
     const int grid_m = (M + BM - 1) / BM, grid_n = (N + BN - 1) / BN;
 
-    // Block renumbering: contiguous range per XCD, then groups of 4 block rows.
-    int pid = blockIdx.x;
+    // With S > 1 the grid holds S copies of the block grid, copy s taking the
+    // groups [G*s/S, G*(s+1)/S) and writing its INT32 partial sums to part[s].
     const int nblocks = grid_m * grid_n;
+    const int split = blockIdx.x / nblocks;
+    const int g0 = (int)((int64_t)G * split / S);
+    const int Gc = (int)((int64_t)G * (split + 1) / S) - g0;  // >= 1: the plan keeps S <= G
+
+    // Block renumbering: contiguous range per XCD, then groups of 4 block rows.
+    int pid = blockIdx.x - split * nblocks;
     if (nblocks % 8 == 0) pid = (pid % 8) * (nblocks / 8) + pid / 8;
     constexpr int kGroupM = 4;
     const int per_group = kGroupM * grid_n;
@@ -246,10 +258,10 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void k_gemm_tile(
 
     // Prologue: group 0 in buffer 0, group 1 in flight to the staging
     // registers, weights of group 0 in flight.
-    tile_load_a(stage, act, a_src, 0);
+    tile_load_a(stage, act, a_src, (size_t)g0 * a_stride);
     tile_store_a<kAPerThr, kThr>(lds_a0, stage);
-    tile_load_a(stage, act, a_src, (size_t)min(1, G - 1) * a_stride);
-    tile_load_b<kG128, TN>(b0q, p0q, bptr, pptr, 0);
+    tile_load_a(stage, act, a_src, (size_t)(g0 + min(1, Gc - 1)) * a_stride);
+    tile_load_b<kG128, TN>(b0q, p0q, bptr, pptr, g0);
     __syncthreads();
 
     // Step h: publish the staged activations of group h+1 into the idle
@@ -262,39 +274,76 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void k_gemm_tile(
     // count finishes with one more step on buffer 0. Group indices of the
     // look-ahead loads are clamped at the end (those loads are never used).
     int h = 0;
-    for (; h + 1 < G; h += 2) {
+    for (; h + 1 < Gc; h += 2) {
         tile_store_a<kAPerThr, kThr>(lds_a1, stage);
-        tile_load_a(stage, act, a_src, (size_t)min(h + 2, G - 1) * a_stride);
-        tile_load_b<kG128, TN>(b1q, p1q, bptr, pptr, h + 1);
+        tile_load_a(stage, act, a_src, (size_t)(g0 + min(h + 2, Gc - 1)) * a_stride);
+        tile_load_b<kG128, TN>(b1q, p1q, bptr, pptr, g0 + h + 1);
         __builtin_amdgcn_sched_barrier(0);
         tile_compute<kG128, TM, TN>(acc, lw0, b0q, p0q);
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
         tile_store_a<kAPerThr, kThr>(lds_a0, stage);
-        tile_load_a(stage, act, a_src, (size_t)min(h + 3, G - 1) * a_stride);
-        tile_load_b<kG128, TN>(b0q, p0q, bptr, pptr, min(h + 2, G - 1));
+        tile_load_a(stage, act, a_src, (size_t)(g0 + min(h + 3, Gc - 1)) * a_stride);
+        tile_load_b<kG128, TN>(b0q, p0q, bptr, pptr, g0 + min(h + 2, Gc - 1));
         __builtin_amdgcn_sched_barrier(0);
         tile_compute<kG128, TM, TN>(acc, lw1, b1q, p1q);
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
     }
-    if (h < G) tile_compute<kG128, TM, TN>(acc, lw0, b0q, p0q);
+    if (h < Gc) tile_compute<kG128, TM, TN>(acc, lw0, b0q, p0q);
 
-    // Epilogue.
+    // Epilogue (with S > 1: the raw partial sums; the reduction kernel adds
+    // them and applies the zero-point compensation and the rescale once).
     const uint8_t* pc_z = params;
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
         const int t = bn * (BN / 16) + wn * TN + i;
         if (t >= tiles) continue;
         const int n = 16 * t + c;
-        const float sc = h2f(s_c[n]);
-        const int zpc = kG128 ? 0 : (int)pc_z[n];
 #pragma unroll
         for (int a = 0; a < TM; ++a) {
             const int m_first = bm * BM + (wm * TM + a) * 16 + 4 * j;
-            store_outputs<kG128>(acc[a][i], m_first, n, M, N, s_x, rowsum, sc, zpc, y, acc_out);
+            if (part) {
+                int32_t* dst = part + (size_t)split * M * N;
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (m_first + v < M) dst[(size_t)(m_first + v) * N + n] = acc[a][i][v];
+            } else {
+                store_outputs<kG128>(acc[a][i], m_first, n, M, N, s_x, rowsum, h2f(s_c[n]),
+                                     kG128 ? 0 : (int)pc_z[n], y, acc_out);
+            }
         }
     }
+}
+
+// Split-K reduction: adds the S partial sums of each output (INT32 addition is
+// exact and order-free), applies the per-channel zero-point compensation and
+// the one-time rescale. Each thread handles four consecutive channels of one
+// row (N is a multiple of 16).
+template <bool kG128>
+__global__ __launch_bounds__(kThreads) void k_splitk_reduce(
+    const int32_t* __restrict__ part, int S, const uint16_t* __restrict__ s_x,
+    const int32_t* __restrict__ rowsum, const uint8_t* __restrict__ pc_z,
+    const uint16_t* __restrict__ s_c, int M, int N, uint16_t* __restrict__ y,
+    int32_t* __restrict__ acc_out) {
+    const int64_t q = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t total = (int64_t)M * N;
+    if (q * 4 >= total) return;
+    const int m = (int)(q * 4 / N), n0 = (int)(q * 4 % N);
+    int32x4 r = reinterpret_cast<const int32x4*>(part)[q];
+    for (int s2 = 1; s2 < S; ++s2) r += reinterpret_cast<const int32x4*>(part + (size_t)s2 * total)[q];
+    const float sx = h2f(s_x[m]);
+    uint16_t out[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int n = n0 + v;
+        int rr = r[v];
+        if (!kG128) rr -= (int)pc_z[n] * rowsum[m];
+        if (acc_out) acc_out[(size_t)m * N + n] = rr;
+        out[v] = output_value(rr, sx, h2f(s_c[n]));
+    }
+    reinterpret_cast<uint2*>(y)[q] = make_uint2(out[0] | ((uint32_t)out[1] << 16),
+                                                out[2] | ((uint32_t)out[3] << 16));
 }
 
 // ---------------------------------------------------------------------------
@@ -697,6 +746,8 @@ struct Plan {
     int kind = kSimple;
     int mb = 0, nt = 0, r = 2, w = 8;  // stream kernel: row blocks, tiles, ring depth, waves
     int bn = 256;                      // 16-row-wave tiled kernel: 128 x bn blocks
+    int s = 1;                         //   and its K splits (partial sums in the workspace)
+    int64_t ws_bytes = 0;
     int group_m = 4;                   // wide kernel: block rows per XCD raster group
     int64_t nblk = 0;
 };
@@ -722,11 +773,11 @@ bool fits_buffer_offsets(int64_t M, int64_t N, int64_t K) {
 //     of 16 waves).
 //   M >= 512: the wide-wave tiled kernel with 128 x 256 blocks.
 //   64 < M < 512: fewer than two 128 x 256 blocks per compute unit exist; the
-//     16-row-wave tiled kernel with 128 x 256 blocks, or 128 x 128 when even
-//     those are too few.
+//     16-row-wave tiled kernel, split over K when its blocks do not cover the
+//     compute units and a workspace is given.
 // Shapes whose offsets do not fit the buffer-load kernels take the reference
 // kernel (M <= 64) or the 16-row-wave tiled kernel (M > 64).
-Plan plan_gemm(int64_t M, int64_t N, int64_t K) {
+Plan plan_gemm(int64_t M, int64_t N, int64_t K, bool have_ws) {
     Plan p;
     const int64_t tiles = N / 16;
     const bool fits = fits_buffer_offsets(M, N, K);
@@ -747,8 +798,17 @@ Plan plan_gemm(int64_t M, int64_t N, int64_t K) {
         p.kind = kWide;
     } else {
         p.kind = kTile;
-        const int64_t gm128 = (M + 127) / 128, gn256 = (N + 255) / 256;
-        p.bn = gm128 * gn256 >= kCUs / 2 ? 256 : 128;
+        const int64_t gm128 = (M + 127) / 128, gn256 = (N + 255) / 256, gn128 = (N + 127) / 128;
+        // 128 x 256 blocks once they alone cover the compute units, else
+        // 128 x 128; if even those are fewer than the compute units, split K
+        // (at least two groups per split) until they cover them. The partial
+        // sums then cost 8 * S * M * N bytes of traffic, small next to the
+        // GEMM for these shapes.
+        p.bn = gm128 * gn256 >= kCUs ? 256 : 128;
+        const int64_t nblk = gm128 * (p.bn == 256 ? gn256 : gn128);
+        if (nblk < kCUs)
+            p.s = (int)std::min<int64_t>(std::min<int64_t>(8, (kCUs + nblk - 1) / nblk), K / kGroup / 2);
+        if (p.s < 1) p.s = 1;
     }
 #ifdef QOQ_TUNING
     if (g_force_kind) {
@@ -762,12 +822,17 @@ Plan plan_gemm(int64_t M, int64_t N, int64_t K) {
     if (g_force_w) p.w = g_force_w;
     if (g_force_bn) p.bn = g_force_bn;
     if (g_force_gm) p.group_m = g_force_gm;
+    if (p.kind == kTile && g_force_nt) p.s = std::max(1, std::min<int>(g_force_nt, (int)(K / kGroup)));
 #endif
     if (p.kind == kStream) p.nblk = (tiles + p.nt - 1) / p.nt;
+    if (p.kind != kTile) p.s = 1;
+    p.ws_bytes = p.s > 1 ? (int64_t)p.s * M * N * 4 : 0;
+    if (!have_ws) p.s = 1;
     return p;
 }
 
 struct GemmArgs {
+    int32_t* part;  // split-K partial sums (workspace), or null
     const int8_t* xq;
     const uint16_t* s_x;
     const int32_t* rowsum;
@@ -817,11 +882,18 @@ void launch_stream(const Plan& p, const GemmArgs& a) {
 }
 
 template <bool kG128, int BM, int BN, int WM, int WN>
-void launch_tile_t(const GemmArgs& a) {
-    const unsigned blocks = (unsigned)(((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN));
+void launch_tile_t(const Plan& p, const GemmArgs& a) {
+    const unsigned blocks = (unsigned)(((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * p.s);
+    int32_t* part = p.s > 1 ? a.part : nullptr;
     hipLaunchKernelGGL((k_gemm_tile<kG128, BM, BN, WM, WN>), dim3(blocks), dim3(WM * WN * 64), 0,
                        a.stream, a.xq, a.s_x, a.rowsum, a.blob, a.s_c, a.M, a.N, a.K, a.y,
-                       a.acc_out);
+                       a.acc_out, p.s, part);
+    if (part) {
+        const int64_t quads = (int64_t)a.M * a.N / 4;
+        hipLaunchKernelGGL(k_splitk_reduce<kG128>, dim3((unsigned)((quads + kThreads - 1) / kThreads)),
+                           dim3(kThreads), 0, a.stream, part, p.s, a.s_x, a.rowsum,
+                           a.blob + (size_t)a.N * a.K / 2, a.s_c, a.M, a.N, a.y, a.acc_out);
+    }
 }
 
 template <bool kG128, int BM, int BN, int WN>
@@ -849,8 +921,8 @@ void launch_plan(const Plan& p, const GemmArgs& a) {
             launch_wide_t<kG128, 128, 256, 4>(a);
             break;
         case kTile:
-            if (p.bn == 256) launch_tile_t<kG128, 128, 256, 2, 4>(a);
-            else launch_tile_t<kG128, 128, 128, 2, 2>(a);
+            if (p.bn == 256) launch_tile_t<kG128, 128, 256, 2, 4>(p, a);
+            else launch_tile_t<kG128, 128, 128, 2, 2>(p, a);
             break;
         default:
             launch_simple<kG128>(a);
@@ -860,17 +932,16 @@ void launch_plan(const Plan& p, const GemmArgs& a) {
 
 }  // namespace
 
-// No current plan needs scratch memory.
-int64_t gemm_workspace_bytes(int /*mode*/, int64_t /*M*/, int64_t /*N*/, int64_t /*K*/) {
-    return 0;
+int64_t gemm_workspace_bytes(int /*mode*/, int64_t M, int64_t N, int64_t K) {
+    return plan_gemm(M, N, K, true).ws_bytes;
 }
 
 void launch_gemm(int mode, const int8_t* xq, const uint16_t* s_x, const int32_t* rowsum,
                  const uint8_t* blob, const uint16_t* s_c, int64_t M, int64_t N, int64_t K,
-                 uint16_t* y, int32_t* acc_out, void* /*ws*/, hipStream_t stream) {
-    const Plan p = plan_gemm(M, N, K);
-    const GemmArgs a{xq,     s_x, rowsum, blob, s_c, (int)M, (int)N, (int)K,
-                     y,      acc_out, stream, p.group_m};
+                 uint16_t* y, int32_t* acc_out, void* ws, hipStream_t stream) {
+    const Plan p = plan_gemm(M, N, K, ws != nullptr);
+    const GemmArgs a{static_cast<int32_t*>(ws), xq, s_x, rowsum, blob, s_c, (int)M, (int)N, (int)K,
+                     y, acc_out, stream, p.group_m};
     if (mode == 0)
         launch_plan<true>(p, a);
     else

@@ -21,10 +21,11 @@ void launch_pack(int mode, const uint8_t* q, const uint8_t* s_g, const uint8_t* 
 void launch_unpack(int mode, const uint8_t* blob, int64_t N, int64_t K, uint8_t* q, uint8_t* s_g,
                    uint8_t* z, hipStream_t stream);
 
-// Workspace bytes the GEMM plan for this shape can use (0: none).
+// Workspace bytes the GEMM plan for this shape uses when given one (0: none).
 int64_t gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K);
 
-// ws: scratch of gemm_workspace_bytes() (currently always 0, so unused).
+// ws: null (a plan without split K is used) or gemm_workspace_bytes() bytes
+// of device memory for split-K partial sums (no initialisation needed).
 void launch_gemm(int mode, const int8_t* xq, const uint16_t* s_x, const int32_t* rowsum,
                  const uint8_t* blob, const uint16_t* s_c, int64_t M, int64_t N, int64_t K,
                  uint16_t* y, int32_t* acc_out, void* ws, hipStream_t stream);

@@ -122,10 +122,10 @@ def test_gemm_validation(lib):
     assert args(blob=U) == ERR_ALIGN
     assert args(acc=U) == ERR_ALIGN
     assert args(ws=U, wsb=1 << 20) == ERR_ALIGN
-    need = lib.qoq_gemm_workspace_bytes(0, 64, 6144, 4096)
-    assert need >= 0
-    if need > 0:
-        assert args(M=64, N=6144, K=4096, ws=A, wsb=need - 1) == ERR_WORKSPACE
+    assert lib.qoq_gemm_workspace_bytes(0, 64, 6144, 4096) == 0  # decode plans need none
+    need = lib.qoq_gemm_workspace_bytes(0, 256, 512, 2048)  # few blocks: split K
+    assert need > 0 and need % (256 * 512 * 4) == 0
+    assert args(M=256, N=512, K=2048, ws=A, wsb=need - 1) == ERR_WORKSPACE
 
 
 def test_workspace_bytes(lib):

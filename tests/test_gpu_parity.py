@@ -119,6 +119,8 @@ GEMM_SHAPES = [
     (129, 32, 640), (257, 80, 128), (512, 512, 1024), (520, 272, 640), (3, 16, 132096),
     # streaming-kernel ring: main loop plus a leftover group, for 1, 2 and 4 row blocks
     (9, 32, 128 * 21), (30, 48, 128 * 67), (48, 64, 128 * 70),
+    # split K over 6 uneven group ranges (13 groups), ragged rows and channels
+    (200, 272, 128 * 13),
 ]
 
 
@@ -181,12 +183,14 @@ def test_gemm_is_deterministic():
 
 
 @pytest.mark.parametrize("mode", MODES)
-@pytest.mark.parametrize("M,N,K", [(64, 6144, 4096), (16, 8192, 8192), (40, 1040, 2048), (5, 400, 640)])
+@pytest.mark.parametrize("M,N,K", [(64, 6144, 4096), (16, 8192, 8192), (40, 1040, 2048), (5, 400, 640),
+                                   (256, 512, 2048), (100, 1040, 1152), (300, 2048, 640)])
 def test_workspace_argument_leaves_results_unchanged(mode, M, N, K):
-    """qoq_w4a8_gemm accepts a caller-provided workspace of
-    qoq_gemm_workspace_bytes() bytes (zero for every current plan); the
-    accumulators must equal those of a call without one, bit for bit, twice
-    in a row, and the packed activations must match the oracle's layout."""
+    """With a workspace of qoq_gemm_workspace_bytes() bytes the plan may split
+    K (M > 64 with few output blocks); the accumulators and outputs must equal
+    those of the unsplit plan (no workspace) bit for bit, twice in a row with
+    the workspace reused (first filled with junk), and the packed activations
+    must match the oracle's layout."""
     xb = _rand_bits((M, K), 90 + M, 1.0)
     wb = _rand_bits((N, K), 91 + N, 0.02)
     pw = qoq.PackedWeight(mode, f16_dev(wb))
@@ -195,13 +199,15 @@ def test_workspace_argument_leaves_results_unchanged(mode, M, N, K):
     print(f"workspace mode={mode} M={M} N={N} K={K} ws={need}", flush=True)
     assert need >= 0
     a0 = torch.empty((M, N), dtype=torch.int32, device=DEV)
-    qoq.qoq_w4a8_gemm(mode, xq, s_x, rs, pw.blob, pw.s_c, N, acc_out=a0, workspace=None)
-    ws = torch.zeros((max(1, need),), dtype=torch.uint8, device=DEV)
+    y0 = qoq.qoq_w4a8_gemm(mode, xq, s_x, rs, pw.blob, pw.s_c, N, acc_out=a0, workspace=None)
+    ws = torch.full((max(16, need),), 0x5A, dtype=torch.uint8, device=DEV)
     for _ in range(2):
         a1 = torch.empty((M, N), dtype=torch.int32, device=DEV)
-        qoq.qoq_w4a8_gemm(mode, xq, s_x, rs, pw.blob, pw.s_c, N, acc_out=a1, workspace=ws)
+        y1 = qoq.qoq_w4a8_gemm(mode, xq, s_x, rs, pw.blob, pw.s_c, N, acc_out=a1, workspace=ws)
+        y2 = qoq.qoq_w4a8_gemm(mode, xq, s_x, rs, pw.blob, pw.s_c, N, workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(a0, a1)
+        assert torch.equal(y0, y1) and torch.equal(y0, y2)
     if M * N * K <= 4e8:
         xq_rm = oracle.quantize_act(xb)[0]
         np.testing.assert_array_equal(host(xq), oracle.pack_act(xq_rm))
