@@ -52,6 +52,9 @@ def parse_args(argv=None):
     p.add_argument("--profile-launches", type=int, default=0,
                    help="instead of timing: launch each kernel of one step this many times on "
                         "cold caches, then a 256 MiB copy as many times (for counter runs)")
+    p.add_argument("--all-layers", action="store_true",
+                   help="instead of the one-line result: time the GEMMs of every layer of "
+                        "every workload and print one line per layer")
     p.add_argument("--pmc-summary", nargs="+", default=None, metavar="DIR",
                    help="instead of timing: read rocprofv3 counter CSVs (FETCH_SIZE run, "
                         "WRITE_SIZE run) of a --profile-launches run and write the traffic "
@@ -171,31 +174,10 @@ def pmc_summary(args, wl, layer) -> int:
     return 0
 
 
-def main(argv=None) -> int:
-    args = parse_args(argv)
-    if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the path is single-GPU and no multi-GPU figure is produced.", file=sys.stderr)
-        return 2
-    if args.steps < 1:
-        print("bench.py: --steps must be >= 1", file=sys.stderr)
-        return 2
-
+def run_layer(args, wl, layer):
+    """Quantize and pack the layer's weights, then time the step over rotating
+    buffer copies; returns the result record (or an int exit code)."""
     from quantized_gemm_qoq_amd import workloads
-
-    wl = workloads.WORKLOADS[args.workload]
-    if args.layer is None and len(wl.layers) != 1:
-        layer_list = ", ".join(l.name for l in wl.layers)
-        print(f"bench.py: workload {wl.name} has several layers ({layer_list}); "
-              "name one with --layer", file=sys.stderr)
-        return 2
-    layers = [l for l in wl.layers if args.layer in (None, l.name)]
-    if not layers:
-        print(f"bench.py: no layer {args.layer} in workload {wl.name}", file=sys.stderr)
-        return 2
-    layer = layers[0]
-    if args.pmc_summary:
-        return pmc_summary(args, wl, layer)
 
     import torch
 
@@ -377,6 +359,49 @@ def main(argv=None) -> int:
         "offline_ms": offline,
         "cpu_baseline": cpu,
     }
+    return out
+
+
+def main(argv=None) -> int:
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the path is single-GPU and no multi-GPU figure is produced.", file=sys.stderr)
+        return 2
+    if args.steps < 1:
+        print("bench.py: --steps must be >= 1", file=sys.stderr)
+        return 2
+
+    from quantized_gemm_qoq_amd import workloads
+
+    wl = workloads.WORKLOADS[args.workload]
+    if args.layer is None and len(wl.layers) != 1:
+        layer_list = ", ".join(l.name for l in wl.layers)
+        print(f"bench.py: workload {wl.name} has several layers ({layer_list}); "
+              "name one with --layer", file=sys.stderr)
+        return 2
+    layers = [l for l in wl.layers if args.layer in (None, l.name)]
+    if not layers:
+        print(f"bench.py: no layer {args.layer} in workload {wl.name}", file=sys.stderr)
+        return 2
+    layer = layers[0]
+    if args.pmc_summary:
+        return pmc_summary(args, wl, layer)
+
+    if args.all_layers:
+        for wl2 in workloads.WORKLOADS.values():
+            for layer2 in wl2.layers:
+                out = run_layer(args, wl2, layer2)
+                if isinstance(out, int):
+                    return out
+                k = {n: {f: v[f] for f in ("avg_us", "GB/s", "TOPS") if f in v}
+                     for n, v in out["kernels"].items()}
+                print(json.dumps({"workload": wl2.name, "layer": layer2.name, "M": layer2.M,
+                                  "K": layer2.K, "N": layer2.N, "kernels": k}), flush=True)
+        return 0
+    out = run_layer(args, wl, layer)
+    if isinstance(out, int):
+        return out
     print(json.dumps(out))
     return 0
 

@@ -19,7 +19,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 
-template <typename T, typename Op>
+template <typename T, typename Op, int kNW = kWaves>
 __device__ __forceinline__ T block_reduce(T v, T* smem, Op wave_op) {
     v = wave_op(v);
     const int wave = threadIdx.x / kWave;
@@ -27,7 +27,7 @@ __device__ __forceinline__ T block_reduce(T v, T* smem, Op wave_op) {
     __syncthreads();
     T r = smem[0];
 #pragma unroll
-    for (int i = 1; i < kWaves; ++i) r = wave_op.combine(r, smem[i]);
+    for (int i = 1; i < kNW; ++i) r = wave_op.combine(r, smem[i]);
     __syncthreads();
     return r;
 }
@@ -118,16 +118,16 @@ __global__ __launch_bounds__(kThreads) void k_quantize_act(const uint16_t* __res
 }
 
 // The same quantization with the row held in registers (CH runs of 16 inputs
-// per thread): one read of the row instead of two. Used for
-// K <= 16 * kThreads * CH.
-template <int CH>
-__global__ __launch_bounds__(kThreads) void k_quantize_act_reg(const uint16_t* __restrict__ x,
-                                                               int M, int K,
-                                                               int8_t* __restrict__ xq,
-                                                               uint16_t* __restrict__ s_x,
-                                                               int32_t* __restrict__ rowsum) {
-    __shared__ unsigned red_u[kWaves];
-    __shared__ int red_i[kWaves];
+// per thread, THR threads per row): one read of the row instead of two. Used
+// for K <= 16 * THR * CH.
+template <int THR, int CH>
+__global__ __launch_bounds__(THR) void k_quantize_act_reg(const uint16_t* __restrict__ x, int M,
+                                                          int K, int8_t* __restrict__ xq,
+                                                          uint16_t* __restrict__ s_x,
+                                                          int32_t* __restrict__ rowsum) {
+    constexpr int kNW = THR / kWave;
+    __shared__ unsigned red_u[kNW];
+    __shared__ int red_i[kNW];
     const int m = blockIdx.x;
     const int U = gridDim.x / 16;  // grid = Mp rows
     const int u = m / 16, r = m % 16;
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize_act_reg(const uint16_t* _
         return ((size_t)g * U + u) * 128 + 64 * s + 16 * j + r;
     };
     if (m >= M) {
-        for (int c = threadIdx.x; c < nchunk; c += kThreads) out[slot(c)] = u32x4{0u, 0u, 0u, 0u};
+        for (int c = threadIdx.x; c < nchunk; c += THR) out[slot(c)] = u32x4{0u, 0u, 0u, 0u};
         return;
     }
     const u32x4* row = reinterpret_cast<const u32x4*>(x + (size_t)m * K);
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize_act_reg(const uint16_t* _
     unsigned amax = 0;
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-        const int c = threadIdx.x + kThreads * i;
+        const int c = threadIdx.x + THR * i;
         v0[i] = u32x4{0u, 0u, 0u, 0u};
         v1[i] = u32x4{0u, 0u, 0u, 0u};
         if (c < nchunk) {
@@ -158,14 +158,14 @@ __global__ __launch_bounds__(kThreads) void k_quantize_act_reg(const uint16_t* _
         for (int e = 0; e < 4; ++e)
             amax = max(amax, max(absmax_bits2(v0[i][e]), absmax_bits2(v1[i][e])));
     }
-    amax = block_reduce(amax, red_u, MaxU{});
+    amax = block_reduce<unsigned, MaxU, kNW>(amax, red_u, MaxU{});
     const uint16_t sbits = f2h(h2f(amax) / 127.0f);
     const float sf = h2f(sbits);
 
     int sum = 0;
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-        const int c = threadIdx.x + kThreads * i;
+        const int c = threadIdx.x + THR * i;
         if (c < nchunk) {
             u32x4 o = u32x4{0u, 0u, 0u, 0u};
             if (sf != 0.0f) {
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize_act_reg(const uint16_t* _
             out[slot(c)] = o;
         }
     }
-    if (rowsum) sum = block_reduce(sum, red_i, SumI{});
+    if (rowsum) sum = block_reduce<int, SumI, kNW>(sum, red_i, SumI{});
     if (threadIdx.x == 0) {
         s_x[m] = sbits;
         if (rowsum) rowsum[m] = sum;
@@ -305,13 +305,15 @@ void launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, ui
                          int32_t* rowsum, hipStream_t stream) {
     const unsigned mp = (unsigned)((M + 15) / 16 * 16);
     const int64_t runs = K / 16;  // 16-input runs per row
-#define QOQ_REG(CHV)                                                                          \
-    hipLaunchKernelGGL(k_quantize_act_reg<CHV>, dim3(mp), dim3(kThreads), 0, stream, x, (int)M, \
-                       (int)K, xq, s_x, rowsum)
-    if (runs <= kThreads) QOQ_REG(1);
-    else if (runs <= 2 * kThreads) QOQ_REG(2);
-    else if (runs <= 4 * kThreads) QOQ_REG(4);
-    else if (runs <= 8 * kThreads) QOQ_REG(8);
+#define QOQ_REG(THRV, CHV)                                                                    \
+    hipLaunchKernelGGL((k_quantize_act_reg<THRV, CHV>), dim3(mp), dim3(THRV), 0, stream, x,      \
+                       (int)M, (int)K, xq, s_x, rowsum)
+    // One or two 16-input runs per thread: 256 threads per row up to K = 8192,
+    // then 1024 (more loads in flight per row, few registers per thread).
+    if (runs <= 256) QOQ_REG(256, 1);
+    else if (runs <= 512) QOQ_REG(256, 2);
+    else if (runs <= 1024) QOQ_REG(1024, 1);
+    else if (runs <= 2048) QOQ_REG(1024, 2);
     else
         hipLaunchKernelGGL(k_quantize_act, dim3(mp), dim3(kThreads), 0, stream, x, (int)M, (int)K,
                            xq, s_x, rowsum);
