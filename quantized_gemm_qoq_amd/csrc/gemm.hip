@@ -644,11 +644,18 @@ __global__ __launch_bounds__(W * 64) void k_gemm_stream(
 
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int nb = blockIdx.x;
     const int G = K / kGroup;
     const int tiles = N / 16;
     const int U = (M + 15) / 16;
     const int c = lane % 16, j = lane / 16;
+    // Block b covers channel tiles [NT*nb, NT*nb + NT) and row tiles
+    // [MB*mh, MB*mh + MB), with b = mh * nblk + nb: the row halves of one
+    // channel band run on the same XCD (blocks are dealt to the XCDs
+    // round-robin), so its weights come from HBM once.
+    const int nblk = (tiles + NT - 1) / NT;
+    const int mh = blockIdx.x / nblk;
+    const int nb = blockIdx.x - mh * nblk;
+    const int u0 = mh * MB;
 
     for (int i = threadIdx.x; i < kPairs * 4 * kWave; i += kThr) red[i] = 0;
     if (kG128)
@@ -678,7 +685,7 @@ __global__ __launch_bounds__(W * 64) void k_gemm_stream(
     const uint32_t a_step = (uint32_t)U * 2048u;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
-        a_off[mb] = (uint32_t)g0 * a_step + (uint32_t)min(mb, U - 1) * 2048u + (uint32_t)lane * 16u;
+        a_off[mb] = (uint32_t)g0 * a_step + (uint32_t)min(u0 + mb, U - 1) * 2048u + (uint32_t)lane * 16u;
 
     int32x4 acc[NT][MB];
 #pragma unroll
@@ -730,8 +737,8 @@ __global__ __launch_bounds__(W * 64) void k_gemm_stream(
 #pragma unroll
         for (int v = 0; v < 4; ++v) a[v] = red[(p * 4 + v) * kWave + lane];
         const int zpc = kG128 ? 0 : (int)pc_z[n];
-        store_outputs<kG128>(a, 16 * mb + 4 * j, n, M, N, s_x, rowsum, h2f(s_c[n]), zpc, y,
-                             acc_out);
+        store_outputs<kG128>(a, 16 * (u0 + mb) + 4 * j, n, M, N, s_x, rowsum, h2f(s_c[n]), zpc,
+                             y, acc_out);
     }
 }
 
@@ -744,7 +751,8 @@ enum Kind { kSimple = 0, kTile = 2, kWide = 3, kStream = 4 };
 
 struct Plan {
     int kind = kSimple;
-    int mb = 0, nt = 0, r = 2, w = 8;  // stream kernel: row blocks, tiles, ring depth, waves
+    int mb = 0, nt = 0, r = 2, w = 8;  // stream kernel: row tiles, channel tiles, ring depth, waves
+    int mgrid = 1;                     //   and workgroups along M
     int bn = 256;                      // 16-row-wave tiled kernel: 128 x bn blocks
     int s = 1;                         //   and its K splits (partial sums in the workspace)
     int64_t ws_bytes = 0;
@@ -767,10 +775,11 @@ bool fits_buffer_offsets(int64_t M, int64_t N, int64_t K) {
 // Measured on MI355X over the Llama-3-8B and Qwen1.5-72B layers:
 //   M <= 64: the streaming kernel; three 16-channel tiles per workgroup once
 //     that still leaves two workgroups per compute unit, else two; for 16 rows
-//     a two-deep ring and 8 waves, for 17..64 rows 16 waves that each load one
+//     a two-deep ring and 8 waves, for 17..32 rows 16 waves that each load one
 //     group at a time (the activation bytes then dominate, and more waves with
 //     fewer groups each beat a deeper ring, which would not fit the registers
-//     of 16 waves).
+//     of 16 waves); for 33..64 rows two 32-row workgroups per band of three
+//     channel tiles.
 //   M >= 512: the wide-wave tiled kernel with 128 x 256 blocks.
 //   64 < M < 512: fewer than two 128 x 256 blocks per compute unit exist; the
 //     16-row-wave tiled kernel, split over K when its blocks do not cover the
@@ -784,14 +793,23 @@ Plan plan_gemm(int64_t M, int64_t N, int64_t K, bool have_ws) {
     if (M <= 64) {
         if (fits) {
             p.kind = kStream;
-            p.mb = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
             p.nt = (tiles + 2) / 3 >= 2 * kCUs ? 3 : 2;
-            if (p.mb == 1) {
+            if (M <= 16) {
+                p.mb = 1;
                 p.r = 2;
                 p.w = 8;
-            } else {
+            } else if (M <= 32) {
+                p.mb = 2;
                 p.r = 1;
                 p.w = 16;
+            } else {
+                // Two workgroups along M (32 rows each) per band of three
+                // channel tiles: every compute unit gets work, and each one
+                // re-reads half the activations.
+                p.mb = 2;
+                p.nt = 3;
+                p.r = 1;
+                p.w = 2 * ((tiles + 2) / 3) <= kCUs ? 16 : 8;
             }
         }
     } else if (M >= 512 && fits) {
@@ -823,8 +841,13 @@ Plan plan_gemm(int64_t M, int64_t N, int64_t K, bool have_ws) {
     if (g_force_bn) p.bn = g_force_bn;
     if (g_force_gm) p.group_m = g_force_gm;
     if (p.kind == kTile && g_force_nt) p.s = std::max(1, std::min<int>(g_force_nt, (int)(K / kGroup)));
+    if (p.kind == kStream && g_force_bn) p.mb = g_force_bn;  // row tiles per workgroup
 #endif
-    if (p.kind == kStream) p.nblk = (tiles + p.nt - 1) / p.nt;
+    if (p.kind == kStream) {
+        const int64_t U = (M + 15) / 16;
+        p.mgrid = (int)((U + p.mb - 1) / p.mb);
+        p.nblk = (tiles + p.nt - 1) / p.nt;
+    }
     if (p.kind != kTile) p.s = 1;
     p.ws_bytes = p.s > 1 ? (int64_t)p.s * M * N * 4 : 0;
     if (!have_ws) p.s = 1;
@@ -847,7 +870,7 @@ struct GemmArgs {
 
 template <bool kG128, int MB, int NT, int R, int W>
 void launch_stream_t(const Plan& p, const GemmArgs& a) {
-    hipLaunchKernelGGL((k_gemm_stream<kG128, MB, NT, R, W>), dim3((unsigned)p.nblk), dim3(W * 64),
+    hipLaunchKernelGGL((k_gemm_stream<kG128, MB, NT, R, W>), dim3((unsigned)(p.nblk * p.mgrid)), dim3(W * 64),
                        0, a.stream, a.xq, a.s_x, a.rowsum, a.blob, a.s_c, a.M, a.N, a.K, a.y,
                        a.acc_out);
 }
