@@ -248,3 +248,64 @@ def test_scales_exhaustive_over_fp16_row_max():
         np.testing.assert_array_equal(host(z), want["z"])
         if mode == G128:
             np.testing.assert_array_equal(host(s_g), want["s_g"])
+
+
+def _decode_channel_codes(tile_band, n, G):
+    """Codes q[n, 0:128*G] of channel n from the bytes of its tile band
+    (all G tiles of channels 16*(n//16) .. +15), walking the packed layout of
+    include/qoq.h backwards: lane 16*j + c, byte 16*lane + 4*d + e holds kappa
+    8*d + e (low nibble) and 8*d + 4 + e (high nibble), kappa = 16*s + i, input
+    k = 128*g + 64*s + 16*j + i."""
+    c = n % 16
+    tiles = tile_band.reshape(G, 64, 16)
+    q = np.zeros(128 * G, np.int64)
+    for j in range(4):
+        lane = tiles[:, 16 * j + c, :].astype(np.int64)  # [G, 16]
+        for b in range(16):
+            d, e = divmod(b, 4)
+            for half in range(2):
+                kappa = 8 * d + 4 * half + e
+                s, i = divmod(kappa, 16)
+                k = 128 * np.arange(G) + 64 * s + 16 * j + i
+                q[k] = (lane[:, b] >> (4 * half)) & 15
+    return q
+
+
+def test_gemm_blob_of_2gib_takes_the_64bit_path():
+    """A weight blob of 2 GiB or more does not fit the buffer-load kernels'
+    31-bit offsets; the plan then falls back to the reference kernel (M <= 64),
+    which addresses with 64-bit pointers. Random codes (any nibble is a valid
+    per-channel code) and random zeros; accumulators and outputs are checked at
+    sampled channels, including the last one, against an independent decode of
+    the blob on the host."""
+    M, N, K = 2, 32768, 131072
+    G = K // 128
+    code_bytes = N * K // 2
+    assert code_bytes >= 1 << 31
+    print(f"2 GiB blob: M={M} N={N} K={K}", flush=True)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(7)
+    blob = torch.randint(0, 256, (qoq.qoq_packed_bytes(PC, N, K),), dtype=torch.uint8,
+                         device=DEV, generator=gen)
+    blob[code_bytes:] = torch.randint(0, 16, (N,), dtype=torch.uint8, device=DEV, generator=gen)
+    s_c = to_dev(workloads.random_fp16((N,), 8, 1e-3).numpy().view(np.uint16), torch.float16)
+    xb = _rand_bits((M, K), 9, 1.0)
+    xq, s_x, rowsum = qoq.qoq_quantize_act(f16_dev(xb))
+    acc = torch.empty((M, N), dtype=torch.int32, device=DEV)
+    y = qoq.qoq_w4a8_gemm(PC, xq, s_x, rowsum, blob, s_c, N, acc_out=acc)
+    torch.cuda.synchronize()
+    oxq, osx, _ = oracle.quantize_act(xb)
+    z_all = host(blob[code_bytes:])
+    sc_bits = host_bits(s_c)
+    acc_h, y_h = host(acc), host_bits(y)
+    for n in (0, 1, 15, 16, 12345, N - 17, N - 1):
+        t = n // 16
+        band = host(blob[t * G * 1024:(t + 1) * G * 1024])
+        q = _decode_channel_codes(band, n, G)
+        want = oxq.astype(np.int64) @ (q - int(z_all[n]))
+        np.testing.assert_array_equal(acc_h[:, n], want)
+        y_want = oracle.epilogue(want.astype(np.int32)[:, None], osx,
+                                 np.array([sc_bits[n]], np.uint16))[:, 0]
+        assert_y_close(y_h[:, n][:, None], y_want[:, None], f"channel {n}")
+    del blob
+    torch.cuda.empty_cache()
