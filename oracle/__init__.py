@@ -68,6 +68,11 @@ def _load():
                 "orc_act_bytes": (I64, [I64, I64]),
                 "orc_pack_act": (I, [P, I64, I64, P]),
                 "orc_f16_to_f64_array": (None, [P, I64, P]),
+                "orc_quantize_weights_w8": (I, [P, I64, I64, P, P]),
+                "orc_w8_packed_bytes": (I64, [I64, I64]),
+                "orc_pack_w8": (I, [P, I64, I64, P]),
+                "orc_gemm_w8": (I, [P, P, I64, I64, I64, P]),
+                "orc_gemm_w8_points": (I, [P, P, I64, I64, I64, I64, P, P, P]),
             }
             for name, (res, args) in sigs.items():
                 fn = getattr(lib, name)
@@ -251,3 +256,63 @@ def forward(mode, x_bits, w_bits):
     acc = gemm(mode, xq, wq["q"], wq["s_g"], wq["z"])
     y = epilogue(acc, s_x, wq["s_c"])
     return {"xq": xq, "s_x": s_x, "rowsum": rowsum, "acc": acc, "y": y, **wq}
+
+
+# --- W8A8 sibling: per-channel symmetric INT8 weights (reading R11) ---------
+
+def quantize_weights_w8(w_bits):
+    """Returns (s_c uint16 [N], q int8 [N,K])."""
+    w = _c(w_bits, np.uint16)
+    N, K = w.shape
+    s_c = np.empty(N, np.uint16)
+    q = np.empty((N, K), np.int8)
+    _check(_load().orc_quantize_weights_w8(_p(w), N, K, _p(s_c), _p(q)), "quantize_weights_w8")
+    return s_c, q
+
+
+def w8_packed_bytes(N, K) -> int:
+    return int(_load().orc_w8_packed_bytes(N, K))
+
+
+def pack_w8(q):
+    q = _c(q, np.int8)
+    N, K = q.shape
+    n = w8_packed_bytes(N, K)
+    if n < 0:
+        raise ValueError("shape not packable")
+    blob = np.empty(n, np.uint8)
+    _check(_load().orc_pack_w8(_p(q), N, K, _p(blob)), "pack_w8")
+    return blob
+
+
+def gemm_w8(xq, q):
+    """Exact accumulator acc int32 [M,N] = Xq . q^T."""
+    xq = _c(xq, np.int8)
+    q = _c(q, np.int8)
+    M, K = xq.shape
+    N = q.shape[0]
+    acc = np.empty((M, N), np.int32)
+    _check(_load().orc_gemm_w8(_p(xq), _p(q), M, N, K, _p(acc)), "gemm_w8")
+    return acc
+
+
+def gemm_w8_points(xq, q, ms, ns):
+    xq = _c(xq, np.int8)
+    q = _c(q, np.int8)
+    M, K = xq.shape
+    N = q.shape[0]
+    ms = _c(np.asarray(ms, np.int64), np.int64)
+    ns = _c(np.asarray(ns, np.int64), np.int64)
+    acc = np.empty(len(ms), np.int32)
+    _check(_load().orc_gemm_w8_points(_p(xq), _p(q), M, N, K, len(ms), _p(ms), _p(ns), _p(acc)),
+           "gemm_w8_points")
+    return acc
+
+
+def forward_w8(x_bits, w_bits):
+    """The W8A8 path on the host: quantize both sides, contract, rescale."""
+    xq, s_x, rowsum = quantize_act(x_bits)
+    s_c, q = quantize_weights_w8(w_bits)
+    acc = gemm_w8(xq, q)
+    y = epilogue(acc, s_x, s_c)
+    return {"xq": xq, "s_x": s_x, "acc": acc, "y": y, "s_c": s_c, "q": q}

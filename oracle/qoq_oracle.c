@@ -50,7 +50,9 @@
  *   R9  the GEMM accumulator is the exact integer sum; per-channel mode's
  *       accumulator is sum_k Xq * (q - z);
  *   R10 the output is acc * s_x * s_c; here it is computed in fp64, where it is
- *       exact (31 + 11 + 11 significant bits <= 53).
+ *       exact (31 + 11 + 11 significant bits <= 53);
+ *   R11 the W8A8 sibling quantizes weights per output channel, symmetric, with
+ *       scale max|W|/127 and the activations' clamp [-128, 127].
  *
  * Inputs must be finite FP16 (passed as raw binary16 bits).
  */
@@ -473,4 +475,99 @@ void orc_f32_to_f16_array(const float* in, int64_t n, uint16_t* out) {
 
 void orc_f16_to_f64_array(const uint16_t* in, int64_t n, double* out) {
     for (int64_t i = 0; i < n; ++i) out[i] = orc_f16_to_f64(in[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* W8A8 sibling ("QServe Guide: W4A8KV4 Quantization for LLM Serving", "The  */
+/* Problem" item 2: weights and activations both INT8 on the INT8 matrix     */
+/* units; weight scaling per output channel and symmetric as in "Deep Dive"  */
+/* part 1, with the 8-bit bound 127 in place of the 4-bit bound 7 -- the    */
+/* reading R11 of the repository's design notes).                           */
+/*   s_c[n] = f16( max_k |W[n,k]| / 127 )          (fp32 division, R2)        */
+/*   q[n,k] = clamp( round(W[n,k] / s_c[n]), -128, 127 )   (R8: q = 0 if s_c = 0) */
+/* |W / s_c| <= 127 * (1 + 2^-11) rounds to at most 127, so -128 never       */
+/* occurs and the weights are symmetric in practice.                        */
+/* ------------------------------------------------------------------------ */
+int orc_quantize_weights_w8(const uint16_t* w, int64_t N, int64_t K, uint16_t* s_c, int8_t* q) {
+    if (N < 0 || K < 1) return ORC_ERR_SHAPE;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        const uint16_t* row = w + n * K;
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float a = fabsf(f16_to_f32(row[k]));
+            if (a > amax) amax = a;
+        }
+        uint16_t sc = orc_f32_to_f16(amax / 127.0f);
+        float scf = f16_to_f32(sc);
+        s_c[n] = sc;
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t v = 0;
+            if (scf != 0.0f) v = clamp64(rne_f32(f16_to_f32(row[k]) / scf), -128, 127);
+            q[n * K + k] = (int8_t)v;
+        }
+    }
+    return ORC_OK;
+}
+
+/* Packed INT8 weights: one 2048-byte tile per (t, g), t = n / 16, g = k / 128,
+ * at byte offset (t * G + g) * 2048. With c = n % 16 and k % 128 = 64 s +
+ * 16 j + i (s in 0..1, j in 0..3, i in 0..15), the byte of (n, k) sits at
+ * 1024 s + 16 (16 j + c) + i within the tile: the same order as the packed
+ * activations, with the channel in place of the row. */
+int64_t orc_w8_packed_bytes(int64_t N, int64_t K) {
+    if (K < GROUP || K % GROUP || N < 16 || N % 16) return -1;
+    return N * K;
+}
+
+int orc_pack_w8(const int8_t* q, int64_t N, int64_t K, uint8_t* blob) {
+    if (orc_w8_packed_bytes(N, K) < 0) return ORC_ERR_SHAPE;
+    const int64_t G = K / GROUP;
+    for (int64_t n = 0; n < N; ++n) {
+        const int64_t t = n / 16, c = n % 16;
+        for (int64_t k = 0; k < K; ++k) {
+            const int64_t g = k / GROUP, kk = k % GROUP;
+            const int64_t s = kk / 64, j = (kk % 64) / 16, i = kk % 16;
+            blob[(t * G + g) * 2048 + 1024 * s + 16 * (16 * j + c) + i] = (uint8_t)q[n * K + k];
+        }
+    }
+    return ORC_OK;
+}
+
+/* acc[m,n] = sum_k Xq[m,k] * q[n,k], exact in int64; a value outside int32 is
+ * an error. The output is the same one-time rescale as for W4A8
+ * (orc_epilogue): Y = acc * s_x[m] * s_c[n]. */
+int orc_gemm_w8(const int8_t* xq, const int8_t* q, int64_t M, int64_t N, int64_t K, int32_t* acc) {
+    if (M < 0 || N < 0 || K < 1) return ORC_ERR_SHAPE;
+    int overflow = 0;
+#pragma omp parallel for schedule(static) reduction(| : overflow)
+    for (int64_t n = 0; n < N; ++n) {
+        const int8_t* wr = q + n * K;
+        for (int64_t m = 0; m < M; ++m) {
+            const int8_t* xr = xq + m * K;
+            int64_t s = 0;
+            for (int64_t k = 0; k < K; ++k) s += (int64_t)xr[k] * wr[k];
+            if (s > INT32_MAX || s < INT32_MIN) overflow = 1;
+            acc[m * N + n] = (int32_t)s;
+        }
+    }
+    return overflow ? ORC_ERR_OVERFLOW : ORC_OK;
+}
+
+int orc_gemm_w8_points(const int8_t* xq, const int8_t* q, int64_t M, int64_t N, int64_t K,
+                       int64_t P, const int64_t* ms, const int64_t* ns, int32_t* acc) {
+    if (K < 1) return ORC_ERR_SHAPE;
+    for (int64_t p = 0; p < P; ++p)
+        if (ms[p] < 0 || ms[p] >= M || ns[p] < 0 || ns[p] >= N) return ORC_ERR_SHAPE;
+    int overflow = 0;
+#pragma omp parallel for schedule(static) reduction(| : overflow)
+    for (int64_t p = 0; p < P; ++p) {
+        const int8_t* xr = xq + ms[p] * K;
+        const int8_t* wr = q + ns[p] * K;
+        int64_t s = 0;
+        for (int64_t k = 0; k < K; ++k) s += (int64_t)xr[k] * wr[k];
+        if (s > INT32_MAX || s < INT32_MIN) overflow = 1;
+        acc[p] = (int32_t)s;
+    }
+    return overflow ? ORC_ERR_OVERFLOW : ORC_OK;
 }

@@ -175,3 +175,50 @@ def test_pack_act_layout_hand_worked():
     want = np.zeros(32 * 256, np.int8)
     want[0], want[1117], want[6146], want[2047] = 1, 2, 3, -4
     np.testing.assert_array_equal(p, want)
+
+
+def _w8_inputs():
+    d = _load("weights_w8.json")
+    K = d["K"]
+    rows = []
+    for row in d["rows"]:
+        w = np.zeros(K, np.float64)
+        for k, v in row["w_nonzero_units"].items():
+            w[int(k)] = v * 2.0 ** row["unit_pow2"]
+        rows.append(w)
+    w = np.array(rows)
+    assert np.array_equal(w.astype(np.float16).astype(np.float64), w)  # exact in FP16
+    return d, w.astype(np.float16).view(np.uint16)
+
+
+def test_weights_w8_golden():
+    d, w = _w8_inputs()
+    s_c, q = oracle.quantize_weights_w8(w)
+    for r, row in enumerate(d["rows"]):
+        assert s_c[r] == row["s_c_bits"], (r, s_c[r])
+        for k, v in row["q_at"].items():
+            assert q[r, int(k)] == v, (r, k)
+        # every entry not listed is zero in the input and in the codes
+        listed = set(int(k) for k in row["w_nonzero_units"])
+        rest = [k for k in range(d["K"]) if k not in listed]
+        assert not q[r, rest].any()
+
+
+def test_pack_w8_layout_golden():
+    d = _load("pack_w8_layout.json")
+    N, K = d["N"], d["K"]
+    q = np.zeros((N, K), np.int8)
+    for idx, (n, k, _, _) in enumerate(d["entries"]):
+        q[n, k] = idx + 1
+    blob = oracle.pack_w8(q)
+    assert blob.size == N * K == oracle.w8_packed_bytes(N, K)
+    want = np.zeros(N * K, np.uint8)
+    for idx, (_, _, off, _) in enumerate(d["entries"]):
+        want[off] = idx + 1
+    np.testing.assert_array_equal(blob, want)
+
+
+def test_w8_pack_size():
+    assert oracle.w8_packed_bytes(16, 128) == 16 * 128
+    assert oracle.w8_packed_bytes(8, 128) == -1
+    assert oracle.w8_packed_bytes(16, 200) == -1

@@ -326,3 +326,94 @@ def test_zero_inputs_give_zero_output():
         assert np.all(res["y"] == 0) and np.all(res["acc"] == 0)
         res = oracle.forward(mode, w[:2], np.zeros((16, 256), np.uint16))
         assert np.all(res["y"] == 0)
+
+
+# --------------------------------------------------------- W8A8 sibling ----
+def test_w8_quant_bounds_random():
+    """Per-channel symmetric INT8: scale within half an FP16 ulp of max|W|/127,
+    codes within 1/2 of W/s_c, the row maximum at +-127, zero rows zero."""
+    w = workloads.random_fp16((64, 1024), 21, 0.02)
+    w[7] = 0.0
+    w[9, :] = -0.25
+    w[11, 3] = 0.7  # an outlier
+    wb = w.numpy().view(np.uint16)
+    s_c_bits, q = oracle.quantize_weights_w8(wb)
+    wf = w.numpy().astype(np.float64)
+    s_c = oracle.f16_bits_to_f64(s_c_bits)
+    amax = np.abs(wf).max(axis=1)
+    nz = amax > 0
+    assert np.all(np.abs(s_c[nz] - amax[nz] / 127) <= (amax[nz] / 127) * 2.0**-11)
+    assert s_c[7] == 0 and not q[7].any()
+    qf = q.astype(np.float64)
+    assert np.abs(qf).max() <= 127
+    assert np.all(np.abs(qf[nz] - wf[nz] / s_c[nz, None]) <= 0.5 + 1e-4)
+    arg = np.abs(wf).argmax(axis=1)
+    assert np.all(np.abs(qf[np.arange(64)[nz], arg[nz]]) == 127)
+    assert np.all(q[9] == -127)
+    # W8 is much finer than W4 per channel.
+    rel8 = np.linalg.norm(qf * s_c[:, None] - wf) / np.linalg.norm(wf)
+    pc = oracle.quantize_weights(PC, wb)
+    what_pc = oracle.dequantize_weights(PC, pc["s_c"], pc["q"], None, pc["z"])
+    rel4 = np.linalg.norm(what_pc - wf) / np.linalg.norm(wf)
+    assert rel8 < rel4 / 8
+
+
+def test_w8_pack_is_the_tile_permutation():
+    """The packed INT8 blob read back through a plain reshape of the written
+    layout (tile t, group g, k-step s, lane block j, channel c, byte i)
+    returns every code."""
+    N, K = 48, 384
+    rng = np.random.default_rng(3)
+    q = rng.integers(-128, 128, size=(N, K), dtype=np.int8)
+    blob = oracle.pack_w8(q).view(np.int8)
+    T, G = N // 16, K // 128
+    v = blob.reshape(T, G, 2, 4, 16, 16)  # [t, g, s, j, c, i]
+    back = v.transpose(0, 4, 1, 2, 3, 5).reshape(N, K)  # n = 16t + c, k = 128g + 64s + 16j + i
+    np.testing.assert_array_equal(back, q)
+
+
+@pytest.mark.parametrize("shape", [(1, 128, 3), (6, 256, 16)])
+def test_w8_gemm_brute_force_tiny(shape):
+    M, K, N = shape
+    x = workloads.random_fp16((M, K), 300 + K, 1.0).numpy().view(np.uint16)
+    w = workloads.random_fp16((N, K), 400 + K, 0.02).numpy().view(np.uint16)
+    xq, _, _ = oracle.quantize_act(x)
+    _, q = oracle.quantize_weights_w8(w)
+    want = np.zeros((M, N), np.int64)
+    for m in range(M):
+        for n in range(N):
+            want[m, n] = sum(int(xq[m, k]) * int(q[n, k]) for k in range(K))
+    acc = oracle.gemm_w8(xq, q)
+    np.testing.assert_array_equal(acc, want)
+    ms = np.repeat(np.arange(M), N)
+    ns = np.tile(np.arange(N), M)
+    np.testing.assert_array_equal(oracle.gemm_w8_points(xq, q, ms, ns), acc.ravel())
+
+
+def test_w8_gemm_matches_library_matmul_and_range():
+    M, K, N = 29, 2048, 80
+    x = workloads.random_fp16((M, K), 41, 1.0).numpy().view(np.uint16)
+    w = workloads.random_fp16((N, K), 42, 0.02).numpy().view(np.uint16)
+    xq, _, _ = oracle.quantize_act(x)
+    _, q = oracle.quantize_weights_w8(w)
+    want = np.matmul(xq.astype(np.int64), q.astype(np.int64).T)
+    np.testing.assert_array_equal(oracle.gemm_w8(xq, q), want)
+    # At the largest K the extreme codes stay inside INT32 (127 * 127 * 132096).
+    Kmax = 132096
+    xa = np.full((1, Kmax), -127, np.int8)
+    qa = np.full((16, Kmax), 127, np.int8)
+    assert np.all(oracle.gemm_w8(xa, qa) == -127 * 127 * Kmax)
+    with pytest.raises(RuntimeError):
+        oracle.gemm_w8(np.full((1, Kmax), -128, np.int8), np.full((16, Kmax), -128, np.int8))
+
+
+def test_w8_end_to_end_approximates_real_product():
+    layer = workloads.WORKLOADS["tiny"].layers[0]
+    x16, w16 = workloads.generate(layer)
+    res = oracle.forward_w8(x16.numpy().view(np.uint16), w16.numpy().view(np.uint16))
+    ref = x16.numpy().astype(np.float64) @ w16.numpy().astype(np.float64).T
+    rel = np.linalg.norm(res["y"] - ref) / np.linalg.norm(ref)
+    assert rel < 0.03, rel
+    w4 = oracle.forward(G128, x16.numpy().view(np.uint16), w16.numpy().view(np.uint16))
+    rel4 = np.linalg.norm(w4["y"] - ref) / np.linalg.norm(ref)
+    assert rel < rel4
