@@ -1,6 +1,6 @@
 /*
- * qoq.h -- C ABI of libqoq, a QoQ W4A8 GEMM (QServe, arXiv 2405.04532) for
- * AMD Instinct MI355X (gfx950).
+ * qoq.h -- C ABI of libqoq, a QoQ W4A8 GEMM (QServe, arXiv 2405.04532) and
+ * its W8A8 sibling for AMD Instinct MI355X (gfx950).
  *
  *   Y[M,N] = X[M,K] * W[N,K]^T
  *
@@ -26,6 +26,12 @@
  *           "High-Throughput Native INT8 Tensor Core GEMMs" (INT32 accumulators).
  *   [WIKI]  "QoQ / QServe — Quantification W4A8KV4", example configuration:
  *           weight group size 128.
+ *   [W8A8]  "QServe Guide: W4A8KV4 Quantization for LLM Serving", "The Problem"
+ *           item 2 (weights and activations both INT8 on the INT8 matrix
+ *           units) and "Deep Dive" part 1 (per-channel symmetric weight
+ *           scaling, here at 8 bits); "QServe: Low Bit Width Does Not Guarantee
+ *           High Throughput", section 3, judgment A (W8A8 suits large batches,
+ *           the format W4A8 is compared against).
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers, allocated and owned by the
@@ -58,7 +64,7 @@
 extern "C" {
 #endif
 
-#define QOQ_ABI_VERSION 2
+#define QOQ_ABI_VERSION 3
 #define QOQ_GROUP 128
 #define QOQ_MAX_K 132096
 
@@ -74,7 +80,7 @@ typedef enum {
     QOQ_ERR_ALIGN = 3,  /* a pointer is not 16-byte aligned */
     QOQ_ERR_MODE = 4,   /* mode is neither QOQ_MODE_G128 nor QOQ_MODE_PER_CHANNEL */
     QOQ_ERR_HIP = 5,    /* the HIP runtime reported an error at launch */
-    QOQ_ERR_WORKSPACE = 6 /* workspace given but smaller than qoq_gemm_workspace_bytes() */
+    QOQ_ERR_WORKSPACE = 6 /* workspace given but smaller than the *_workspace_bytes() value */
 } qoq_status;
 
 /* QOQ_ABI_VERSION of the loaded library. */
@@ -200,6 +206,56 @@ int64_t qoq_gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K);
 qoq_status qoq_w4a8_gemm(int mode, const int8_t* xq, const uint16_t* s_x, const int32_t* rowsum,
                          const void* blob, const uint16_t* s_c, int64_t M, int64_t N, int64_t K,
                          uint16_t* y, int32_t* acc_out, void* workspace, int64_t workspace_bytes,
+                         void* stream);
+
+/*
+ * ---- W8A8 sibling ([W8A8]) ------------------------------------------------
+ * The same per-token INT8 activations (qoq_quantize_act) against INT8 weights,
+ * for comparing the formats on one harness: twice the weight bytes of W4A8,
+ * no unpack in the main loop.
+ *
+ * Weight quantization, offline:
+ *   w   [N,K] FP16 row-major; q [N,K] int8 row-major; s_c [N] FP16.
+ *   s_c[n] = f16(max_k |w[n,k]| / 127)
+ *   q      = clamp(round(w / s_c), -128, 127)   (|w / s_c| <= 127 * (1 + 2^-11)
+ *            rounds to at most 127, so the codes are symmetric in practice)
+ *   A scale of 0 gives q = 0 for that row. Shapes as for qoq_quantize_weights.
+ */
+qoq_status qoq_w8a8_quantize_weights(const uint16_t* w, int64_t N, int64_t K, int8_t* q,
+                                     uint16_t* s_c, void* stream);
+
+/*
+ * Size of the packed INT8 weights (N*K bytes), or -1 for an unsupported shape.
+ * Tiles of 16 output channels x 128 inputs, 2048 bytes each; tile (t, g) starts
+ * at byte (t*G + g)*2048. With c = n % 16 and k % 128 = 64*s + 16*j + i, the
+ * byte of (n, k) is at 1024*s + 16*(16*j + c) + i within its tile -- the order
+ * of the packed activations with the channel in place of the row, so that one
+ * 1 KB coalesced read gives every lane of a wave its MFMA B operand for one
+ * k-step.
+ */
+int64_t qoq_w8a8_packed_bytes(int64_t N, int64_t K);
+
+/* Pack row-major INT8 weights q [N,K] into `blob` (qoq_w8a8_packed_bytes(N, K)
+ * bytes). Needs N >= 16. */
+qoq_status qoq_w8a8_pack_weights(const int8_t* q, int64_t N, int64_t K, void* blob,
+                                 void* stream);
+
+/* Workspace bytes of qoq_w8a8_gemm's plan for this shape (0: none), or -1 for
+ * an unsupported shape; the same split-K rule as qoq_gemm_workspace_bytes. */
+int64_t qoq_w8a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * W8A8 GEMM with the FP16 epilogue.
+ *   xq, s_x from qoq_quantize_act (rowsum is not needed), blob from
+ *   qoq_w8a8_pack_weights, s_c [N] FP16 from qoq_w8a8_quantize_weights.
+ *   acc[m,n] = sum_k xq[m,k] * q[n,k]                            (exact INT32)
+ *   y[m,n]   = f16( (f32(acc) * f32(s_x[m])) * f32(s_c[n]) )     (FP16 [M,N])
+ *   acc_out, workspace and errors as for qoq_w4a8_gemm (the workspace bound is
+ *   qoq_w8a8_gemm_workspace_bytes).
+ */
+qoq_status qoq_w8a8_gemm(const int8_t* xq, const uint16_t* s_x, const void* blob,
+                         const uint16_t* s_c, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                         int32_t* acc_out, void* workspace, int64_t workspace_bytes,
                          void* stream);
 
 #ifdef __cplusplus

@@ -1,4 +1,4 @@
-"""QoQ W4A8 GEMM for AMD Instinct MI355X (gfx950).
+"""QoQ W4A8 GEMM (and its W8A8 sibling) for AMD Instinct MI355X (gfx950).
 
 Python binding of ``libqoq.so`` (the C ABI declared in ``include/qoq.h``). The
 functions carry the C names and do argument marshalling only: every step of
@@ -21,6 +21,7 @@ MODE_PER_CHANNEL = 1
 GROUP = 128
 MAX_K = 132096
 MODES = {"g128": MODE_G128, "per_channel": MODE_PER_CHANNEL}
+W8A8 = "w8a8"  # the INT8-weight sibling format (its own entry points)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqoq.so")
@@ -37,6 +38,11 @@ EXPORTED = (
     "qoq_quantize_act",
     "qoq_gemm_workspace_bytes",
     "qoq_w4a8_gemm",
+    "qoq_w8a8_quantize_weights",
+    "qoq_w8a8_packed_bytes",
+    "qoq_w8a8_pack_weights",
+    "qoq_w8a8_gemm_workspace_bytes",
+    "qoq_w8a8_gemm",
 )
 
 
@@ -71,6 +77,11 @@ def load_library():
             "qoq_quantize_act": (I, [P, I64, I64, P, P, P, P]),
             "qoq_gemm_workspace_bytes": (I64, [I, I64, I64, I64]),
             "qoq_w4a8_gemm": (I, [I, P, P, P, P, P, I64, I64, I64, P, P, P, I64, P]),
+            "qoq_w8a8_quantize_weights": (I, [P, I64, I64, P, P, P]),
+            "qoq_w8a8_packed_bytes": (I64, [I64, I64]),
+            "qoq_w8a8_pack_weights": (I, [P, I64, I64, P, P]),
+            "qoq_w8a8_gemm_workspace_bytes": (I64, [I64, I64, I64]),
+            "qoq_w8a8_gemm": (I, [P, P, P, P, I64, I64, I64, P, P, P, I64, P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(lib, name)
@@ -226,11 +237,14 @@ _workspaces = {}
 
 def gemm_workspace(mode, M: int, N: int, K: int, device) -> Optional[torch.Tensor]:
     """The device's shared workspace when the plan for this shape uses one
-    (split-K partial sums), else None.
+    (split-K partial sums), else None. ``mode`` is a W4 mode or ``"w8a8"``.
 
     One workspace per device is shared by every call that does not bring its
     own, so calls issued concurrently on different streams must pass their own."""
-    need = qoq_gemm_workspace_bytes(mode, M, N, K)
+    if mode == W8A8:
+        need = qoq_w8a8_gemm_workspace_bytes(M, N, K)
+    else:
+        need = qoq_gemm_workspace_bytes(mode, M, N, K)
     if need <= 0:
         return None
     dev = torch.device(device)
@@ -288,17 +302,102 @@ def qoq_w4a8_gemm(mode, xq: torch.Tensor, s_x: torch.Tensor, rowsum: Optional[to
     return y
 
 
+# ---- W8A8 sibling ---------------------------------------------------------
+
+def qoq_w8a8_packed_bytes(N: int, K: int) -> int:
+    return int(load_library().qoq_w8a8_packed_bytes(int(N), int(K)))
+
+
+def qoq_w8a8_quantize_weights(w: torch.Tensor, q=None, s_c=None):
+    """W [N,K] fp16 -> (q int8 [N,K], s_c fp16 [N]), per-channel symmetric INT8."""
+    _need(w, torch.float16, "w")
+    N, K = w.shape
+    dev = w.device
+    q = q if q is not None else torch.empty((N, K), dtype=torch.int8, device=dev)
+    s_c = s_c if s_c is not None else torch.empty((N,), dtype=torch.float16, device=dev)
+    _need(q, torch.int8, "q", (N, K))
+    _need(s_c, torch.float16, "s_c", (N,))
+    st = load_library().qoq_w8a8_quantize_weights(_ptr(w), N, K, _ptr(q), _ptr(s_c), _stream(w))
+    _check(st, "qoq_w8a8_quantize_weights")
+    return q, s_c
+
+
+def qoq_w8a8_pack_weights(q: torch.Tensor, blob: Optional[torch.Tensor] = None) -> torch.Tensor:
+    _need(q, torch.int8, "q")
+    N, K = q.shape
+    nbytes = qoq_w8a8_packed_bytes(N, K)
+    if nbytes < 0:
+        raise QoQError(f"qoq_w8a8_pack_weights: unsupported shape N={N} K={K}")
+    blob = blob if blob is not None else torch.empty((nbytes,), dtype=torch.uint8, device=q.device)
+    _need(blob, torch.uint8, "blob", (nbytes,))
+    st = load_library().qoq_w8a8_pack_weights(_ptr(q), N, K, _ptr(blob), _stream(q))
+    _check(st, "qoq_w8a8_pack_weights")
+    return blob
+
+
+def qoq_w8a8_gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(load_library().qoq_w8a8_gemm_workspace_bytes(int(M), int(N), int(K)))
+
+
+def qoq_w8a8_gemm(xq: torch.Tensor, s_x: torch.Tensor, blob: torch.Tensor, s_c: torch.Tensor,
+                  N: int, y=None, acc_out=None, workspace="auto", K: Optional[int] = None):
+    """Y [M,N] fp16 = rescale(sum_k xq * q); acc_out (int32 [M,N]) optional.
+
+    Arguments as for qoq_w4a8_gemm, with blob from qoq_w8a8_pack_weights."""
+    _need(xq, torch.int8, "xq")
+    _need(s_x, torch.float16, "s_x")
+    M = s_x.numel()
+    dev = xq.device
+    mp = (M + 15) // 16 * 16
+    if K is None:
+        if mp == 0:
+            raise QoQError("qoq_w8a8_gemm: K must be given when M == 0")
+        K = xq.numel() // mp
+    if xq.numel() != mp * K:
+        raise QoQError(f"xq has {xq.numel()} bytes, expected {mp} x {K}")
+    _need(s_c, torch.float16, "s_c", (N,))
+    _need(blob, torch.uint8, "blob")
+    y = y if y is not None else torch.empty((M, N), dtype=torch.float16, device=dev)
+    _need(y, torch.float16, "y", (M, N))
+    if acc_out is not None:
+        _need(acc_out, torch.int32, "acc_out", (M, N))
+    nbytes = qoq_w8a8_packed_bytes(N, K)
+    if M and N and blob.numel() != nbytes:
+        raise QoQError(f"blob has {blob.numel()} bytes, expected {nbytes}")
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a tensor")
+        workspace = gemm_workspace(W8A8, M, N, K, dev) if M and N else None
+    ws_bytes = 0
+    if workspace is not None:
+        _need(workspace, torch.uint8, "workspace")
+        ws_bytes = workspace.numel()
+    st = load_library().qoq_w8a8_gemm(_ptr(xq), _ptr(s_x), _ptr(blob), _ptr(s_c), M, N, K,
+                                      _ptr(y), _ptr(acc_out), _ptr(workspace), ws_bytes,
+                                      _stream(xq))
+    _check(st, "qoq_w8a8_gemm")
+    return y
+
+
 class PackedWeight:
-    """A weight matrix quantized and packed once (offline), kept resident."""
+    """A weight matrix quantized and packed once (offline), kept resident.
+
+    ``mode``: ``"g128"``, ``"per_channel"`` (W4A8) or ``"w8a8"`` (INT8 weights)."""
 
     def __init__(self, mode, w: torch.Tensor):
-        self.mode = _mode(mode)
+        self.mode = W8A8 if mode == W8A8 else _mode(mode)
         self.N, self.K = w.shape
-        q, self.s_c, s_g, z = qoq_quantize_weights(self.mode, w)
-        self.blob = qoq_pack_weights(self.mode, q, s_g, z)
+        if self.mode == W8A8:
+            q, self.s_c = qoq_w8a8_quantize_weights(w)
+            self.blob = qoq_w8a8_pack_weights(q)
+        else:
+            q, self.s_c, s_g, z = qoq_quantize_weights(self.mode, w)
+            self.blob = qoq_pack_weights(self.mode, q, s_g, z)
 
     def forward(self, x: torch.Tensor, y=None) -> torch.Tensor:
-        """Per-call path: per-token INT8 quantization of x, then the W4A8 GEMM."""
+        """Per-call path: per-token INT8 quantization of x, then the GEMM."""
         xq, s_x, rowsum = qoq_quantize_act(x, want_rowsum=self.mode == MODE_PER_CHANNEL)
+        if self.mode == W8A8:
+            return qoq_w8a8_gemm(xq, s_x, self.blob, self.s_c, self.N, y=y, K=self.K)
         return qoq_w4a8_gemm(self.mode, xq, s_x, rowsum, self.blob, self.s_c, self.N, y=y,
                              K=self.K)

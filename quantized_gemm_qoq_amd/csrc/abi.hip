@@ -39,7 +39,7 @@ const char* qoq_status_str(int status) {
         case QOQ_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         case QOQ_ERR_MODE: return "unknown quantization mode";
         case QOQ_ERR_HIP: return "HIP runtime error at launch";
-        case QOQ_ERR_WORKSPACE: return "workspace smaller than qoq_gemm_workspace_bytes()";
+        case QOQ_ERR_WORKSPACE: return "workspace smaller than the GEMM plan needs";
         default: return "unknown status";
     }
 }
@@ -136,6 +136,53 @@ qoq_status qoq_w4a8_gemm(int mode, const int8_t* xq, const uint16_t* s_x, const 
     return launch_checked([&] {
         qoq::launch_gemm(mode, xq, s_x, rowsum, static_cast<const uint8_t*>(blob), s_c, M, N, K, y,
                          acc_out, workspace, as_stream(stream));
+    });
+}
+
+int64_t qoq_w8a8_packed_bytes(int64_t N, int64_t K) {
+    if (N < 16 || N % 16 || !valid_k(K)) return -1;
+    return N * K;
+}
+
+qoq_status qoq_w8a8_quantize_weights(const uint16_t* w, int64_t N, int64_t K, int8_t* q,
+                                     uint16_t* s_c, void* stream) {
+    if (N < 0 || N % 16 || !valid_k(K)) return QOQ_ERR_SHAPE;
+    if (N == 0) return QOQ_OK;
+    if (!w || !q || !s_c) return QOQ_ERR_NULL;
+    if (!aligned16(w) || !aligned16(q) || !aligned16(s_c)) return QOQ_ERR_ALIGN;
+    return launch_checked(
+        [&] { qoq::launch_quantize_weights_w8(w, N, K, q, s_c, as_stream(stream)); });
+}
+
+qoq_status qoq_w8a8_pack_weights(const int8_t* q, int64_t N, int64_t K, void* blob, void* stream) {
+    if (N < 16 || N % 16 || !valid_k(K)) return QOQ_ERR_SHAPE;
+    if (!q || !blob) return QOQ_ERR_NULL;
+    if (!aligned16(q) || !aligned16(blob)) return QOQ_ERR_ALIGN;
+    return launch_checked(
+        [&] { qoq::launch_pack_w8(q, N, K, static_cast<uint8_t*>(blob), as_stream(stream)); });
+}
+
+int64_t qoq_w8a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || M > INT32_MAX || N < 0 || N % 16 || N > INT32_MAX || !valid_k(K)) return -1;
+    if (M == 0 || N == 0) return 0;
+    return qoq::gemm_workspace_bytes(qoq::kGemmFmtW8, M, N, K);
+}
+
+qoq_status qoq_w8a8_gemm(const int8_t* xq, const uint16_t* s_x, const void* blob,
+                         const uint16_t* s_c, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                         int32_t* acc_out, void* workspace, int64_t workspace_bytes, void* stream) {
+    if (M < 0 || M > INT32_MAX - 15 || N < 0 || N % 16 || N > INT32_MAX || !valid_k(K))
+        return QOQ_ERR_SHAPE;
+    if (M == 0 || N == 0) return QOQ_OK;
+    if (!xq || !s_x || !blob || !s_c || !y) return QOQ_ERR_NULL;
+    if (!aligned16(xq) || !aligned16(s_x) || !aligned16(blob) || !aligned16(s_c) ||
+        !aligned16(y) || (acc_out && !aligned16(acc_out)) || (workspace && !aligned16(workspace)))
+        return QOQ_ERR_ALIGN;
+    if (workspace && workspace_bytes < qoq::gemm_workspace_bytes(qoq::kGemmFmtW8, M, N, K))
+        return QOQ_ERR_WORKSPACE;
+    return launch_checked([&] {
+        qoq::launch_gemm(qoq::kGemmFmtW8, xq, s_x, nullptr, static_cast<const uint8_t*>(blob), s_c,
+                         M, N, K, y, acc_out, workspace, as_stream(stream));
     });
 }
 

@@ -1,4 +1,5 @@
-// gemm.hip -- W4A8 GEMM on the gfx950 INT8 matrix cores.
+// gemm.hip -- W4A8 GEMM (and its W8A8 sibling) on the gfx950 INT8 matrix
+// cores.
 //
 //   acc[m,n] = sum_k xq[m,k] * W8^[n,k]   (exact INT32)
 //   y[m,n]   = f16((f32(acc) * s_x[m]) * s_c[n])
@@ -10,7 +11,8 @@
 // mode feeds the codes themselves and subtracts z[n] * rowsum[m] in the
 // epilogue. The rescale by the per-token and per-channel scales happens once,
 // after the integer sum ("QServe Guide: W4A8KV4 Quantization for LLM Serving",
-// Deep Dive part 1).
+// Deep Dive part 1). The W8A8 sibling (the same page, "The Problem" item 2)
+// stores W8^ itself, per-channel symmetric INT8, in the same operand order.
 //
 // Matrix-core mapping (v_mfma_i32_16x16x64_i8): A = activations (16 rows m),
 // B = weights (16 channels n). For both operands lane l holds row/channel
@@ -28,6 +30,36 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / kWave;
 
+// Weight formats of the packed blob (every kernel below is instantiated per
+// format):
+//   kFmtG128 UINT4 codes + one parameter byte per (channel, group): unpacked
+//            to (q - z) * s_g in registers;
+//   kFmtPC   UINT4 codes + one zero byte per channel: the codes feed the
+//            matrix cores and z[n] * rowsum[m] is subtracted in the epilogue;
+//   kFmtW8   INT8 weights in the operand order (no unpack, no parameters).
+enum : int { kFmtG128 = 0, kFmtPC = 1, kFmtW8 = 2 };
+template <int F>
+struct Fmt {
+    static constexpr bool kG128 = F == kFmtG128;
+    static constexpr bool kZp = F == kFmtPC;          // zero-point in the epilogue
+    static constexpr int kVec = F == kFmtW8 ? 2 : 1;  // 16-byte vectors per lane per group
+};
+
+// Bytes of the weight codes (the parameters, if any, follow them).
+__host__ __device__ __forceinline__ size_t code_bytes_of(int fmt, int64_t N, int64_t K) {
+    return fmt == kFmtW8 ? (size_t)N * K : (size_t)N * K / 2;
+}
+
+// One k-step (KS = 0 or 1) MFMA B operand of a lane from its loaded weight
+// vectors: INT8 weights are the operand; UINT4 codes are unpacked.
+template <int F, int KS>
+__device__ __forceinline__ int32x4 b_operand(const u32x4 (&p)[Fmt<F>::kVec], uint32_t gw) {
+    if constexpr (F == kFmtW8)
+        return __builtin_bit_cast(int32x4, p[KS]);
+    else
+        return unpack_half<F == kFmtG128, KS>(p[0], gw);
+}
+
 // FP16 output of one accumulator: (f32(acc) * s_x) * s_c, each product rounded
 // to fp32, then the result rounded to FP16.
 __device__ __forceinline__ uint16_t output_value(int r, float sx, float sc) {
@@ -39,7 +71,7 @@ __device__ __forceinline__ uint16_t output_value(int r, float sx, float sc) {
 }
 
 // Epilogue for one lane's four accumulator rows of one channel.
-template <bool kG128>
+template <int F>
 __device__ __forceinline__ void store_outputs(int32x4 a, int m_first, int n, int M, int N,
                                               const uint16_t* __restrict__ s_x,
                                               const int32_t* __restrict__ rowsum, float sc,
@@ -50,7 +82,7 @@ __device__ __forceinline__ void store_outputs(int32x4 a, int m_first, int n, int
         const int m = m_first + v;
         if (m < M) {
             int r = a[v];
-            if (!kG128) r -= zpc * rowsum[m];
+            if (Fmt<F>::kZp) r -= zpc * rowsum[m];
             const size_t o = (size_t)m * N + n;
             if (acc_out) acc_out[o] = r;
             y[o] = output_value(r, h2f(s_x[m]), sc);
@@ -61,7 +93,7 @@ __device__ __forceinline__ void store_outputs(int32x4 a, int m_first, int n, int
 // ---------------------------------------------------------------------------
 // Reference kernel: each wave owns one 16-channel tile and 64 rows, and streams
 // the whole K. Used where no tuned kernel applies.
-template <bool kG128>
+template <int F>
 __global__ __launch_bounds__(kThreads) void k_gemm_simple(
     const int8_t* __restrict__ xq, const uint16_t* __restrict__ s_x,
     const int32_t* __restrict__ rowsum, const uint8_t* __restrict__ blob,
@@ -77,8 +109,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm_simple(
     const int c = lane % 16;
     const int j = lane / 16;
     const int n = t * 16 + c;
-    const uint4* tiles = reinterpret_cast<const uint4*>(blob) + (size_t)t * G * kWave + lane;
-    const uint8_t* params = blob + (size_t)N * K / 2;
+    constexpr int kV = Fmt<F>::kVec;
+    constexpr bool kG128 = Fmt<F>::kG128;
+    const u32x4* tiles = reinterpret_cast<const u32x4*>(blob) + (size_t)t * G * kWave * kV + lane;
+    const uint8_t* params = blob + code_bytes_of(F, N, K);
     const int32x4* act = reinterpret_cast<const int32x4*>(xq) + lane;
 
     int32x4 acc[4];
@@ -86,11 +120,12 @@ __global__ __launch_bounds__(kThreads) void k_gemm_simple(
     for (int i = 0; i < 4; ++i) acc[i] = int32x4{0, 0, 0, 0};
 
     for (int g = 0; g < G; ++g) {
-        const u32x4 p = reinterpret_cast<const u32x4*>(tiles)[(size_t)g * kWave];
-        GroupConst gc{0u, 0u};
-        if (kG128) gc = group_const(params[((size_t)t * G + g) * 16 + c]);
-        int32x4 b0, b1;
-        unpack_lane<kG128>(p, gc, b0, b1);
+        u32x4 p[kV];
+#pragma unroll
+        for (int v = 0; v < kV; ++v) p[v] = tiles[((size_t)g * kV + v) * kWave];
+        const uint32_t gw = kG128 ? group_word(params[((size_t)t * G + g) * 16 + c]) : 0u;
+        const int32x4 b0 = b_operand<F, 0>(p, gw);
+        const int32x4 b1 = b_operand<F, 1>(p, gw);
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
             const int u = m0 / 16 + mb;
@@ -103,11 +138,11 @@ __global__ __launch_bounds__(kThreads) void k_gemm_simple(
     }
 
     const float sc = h2f(s_c[n]);
-    const int zpc = kG128 ? 0 : (int)params[n];
+    const int zpc = Fmt<F>::kZp ? (int)params[n] : 0;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
-        store_outputs<kG128>(acc[mb], m0 + 16 * mb + 4 * j, n, M, N, s_x, rowsum, sc, zpc, y,
-                             acc_out);
+        store_outputs<F>(acc[mb], m0 + 16 * mb + 4 * j, n, M, N, s_x, rowsum, sc, zpc, y,
+                         acc_out);
 }
 
 // ---------------------------------------------------------------------------
@@ -142,29 +177,37 @@ __device__ __forceinline__ void tile_store_a(u32x4* buf, const u32x4 (&stage)[N]
     for (int v = 0; v < N; ++v) buf[threadIdx.x + v * kThr] = stage[v];
 }
 
-template <bool kG128, int TN>
-__device__ __forceinline__ void tile_load_b(u32x4 (&bq)[TN], uint32_t (&pq)[TN],
+template <int F, int TN>
+__device__ __forceinline__ void tile_load_b(u32x4 (&bq)[TN][Fmt<F>::kVec], uint32_t (&pq)[TN],
                                             const u32x4* const (&bptr)[TN],
                                             const uint8_t* const (&pptr)[TN], int g) {
+    constexpr int kV = Fmt<F>::kVec;
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
-        bq[i] = bptr[i][(size_t)g * kWave];
-        if (kG128) pq[i] = pptr[i][(size_t)g * 16];
+#pragma unroll
+        for (int v = 0; v < kV; ++v) bq[i][v] = bptr[i][((size_t)g * kV + v) * kWave];
+        if (Fmt<F>::kG128) pq[i] = pptr[i][(size_t)g * 16];
     }
 }
 
 // One k-step: unpack this wave's TN weight tiles, read its TM activation
 // tiles from LDS (lw: the wave's first tile, lane offset applied) and issue
 // TM x TN x 2 matrix-core operations.
-template <bool kG128, int TM, int TN>
+template <int F, int TM, int TN>
 __device__ __forceinline__ void tile_compute(int32x4 (&acc)[TM][TN], const u32x4* lw,
-                                             const u32x4 (&bq)[TN], const uint32_t (&pq)[TN]) {
+                                             const u32x4 (&bq)[TN][Fmt<F>::kVec],
+                                             const uint32_t (&pq)[TN]) {
     int32x4 b[TN][2];
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
-        GroupConst gc{0u, 0u};
-        if (kG128) gc = group_const(pq[i]);
-        unpack_lane<kG128>(bq[i], gc, b[i][0], b[i][1]);
+        if constexpr (F == kFmtW8) {
+            b[i][0] = __builtin_bit_cast(int32x4, bq[i][0]);
+            b[i][1] = __builtin_bit_cast(int32x4, bq[i][1]);
+        } else {
+            GroupConst gc{0u, 0u};
+            if (Fmt<F>::kG128) gc = group_const(pq[i]);
+            unpack_lane<Fmt<F>::kG128>(bq[i][0], gc, b[i][0], b[i][1]);
+        }
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -177,7 +220,7 @@ __device__ __forceinline__ void tile_compute(int32x4 (&acc)[TM][TN], const u32x4
     }
 }
 
-template <bool kG128, int BM, int BN, int WM, int WN>
+template <int F, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(WM * WN * 64, 2) void k_gemm_tile(
     const int8_t* __restrict__ xq, const uint16_t* __restrict__ s_x,
     const int32_t* __restrict__ rowsum, const uint8_t* __restrict__ blob,
@@ -234,13 +277,14 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void k_gemm_tile(
     const size_t a_stride = (size_t)U * 128;  // vectors per group
 
     // Weight tiles of this wave (clamped for the ragged n tail).
+    constexpr int kV = Fmt<F>::kVec;
     const u32x4* bptr[TN];
     const uint8_t* pptr[TN];
-    const uint8_t* params = blob + (size_t)N * K / 2;
+    const uint8_t* params = blob + code_bytes_of(F, N, K);
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
         const int t = min(bn * (BN / 16) + wn * TN + i, tiles - 1);
-        bptr[i] = reinterpret_cast<const u32x4*>(blob) + (size_t)t * G * kWave + lane;
+        bptr[i] = reinterpret_cast<const u32x4*>(blob) + (size_t)t * G * kWave * kV + lane;
         pptr[i] = params + (size_t)t * G * 16 + c;
     }
 
@@ -251,7 +295,7 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void k_gemm_tile(
         for (int b = 0; b < TN; ++b) acc[a][b] = int32x4{0, 0, 0, 0};
 
     u32x4 stage[kAPerThr];
-    u32x4 b0q[TN], b1q[TN];
+    u32x4 b0q[TN][kV], b1q[TN][kV];
     uint32_t p0q[TN], p1q[TN];
     const u32x4* lw0 = lds_a0 + (size_t)(wm * TM) * 128 + lane;
     const u32x4* lw1 = lds_a1 + (size_t)(wm * TM) * 128 + lane;
@@ -261,7 +305,7 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void k_gemm_tile(
     tile_load_a(stage, act, a_src, (size_t)g0 * a_stride);
     tile_store_a<kAPerThr, kThr>(lds_a0, stage);
     tile_load_a(stage, act, a_src, (size_t)(g0 + min(1, Gc - 1)) * a_stride);
-    tile_load_b<kG128, TN>(b0q, p0q, bptr, pptr, g0);
+    tile_load_b<F, TN>(b0q, p0q, bptr, pptr, g0);
     __syncthreads();
 
     // Step h: publish the staged activations of group h+1 into the idle
@@ -277,20 +321,20 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void k_gemm_tile(
     for (; h + 1 < Gc; h += 2) {
         tile_store_a<kAPerThr, kThr>(lds_a1, stage);
         tile_load_a(stage, act, a_src, (size_t)(g0 + min(h + 2, Gc - 1)) * a_stride);
-        tile_load_b<kG128, TN>(b1q, p1q, bptr, pptr, g0 + h + 1);
+        tile_load_b<F, TN>(b1q, p1q, bptr, pptr, g0 + h + 1);
         __builtin_amdgcn_sched_barrier(0);
-        tile_compute<kG128, TM, TN>(acc, lw0, b0q, p0q);
+        tile_compute<F, TM, TN>(acc, lw0, b0q, p0q);
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
         tile_store_a<kAPerThr, kThr>(lds_a0, stage);
         tile_load_a(stage, act, a_src, (size_t)(g0 + min(h + 3, Gc - 1)) * a_stride);
-        tile_load_b<kG128, TN>(b0q, p0q, bptr, pptr, g0 + min(h + 2, Gc - 1));
+        tile_load_b<F, TN>(b0q, p0q, bptr, pptr, g0 + min(h + 2, Gc - 1));
         __builtin_amdgcn_sched_barrier(0);
-        tile_compute<kG128, TM, TN>(acc, lw1, b1q, p1q);
+        tile_compute<F, TM, TN>(acc, lw1, b1q, p1q);
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
     }
-    if (h < Gc) tile_compute<kG128, TM, TN>(acc, lw0, b0q, p0q);
+    if (h < Gc) tile_compute<F, TM, TN>(acc, lw0, b0q, p0q);
 
     // Epilogue (with S > 1: the raw partial sums; the reduction kernel adds
     // them and applies the zero-point compensation and the rescale once).
@@ -309,8 +353,8 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void k_gemm_tile(
                 for (int v = 0; v < 4; ++v)
                     if (m_first + v < M) dst[(size_t)(m_first + v) * N + n] = acc[a][i][v];
             } else {
-                store_outputs<kG128>(acc[a][i], m_first, n, M, N, s_x, rowsum, h2f(s_c[n]),
-                                     kG128 ? 0 : (int)pc_z[n], y, acc_out);
+                store_outputs<F>(acc[a][i], m_first, n, M, N, s_x, rowsum, h2f(s_c[n]),
+                                 Fmt<F>::kZp ? (int)pc_z[n] : 0, y, acc_out);
             }
         }
     }
@@ -320,7 +364,7 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void k_gemm_tile(
 // exact and order-free), applies the per-channel zero-point compensation and
 // the one-time rescale. Each thread handles four consecutive channels of one
 // row (N is a multiple of 16).
-template <bool kG128>
+template <int F>
 __global__ __launch_bounds__(kThreads) void k_splitk_reduce(
     const int32_t* __restrict__ part, int S, const uint16_t* __restrict__ s_x,
     const int32_t* __restrict__ rowsum, const uint8_t* __restrict__ pc_z,
@@ -338,7 +382,7 @@ __global__ __launch_bounds__(kThreads) void k_splitk_reduce(
     for (int v = 0; v < 4; ++v) {
         const int n = n0 + v;
         int rr = r[v];
-        if (!kG128) rr -= (int)pc_z[n] * rowsum[m];
+        if (Fmt<F>::kZp) rr -= (int)pc_z[n] * rowsum[m];
         if (acc_out) acc_out[(size_t)m * N + n] = rr;
         out[v] = output_value(rr, sx, h2f(s_c[n]));
     }
@@ -373,15 +417,18 @@ __device__ __forceinline__ void wide_load_a(u32x4 (&stage)[N], __amdgpu_buffer_r
         stage[v] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)a_off[v], (int)soff, 0);
 }
 
-template <bool kG128, int TN>
-__device__ __forceinline__ void wide_load_b(u32x4 (&bq)[TN], uint32_t (&pq)[TN],
+template <int F, int TN>
+__device__ __forceinline__ void wide_load_b(u32x4 (&bq)[TN][Fmt<F>::kVec], uint32_t (&pq)[TN],
                                             __amdgpu_buffer_rsrc_t rb, __amdgpu_buffer_rsrc_t rp,
                                             const uint32_t (&b_off)[TN],
                                             const uint32_t (&p_off)[TN], int g) {
+    constexpr int kV = Fmt<F>::kVec;
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
-        bq[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)b_off[i], g * 1024, 0);
-        if (kG128) pq[i] = __builtin_amdgcn_raw_buffer_load_b8(rp, (int)p_off[i], g * 16, 0);
+#pragma unroll
+        for (int v = 0; v < kV; ++v)
+            bq[i][v] = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)b_off[i], (g * kV + v) * 1024, 0);
+        if (Fmt<F>::kG128) pq[i] = __builtin_amdgcn_raw_buffer_load_b8(rp, (int)p_off[i], g * 16, 0);
     }
 }
 
@@ -390,18 +437,19 @@ __device__ __forceinline__ void wide_load_b(u32x4 (&bq)[TN], uint32_t (&pq)[TN],
 // just ahead of its use. The group pattern at the end asks the scheduler to
 // interleave the k-step-1 unpack and the LDS reads with the k-step-0
 // matrix-core operations.
-template <bool kG128, int TM, int TN>
+template <int F, int TM, int TN>
 __device__ __forceinline__ void wide_compute(int32x4 (&acc)[TM][TN], const u32x4* lw,
-                                             const u32x4 (&bq)[TN], const uint32_t (&pq)[TN],
-                                             const uint32_t* lut) {
+                                             const u32x4 (&bq)[TN][Fmt<F>::kVec],
+                                             const uint32_t (&pq)[TN], const uint32_t* lut) {
+    constexpr bool kG128 = Fmt<F>::kG128;
     uint32_t gw[TN];
 #pragma unroll
     for (int i = 0; i < TN; ++i) gw[i] = kG128 ? lut[pq[i] & 0xFFu] : 0u;
     int32x4 b0[TN], b1[TN];
 #pragma unroll
-    for (int i = 0; i < TN; ++i) b0[i] = unpack_half<kG128, 0>(bq[i], gw[i]);
+    for (int i = 0; i < TN; ++i) b0[i] = b_operand<F, 0>(bq[i], gw[i]);
 #pragma unroll
-    for (int i = 0; i < TN; ++i) b1[i] = unpack_half<kG128, 1>(bq[i], gw[i]);
+    for (int i = 0; i < TN; ++i) b1[i] = b_operand<F, 1>(bq[i], gw[i]);
 #pragma unroll
     for (int a = 0; a < TM; ++a) {
         const int32x4 af = __builtin_bit_cast(int32x4, lw[a * 128]);
@@ -414,20 +462,21 @@ __device__ __forceinline__ void wide_compute(int32x4 (&acc)[TM][TN], const u32x4
 #pragma unroll
         for (int i = 0; i < TN; ++i) acc[a][i] = mfma16x16x64(af, b1[i], acc[a][i]);
     }
-    // Scheduling pattern (masks: 0x2 VALU, 0x8 MFMA, 0x100 LDS read).
-    constexpr int kUnpackHalf = (kG128 ? 14 : 6) * TN;  // VALU per k-step unpack
+    // Scheduling pattern (masks: 0x2 VALU, 0x8 MFMA, 0x100 LDS read). INT8
+    // weights need no unpack: only the LDS reads are interleaved.
+    constexpr int kUnpackHalf = (F == kFmtG128 ? 14 : F == kFmtPC ? 6 : 0) * TN;
     constexpr int kValuPerRow = (kUnpackHalf + TM - 1) / TM;
     if (kG128) {
         __builtin_amdgcn_sched_group_barrier(0x002, TN, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, TN, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x002, kUnpackHalf, 0);
+    if (kUnpackHalf > 0) __builtin_amdgcn_sched_group_barrier(0x002, kUnpackHalf, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
     for (int a = 0; a < TM; ++a) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, kValuPerRow, 0);
+        if (kValuPerRow > 0) __builtin_amdgcn_sched_group_barrier(0x002, kValuPerRow, 0);
     }
 #pragma unroll
     for (int a = 0; a < TM; ++a) {
@@ -436,7 +485,7 @@ __device__ __forceinline__ void wide_compute(int32x4 (&acc)[TM][TN], const u32x4
     }
 }
 
-template <bool kG128, int BM, int BN, int WN>
+template <int F, int BM, int BN, int WN>
 __global__ __launch_bounds__(WN * 64, 2) void k_gemm_wide(
     const int8_t* __restrict__ xq, const uint16_t* __restrict__ s_x,
     const int32_t* __restrict__ rowsum, const uint8_t* __restrict__ blob,
@@ -471,10 +520,12 @@ __global__ __launch_bounds__(WN * 64, 2) void k_gemm_wide(
     const int bm = first_m + (pid % per_group) % gsz;
     const int bn = (pid % per_group) / gsz;
 
+    constexpr bool kG128 = Fmt<F>::kG128;
+    constexpr int kV = Fmt<F>::kVec;
     if (kG128)
         for (int i = threadIdx.x; i < 256; i += kThr) lut[i] = group_word((uint32_t)i);
 
-    const size_t code_bytes = (size_t)N * K / 2;
+    const size_t code_bytes = code_bytes_of(F, N, K);
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
         (void*)xq, (short)0, (int)((uint32_t)G * (uint32_t)U * 2048u), kBufferConfig);
     const __amdgpu_buffer_rsrc_t rb =
@@ -500,7 +551,7 @@ __global__ __launch_bounds__(WN * 64, 2) void k_gemm_wide(
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
         const int t = min(bn * (BN / 16) + wave * TN + i, tiles - 1);
-        b_off[i] = ((uint32_t)t * (uint32_t)G * 64u + (uint32_t)lane) * 16u;
+        b_off[i] = ((uint32_t)t * (uint32_t)G * 64u * kV + (uint32_t)lane) * 16u;
         p_off[i] = (uint32_t)t * (uint32_t)G * 16u + (uint32_t)c;
     }
 
@@ -511,7 +562,7 @@ __global__ __launch_bounds__(WN * 64, 2) void k_gemm_wide(
         for (int b = 0; b < TN; ++b) acc[a][b] = int32x4{0, 0, 0, 0};
 
     u32x4 stage[kAPerThr];
-    u32x4 b0q[TN], b1q[TN];
+    u32x4 b0q[TN][kV], b1q[TN][kV];
     uint32_t p0q[TN], p1q[TN];
     const u32x4* lw0 = lds_a0 + lane;
     const u32x4* lw1 = lds_a1 + lane;
@@ -521,7 +572,7 @@ __global__ __launch_bounds__(WN * 64, 2) void k_gemm_wide(
     wide_load_a(stage, ra, a_off, 0u);
     tile_store_a<kAPerThr, kThr>(lds_a0, stage);
     wide_load_a(stage, ra, a_off, (uint32_t)min(1, G - 1) * a_step);
-    wide_load_b<kG128, TN>(b0q, p0q, rb, rp, b_off, p_off, 0);
+    wide_load_b<F, TN>(b0q, p0q, rb, rp, b_off, p_off, 0);
     __syncthreads();
 
     // Step h: issue the weight loads of group h+1, run group h, then publish
@@ -534,22 +585,22 @@ __global__ __launch_bounds__(WN * 64, 2) void k_gemm_wide(
     // with one more step. Look-ahead group indices are clamped at the end.
     int h = 0;
     for (; h + 1 < G; h += 2) {
-        wide_load_b<kG128, TN>(b1q, p1q, rb, rp, b_off, p_off, h + 1);
+        wide_load_b<F, TN>(b1q, p1q, rb, rp, b_off, p_off, h + 1);
         __builtin_amdgcn_sched_barrier(0);
-        wide_compute<kG128, TM, TN>(acc, lw0, b0q, p0q, lut);
+        wide_compute<F, TM, TN>(acc, lw0, b0q, p0q, lut);
         __builtin_amdgcn_sched_barrier(0);
         tile_store_a<kAPerThr, kThr>(lds_a1, stage);
         wide_load_a(stage, ra, a_off, (uint32_t)min(h + 2, G - 1) * a_step);
         __syncthreads();
-        wide_load_b<kG128, TN>(b0q, p0q, rb, rp, b_off, p_off, min(h + 2, G - 1));
+        wide_load_b<F, TN>(b0q, p0q, rb, rp, b_off, p_off, min(h + 2, G - 1));
         __builtin_amdgcn_sched_barrier(0);
-        wide_compute<kG128, TM, TN>(acc, lw1, b1q, p1q, lut);
+        wide_compute<F, TM, TN>(acc, lw1, b1q, p1q, lut);
         __builtin_amdgcn_sched_barrier(0);
         tile_store_a<kAPerThr, kThr>(lds_a0, stage);
         wide_load_a(stage, ra, a_off, (uint32_t)min(h + 3, G - 1) * a_step);
         __syncthreads();
     }
-    if (h < G) wide_compute<kG128, TM, TN>(acc, lw0, b0q, p0q, lut);
+    if (h < G) wide_compute<F, TM, TN>(acc, lw0, b0q, p0q, lut);
 
     // Epilogue.
     const uint8_t* pc_z = blob + code_bytes;
@@ -559,11 +610,11 @@ __global__ __launch_bounds__(WN * 64, 2) void k_gemm_wide(
         if (t >= tiles) continue;
         const int n = 16 * t + c;
         const float sc = h2f(s_c[n]);
-        const int zpc = kG128 ? 0 : (int)pc_z[n];
+        const int zpc = Fmt<F>::kZp ? (int)pc_z[n] : 0;
 #pragma unroll
         for (int a = 0; a < TM; ++a) {
             const int m_first = bm * BM + a * 16 + 4 * j;
-            store_outputs<kG128>(acc[a][i], m_first, n, M, N, s_x, rowsum, sc, zpc, y, acc_out);
+            store_outputs<F>(acc[a][i], m_first, n, M, N, s_x, rowsum, sc, zpc, y, acc_out);
         }
     }
 }
@@ -586,19 +637,21 @@ __global__ __launch_bounds__(WN * 64, 2) void k_gemm_wide(
 // runs the epilogue for a share of the (tile, row block) pairs.
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
-template <bool kG128, int MB, int NT>
-__device__ __forceinline__ void stream_load(u32x4 (&bq)[NT], uint32_t (&pq)[NT],
+template <int F, int MB, int NT>
+__device__ __forceinline__ void stream_load(u32x4 (&bq)[NT][Fmt<F>::kVec], uint32_t (&pq)[NT],
                                             int32x4 (&aq)[MB][2], __amdgpu_buffer_rsrc_t rb,
                                             __amdgpu_buffer_rsrc_t rp, __amdgpu_buffer_rsrc_t ra,
                                             const uint32_t (&b_off)[NT],
                                             const uint32_t (&p_off)[NT],
                                             const uint32_t (&a_off)[MB], int gi, bool valid,
                                             uint32_t a_step) {
+    constexpr int kV = Fmt<F>::kVec;
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
-        const uint32_t ob = valid ? b_off[i] + (uint32_t)gi * 1024u : kOutOfRange;
-        bq[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)ob, 0, 0);
-        if (kG128) {
+        const uint32_t ob = valid ? b_off[i] + (uint32_t)gi * (1024u * kV) : kOutOfRange;
+        bq[i][0] = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)ob, 0, 0);
+        if constexpr (kV == 2) bq[i][1] = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)ob, 1024, 0);
+        if (Fmt<F>::kG128) {
             const uint32_t op = valid ? p_off[i] + (uint32_t)gi * 16u : kOutOfRange;
             pq[i] = __builtin_amdgcn_raw_buffer_load_b8(rp, (int)op, 0, 0);
         }
@@ -612,25 +665,26 @@ __device__ __forceinline__ void stream_load(u32x4 (&bq)[NT], uint32_t (&pq)[NT],
     }
 }
 
-template <bool kG128, int MB, int NT>
-__device__ __forceinline__ void stream_compute(int32x4 (&acc)[NT][MB], const u32x4 (&bq)[NT],
+template <int F, int MB, int NT>
+__device__ __forceinline__ void stream_compute(int32x4 (&acc)[NT][MB],
+                                               const u32x4 (&bq)[NT][Fmt<F>::kVec],
                                                const uint32_t (&pq)[NT],
                                                const int32x4 (&aq)[MB][2], const uint32_t* lut) {
     uint32_t gw[NT];
 #pragma unroll
-    for (int i = 0; i < NT; ++i) gw[i] = kG128 ? lut[pq[i] & 0xFFu] : 0u;
+    for (int i = 0; i < NT; ++i) gw[i] = Fmt<F>::kG128 ? lut[pq[i] & 0xFFu] : 0u;
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
-        const int32x4 b0 = unpack_half<kG128, 0>(bq[i], gw[i]);
+        const int32x4 b0 = b_operand<F, 0>(bq[i], gw[i]);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) acc[i][mb] = mfma16x16x64(aq[mb][0], b0, acc[i][mb]);
-        const int32x4 b1 = unpack_half<kG128, 1>(bq[i], gw[i]);
+        const int32x4 b1 = b_operand<F, 1>(bq[i], gw[i]);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) acc[i][mb] = mfma16x16x64(aq[mb][1], b1, acc[i][mb]);
     }
 }
 
-template <bool kG128, int MB, int NT, int R, int W>
+template <int F, int MB, int NT, int R, int W>
 __global__ __launch_bounds__(W * 64) void k_gemm_stream(
     const int8_t* __restrict__ xq, const uint16_t* __restrict__ s_x,
     const int32_t* __restrict__ rowsum, const uint8_t* __restrict__ blob,
@@ -657,6 +711,8 @@ __global__ __launch_bounds__(W * 64) void k_gemm_stream(
     const int nb = blockIdx.x - mh * nblk;
     const int u0 = mh * MB;
 
+    constexpr bool kG128 = Fmt<F>::kG128;
+    constexpr int kV = Fmt<F>::kVec;
     for (int i = threadIdx.x; i < kPairs * 4 * kWave; i += kThr) red[i] = 0;
     if (kG128)
         for (int i = threadIdx.x; i < 256; i += kThr) lut[i] = group_word((uint32_t)i);
@@ -665,7 +721,7 @@ __global__ __launch_bounds__(W * 64) void k_gemm_stream(
     const int g0 = G * wave / W;
     const int count = G * (wave + 1) / W - g0;
 
-    const size_t code_bytes = (size_t)N * K / 2;
+    const size_t code_bytes = code_bytes_of(F, N, K);
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
         (void*)xq, (short)0, (int)((uint32_t)G * (uint32_t)U * 2048u), kBufferConfig);
     const __amdgpu_buffer_rsrc_t rb =
@@ -679,7 +735,7 @@ __global__ __launch_bounds__(W * 64) void k_gemm_stream(
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
         const int t = min(nb * NT + i, tiles - 1);
-        b_off[i] = ((uint32_t)t * (uint32_t)G + (uint32_t)g0) * 1024u + (uint32_t)lane * 16u;
+        b_off[i] = ((uint32_t)t * (uint32_t)G + (uint32_t)g0) * (1024u * kV) + (uint32_t)lane * 16u;
         p_off[i] = ((uint32_t)t * (uint32_t)G + (uint32_t)g0) * 16u + (uint32_t)c;
     }
     const uint32_t a_step = (uint32_t)U * 2048u;
@@ -693,28 +749,28 @@ __global__ __launch_bounds__(W * 64) void k_gemm_stream(
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) acc[i][mb] = int32x4{0, 0, 0, 0};
 
-    u32x4 bq[R][NT];
+    u32x4 bq[R][NT][kV];
     uint32_t pq[R][NT];
     int32x4 aq[R][MB][2];
     const int main_count = count / R * R;
 #pragma unroll
     for (int r = 0; r < R - 1; ++r)
-        stream_load<kG128, MB, NT>(bq[r], pq[r], aq[r], rb, rp, ra, b_off, p_off, a_off, r,
+        stream_load<F, MB, NT>(bq[r], pq[r], aq[r], rb, rp, ra, b_off, p_off, a_off, r,
                                    r < main_count, a_step);
     for (int h = 0; h < main_count; h += R) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int nxt = h + r + R - 1;
-            stream_load<kG128, MB, NT>(bq[(r + R - 1) % R], pq[(r + R - 1) % R],
+            stream_load<F, MB, NT>(bq[(r + R - 1) % R], pq[(r + R - 1) % R],
                                        aq[(r + R - 1) % R], rb, rp, ra, b_off, p_off, a_off, nxt,
                                        nxt < main_count, a_step);
-            stream_compute<kG128, MB, NT>(acc, bq[r], pq[r], aq[r], lut);
+            stream_compute<F, MB, NT>(acc, bq[r], pq[r], aq[r], lut);
         }
     }
     for (int h = main_count; h < count; ++h) {
-        stream_load<kG128, MB, NT>(bq[0], pq[0], aq[0], rb, rp, ra, b_off, p_off, a_off, h, true,
+        stream_load<F, MB, NT>(bq[0], pq[0], aq[0], rb, rp, ra, b_off, p_off, a_off, h, true,
                                    a_step);
-        stream_compute<kG128, MB, NT>(acc, bq[0], pq[0], aq[0], lut);
+        stream_compute<F, MB, NT>(acc, bq[0], pq[0], aq[0], lut);
     }
 
     // Sum the waves' partial tiles in LDS.
@@ -736,8 +792,8 @@ __global__ __launch_bounds__(W * 64) void k_gemm_stream(
         int32x4 a;
 #pragma unroll
         for (int v = 0; v < 4; ++v) a[v] = red[(p * 4 + v) * kWave + lane];
-        const int zpc = kG128 ? 0 : (int)pc_z[n];
-        store_outputs<kG128>(a, 16 * (u0 + mb) + 4 * j, n, M, N, s_x, rowsum, h2f(s_c[n]), zpc,
+        const int zpc = Fmt<F>::kZp ? (int)pc_z[n] : 0;
+        store_outputs<F>(a, 16 * (u0 + mb) + 4 * j, n, M, N, s_x, rowsum, h2f(s_c[n]), zpc,
                              y, acc_out);
     }
 }
@@ -766,10 +822,10 @@ int g_force_kind = 0, g_force_nt = 0, g_force_r = 0, g_force_w = 0, g_force_bn =
 
 // The buffer-load kernels form 32-bit byte offsets, and mark prefetches past
 // the end with offset 2^31: every real offset must stay below that.
-bool fits_buffer_offsets(int64_t M, int64_t N, int64_t K) {
+bool fits_buffer_offsets(int fmt, int64_t M, int64_t N, int64_t K) {
     const int64_t G = K / kGroup, U = (M + 15) / 16;
-    return G * U * 2048 < (int64_t(1) << 31) && N * K / 2 < (int64_t(1) << 31) &&
-           N * G < (int64_t(1) << 31);
+    return G * U * 2048 < (int64_t(1) << 31) &&
+           (int64_t)code_bytes_of(fmt, N, K) < (int64_t(1) << 31) && N * G < (int64_t(1) << 31);
 }
 
 // Measured on MI355X over the Llama-3-8B and Qwen1.5-72B layers:
@@ -786,10 +842,10 @@ bool fits_buffer_offsets(int64_t M, int64_t N, int64_t K) {
 //     compute units and a workspace is given.
 // Shapes whose offsets do not fit the buffer-load kernels take the reference
 // kernel (M <= 64) or the 16-row-wave tiled kernel (M > 64).
-Plan plan_gemm(int64_t M, int64_t N, int64_t K, bool have_ws) {
+Plan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, bool have_ws) {
     Plan p;
     const int64_t tiles = N / 16;
-    const bool fits = fits_buffer_offsets(M, N, K);
+    const bool fits = fits_buffer_offsets(fmt, M, N, K);
     if (M <= 64) {
         if (fits) {
             p.kind = kStream;
@@ -868,107 +924,109 @@ struct GemmArgs {
     int group_m;
 };
 
-template <bool kG128, int MB, int NT, int R, int W>
+template <int F, int MB, int NT, int R, int W>
 void launch_stream_t(const Plan& p, const GemmArgs& a) {
-    hipLaunchKernelGGL((k_gemm_stream<kG128, MB, NT, R, W>), dim3((unsigned)(p.nblk * p.mgrid)), dim3(W * 64),
+    hipLaunchKernelGGL((k_gemm_stream<F, MB, NT, R, W>), dim3((unsigned)(p.nblk * p.mgrid)), dim3(W * 64),
                        0, a.stream, a.xq, a.s_x, a.rowsum, a.blob, a.s_c, a.M, a.N, a.K, a.y,
                        a.acc_out);
 }
 
-template <bool kG128, int MB, int NT>
+template <int F, int MB, int NT>
 void launch_stream_rw(const Plan& p, const GemmArgs& a) {
 #ifdef QOQ_TUNING
-    if (p.r == 4 && p.w == 4) { launch_stream_t<kG128, MB, NT, 4, 4>(p, a); return; }
-    if (p.r == 2 && p.w == 4) { launch_stream_t<kG128, MB, NT, 2, 4>(p, a); return; }
-    if (p.r == 4 && p.w == 8) { launch_stream_t<kG128, MB, NT, 4, 8>(p, a); return; }
-    if (p.r == 2 && p.w == 16) { launch_stream_t<kG128, MB, NT, 2, 16>(p, a); return; }
-    if (p.r == 1 && p.w == 8) { launch_stream_t<kG128, MB, NT, 1, 8>(p, a); return; }
+    if (p.r == 4 && p.w == 4) { launch_stream_t<F, MB, NT, 4, 4>(p, a); return; }
+    if (p.r == 2 && p.w == 4) { launch_stream_t<F, MB, NT, 2, 4>(p, a); return; }
+    if (p.r == 4 && p.w == 8) { launch_stream_t<F, MB, NT, 4, 8>(p, a); return; }
+    if (p.r == 2 && p.w == 16) { launch_stream_t<F, MB, NT, 2, 16>(p, a); return; }
+    if (p.r == 1 && p.w == 8) { launch_stream_t<F, MB, NT, 1, 8>(p, a); return; }
 #endif
-    if (p.r == 1) launch_stream_t<kG128, MB, NT, 1, 16>(p, a);
-    else launch_stream_t<kG128, MB, NT, 2, 8>(p, a);
+    if (p.r == 1) launch_stream_t<F, MB, NT, 1, 16>(p, a);
+    else launch_stream_t<F, MB, NT, 2, 8>(p, a);
 }
 
-template <bool kG128, int MB>
+template <int F, int MB>
 void launch_stream_nt(const Plan& p, const GemmArgs& a) {
 #ifdef QOQ_TUNING
-    if (p.nt == 1) { launch_stream_rw<kG128, MB, 1>(p, a); return; }
+    if (p.nt == 1) { launch_stream_rw<F, MB, 1>(p, a); return; }
 #endif
-    if (p.nt == 3) launch_stream_rw<kG128, MB, 3>(p, a);
-    else launch_stream_rw<kG128, MB, 2>(p, a);
+    if (p.nt == 3) launch_stream_rw<F, MB, 3>(p, a);
+    else launch_stream_rw<F, MB, 2>(p, a);
 }
 
-template <bool kG128>
+template <int F>
 void launch_stream(const Plan& p, const GemmArgs& a) {
-    if (p.mb == 1) launch_stream_nt<kG128, 1>(p, a);
-    else if (p.mb == 2) launch_stream_nt<kG128, 2>(p, a);
-    else launch_stream_nt<kG128, 4>(p, a);
+    if (p.mb == 1) launch_stream_nt<F, 1>(p, a);
+    else if (p.mb == 2) launch_stream_nt<F, 2>(p, a);
+    else launch_stream_nt<F, 4>(p, a);
 }
 
-template <bool kG128, int BM, int BN, int WM, int WN>
+template <int F, int BM, int BN, int WM, int WN>
 void launch_tile_t(const Plan& p, const GemmArgs& a) {
     const unsigned blocks = (unsigned)(((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * p.s);
     int32_t* part = p.s > 1 ? a.part : nullptr;
-    hipLaunchKernelGGL((k_gemm_tile<kG128, BM, BN, WM, WN>), dim3(blocks), dim3(WM * WN * 64), 0,
+    hipLaunchKernelGGL((k_gemm_tile<F, BM, BN, WM, WN>), dim3(blocks), dim3(WM * WN * 64), 0,
                        a.stream, a.xq, a.s_x, a.rowsum, a.blob, a.s_c, a.M, a.N, a.K, a.y,
                        a.acc_out, p.s, part);
     if (part) {
         const int64_t quads = (int64_t)a.M * a.N / 4;
-        hipLaunchKernelGGL(k_splitk_reduce<kG128>, dim3((unsigned)((quads + kThreads - 1) / kThreads)),
+        hipLaunchKernelGGL(k_splitk_reduce<F>, dim3((unsigned)((quads + kThreads - 1) / kThreads)),
                            dim3(kThreads), 0, a.stream, part, p.s, a.s_x, a.rowsum,
-                           a.blob + (size_t)a.N * a.K / 2, a.s_c, a.M, a.N, a.y, a.acc_out);
+                           a.blob + code_bytes_of(F, a.N, a.K), a.s_c, a.M, a.N, a.y, a.acc_out);
     }
 }
 
-template <bool kG128, int BM, int BN, int WN>
+template <int F, int BM, int BN, int WN>
 void launch_wide_t(const GemmArgs& a) {
     const unsigned blocks = (unsigned)(((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN));
-    hipLaunchKernelGGL((k_gemm_wide<kG128, BM, BN, WN>), dim3(blocks), dim3(WN * 64), 0, a.stream,
+    hipLaunchKernelGGL((k_gemm_wide<F, BM, BN, WN>), dim3(blocks), dim3(WN * 64), 0, a.stream,
                        a.xq, a.s_x, a.rowsum, a.blob, a.s_c, a.M, a.N, a.K, a.y, a.acc_out,
                        a.group_m);
 }
 
-template <bool kG128>
+template <int F>
 void launch_simple(const GemmArgs& a) {
     const dim3 grid((unsigned)((a.N / 16 + 3) / 4), (unsigned)((a.M + 63) / 64));
-    hipLaunchKernelGGL(k_gemm_simple<kG128>, grid, dim3(kThreads), 0, a.stream, a.xq, a.s_x,
+    hipLaunchKernelGGL(k_gemm_simple<F>, grid, dim3(kThreads), 0, a.stream, a.xq, a.s_x,
                        a.rowsum, a.blob, a.s_c, a.M, a.N, a.K, a.y, a.acc_out);
 }
 
-template <bool kG128>
+template <int F>
 void launch_plan(const Plan& p, const GemmArgs& a) {
     switch (p.kind) {
         case kStream:
-            launch_stream<kG128>(p, a);
+            launch_stream<F>(p, a);
             break;
         case kWide:
-            launch_wide_t<kG128, 128, 256, 4>(a);
+            launch_wide_t<F, 128, 256, 4>(a);
             break;
         case kTile:
-            if (p.bn == 256) launch_tile_t<kG128, 128, 256, 2, 4>(p, a);
-            else launch_tile_t<kG128, 128, 128, 2, 2>(p, a);
+            if (p.bn == 256) launch_tile_t<F, 128, 256, 2, 4>(p, a);
+            else launch_tile_t<F, 128, 128, 2, 2>(p, a);
             break;
         default:
-            launch_simple<kG128>(a);
+            launch_simple<F>(a);
             break;
     }
 }
 
 }  // namespace
 
-int64_t gemm_workspace_bytes(int /*mode*/, int64_t M, int64_t N, int64_t K) {
-    return plan_gemm(M, N, K, true).ws_bytes;
+int64_t gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K) {
+    return plan_gemm(fmt, M, N, K, true).ws_bytes;
 }
 
-void launch_gemm(int mode, const int8_t* xq, const uint16_t* s_x, const int32_t* rowsum,
+void launch_gemm(int fmt, const int8_t* xq, const uint16_t* s_x, const int32_t* rowsum,
                  const uint8_t* blob, const uint16_t* s_c, int64_t M, int64_t N, int64_t K,
                  uint16_t* y, int32_t* acc_out, void* ws, hipStream_t stream) {
-    const Plan p = plan_gemm(M, N, K, ws != nullptr);
+    const Plan p = plan_gemm(fmt, M, N, K, ws != nullptr);
     const GemmArgs a{static_cast<int32_t*>(ws), xq, s_x, rowsum, blob, s_c, (int)M, (int)N, (int)K,
                      y, acc_out, stream, p.group_m};
-    if (mode == 0)
-        launch_plan<true>(p, a);
+    if (fmt == kFmtG128)
+        launch_plan<kFmtG128>(p, a);
+    else if (fmt == kFmtPC)
+        launch_plan<kFmtPC>(p, a);
     else
-        launch_plan<false>(p, a);
+        launch_plan<kFmtW8>(p, a);
 }
 
 #ifdef QOQ_TUNING

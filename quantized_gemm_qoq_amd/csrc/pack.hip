@@ -1,5 +1,5 @@
-// pack.hip -- offline reorder of UINT4 codes into the gfx950 MFMA operand
-// order, and its inverse.
+// pack.hip -- offline reorder of UINT4 codes (and of the INT8 weights of the
+// W8A8 sibling) into the gfx950 MFMA operand order, and its inverse.
 //
 // The pages' procedure reorders the W4 packs offline so that the fragments the
 // matrix units consume next to each other need no extra address arithmetic
@@ -104,6 +104,24 @@ __global__ __launch_bounds__(kThreads) void k_copy_bytes(const uint8_t* __restri
     if (tid < n) dst[tid] = src[tid];
 }
 
+// INT8 weights: one thread per 16-byte slot of the blob. Slot index
+// (((t * G + g) * 2 + s) * 4 + j) * 16 + c holds inputs 128g + 64s + 16j + 0..15
+// of channel 16t + c, which is the B operand of lane 16j + c for k-step s.
+__global__ __launch_bounds__(kThreads) void k_pack_w8(const int8_t* __restrict__ q, int64_t N,
+                                                      int K, uint8_t* __restrict__ blob) {
+    const int64_t tid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int G = K / kGroup;
+    if (tid >= N * K / 16) return;
+    const int c = (int)(tid % 16);
+    const int j = (int)((tid / 16) % 4);
+    const int s = (int)((tid / 64) % 2);
+    const int64_t tg = tid / 128;
+    const int64_t t = tg / G;
+    const int g = (int)(tg % G);
+    const int8_t* src = q + (16 * t + c) * K + g * kGroup + 64 * s + 16 * j;
+    reinterpret_cast<uint4*>(blob)[tid] = *reinterpret_cast<const uint4*>(src);
+}
+
 unsigned blocks_for(int64_t threads) { return (unsigned)((threads + kThreads - 1) / kThreads); }
 
 }  // namespace
@@ -144,6 +162,11 @@ void launch_unpack(int mode, const uint8_t* blob, int64_t N, int64_t K, uint8_t*
         hipLaunchKernelGGL(k_copy_bytes, dim3(blocks_for(N)), dim3(kThreads), 0, stream, params, N,
                            z);
     }
+}
+
+void launch_pack_w8(const int8_t* q, int64_t N, int64_t K, uint8_t* blob, hipStream_t stream) {
+    hipLaunchKernelGGL(k_pack_w8, dim3(blocks_for(N * K / 16)), dim3(kThreads), 0, stream, q, N,
+                       (int)K, blob);
 }
 
 }  // namespace qoq

@@ -21,12 +21,21 @@ void launch_pack(int mode, const uint8_t* q, const uint8_t* s_g, const uint8_t* 
 void launch_unpack(int mode, const uint8_t* blob, int64_t N, int64_t K, uint8_t* q, uint8_t* s_g,
                    uint8_t* z, hipStream_t stream);
 
+// INT8 weights of the W8A8 sibling: per-channel symmetric quantization, and
+// the reorder into the operand order (N * K bytes).
+void launch_quantize_weights_w8(const uint16_t* w, int64_t N, int64_t K, int8_t* q, uint16_t* s_c,
+                                hipStream_t stream);
+void launch_pack_w8(const int8_t* q, int64_t N, int64_t K, uint8_t* blob, hipStream_t stream);
+
+// Weight format of a GEMM call: 0 g128 UINT4, 1 per-channel UINT4, 2 INT8.
+constexpr int kGemmFmtW8 = 2;
+
 // Workspace bytes the GEMM plan for this shape uses when given one (0: none).
-int64_t gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K);
+int64_t gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K);
 
 // ws: null (a plan without split K is used) or gemm_workspace_bytes() bytes
 // of device memory for split-K partial sums (no initialisation needed).
-void launch_gemm(int mode, const int8_t* xq, const uint16_t* s_x, const int32_t* rowsum,
+void launch_gemm(int fmt, const int8_t* xq, const uint16_t* s_x, const int32_t* rowsum,
                  const uint8_t* blob, const uint16_t* s_c, int64_t M, int64_t N, int64_t K,
                  uint16_t* y, int32_t* acc_out, void* ws, hipStream_t stream);
 

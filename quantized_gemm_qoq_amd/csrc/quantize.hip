@@ -1,5 +1,6 @@
 // quantize.hip -- per-token INT8 activation quantization and the offline
-// weight quantizers (progressive g128 and per-channel UINT4), for gfx950.
+// weight quantizers (progressive g128 and per-channel UINT4, and the INT8
+// weights of the W8A8 sibling), for gfx950.
 //
 // Method: QServe / QoQ (arXiv 2405.04532).
 //   Activations: "QServe Guide: W4A8KV4 Quantization for LLM Serving", Deep Dive
@@ -299,7 +300,55 @@ __global__ __launch_bounds__(kThreads) void k_quantize_weights_pc(
     }
 }
 
+// W8A8 sibling: per-channel symmetric INT8 ("QServe Guide: W4A8KV4
+// Quantization for LLM Serving", "The Problem" item 2, with the per-channel
+// symmetric scaling of "Deep Dive" part 1 at 8 bits): s_c = f16(max|W|/127),
+// q = clamp(round(W / s_c), -128, 127). One workgroup per output channel.
+__global__ __launch_bounds__(kThreads) void k_quantize_weights_w8(const uint16_t* __restrict__ w,
+                                                                  int K, int8_t* __restrict__ q,
+                                                                  uint16_t* __restrict__ s_c) {
+    __shared__ unsigned red_u[kWaves];
+    const size_t n = blockIdx.x;
+    const uint4* rowv = reinterpret_cast<const uint4*>(w + n * (size_t)K);
+    const int nvec = K / 8;
+
+    unsigned amax = 0;
+    for (int i = threadIdx.x; i < nvec; i += kThreads) {
+        const uint4 v = rowv[i];
+        amax = max(amax, max(max(absmax_bits2(v.x), absmax_bits2(v.y)),
+                             max(absmax_bits2(v.z), absmax_bits2(v.w))));
+    }
+    amax = block_reduce(amax, red_u, MaxU{});
+    const uint16_t scbits = f2h(h2f(amax) / 127.0f);
+    const float scf = h2f(scbits);
+    if (threadIdx.x == 0) s_c[n] = scbits;
+
+    uint2* out = reinterpret_cast<uint2*>(q + n * (size_t)K);
+    for (int i = threadIdx.x; i < nvec; i += kThreads) {
+        uint2 o = {0u, 0u};
+        if (scf != 0.0f) {
+            const uint4 v = rowv[i];
+            const uint32_t ws[4] = {v.x, v.y, v.z, v.w};
+            uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                packed[e >> 2] |= (uint32_t)(quant_act1((e & 1) ? (ws[e >> 1] >> 16)
+                                                                : (ws[e >> 1] & 0xFFFFu),
+                                                        scf) & 0xFF)
+                                  << (8 * (e & 3));
+            o = make_uint2(packed[0], packed[1]);
+        }
+        out[i] = o;
+    }
+}
+
 }  // namespace
+
+void launch_quantize_weights_w8(const uint16_t* w, int64_t N, int64_t K, int8_t* q, uint16_t* s_c,
+                                hipStream_t stream) {
+    hipLaunchKernelGGL(k_quantize_weights_w8, dim3((unsigned)N), dim3(kThreads), 0, stream, w,
+                       (int)K, q, s_c);
+}
 
 void launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, uint16_t* s_x,
                          int32_t* rowsum, hipStream_t stream) {

@@ -135,3 +135,33 @@ def test_workspace_bytes(lib):
     assert f(0, 0, 16, 128) == 0
     assert f(0, 8, 16, 128) >= 0
     assert f(0, 64, 6144, 4096) % 16 == 0
+
+
+def test_w8a8_validation(lib):
+    assert lib.qoq_w8a8_packed_bytes(16, 128) == 16 * 128
+    assert lib.qoq_w8a8_packed_bytes(15, 128) == -1
+    assert lib.qoq_w8a8_packed_bytes(16, 100) == -1
+    q = lib.qoq_w8a8_quantize_weights
+    assert q(A, 0, 128, NUL, NUL, NUL) == OK
+    assert q(A, 24, 128, A, A, NUL) == ERR_SHAPE
+    assert q(A, 16, 128, NUL, A, NUL) == ERR_NULL
+    assert q(U, 16, 128, A, A, NUL) == ERR_ALIGN
+    p = lib.qoq_w8a8_pack_weights
+    assert p(A, 0, 128, A, NUL) == ERR_SHAPE
+    assert p(A, 16, 128, NUL, NUL) == ERR_NULL
+    assert p(A, 16, 128, U, NUL) == ERR_ALIGN
+    f = lib.qoq_w8a8_gemm
+    def args(xq=A, sx=A, blob=A, sc=A, M=8, N=16, K=128, y=A, acc=NUL, ws=NUL, wsb=0):
+        return f(xq, sx, blob, sc, M, N, K, y, acc, ws, wsb, NUL)
+    assert args(M=0) == OK
+    assert args(N=8) == ERR_SHAPE
+    assert args(K=200) == ERR_SHAPE
+    assert args(blob=NUL) == ERR_NULL
+    assert args(y=U) == ERR_ALIGN
+    w = lib.qoq_w8a8_gemm_workspace_bytes
+    assert w(64, 6144, 4096) == 0
+    need = w(256, 512, 2048)
+    assert need > 0 and need % (256 * 512 * 4) == 0
+    assert args(M=256, N=512, K=2048, ws=A, wsb=need - 1) == ERR_WORKSPACE
+    assert w(8, 15, 128) == -1
+
