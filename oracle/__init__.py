@@ -73,6 +73,8 @@ def _load():
                 "orc_pack_w8": (I, [P, I64, I64, P]),
                 "orc_gemm_w8": (I, [P, P, I64, I64, I64, P]),
                 "orc_gemm_w8_points": (I, [P, P, I64, I64, I64, I64, P, P, P]),
+                "orc_gemm_w4a16": (I, [I, P, P, P, P, P, I64, I64, I64, P, P]),
+                "orc_gemm_w4a16_points": (I, [I, P, P, P, P, P, I64, I64, I64, I64, P, P, P, P]),
             }
             for name, (res, args) in sigs.items():
                 fn = getattr(lib, name)
@@ -316,3 +318,44 @@ def forward_w8(x_bits, w_bits):
     acc = gemm_w8(xq, q)
     y = epilogue(acc, s_x, s_c)
     return {"xq": xq, "s_x": s_x, "acc": acc, "y": y, "s_c": s_c, "q": q}
+
+
+# --- W4A16 sibling: FP16 activations, the same 4-bit weights (reading R12) --
+
+def gemm_w4a16(mode, x_bits, s_c, q, s_g, z):
+    """(y, absum) float64 [M,N]: y = X . W^T with W^ = s_c * s_g * (q - z)
+    (per-channel: s_c * (q - z)); absum = s_c * sum_k |X * W8^|."""
+    x = _c(x_bits, np.uint16)
+    q = _c(q, np.uint8)
+    M, K = x.shape
+    N = q.shape[0]
+    y = np.empty((M, N), np.float64)
+    a = np.empty((M, N), np.float64)
+    sg = None if s_g is None else _c(s_g, np.uint8)
+    _check(_load().orc_gemm_w4a16(mode, _p(x), _p(_c(s_c, np.uint16)), _p(q), _p(sg),
+                                  _p(_c(z, np.uint8)), M, N, K, _p(y), _p(a)), "gemm_w4a16")
+    return y, a
+
+
+def gemm_w4a16_points(mode, x_bits, s_c, q, s_g, z, ms, ns):
+    x = _c(x_bits, np.uint16)
+    q = _c(q, np.uint8)
+    M, K = x.shape
+    N = q.shape[0]
+    ms = _c(np.asarray(ms, np.int64), np.int64)
+    ns = _c(np.asarray(ns, np.int64), np.int64)
+    y = np.empty(len(ms), np.float64)
+    a = np.empty(len(ms), np.float64)
+    sg = None if s_g is None else _c(s_g, np.uint8)
+    _check(_load().orc_gemm_w4a16_points(mode, _p(x), _p(_c(s_c, np.uint16)), _p(q), _p(sg),
+                                         _p(_c(z, np.uint8)), M, N, K, len(ms), _p(ms), _p(ns),
+                                         _p(y), _p(a)), "gemm_w4a16_points")
+    return y, a
+
+
+def forward_w4a16(mode, x_bits, w_bits):
+    """The W4A16 path on the host: quantize the weights (QoQ, either mode), contract
+    the FP16 activations with the dequantized weights."""
+    wq = quantize_weights(mode, w_bits)
+    y, absum = gemm_w4a16(mode, x_bits, wq["s_c"], wq["q"], wq["s_g"], wq["z"])
+    return {"y": y, "absum": absum, **wq}

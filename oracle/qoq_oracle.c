@@ -52,7 +52,10 @@
  *   R10 the output is acc * s_x * s_c; here it is computed in fp64, where it is
  *       exact (31 + 11 + 11 significant bits <= 53);
  *   R11 the W8A8 sibling quantizes weights per output channel, symmetric, with
- *       scale max|W|/127 and the activations' clamp [-128, 127].
+ *       scale max|W|/127 and the activations' clamp [-128, 127];
+ *   R12 the W4A16 sibling keeps the activations in FP16 and reads the same QoQ
+ *       4-bit weights, so that it differs from W4A8 only in the activation
+ *       precision.
  *
  * Inputs must be finite FP16 (passed as raw binary16 bits).
  */
@@ -570,4 +573,79 @@ int orc_gemm_w8_points(const int8_t* xq, const int8_t* q, int64_t M, int64_t N, 
         acc[p] = (int32_t)s;
     }
     return overflow ? ORC_ERR_OVERFLOW : ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* W4A16 sibling ("QServe Guide: W4A8KV4 Quantization for LLM Serving", "The */
+/* Problem" item 1: 4-bit weights dequantized in the main loop, activations  */
+/* kept in FP16, FP16 matrix units; "QServe: Low Bit Width Does Not          */
+/* Guarantee High Throughput", section 2, the W4A16 failure mode). Reading   */
+/* R12: the weights are the same QoQ 4-bit weights as W4A8 (either mode),    */
+/* so that the two formats differ only in the activation precision:          */
+/*   Y[m,n] = sum_k X[m,k] * W^[n,k],  W^ = s_c * s_g * (q - z)              */
+/*          = s_c[n] * sum_k X[m,k] * W8^[n,k]                               */
+/* The inner sum is taken in fp64 over the integer weights W8^ (every term   */
+/* X * W8^ is exact in fp64, and so is the final product by s_c up to one    */
+/* rounding); absum[m,n] = s_c[n] * sum_k |X[m,k] * W8^[n,k]| is returned     */
+/* for the error bound of an fp32 accumulation (absum may be NULL).          */
+/* ------------------------------------------------------------------------ */
+int orc_gemm_w4a16(int mode, const uint16_t* x, const uint16_t* s_c, const uint8_t* q,
+                   const uint8_t* s_g, const uint8_t* z, int64_t M, int64_t N, int64_t K,
+                   double* y, double* absum) {
+    if (mode != ORC_MODE_G128 && mode != ORC_MODE_PER_CHANNEL) return ORC_ERR_MODE;
+    if (M < 0 || N < 0 || K < 1 || (mode == ORC_MODE_G128 && K % GROUP)) return ORC_ERR_SHAPE;
+#pragma omp parallel
+    {
+        int64_t* wrow = (int64_t*)malloc((size_t)K * sizeof(int64_t));
+        double* xrow = (double*)malloc((size_t)K * sizeof(double));
+#pragma omp for schedule(static)
+        for (int64_t n = 0; n < N; ++n) {
+            weight_row_int(mode, q, s_g, z, n, K, wrow);
+            const double sc = orc_f16_to_f64(s_c[n]);
+            for (int64_t m = 0; m < M; ++m) {
+                for (int64_t k = 0; k < K; ++k) xrow[k] = orc_f16_to_f64(x[m * K + k]);
+                double s = 0.0, a = 0.0;
+                for (int64_t k = 0; k < K; ++k) {
+                    const double t = xrow[k] * (double)wrow[k];
+                    s += t;
+                    a += fabs(t);
+                }
+                y[m * N + n] = s * sc;
+                if (absum) absum[m * N + n] = a * sc;
+            }
+        }
+        free(wrow);
+        free(xrow);
+    }
+    return ORC_OK;
+}
+
+/* The same at P chosen (m, n) points. */
+int orc_gemm_w4a16_points(int mode, const uint16_t* x, const uint16_t* s_c, const uint8_t* q,
+                          const uint8_t* s_g, const uint8_t* z, int64_t M, int64_t N, int64_t K,
+                          int64_t P, const int64_t* ms, const int64_t* ns, double* y,
+                          double* absum) {
+    if (mode != ORC_MODE_G128 && mode != ORC_MODE_PER_CHANNEL) return ORC_ERR_MODE;
+    if (K < 1 || (mode == ORC_MODE_G128 && K % GROUP)) return ORC_ERR_SHAPE;
+    for (int64_t p = 0; p < P; ++p)
+        if (ms[p] < 0 || ms[p] >= M || ns[p] < 0 || ns[p] >= N) return ORC_ERR_SHAPE;
+    const int64_t G = K / GROUP;
+#pragma omp parallel for schedule(static)
+    for (int64_t p = 0; p < P; ++p) {
+        const int64_t m = ms[p], n = ns[p];
+        double s = 0.0, a = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const int64_t wv =
+                mode == ORC_MODE_G128
+                    ? ((int64_t)q[n * K + k] - z[n * G + k / GROUP]) * s_g[n * G + k / GROUP]
+                    : (int64_t)q[n * K + k] - z[n];
+            const double t = orc_f16_to_f64(x[m * K + k]) * (double)wv;
+            s += t;
+            a += fabs(t);
+        }
+        const double sc = orc_f16_to_f64(s_c[n]);
+        y[p] = s * sc;
+        if (absum) absum[p] = a * sc;
+    }
+    return ORC_OK;
 }

@@ -222,3 +222,20 @@ def test_w8_pack_size():
     assert oracle.w8_packed_bytes(16, 128) == 16 * 128
     assert oracle.w8_packed_bytes(8, 128) == -1
     assert oracle.w8_packed_bytes(16, 200) == -1
+
+
+def test_w4a16_reproduces_hand_worked_w4a8_example():
+    """W4A16 with FP16 activations X = s_x * xq (exact in FP16) must give the
+    hand-worked W4A8 outputs of gemm.json: Y = s_c * sum_k X * W8^ =
+    s_x * s_c * acc, the same exact values."""
+    g = _load("gemm.json")["g128"]
+    _, w = _g128_inputs()
+    wq = oracle.quantize_weights(oracle.MODE_G128, w)
+    xq = _xq_from(g["xq_nonzero"], g["K"]).astype(np.float64)
+    s_x = np.array(g["s_x_bits"], np.uint16).view(np.float16).astype(np.float64)
+    x = (xq * s_x[:, None]).astype(np.float16)
+    assert np.array_equal(x.astype(np.float64), xq * s_x[:, None])
+    y, absum = oracle.gemm_w4a16(oracle.MODE_G128, x.view(np.uint16), wq["s_c"], wq["q"],
+                                 wq["s_g"], wq["z"])
+    np.testing.assert_array_equal(y, np.array(g["y"]))
+    assert np.all(absum >= np.abs(y))

@@ -417,3 +417,61 @@ def test_w8_end_to_end_approximates_real_product():
     w4 = oracle.forward(G128, x16.numpy().view(np.uint16), w16.numpy().view(np.uint16))
     rel4 = np.linalg.norm(w4["y"] - ref) / np.linalg.norm(ref)
     assert rel < rel4
+
+
+# -------------------------------------------------------- W4A16 sibling ----
+def test_w4a16_matches_exact_rational_sum():
+    """The fp64 contraction against exact rational arithmetic (Python
+    fractions) on a small case spanning two groups and both modes."""
+    from fractions import Fraction
+    M, K, N = 3, 256, 16
+    x = workloads.random_fp16((M, K), 51, 1.0).numpy()
+    x[0, 5] = np.float16(6e-8)  # a subnormal activation
+    w = workloads.random_fp16((N, K), 52, 0.02).numpy().view(np.uint16)
+    for mode in (G128, PC):
+        wq = oracle.quantize_weights(mode, w)
+        y, absum = oracle.gemm_w4a16(mode, x.view(np.uint16), wq["s_c"], wq["q"], wq["s_g"],
+                                     wq["z"])
+        sc = oracle.f16_bits_to_f64(wq["s_c"])
+        for m in range(M):
+            for n in range(N):
+                tot = Fraction(0)
+                for k in range(K):
+                    if mode == G128:
+                        wv = (int(wq["q"][n, k]) - int(wq["z"][n, k // 128])) * int(wq["s_g"][n, k // 128])
+                    else:
+                        wv = int(wq["q"][n, k]) - int(wq["z"][n])
+                    tot += Fraction(float(x[m, k])) * wv
+                exact = tot * Fraction(float(sc[n]))
+                assert abs(Fraction(y[m, n]) - exact) <= Fraction(2.0**-50) * Fraction(absum[m, n]) + Fraction(2.0**-1074)
+
+
+def test_w4a16_matches_library_matmul_of_dequantized_weights():
+    M, K, N = 19, 1024, 64
+    x = workloads.random_fp16((M, K), 53, 1.0).numpy()
+    w = workloads.random_fp16((N, K), 54, 0.02).numpy().view(np.uint16)
+    for mode in (G128, PC):
+        wq = oracle.quantize_weights(mode, w)
+        what = oracle.dequantize_weights(mode, wq["s_c"], wq["q"], wq["s_g"], wq["z"])
+        want = np.matmul(x.astype(np.float64), what.T)
+        y, absum = oracle.gemm_w4a16(mode, x.view(np.uint16), wq["s_c"], wq["q"], wq["s_g"], wq["z"])
+        assert np.all(np.abs(y - want) <= 1e-13 * absum)
+        ms = np.array([0, M - 1, 7]); ns = np.array([N - 1, 0, 33])
+        yp, ap = oracle.gemm_w4a16_points(mode, x.view(np.uint16), wq["s_c"], wq["q"], wq["s_g"],
+                                          wq["z"], ms, ns)
+        np.testing.assert_array_equal(yp, y[ms, ns])
+        np.testing.assert_array_equal(ap, absum[ms, ns])
+
+
+def test_w4a16_end_to_end_is_closer_than_w4a8():
+    """Keeping the activations in FP16 removes the activation rounding: W4A16
+    approximates X W^T at least as well as W4A8 on the same weights."""
+    layer = workloads.WORKLOADS["tiny"].layers[0]
+    x16, w16 = workloads.generate(layer)
+    xb, wb = x16.numpy().view(np.uint16), w16.numpy().view(np.uint16)
+    ref = x16.numpy().astype(np.float64) @ w16.numpy().astype(np.float64).T
+    a16 = oracle.forward_w4a16(G128, xb, wb)
+    a8 = oracle.forward(G128, xb, wb)
+    r16 = np.linalg.norm(a16["y"] - ref) / np.linalg.norm(ref)
+    r8 = np.linalg.norm(a8["y"] - ref) / np.linalg.norm(ref)
+    assert r16 <= r8 < 0.15
