@@ -1,6 +1,6 @@
 /*
  * qoq.h -- C ABI of libqoq, a QoQ W4A8 GEMM (QServe, arXiv 2405.04532) and
- * its W8A8 sibling for AMD Instinct MI355X (gfx950).
+ * its W8A8 and W4A16 siblings for AMD Instinct MI355X (gfx950).
  *
  *   Y[M,N] = X[M,K] * W[N,K]^T
  *
@@ -32,6 +32,11 @@
  *           scaling, here at 8 bits); "QServe: Low Bit Width Does Not Guarantee
  *           High Throughput", section 3, judgment A (W8A8 suits large batches,
  *           the format W4A8 is compared against).
+ *   [W4A16] "QServe Guide: W4A8KV4 Quantization for LLM Serving", "The Problem"
+ *           item 1 (4-bit weights dequantized to FP16 in the main loop, FP16
+ *           activations, FP16 matrix units); "QServe: Low Bit Width Does Not
+ *           Guarantee High Throughput", section 2 (the W4A16 failure mode and
+ *           its small-batch roofline advantage).
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers, allocated and owned by the
@@ -257,6 +262,26 @@ qoq_status qoq_w8a8_gemm(const int8_t* xq, const uint16_t* s_x, const void* blob
                          const uint16_t* s_c, int64_t M, int64_t N, int64_t K, uint16_t* y,
                          int32_t* acc_out, void* workspace, int64_t workspace_bytes,
                          void* stream);
+
+/*
+ * ---- W4A16 sibling ([W4A16]) ----------------------------------------------
+ * FP16 activations against the same QoQ 4-bit weights (the blob and s_c of
+ * qoq_quantize_weights / qoq_pack_weights, either mode), so that it differs
+ * from qoq_w4a8_gemm only in the activation precision. The codes are
+ * dequantized to FP16 in the main loop and multiplied on the FP16 matrix cores
+ * with FP32 accumulation:
+ *   x   [M,K] FP16 row-major (not quantized).
+ *   acc[m,n] = sum_k x[m,k] * W8^[n,k]   in FP32, W8^ = (q - z) * s_g (g128) or
+ *              q - z (per-channel), each product exact; the order of the FP32
+ *              additions is the kernel's and is not specified, so acc lies
+ *              within (K - 1) * 2^-24 * sum_k |x * W8^| of the exact sum.
+ *   y[m,n]   = f16(f32(acc) * f32(s_c[n]))               (FP16 [M,N])
+ *   acc_out  [M,N] float receives acc when not NULL (for inspection).
+ * No workspace. Errors as for qoq_w4a8_gemm.
+ */
+qoq_status qoq_w4a16_gemm(int mode, const uint16_t* x, const void* blob, const uint16_t* s_c,
+                          int64_t M, int64_t N, int64_t K, uint16_t* y, float* acc_out,
+                          void* stream);
 
 #ifdef __cplusplus
 }

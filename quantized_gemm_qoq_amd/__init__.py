@@ -1,4 +1,4 @@
-"""QoQ W4A8 GEMM (and its W8A8 sibling) for AMD Instinct MI355X (gfx950).
+"""QoQ W4A8 GEMM (and its W8A8 and W4A16 siblings) for AMD Instinct MI355X (gfx950).
 
 Python binding of ``libqoq.so`` (the C ABI declared in ``include/qoq.h``). The
 functions carry the C names and do argument marshalling only: every step of
@@ -43,6 +43,7 @@ EXPORTED = (
     "qoq_w8a8_pack_weights",
     "qoq_w8a8_gemm_workspace_bytes",
     "qoq_w8a8_gemm",
+    "qoq_w4a16_gemm",
 )
 
 
@@ -82,6 +83,7 @@ def load_library():
             "qoq_w8a8_pack_weights": (I, [P, I64, I64, P, P]),
             "qoq_w8a8_gemm_workspace_bytes": (I64, [I64, I64, I64]),
             "qoq_w8a8_gemm": (I, [P, P, P, P, I64, I64, I64, P, P, P, I64, P]),
+            "qoq_w4a16_gemm": (I, [I, P, P, P, I64, I64, I64, P, P, P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(lib, name)
@@ -379,6 +381,31 @@ def qoq_w8a8_gemm(xq: torch.Tensor, s_x: torch.Tensor, blob: torch.Tensor, s_c: 
     return y
 
 
+# ---- W4A16 sibling --------------------------------------------------------
+
+def qoq_w4a16_gemm(mode, x: torch.Tensor, blob: torch.Tensor, s_c: torch.Tensor, N: int,
+                   y=None, acc_out=None):
+    """Y [M,N] fp16 = f16(s_c * sum_k x * W8^) with FP16 x [M,K] (not quantized)
+    and the W4 blob of qoq_pack_weights; acc_out (float32 [M,N]) optional."""
+    mode = _mode(mode)
+    _need(x, torch.float16, "x")
+    M, K = x.shape
+    dev = x.device
+    _need(s_c, torch.float16, "s_c", (N,))
+    _need(blob, torch.uint8, "blob")
+    y = y if y is not None else torch.empty((M, N), dtype=torch.float16, device=dev)
+    _need(y, torch.float16, "y", (M, N))
+    if acc_out is not None:
+        _need(acc_out, torch.float32, "acc_out", (M, N))
+    nbytes = qoq_packed_bytes(mode, N, K)
+    if M and N and blob.numel() != nbytes:
+        raise QoQError(f"blob has {blob.numel()} bytes, expected {nbytes}")
+    st = load_library().qoq_w4a16_gemm(mode, _ptr(x), _ptr(blob), _ptr(s_c), M, N, K, _ptr(y),
+                                       _ptr(acc_out), _stream(x))
+    _check(st, "qoq_w4a16_gemm")
+    return y
+
+
 class PackedWeight:
     """A weight matrix quantized and packed once (offline), kept resident.
 
@@ -401,3 +428,9 @@ class PackedWeight:
             return qoq_w8a8_gemm(xq, s_x, self.blob, self.s_c, self.N, y=y, K=self.K)
         return qoq_w4a8_gemm(self.mode, xq, s_x, rowsum, self.blob, self.s_c, self.N, y=y,
                              K=self.K)
+
+    def forward_fp16(self, x: torch.Tensor, y=None) -> torch.Tensor:
+        """The W4A16 sibling on the same 4-bit weights: FP16 x, no quantization."""
+        if self.mode == W8A8:
+            raise QoQError("forward_fp16 needs 4-bit weights")
+        return qoq_w4a16_gemm(self.mode, x, self.blob, self.s_c, self.N, y=y)

@@ -186,4 +186,21 @@ qoq_status qoq_w8a8_gemm(const int8_t* xq, const uint16_t* s_x, const void* blob
     });
 }
 
+qoq_status qoq_w4a16_gemm(int mode, const uint16_t* x, const void* blob, const uint16_t* s_c,
+                          int64_t M, int64_t N, int64_t K, uint16_t* y, float* acc_out,
+                          void* stream) {
+    if (!valid_mode(mode)) return QOQ_ERR_MODE;
+    if (M < 0 || M > INT32_MAX || N < 0 || N % 16 || N > INT32_MAX || !valid_k(K))
+        return QOQ_ERR_SHAPE;
+    if (M == 0 || N == 0) return QOQ_OK;
+    if (!x || !blob || !s_c || !y) return QOQ_ERR_NULL;
+    if (!aligned16(x) || !aligned16(blob) || !aligned16(s_c) || !aligned16(y) ||
+        (acc_out && !aligned16(acc_out)))
+        return QOQ_ERR_ALIGN;
+    return launch_checked([&] {
+        qoq::launch_gemm_w4a16(mode, x, static_cast<const uint8_t*>(blob), s_c, M, N, K, y, acc_out,
+                               as_stream(stream));
+    });
+}
+
 }  // extern "C"

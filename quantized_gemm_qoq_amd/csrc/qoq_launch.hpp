@@ -39,4 +39,11 @@ void launch_gemm(int fmt, const int8_t* xq, const uint16_t* s_x, const int32_t* 
                  const uint8_t* blob, const uint16_t* s_c, int64_t M, int64_t N, int64_t K,
                  uint16_t* y, int32_t* acc_out, void* ws, hipStream_t stream);
 
+// W4A16 sibling: FP16 activations x [M,K] (row-major) against the W4 blob of
+// qoq_pack_weights (either mode); acc_out (fp32 [M,N], may be null) receives
+// the accumulators before the per-channel scale.
+void launch_gemm_w4a16(int mode, const uint16_t* x, const uint8_t* blob, const uint16_t* s_c,
+                       int64_t M, int64_t N, int64_t K, uint16_t* y, float* acc_out,
+                       hipStream_t stream);
+
 }  // namespace qoq

@@ -165,3 +165,18 @@ def test_w8a8_validation(lib):
     assert args(M=256, N=512, K=2048, ws=A, wsb=need - 1) == ERR_WORKSPACE
     assert w(8, 15, 128) == -1
 
+
+def test_w4a16_validation(lib):
+    f = lib.qoq_w4a16_gemm
+    def args(mode=0, x=A, blob=A, sc=A, M=8, N=16, K=128, y=A, acc=NUL):
+        return f(mode, x, blob, sc, M, N, K, y, acc, NUL)
+    assert args(mode=3) == ERR_MODE
+    assert args(M=0) == OK
+    assert args(M=-1) == ERR_SHAPE
+    assert args(N=24 + 1) == ERR_SHAPE
+    assert args(K=384 + 64) == ERR_SHAPE
+    assert args(x=NUL) == ERR_NULL
+    assert args(sc=NUL) == ERR_NULL
+    assert args(x=U) == ERR_ALIGN
+    assert args(acc=U) == ERR_ALIGN
+
