@@ -55,6 +55,11 @@ def parse_args(argv=None):
     p.add_argument("--all-layers", action="store_true",
                    help="instead of the one-line result: time the GEMMs of every layer of "
                         "every workload and print one line per layer")
+    p.add_argument("--formats", action="store_true",
+                   help="instead of the one-line result: per layer (of --workload, or of every "
+                        "workload with --all-layers), time the per-call path in each weight/"
+                        "activation format -- W4A8 g128 and per-channel, W8A8, W4A16 -- and "
+                        "print one line per layer")
     p.add_argument("--pmc-summary", nargs="+", default=None, metavar="DIR",
                    help="instead of timing: read rocprofv3 counter CSVs (FETCH_SIZE run, "
                         "WRITE_SIZE run) of a --profile-launches run and write the traffic "
@@ -388,6 +393,15 @@ def main(argv=None) -> int:
     if args.pmc_summary:
         return pmc_summary(args, wl, layer)
 
+    if args.formats:
+        todo = [(w, l) for w in (workloads.WORKLOADS.values() if args.all_layers else [wl])
+                for l in w.layers if args.all_layers or args.layer in (None, l.name)]
+        for wl2, layer2 in todo:
+            out = format_compare(args, wl2, layer2)
+            if isinstance(out, int):
+                return out
+            print(json.dumps(out), flush=True)
+        return 0
     if args.all_layers:
         for wl2 in workloads.WORKLOADS.values():
             for layer2 in wl2.layers:
@@ -404,6 +418,96 @@ def main(argv=None) -> int:
         return out
     print(json.dumps(out))
     return 0
+
+
+FORMATS = ("w4a8_g128", "w4a8_per_channel", "w8a8", "w4a16_g128")
+
+
+def format_compare(args, wl, layer):
+    """Time one layer's per-call path in every format on the same synthetic
+    weights and activations: the kernels alone and the whole call (W4A8 and
+    W8A8 quantize the FP16 activations per token first; W4A16 takes them as
+    they are). Each format rotates through its own buffer copies (>= the
+    --rotate-mib total), so the figures are HBM figures."""
+    from quantized_gemm_qoq_amd import workloads
+
+    import torch
+
+    import quantized_gemm_qoq_amd as qoq
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 3
+    dev = torch.device("cuda:0")
+    M, N, K = layer.M, layer.N, layer.K
+    x16, w16 = workloads.generate(layer)
+    x_dev, w_dev = x16.to(dev), w16.to(dev)
+    res = {"workload": wl.name, "layer": layer.name, "M": M, "K": K, "N": N, "formats": {}}
+
+    def avg_us(fns, launches):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(launches):
+                fns[i % len(fns)]()
+        g.replay()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / launches
+
+    for fmt in FORMATS:
+        mode = {"w4a8_g128": qoq.MODE_G128, "w4a8_per_channel": qoq.MODE_PER_CHANNEL,
+                "w8a8": qoq.W8A8, "w4a16_g128": qoq.MODE_G128}[fmt]
+        pw = qoq.PackedWeight(mode, w_dev)
+        quantized = fmt != "w4a16_g128"
+        per = pw.blob.numel() + 2 * M * K + 2 * M * N + (M * K if quantized else 0)
+        R = max(2, math.ceil(args.rotate_mib * 2**20 / per))
+        L = max(R, args.kernel_launches // R * R)
+        sets = []
+        for _ in range(R):
+            st = {"x": x_dev.clone(), "blob": pw.blob.clone(),
+                  "y": torch.empty((M, N), dtype=torch.float16, device=dev)}
+            if quantized:
+                st["xq"], st["s_x"], st["rs"] = qoq.qoq_quantize_act(
+                    x_dev, want_rowsum=mode == qoq.MODE_PER_CHANNEL)
+            sets.append(st)
+        ws = None
+        if quantized:
+            ws = qoq.gemm_workspace(mode, M, N, K, dev)
+
+        def gemm(st):
+            if fmt == "w4a16_g128":
+                qoq.qoq_w4a16_gemm(mode, st["x"], st["blob"], pw.s_c, N, y=st["y"])
+            elif fmt == "w8a8":
+                qoq.qoq_w8a8_gemm(st["xq"], st["s_x"], st["blob"], pw.s_c, N, y=st["y"], workspace=ws)
+            else:
+                qoq.qoq_w4a8_gemm(mode, st["xq"], st["s_x"], st["rs"], st["blob"], pw.s_c, N,
+                                  y=st["y"], workspace=ws)
+
+        def call(st):
+            if quantized:
+                qoq.qoq_quantize_act(st["x"], st["xq"], st["s_x"], st["rs"])
+            gemm(st)
+
+        for st in sets[:2]:
+            call(st)
+        torch.cuda.synchronize()
+        g_us = avg_us([lambda st=st: gemm(st) for st in sets], L)
+        c_us = avg_us([lambda st=st: call(st) for st in sets], L)
+        res["formats"][fmt] = {"gemm_us": round(g_us, 3), "call_us": round(c_us, 3),
+                               "weight_MB": round(pw.blob.numel() / 1e6, 2),
+                               "gemm_TOPS": round(2 * M * N * K / g_us / 1e6, 1),
+                               "call_TOPS": round(2 * M * N * K / c_us / 1e6, 1)}
+        del sets, pw
+        torch.cuda.empty_cache()
+    best = min(res["formats"], key=lambda f: res["formats"][f]["call_us"])
+    res["fastest_call"] = best
+    return res
 
 
 def describe_data(layer) -> str:

@@ -101,7 +101,8 @@ __device__ __forceinline__ void store4(float4v a, int m_first, int n, int M, int
 }
 
 // ---------------------------------------------------------------------------
-// Decode kernel (M <= 64): the structure of the W4A8 streaming kernel. A
+// Streaming kernel (decode, and up to 256 rows on narrow layers): the
+// structure of the W4A8 streaming kernel. A
 // workgroup of W waves owns NT channel tiles and MB row tiles; wave w takes
 // the contiguous groups [G*w/W, G*(w+1)/W). Weights stream through a ring of R
 // register sets (16 bytes per lane per tile per group); activations are read
@@ -428,16 +429,52 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void k_w4a16_tile(
 }
 
 // ---------------------------------------------------------------------------
-constexpr int kCUs = 256;
-
-template <bool kG128, int MB, int NT>
+template <bool kG128, int MB, int NT, int R = 2, int W = 8>
 void launch_w16_stream(int64_t M, int64_t N, int64_t K, const uint16_t* x, const uint8_t* blob,
                        const uint16_t* s_c, uint16_t* y, float* acc_out, hipStream_t stream) {
     const int64_t tiles = N / 16, U = (M + 15) / 16;
     const unsigned blocks = (unsigned)(((tiles + NT - 1) / NT) * ((U + MB - 1) / MB));
-    hipLaunchKernelGGL((k_w4a16_stream<kG128, MB, NT, 2, 8>), dim3(blocks), dim3(8 * 64), 0,
+    hipLaunchKernelGGL((k_w4a16_stream<kG128, MB, NT, R, W>), dim3(blocks), dim3(W * 64), 0,
                        stream, x, blob, s_c, (int)M, (int)N, (int)K, y, acc_out);
 }
+
+#ifdef QOQ_TUNING
+int g_w16_mb = 0, g_w16_nt = 0, g_w16_w = 0, g_w16_r = 0;
+
+template <bool kG128, int MB, int NT>
+bool tune_w16_rw(int64_t M, int64_t N, int64_t K, const uint16_t* x, const uint8_t* blob,
+                 const uint16_t* s_c, uint16_t* y, float* acc_out, hipStream_t stream) {
+#define QOQ_W16(RV, WV)                                                                        \
+    if (g_w16_r == RV && g_w16_w == WV) {                                                     \
+        if constexpr (WV * NT * MB <= 64)                                                     \
+            launch_w16_stream<kG128, MB, NT, RV, WV>(M, N, K, x, blob, s_c, y, acc_out, stream); \
+        return WV * NT * MB <= 64;                                                            \
+    }
+    QOQ_W16(2, 8) QOQ_W16(1, 16) QOQ_W16(2, 4) QOQ_W16(1, 8) QOQ_W16(2, 16) QOQ_W16(1, 4)
+#undef QOQ_W16
+    return false;
+}
+
+template <bool kG128, int MB>
+bool tune_w16_nt(int64_t M, int64_t N, int64_t K, const uint16_t* x, const uint8_t* blob,
+                 const uint16_t* s_c, uint16_t* y, float* acc_out, hipStream_t stream) {
+    if (g_w16_nt == 1) return tune_w16_rw<kG128, MB, 1>(M, N, K, x, blob, s_c, y, acc_out, stream);
+    if (g_w16_nt == 2) return tune_w16_rw<kG128, MB, 2>(M, N, K, x, blob, s_c, y, acc_out, stream);
+    if (g_w16_nt == 3) return tune_w16_rw<kG128, MB, 3>(M, N, K, x, blob, s_c, y, acc_out, stream);
+    if (g_w16_nt == 4) return tune_w16_rw<kG128, MB, 4>(M, N, K, x, blob, s_c, y, acc_out, stream);
+    return false;
+}
+
+template <bool kG128>
+bool tune_w16(int64_t M, int64_t N, int64_t K, const uint16_t* x, const uint8_t* blob,
+              const uint16_t* s_c, uint16_t* y, float* acc_out, hipStream_t stream) {
+    if (!g_w16_mb || M > 256) return false;
+    if (g_w16_mb == 1) return tune_w16_nt<kG128, 1>(M, N, K, x, blob, s_c, y, acc_out, stream);
+    if (g_w16_mb == 2) return tune_w16_nt<kG128, 2>(M, N, K, x, blob, s_c, y, acc_out, stream);
+    if (g_w16_mb == 4) return tune_w16_nt<kG128, 4>(M, N, K, x, blob, s_c, y, acc_out, stream);
+    return false;
+}
+#endif
 
 template <bool kG128, int BN, int WN>
 void launch_w16_tile(int64_t M, int64_t N, int64_t K, const uint16_t* x, const uint8_t* blob,
@@ -451,25 +488,61 @@ template <bool kG128>
 void launch_w16(int64_t M, int64_t N, int64_t K, const uint16_t* x, const uint8_t* blob,
                 const uint16_t* s_c, uint16_t* y, float* acc_out, hipStream_t stream) {
     const int64_t tiles = N / 16;
+#ifdef QOQ_TUNING
+    if (kG128 && tune_w16<kG128>(M, N, K, x, blob, s_c, y, acc_out, stream)) return;
+#endif
     // The streaming kernel forms 32-bit byte offsets into the codes and the rows.
     const bool fits = N * K / 2 < (int64_t(1) << 31) && N * (K / kGroup) < (int64_t(1) << 31);
     if (M <= 64 && fits) {
-        // Three channel tiles per workgroup while that leaves two per compute
-        // unit, else two; one row tile per workgroup up to 16 rows, else two.
-        const bool nt3 = (tiles + 2) / 3 >= 2 * kCUs;
-        if (M <= 16) {
-            if (nt3) launch_w16_stream<kG128, 1, 3>(M, N, K, x, blob, s_c, y, acc_out, stream);
-            else launch_w16_stream<kG128, 1, 2>(M, N, K, x, blob, s_c, y, acc_out, stream);
+        // Measured on MI355X over the Llama-3-8B and Qwen1.5-72B decode layers
+        // (one load set in flight per wave beat a two-deep ring everywhere):
+        //   >= 1024 channel tiles: four tiles and four waves per workgroup
+        //     (enough workgroups to keep every compute unit streaming);
+        //   fewer tiles: 17..64 rows take three tiles per workgroup (the
+        //     activation rows are re-read once per workgroup, so wider
+        //     workgroups read them fewer times), up to 16 rows two;
+        //   33..64 rows: two row tiles and four waves per workgroup; up to 32
+        //     rows one row tile, with 16 waves when K has at most 64 groups
+        //     (more waves, fewer groups each) and 8 otherwise.
+        const int64_t G = K / kGroup;
+        auto go = [&](auto launcher) { launcher(M, N, K, x, blob, s_c, y, acc_out, stream); };
+        if (tiles >= 1024) {
+            if (M <= 32) go(launch_w16_stream<kG128, 1, 4, 1, 4>);
+            else go(launch_w16_stream<kG128, 2, 4, 1, 4>);
+        } else if (M > 32) {
+            go(launch_w16_stream<kG128, 2, 3, 1, 4>);
+        } else if (M > 16) {
+            if (G <= 64) go(launch_w16_stream<kG128, 1, 3, 1, 16>);
+            else go(launch_w16_stream<kG128, 1, 3, 1, 8>);
         } else {
-            if (nt3) launch_w16_stream<kG128, 2, 3>(M, N, K, x, blob, s_c, y, acc_out, stream);
-            else launch_w16_stream<kG128, 2, 2>(M, N, K, x, blob, s_c, y, acc_out, stream);
+            if (G <= 64) go(launch_w16_stream<kG128, 1, 2, 1, 16>);
+            else go(launch_w16_stream<kG128, 1, 2, 1, 8>);
         }
+        return;
+    }
+    // 65..256 rows: the streaming kernel with 64-row workgroups while the
+    // tiled kernel would have fewer than 128 workgroups (it then leaves most
+    // compute units idle); the tiled kernel otherwise.
+    const int64_t tile_blocks = ((M + 127) / 128) * ((N + 255) / 256);
+    if (M <= 256 && fits && tile_blocks < 128) {
+        launch_w16_stream<kG128, 4, 4, 1, 4>(M, N, K, x, blob, s_c, y, acc_out, stream);
         return;
     }
     launch_w16_tile<kG128, 256, 4>(M, N, K, x, blob, s_c, y, acc_out, stream);
 }
 
 }  // namespace
+
+#ifdef QOQ_TUNING
+// Decode-kernel overrides for measurement builds (g128 only): row tiles and
+// channel tiles per workgroup, waves, ring depth; mb = 0 restores the plan.
+extern "C" void qoq_tuning_force_w16(int mb, int nt, int w, int r) {
+    g_w16_mb = mb;
+    g_w16_nt = nt;
+    g_w16_w = w;
+    g_w16_r = r;
+}
+#endif
 
 void launch_gemm_w4a16(int mode, const uint16_t* x, const uint8_t* blob, const uint16_t* s_c,
                        int64_t M, int64_t N, int64_t K, uint16_t* y, float* acc_out,
