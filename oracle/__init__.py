@@ -260,7 +260,7 @@ def forward(mode, x_bits, w_bits):
     return {"xq": xq, "s_x": s_x, "rowsum": rowsum, "acc": acc, "y": y, **wq}
 
 
-# --- W8A8 sibling: per-channel symmetric INT8 weights (reading R11) ---------
+# --- W8A8 sibling: per-channel symmetric INT8 weights (reading R13) ---------
 
 def quantize_weights_w8(w_bits):
     """Returns (s_c uint16 [N], q int8 [N,K])."""
@@ -320,7 +320,7 @@ def forward_w8(x_bits, w_bits):
     return {"xq": xq, "s_x": s_x, "acc": acc, "y": y, "s_c": s_c, "q": q}
 
 
-# --- W4A16 sibling: FP16 activations, the same 4-bit weights (reading R12) --
+# --- W4A16 sibling: FP16 activations, the same 4-bit weights (reading R14) --
 
 def gemm_w4a16(mode, x_bits, s_c, q, s_g, z):
     """(y, absum) float64 [M,N]: y = X . W^T with W^ = s_c * s_g * (q - z)

@@ -32,8 +32,8 @@
  *   [WIKI] "QoQ / QServe — Quantification W4A8KV4" (brain.gartu.xyz), example
  *         configuration: weight group size 128.
  *
- * Readings where the pages are silent (each is listed with its reason in the
- * design notes of the repository):
+ * Readings where the pages are silent (numbered as in the rest of the
+ * repository):
  *   R1  every "round" is round-half-to-even;
  *   R2  scales are computed in IEEE fp32 (one rounding per operation), stored as
  *       FP16 (round to nearest even), and the stored FP16 value is the one used
@@ -51,9 +51,9 @@
  *       accumulator is sum_k Xq * (q - z);
  *   R10 the output is acc * s_x * s_c; here it is computed in fp64, where it is
  *       exact (31 + 11 + 11 significant bits <= 53);
- *   R11 the W8A8 sibling quantizes weights per output channel, symmetric, with
+ *   R13 the W8A8 sibling quantizes weights per output channel, symmetric, with
  *       scale max|W|/127 and the activations' clamp [-128, 127];
- *   R12 the W4A16 sibling keeps the activations in FP16 and reads the same QoQ
+ *   R14 the W4A16 sibling keeps the activations in FP16 and reads the same QoQ
  *       4-bit weights, so that it differs from W4A8 only in the activation
  *       precision.
  *
@@ -484,8 +484,8 @@ void orc_f16_to_f64_array(const uint16_t* in, int64_t n, double* out) {
 /* W8A8 sibling ("QServe Guide: W4A8KV4 Quantization for LLM Serving", "The  */
 /* Problem" item 2: weights and activations both INT8 on the INT8 matrix     */
 /* units; weight scaling per output channel and symmetric as in "Deep Dive"  */
-/* part 1, with the 8-bit bound 127 in place of the 4-bit bound 7 -- the    */
-/* reading R11 of the repository's design notes).                           */
+/* part 1, with the 8-bit bound 127 in place of the 4-bit bound 7: reading  */
+/* R13 above).                                                              */
 /*   s_c[n] = f16( max_k |W[n,k]| / 127 )          (fp32 division, R2)        */
 /*   q[n,k] = clamp( round(W[n,k] / s_c[n]), -128, 127 )   (R8: q = 0 if s_c = 0) */
 /* |W / s_c| <= 127 * (1 + 2^-11) rounds to at most 127, so -128 never       */
@@ -580,7 +580,7 @@ int orc_gemm_w8_points(const int8_t* xq, const int8_t* q, int64_t M, int64_t N, 
 /* Problem" item 1: 4-bit weights dequantized in the main loop, activations  */
 /* kept in FP16, FP16 matrix units; "QServe: Low Bit Width Does Not          */
 /* Guarantee High Throughput", section 2, the W4A16 failure mode). Reading   */
-/* R12: the weights are the same QoQ 4-bit weights as W4A8 (either mode),    */
+/* R14: the weights are the same QoQ 4-bit weights as W4A8 (either mode),    */
 /* so that the two formats differ only in the activation precision:          */
 /*   Y[m,n] = sum_k X[m,k] * W^[n,k],  W^ = s_c * s_g * (q - z)              */
 /*          = s_c[n] * sum_k X[m,k] * W8^[n,k]                               */
