@@ -75,6 +75,8 @@ def _load():
                 "orc_gemm_w8_points": (I, [P, P, I64, I64, I64, I64, P, P, P]),
                 "orc_gemm_w4a16": (I, [I, P, P, P, P, P, I64, I64, I64, P, P]),
                 "orc_gemm_w4a16_points": (I, [I, P, P, P, P, P, I64, I64, I64, I64, P, P, P, P]),
+                "orc_exp_f32_array": (None, [P, I64, P]),
+                "orc_silu_mul": (I, [P, I64, I64, P]),
             }
             for name, (res, args) in sigs.items():
                 fn = getattr(lib, name)
@@ -359,3 +361,32 @@ def forward_w4a16(mode, x_bits, w_bits):
     wq = quantize_weights(mode, w_bits)
     y, absum = gemm_w4a16(mode, x_bits, wq["s_c"], wq["q"], wq["s_g"], wq["z"])
     return {"y": y, "absum": absum, **wq}
+
+
+# --- Fused producer of the down projection's input (reading R15) -----------
+
+def exp_f32(values) -> np.ndarray:
+    """The oracle's fp32 exponential (Cody-Waite reduction + degree-7 Taylor)."""
+    v = np.ascontiguousarray(np.asarray(values, dtype=np.float32).ravel())
+    out = np.empty(v.size, np.float32)
+    _load().orc_exp_f32_array(_p(v), v.size, _p(out))
+    return out
+
+
+def silu_mul(gate_up_bits):
+    """gate_up [M, 2I] FP16 bits -> h [M, I] FP16 bits, h = f16(SiLU(gate) * up)."""
+    gu = _c(gate_up_bits, np.uint16)
+    M, I2 = gu.shape
+    if I2 % 2:
+        raise ValueError("gate_up must have an even number of columns")
+    h = np.empty((M, I2 // 2), np.uint16)
+    _check(_load().orc_silu_mul(_p(gu), M, I2 // 2, _p(h)), "silu_mul")
+    return h
+
+
+def silu_mul_quantize_act(gate_up_bits):
+    """The fused producer: (h, xq, s_x, rowsum) with h = f16(SiLU(gate) * up)
+    and (xq, s_x, rowsum) = quantize_act(h)."""
+    h = silu_mul(gate_up_bits)
+    xq, s_x, rowsum = quantize_act(h)
+    return h, xq, s_x, rowsum

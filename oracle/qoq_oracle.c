@@ -55,7 +55,10 @@
  *       scale max|W|/127 and the activations' clamp [-128, 127];
  *   R14 the W4A16 sibling keeps the activations in FP16 and reads the same QoQ
  *       4-bit weights, so that it differs from W4A8 only in the activation
- *       precision.
+ *       precision;
+ *   R15 the fused producer of the down projection's input rounds
+ *       SiLU(gate) * up to FP16 before quantizing it, with the exponential
+ *       defined step by step below (orc_exp_f32).
  *
  * Inputs must be finite FP16 (passed as raw binary16 bits).
  */
@@ -646,6 +649,76 @@ int orc_gemm_w4a16_points(int mode, const uint16_t* x, const uint16_t* s_c, cons
         const double sc = orc_f16_to_f64(s_c[n]);
         y[p] = s * sc;
         if (absum) absum[p] = a * sc;
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Fused producer of the down projection's input (reading R15): the MLP's   */
+/* h = SiLU(gate) * up, rounded to FP16, then the per-token INT8            */
+/* quantization of orc_quantize_act. The pages quantize the activations     */
+/* that feed each INT8 GEMM per token ("QServe Guide: W4A8KV4 Quantization  */
+/* for LLM Serving", Deep Dive part 1); the input of the down projection is */
+/* the product of the gate and up projections of the same MLP, whose        */
+/* outputs are one fused [M, 2I] matrix here (gate in columns 0..I-1, up in */
+/* columns I..2I-1).                                                        */
+/*                                                                          */
+/* The exponential is defined here, step by step, so that the GPU computes  */
+/* the same FP32 value (the quantized codes depend on it): Cody and Waite's */
+/* range reduction x = n ln2 + r with ln2 split in two parts (the first     */
+/* with trailing zero bits, so that n * ln2_hi is exact), then exp(r) by    */
+/* its Taylor polynomial of degree 7 in Horner form, then the scaling by    */
+/* 2^n. Every step is one IEEE fp32 operation (no fused multiply-add):      */
+/*   x > 88  -> +inf;  x < -86 -> 0   (keeps 2^n and the result normal)     */
+/*   n = rint(x * log2(e))                                                  */
+/*   r = (x - n * ln2_hi) - n * ln2_lo                                      */
+/*   p = (((((((1/7! r + 1/6!) r + 1/5!) r + 1/4!) r + 1/3!) r + 1/2) r + 1) r + 1 */
+/*   exp(x) = p * 2^n                                                       */
+/* The constants are the fp32 roundings of the stated real numbers.          */
+/* ------------------------------------------------------------------------ */
+#define ORC_LN2_HI 0.693145751953125f /* ln 2 to 16 significant bits (exact in fp32) */
+
+float orc_exp_f32(float x) {
+    if (x > 88.0f) return INFINITY;
+    if (x < -86.0f) return 0.0f;
+    const float log2e = (float)1.4426950408889634;   /* 1 / ln 2 */
+    const float ln2_lo = (float)(0.6931471805599453 - 0.693145751953125);
+    const float n = rintf(x * log2e);
+    const float r = (x - n * ORC_LN2_HI) - n * ln2_lo;
+    float p = (float)(1.0 / 5040.0);
+    p = p * r + (float)(1.0 / 720.0);
+    p = p * r + (float)(1.0 / 120.0);
+    p = p * r + (float)(1.0 / 24.0);
+    p = p * r + (float)(1.0 / 6.0);
+    p = p * r + 0.5f;
+    p = p * r + 1.0f;
+    p = p * r + 1.0f;
+    /* 2^n as an fp32 bit pattern (n in [-124, 127] after the clamps) */
+    const int32_t ni = (int32_t)n;
+    const uint32_t bits = (uint32_t)(ni + 127) << 23;
+    float scale;
+    memcpy(&scale, &bits, sizeof scale);
+    return p * scale;
+}
+
+void orc_exp_f32_array(const float* in, int64_t n, float* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_exp_f32(in[i]);
+}
+
+/* h[m,k] = f16( (g / (1 + exp(-g))) * u ), g = gate_up[m, k], u = gate_up[m, I + k],
+ * every operation in IEEE fp32 (reading R15). */
+int orc_silu_mul(const uint16_t* gate_up, int64_t M, int64_t I, uint16_t* h) {
+    if (M < 0 || I < 1) return ORC_ERR_SHAPE;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t* row = gate_up + m * 2 * I;
+        for (int64_t k = 0; k < I; ++k) {
+            const float g = f16_to_f32(row[k]);
+            const float u = f16_to_f32(row[I + k]);
+            const float t = 1.0f + orc_exp_f32(-g);
+            const float s = g / t;
+            h[m * I + k] = orc_f32_to_f16(s * u);
+        }
     }
     return ORC_OK;
 }

@@ -239,3 +239,27 @@ def test_w4a16_reproduces_hand_worked_w4a8_example():
                                  wq["s_g"], wq["z"])
     np.testing.assert_array_equal(y, np.array(g["y"]))
     assert np.all(absum >= np.abs(y))
+
+
+def test_silu_mul_golden():
+    """SiLU(gate) * up at the exponential's cut-offs and at zero, and the
+    per-token quantization of the resulting row (hand-worked)."""
+    d = _load("silu_mul.json")
+    I = d["I"]
+    gu = np.zeros((len(d["cases"]) + 1, 2 * I), np.float16)
+    for r, c in enumerate(d["cases"]):
+        gu[r, 0] = c["g"]
+        gu[r, I] = c["u"]
+    for k, c in enumerate(d["cases"]):  # the last row holds every case
+        gu[-1, k] = c["g"]
+        gu[-1, I + k] = c["u"]
+    h, xq, s_x, rowsum = oracle.silu_mul_quantize_act(gu.view(np.uint16))
+    for r, c in enumerate(d["cases"]):
+        assert h[r, 0] == c["h_bits"], (r, h[r, 0])
+    qr = d["quantized_row"]
+    assert s_x[-1] == qr["s_x_bits"]
+    want = np.zeros(I, np.int8)
+    for k, v in qr["xq_nonzero"].items():
+        want[int(k)] = v
+    np.testing.assert_array_equal(xq[-1], want)
+    assert rowsum[-1] == qr["rowsum"]

@@ -475,3 +475,47 @@ def test_w4a16_end_to_end_is_closer_than_w4a8():
     r16 = np.linalg.norm(a16["y"] - ref) / np.linalg.norm(ref)
     r8 = np.linalg.norm(a8["y"] - ref) / np.linalg.norm(ref)
     assert r16 <= r8 < 0.15
+
+
+# --------------------------------------------------- fused SiLU * up + quant ----
+def test_exp_f32_against_libm():
+    """The oracle's fp32 exponential is within 1.5 fp32 ulps of the exact
+    value over its whole finite range, exact at 0, and follows its cut-offs."""
+    x = np.concatenate([np.linspace(-86, 88, 1_000_001), np.linspace(-1, 1, 200_001),
+                        np.array([-86.0, 88.0, 1e-30, -1e-30])]).astype(np.float32)
+    e = oracle.exp_f32(x).astype(np.float64)
+    ref = np.exp(x.astype(np.float64))
+    ulp = np.spacing(ref.astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(e - ref) <= 1.5 * ulp)
+    assert oracle.exp_f32([0.0])[0] == 1.0
+    assert np.all(oracle.exp_f32([88.001, 100.0, 65504.0]) == np.inf)
+    assert np.all(oracle.exp_f32([-86.001, -100.0, -65504.0]) == 0.0)
+
+
+def test_silu_mul_matches_fp64_definition():
+    """h = f16(SiLU(g) * u) is within one FP16 rounding (plus a few fp32 ulps)
+    of the exact product, and equals the FP16 rounding of the fp64 value
+    almost everywhere (a difference needs the fp32 value and the fp64 value on
+    opposite sides of an FP16 rounding boundary)."""
+    M, I = 64, 1024
+    g = (workloads.random_fp16((M, I), 61, 3.0)).numpy()
+    u = (workloads.random_fp16((M, I), 62, 1.0)).numpy()
+    g[0, :8] = [0, 1e-4, -1e-4, 20, -20, 87, -87, 11.0]
+    gu = np.concatenate([g, u], axis=1)
+    h = oracle.silu_mul(gu.view(np.uint16)).view(np.float16).astype(np.float64)
+    gd, ud = g.astype(np.float64), u.astype(np.float64)
+    exact = gd / (1.0 + np.exp(-gd)) * ud
+    ulp16 = np.spacing(np.abs(exact).astype(np.float16)).astype(np.float64)
+    assert np.all(np.abs(h - exact) <= 0.5 * ulp16 + 2.0**-20 * np.abs(exact) + 2.0**-25)
+    same = h == exact.astype(np.float16).astype(np.float64)
+    assert same.mean() > 0.999
+
+
+def test_silu_mul_quantize_is_the_composition():
+    M, I = 5, 384
+    gu = workloads.random_fp16((M, 2 * I), 63, 2.0).numpy().view(np.uint16)
+    h, xq, s_x, rowsum = oracle.silu_mul_quantize_act(gu)
+    xq2, s_x2, rs2 = oracle.quantize_act(oracle.silu_mul(gu))
+    np.testing.assert_array_equal(xq, xq2)
+    np.testing.assert_array_equal(s_x, s_x2)
+    np.testing.assert_array_equal(rowsum, rs2)
