@@ -60,6 +60,10 @@ def parse_args(argv=None):
                         "workload with --all-layers), time the per-call path in each weight/"
                         "activation format -- W4A8 g128 and per-channel, W8A8, W4A16 -- and "
                         "print one line per layer")
+    p.add_argument("--producer", action="store_true",
+                   help="instead of the one-line result: time the fused SiLU(gate)*up + "
+                        "per-token quantization against the unfused path (torch SiLU*up "
+                        "writing h, then qoq_quantize_act) for every down-projection layer")
     p.add_argument("--pmc-summary", nargs="+", default=None, metavar="DIR",
                    help="instead of timing: read rocprofv3 counter CSVs (FETCH_SIZE run, "
                         "WRITE_SIZE run) of a --profile-launches run and write the traffic "
@@ -393,6 +397,15 @@ def main(argv=None) -> int:
     if args.pmc_summary:
         return pmc_summary(args, wl, layer)
 
+    if args.producer:
+        for wl2 in workloads.WORKLOADS.values():
+            for layer2 in wl2.layers:
+                if "down" in layer2.name:
+                    out = producer_compare(args, layer2)
+                    if isinstance(out, int):
+                        return out
+                    print(json.dumps(out), flush=True)
+        return 0
     if args.formats:
         todo = [(w, l) for w in (workloads.WORKLOADS.values() if args.all_layers else [wl])
                 for l in w.layers if args.all_layers or args.layer in (None, l.name)]
@@ -418,6 +431,64 @@ def main(argv=None) -> int:
         return out
     print(json.dumps(out))
     return 0
+
+
+def producer_compare(args, layer):
+    """Fused producer vs unfused path for the input of a down projection with
+    M rows and I = K inputs; the gate_up matrix [M, 2I] is synthetic N(0,1)
+    FP16 (seeded with the layer's seed). HBM figures over rotating copies."""
+    import torch
+
+    import quantized_gemm_qoq_amd as qoq
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 3
+    dev = torch.device("cuda:0")
+    M, I = layer.M, layer.K
+    g = torch.Generator(device="cpu")
+    g.manual_seed(layer.seed)
+    gu = torch.randn(M, 2 * I, generator=g).to(torch.float16).to(dev)
+    per = 2 * M * 2 * I + 2 * M * I + M * I
+    R = max(2, math.ceil(args.rotate_mib * 2**20 / per))
+    sets = [{"gu": gu.clone(), "h": torch.empty((M, I), dtype=torch.float16, device=dev),
+             "xq": torch.empty((qoq.qoq_act_bytes(M, I),), dtype=torch.int8, device=dev),
+             "s_x": torch.empty((M,), dtype=torch.float16, device=dev),
+             "rs": torch.empty((M,), dtype=torch.int32, device=dev)} for _ in range(R)]
+    L = max(R, args.kernel_launches // R * R)
+
+    def fused(st):
+        qoq.qoq_silu_mul_quantize_act(st["gu"], st["xq"], st["s_x"], st["rs"])
+
+    def unfused(st):
+        torch.mul(torch.nn.functional.silu(st["gu"][:, :I]), st["gu"][:, I:], out=st["h"])
+        qoq.qoq_quantize_act(st["h"], st["xq"], st["s_x"], st["rs"])
+
+    def avg_us(fn):
+        for st in sets[:2]:
+            fn(st)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for i in range(L):
+                fn(sets[i % R])
+        gr.replay()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        gr.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / L
+
+    f_us, u_us = avg_us(fused), avg_us(unfused)
+    f_bytes = 4 * M * I + M * I + 6 * M  # read gate_up, write codes, scale, row sum
+    return {"layer": layer.name, "M": M, "I": I, "fused_us": round(f_us, 3),
+            "unfused_us": round(u_us, 3), "speedup": round(u_us / f_us, 2),
+            "fused_GBs": round(f_bytes / f_us / 1e3, 1),
+            "fused_frac_of_hbm": round(f_bytes / f_us / 1e3 / HBM_PEAK_GBS, 3)}
 
 
 FORMATS = ("w4a8_g128", "w4a8_per_channel", "w8a8", "w4a16_g128")

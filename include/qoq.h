@@ -264,6 +264,27 @@ qoq_status qoq_w8a8_gemm(const int8_t* xq, const uint16_t* s_x, const void* blob
                          void* stream);
 
 /*
+ * ---- Fused producer of the down projection's input -------------------------
+ * ([GUIDE] "High-Throughput Native INT8 Tensor Core GEMMs": the GEMM writes
+ * FP16 back for the operators that follow; Deep Dive part 1: every INT8 GEMM
+ * input is quantized per token.) In the MLP the down projection's input is
+ * SiLU(gate) * up of the gate_up GEMM's FP16 output; this call produces it and
+ * quantizes it in one pass over the gate_up rows:
+ *   gate_up [M, 2I] FP16 row-major: gate = columns 0..I-1, up = columns I..2I-1
+ *   h[m,k]  = f16( (g / (1 + exp(-g))) * u )   g = gate, u = up, each step one
+ *             IEEE fp32 operation, with exp(x) defined as: +inf for x > 88,
+ *             0 for x < -86, else n = rint(x * log2(e)),
+ *             r = (x - n * 0.693145751953125) - n * (ln 2 - 0.693145751953125),
+ *             p = the degree-7 Taylor polynomial of e^r in Horner form
+ *             (coefficients 1/k! rounded to fp32), exp = p * 2^n
+ *             (Cody and Waite's reduction; within 1.2 fp32 ulps of e^x)
+ *   then xq, s_x, rowsum exactly as qoq_quantize_act(h, M, I, ...).
+ *   h [M, I] FP16 receives h when not NULL. I follows the K rules.
+ */
+qoq_status qoq_silu_mul_quantize_act(const uint16_t* gate_up, int64_t M, int64_t I, int8_t* xq,
+                                     uint16_t* s_x, int32_t* rowsum, uint16_t* h, void* stream);
+
+/*
  * ---- W4A16 sibling ([W4A16]) ----------------------------------------------
  * FP16 activations against the same QoQ 4-bit weights (the blob and s_c of
  * qoq_quantize_weights / qoq_pack_weights, either mode), so that it differs

@@ -44,6 +44,7 @@ EXPORTED = (
     "qoq_w8a8_gemm_workspace_bytes",
     "qoq_w8a8_gemm",
     "qoq_w4a16_gemm",
+    "qoq_silu_mul_quantize_act",
 )
 
 
@@ -84,6 +85,7 @@ def load_library():
             "qoq_w8a8_gemm_workspace_bytes": (I64, [I64, I64, I64]),
             "qoq_w8a8_gemm": (I, [P, P, P, P, I64, I64, I64, P, P, P, I64, P]),
             "qoq_w4a16_gemm": (I, [I, P, P, P, I64, I64, I64, P, P, P]),
+            "qoq_silu_mul_quantize_act": (I, [P, I64, I64, P, P, P, P, P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(lib, name)
@@ -227,6 +229,36 @@ def qoq_quantize_act(x: torch.Tensor, xq=None, s_x=None, rowsum=None, want_rowsu
     st = load_library().qoq_quantize_act(_ptr(x), M, K, _ptr(xq), _ptr(s_x), _ptr(rowsum),
                                          _stream(x))
     _check(st, "qoq_quantize_act")
+    return xq, s_x, rowsum
+
+
+def qoq_silu_mul_quantize_act(gate_up: torch.Tensor, xq=None, s_x=None, rowsum=None,
+                              want_rowsum: bool = True, h=None):
+    """gate_up [M, 2I] fp16 -> (xq, s_x, rowsum | None) of h = f16(SiLU(gate) * up),
+    gate = columns 0..I-1, up = columns I..2I-1; the same outputs as
+    qoq_quantize_act(h). h (fp16 [M, I]) is written too when given."""
+    _need(gate_up, torch.float16, "gate_up")
+    M, I2 = gate_up.shape
+    if I2 % 2:
+        raise QoQError("gate_up must have an even number of columns")
+    I = I2 // 2
+    dev = gate_up.device
+    nbytes = qoq_act_bytes(M, I)
+    if nbytes < 0:
+        raise QoQError(f"qoq_silu_mul_quantize_act: unsupported shape M={M} I={I}")
+    xq = xq if xq is not None else torch.empty((nbytes,), dtype=torch.int8, device=dev)
+    s_x = s_x if s_x is not None else torch.empty((M,), dtype=torch.float16, device=dev)
+    if rowsum is None and want_rowsum:
+        rowsum = torch.empty((M,), dtype=torch.int32, device=dev)
+    _need(xq, torch.int8, "xq", (nbytes,))
+    _need(s_x, torch.float16, "s_x", (M,))
+    if rowsum is not None:
+        _need(rowsum, torch.int32, "rowsum", (M,))
+    if h is not None:
+        _need(h, torch.float16, "h", (M, I))
+    st = load_library().qoq_silu_mul_quantize_act(_ptr(gate_up), M, I, _ptr(xq), _ptr(s_x),
+                                                  _ptr(rowsum), _ptr(h), _stream(gate_up))
+    _check(st, "qoq_silu_mul_quantize_act")
     return xq, s_x, rowsum
 
 

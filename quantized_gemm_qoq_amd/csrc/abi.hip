@@ -186,6 +186,19 @@ qoq_status qoq_w8a8_gemm(const int8_t* xq, const uint16_t* s_x, const void* blob
     });
 }
 
+qoq_status qoq_silu_mul_quantize_act(const uint16_t* gate_up, int64_t M, int64_t I, int8_t* xq,
+                                     uint16_t* s_x, int32_t* rowsum, uint16_t* h, void* stream) {
+    if (M < 0 || M > INT32_MAX - 15 || !valid_k(I)) return QOQ_ERR_SHAPE;
+    if (M == 0) return QOQ_OK;
+    if (!gate_up || !xq || !s_x) return QOQ_ERR_NULL;
+    if (!aligned16(gate_up) || !aligned16(xq) || !aligned16(s_x) || (rowsum && !aligned16(rowsum)) ||
+        (h && !aligned16(h)))
+        return QOQ_ERR_ALIGN;
+    return launch_checked([&] {
+        qoq::launch_silu_mul_quantize_act(gate_up, M, I, xq, s_x, rowsum, h, as_stream(stream));
+    });
+}
+
 qoq_status qoq_w4a16_gemm(int mode, const uint16_t* x, const void* blob, const uint16_t* s_c,
                           int64_t M, int64_t N, int64_t K, uint16_t* y, float* acc_out,
                           void* stream) {

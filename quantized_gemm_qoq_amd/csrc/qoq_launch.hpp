@@ -21,6 +21,13 @@ void launch_pack(int mode, const uint8_t* q, const uint8_t* s_g, const uint8_t* 
 void launch_unpack(int mode, const uint8_t* blob, int64_t N, int64_t K, uint8_t* q, uint8_t* s_g,
                    uint8_t* z, hipStream_t stream);
 
+// Fused producer of the down projection's input: h = f16(SiLU(gate) * up)
+// from gate_up [M, 2I], then the per-token quantization of launch_quantize_act
+// (same outputs); h [M, I] is written when not null.
+void launch_silu_mul_quantize_act(const uint16_t* gate_up, int64_t M, int64_t I, int8_t* xq,
+                                  uint16_t* s_x, int32_t* rowsum, uint16_t* h,
+                                  hipStream_t stream);
+
 // INT8 weights of the W8A8 sibling: per-channel symmetric quantization, and
 // the reorder into the operand order (N * K bytes).
 void launch_quantize_weights_w8(const uint16_t* w, int64_t N, int64_t K, int8_t* q, uint16_t* s_c,

@@ -300,6 +300,199 @@ __global__ __launch_bounds__(kThreads) void k_quantize_weights_pc(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Fused producer of the down projection's input: h = f16(SiLU(gate) * up)
+// from the fused gate_up output [M, 2I] (gate in columns 0..I-1, up in
+// columns I..2I-1), then the per-token quantization above -- one pass over
+// the gate_up rows instead of a SiLU pass that writes h and a quantization
+// pass that reads it back.
+//
+// The exponential is computed step by step so that the result is a fixed
+// function of the input (the codes depend on it): Cody and Waite's range
+// reduction x = n ln2 + r with ln2 split in two (the first part has trailing
+// zero bits, so n * ln2_hi is exact), the Taylor polynomial of exp(r) to degree
+// 7 in Horner form, and the scaling by 2^n built as an exponent field. Each
+// line is one IEEE fp32 operation (the build forbids contraction into fused
+// multiply-adds); inputs above 88 give +inf and below -86 give 0, which keeps
+// 2^n and the result normal numbers.
+__device__ __forceinline__ float exp_steps(float x) {
+    if (x > 88.0f) return __builtin_inff();
+    if (x < -86.0f) return 0.0f;
+    const float log2e = (float)1.4426950408889634;  // 1 / ln 2
+    const float ln2_hi = 0.693145751953125f;          // ln 2 to 16 significant bits
+    const float ln2_lo = (float)(0.6931471805599453 - 0.693145751953125);
+    const float n = rintf(x * log2e);
+    const float r = (x - n * ln2_hi) - n * ln2_lo;
+    float p = (float)(1.0 / 5040.0);
+    p = p * r + (float)(1.0 / 720.0);
+    p = p * r + (float)(1.0 / 120.0);
+    p = p * r + (float)(1.0 / 24.0);
+    p = p * r + (float)(1.0 / 6.0);
+    p = p * r + 0.5f;
+    p = p * r + 1.0f;
+    p = p * r + 1.0f;
+    const uint32_t bits = (uint32_t)((int)n + 127) << 23;
+    return p * __builtin_bit_cast(float, bits);
+}
+
+// h = f16((g / (1 + exp(-g))) * u) for one FP16 pair; the barrier keeps the
+// product and the conversion two roundings.
+__device__ __forceinline__ uint32_t silu_mul1(uint32_t gbits, uint32_t ubits) {
+    const float g = h2f(gbits);
+    const float t = 1.0f + exp_steps(-g);
+    float v = (g / t) * h2f(ubits);
+    asm("" : "+v"(v));
+    return f2h(v);
+}
+
+// Eight outputs from four words of gate and four of up (two FP16 per word).
+__device__ __forceinline__ u32x4 silu_mul8(u32x4 g, u32x4 u) {
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        o[e] = silu_mul1(g[e] & 0xFFFFu, u[e] & 0xFFFFu) | (silu_mul1(g[e] >> 16, u[e] >> 16) << 16);
+    return o;
+}
+
+// Row held in registers (CH runs of 16 outputs per thread, THR threads per
+// row), for I <= 16 * THR * CH; h (FP16 [M, I]) is written too when asked for.
+template <int THR, int CH>
+__global__ __launch_bounds__(THR) void k_silu_quant_reg(const uint16_t* __restrict__ gu, int M,
+                                                        int I, int8_t* __restrict__ xq,
+                                                        uint16_t* __restrict__ s_x,
+                                                        int32_t* __restrict__ rowsum,
+                                                        uint16_t* __restrict__ h_out) {
+    constexpr int kNW = THR / kWave;
+    __shared__ unsigned red_u[kNW];
+    __shared__ int red_i[kNW];
+    const int m = blockIdx.x;
+    const int U = gridDim.x / 16;
+    const int u = m / 16, r = m % 16;
+    const int nchunk = I / 16;
+    u32x4* out = reinterpret_cast<u32x4*>(xq);
+    auto slot = [&](int c) {
+        const int g = c / 8, s = (c / 4) % 2, j = c % 4;
+        return ((size_t)g * U + u) * 128 + 64 * s + 16 * j + r;
+    };
+    if (m >= M) {
+        for (int c = threadIdx.x; c < nchunk; c += THR) out[slot(c)] = u32x4{0u, 0u, 0u, 0u};
+        return;
+    }
+    const u32x4* grow = reinterpret_cast<const u32x4*>(gu + (size_t)m * 2 * I);
+    const u32x4* urow = reinterpret_cast<const u32x4*>(gu + (size_t)m * 2 * I + I);
+    u32x4* hrow = h_out ? reinterpret_cast<u32x4*>(h_out + (size_t)m * I) : nullptr;
+    u32x4 v0[CH], v1[CH];
+    unsigned amax = 0;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int c = threadIdx.x + THR * i;
+        v0[i] = u32x4{0u, 0u, 0u, 0u};
+        v1[i] = u32x4{0u, 0u, 0u, 0u};
+        if (c < nchunk) {
+            v0[i] = silu_mul8(grow[2 * c], urow[2 * c]);
+            v1[i] = silu_mul8(grow[2 * c + 1], urow[2 * c + 1]);
+            if (hrow) {
+                hrow[2 * c] = v0[i];
+                hrow[2 * c + 1] = v1[i];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            amax = max(amax, max(absmax_bits2(v0[i][e]), absmax_bits2(v1[i][e])));
+    }
+    amax = block_reduce<unsigned, MaxU, kNW>(amax, red_u, MaxU{});
+    const uint16_t sbits = f2h(h2f(amax) / 127.0f);
+    const float sf = h2f(sbits);
+
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int c = threadIdx.x + THR * i;
+        if (c < nchunk) {
+            u32x4 o = u32x4{0u, 0u, 0u, 0u};
+            if (sf != 0.0f) {
+                const uint32_t w[8] = {v0[i][0], v0[i][1], v0[i][2], v0[i][3],
+                                       v1[i][0], v1[i][1], v1[i][2], v1[i][3]};
+                uint32_t packed[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const uint32_t hb = (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu);
+                    const int q = quant_act1(hb, sf);
+                    sum += q;
+                    packed[e >> 2] |= (uint32_t)(q & 0xFF) << (8 * (e & 3));
+                }
+                o = u32x4{packed[0], packed[1], packed[2], packed[3]};
+            }
+            out[slot(c)] = o;
+        }
+    }
+    if (rowsum) sum = block_reduce<int, SumI, kNW>(sum, red_i, SumI{});
+    if (threadIdx.x == 0) {
+        s_x[m] = sbits;
+        if (rowsum) rowsum[m] = sum;
+    }
+}
+
+// Larger I: two passes over the gate_up row (the second recomputes h).
+__global__ __launch_bounds__(kThreads) void k_silu_quant(const uint16_t* __restrict__ gu, int M,
+                                                         int I, int8_t* __restrict__ xq,
+                                                         uint16_t* __restrict__ s_x,
+                                                         int32_t* __restrict__ rowsum,
+                                                         uint16_t* __restrict__ h_out) {
+    __shared__ unsigned red_u[kWaves];
+    __shared__ int red_i[kWaves];
+    const int m = blockIdx.x;
+    const int U = gridDim.x / 16;
+    const int u = m / 16, r = m % 16;
+    const int nchunk = I / 16;
+    uint4* out = reinterpret_cast<uint4*>(xq);
+    auto slot = [&](int c) {
+        const int g = c / 8, s = (c / 4) % 2, j = c % 4;
+        return ((size_t)g * U + u) * 128 + 64 * s + 16 * j + r;
+    };
+    if (m >= M) {
+        for (int c = threadIdx.x; c < nchunk; c += kThreads) out[slot(c)] = make_uint4(0, 0, 0, 0);
+        return;
+    }
+    const u32x4* grow = reinterpret_cast<const u32x4*>(gu + (size_t)m * 2 * I);
+    const u32x4* urow = reinterpret_cast<const u32x4*>(gu + (size_t)m * 2 * I + I);
+    u32x4* hrow = h_out ? reinterpret_cast<u32x4*>(h_out + (size_t)m * I) : nullptr;
+    unsigned amax = 0;
+    for (int i = threadIdx.x; i < I / 8; i += kThreads) {
+        const u32x4 h = silu_mul8(grow[i], urow[i]);
+        if (hrow) hrow[i] = h;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) amax = max(amax, absmax_bits2(h[e]));
+    }
+    amax = block_reduce(amax, red_u, MaxU{});
+    const uint16_t sbits = f2h(h2f(amax) / 127.0f);
+    const float sf = h2f(sbits);
+    int sum = 0;
+    for (int c = threadIdx.x; c < nchunk; c += kThreads) {
+        uint4 o = make_uint4(0, 0, 0, 0);
+        if (sf != 0.0f) {
+            const u32x4 h0 = silu_mul8(grow[2 * c], urow[2 * c]);
+            const u32x4 h1 = silu_mul8(grow[2 * c + 1], urow[2 * c + 1]);
+            const uint32_t w[8] = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+            uint32_t packed[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const uint32_t hb = (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu);
+                const int q = quant_act1(hb, sf);
+                sum += q;
+                packed[e >> 2] |= (uint32_t)(q & 0xFF) << (8 * (e & 3));
+            }
+            o = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+        }
+        out[slot(c)] = o;
+    }
+    if (rowsum) sum = block_reduce(sum, red_i, SumI{});
+    if (threadIdx.x == 0) {
+        s_x[m] = sbits;
+        if (rowsum) rowsum[m] = sum;
+    }
+}
+
 // W8A8 sibling: per-channel symmetric INT8 ("QServe Guide: W4A8KV4
 // Quantization for LLM Serving", "The Problem" item 2, with the per-channel
 // symmetric scaling of "Deep Dive" part 1 at 8 bits): s_c = f16(max|W|/127),
@@ -343,6 +536,24 @@ __global__ __launch_bounds__(kThreads) void k_quantize_weights_w8(const uint16_t
 }
 
 }  // namespace
+
+void launch_silu_mul_quantize_act(const uint16_t* gate_up, int64_t M, int64_t I, int8_t* xq,
+                                  uint16_t* s_x, int32_t* rowsum, uint16_t* h,
+                                  hipStream_t stream) {
+    const unsigned mp = (unsigned)((M + 15) / 16 * 16);
+    const int64_t runs = I / 16;
+#define QOQ_SQ(THRV, CHV)                                                                     \
+    hipLaunchKernelGGL((k_silu_quant_reg<THRV, CHV>), dim3(mp), dim3(THRV), 0, stream, gate_up, \
+                       (int)M, (int)I, xq, s_x, rowsum, h)
+    if (runs <= 256) QOQ_SQ(256, 1);
+    else if (runs <= 512) QOQ_SQ(256, 2);
+    else if (runs <= 1024) QOQ_SQ(1024, 1);
+    else if (runs <= 2048) QOQ_SQ(1024, 2);
+    else
+        hipLaunchKernelGGL(k_silu_quant, dim3(mp), dim3(kThreads), 0, stream, gate_up, (int)M,
+                           (int)I, xq, s_x, rowsum, h);
+#undef QOQ_SQ
+}
 
 void launch_quantize_weights_w8(const uint16_t* w, int64_t N, int64_t K, int8_t* q, uint16_t* s_c,
                                 hipStream_t stream) {

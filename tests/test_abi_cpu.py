@@ -180,3 +180,14 @@ def test_w4a16_validation(lib):
     assert args(x=U) == ERR_ALIGN
     assert args(acc=U) == ERR_ALIGN
 
+
+def test_silu_mul_quantize_validation(lib):
+    f = lib.qoq_silu_mul_quantize_act
+    assert f(A, 0, 128, A, A, A, NUL, NUL) == OK
+    assert f(A, -1, 128, A, A, A, NUL, NUL) == ERR_SHAPE
+    assert f(A, 4, 100, A, A, A, NUL, NUL) == ERR_SHAPE
+    assert f(NUL, 4, 128, A, A, A, NUL, NUL) == ERR_NULL
+    assert f(A, 4, 128, A, NUL, A, NUL, NUL) == ERR_NULL
+    assert f(U, 4, 128, A, A, A, NUL, NUL) == ERR_ALIGN
+    assert f(A, 4, 128, A, A, A, U, NUL) == ERR_ALIGN
+
