@@ -140,9 +140,13 @@ def pmc_summary(args, wl, layer) -> int:
             with open(f) as fh:
                 for r in csv.DictReader(fh):
                     name = r["Kernel_Name"]
-                    if "k_gemm" in name:
-                        mode = "g128" if ("<true" in name or "ILb1E" in name) else "per_channel"
-                        key = "w4a8_gemm_" + mode
+                    if "k_gemm" in name or "k_splitk_reduce" in name:
+                        # first template argument: the weight format (0 g128, 1 per-channel, 2 INT8)
+                        fmt = name.split("<", 1)[1].split(",")[0].split(">")[0].strip()
+                        mode = {"0": "g128", "1": "per_channel", "2": "w8a8"}.get(fmt)
+                        if mode is None:
+                            continue
+                        key = ("w4a8_gemm_" + mode) if mode != "w8a8" else "w8a8_gemm"
                     elif "k_quantize_act" in name:
                         key = "quantize_act"
                     elif "copyBuffer" in name:
