@@ -77,6 +77,10 @@ def _load():
                 "orc_gemm_w4a16_points": (I, [I, P, P, P, P, P, I64, I64, I64, I64, P, P, P, P]),
                 "orc_exp_f32_array": (None, [P, I64, P]),
                 "orc_silu_mul": (I, [P, I64, I64, P]),
+                "orc_kv4_smooth_scales": (I, [P, I64, I64, I64, P]),
+                "orc_kv4_quantize": (I, [P, P, P, I64, I64, I64, I64, I64, P, P, P, P, P, P]),
+                "orc_kv4_decode_attention": (I, [P, P, P, P, P, P, P, P, P, I64, I64, I64, I64,
+                                                 I64, P]),
             }
             for name, (res, args) in sigs.items():
                 fn = getattr(lib, name)
@@ -390,3 +394,47 @@ def silu_mul_quantize_act(gate_up_bits):
     h = silu_mul(gate_up_bits)
     xq, s_x, rowsum = quantize_act(h)
     return h, xq, s_x, rowsum
+
+
+# --- KV4 decode attention with SmoothAttention (reading R16) ---------------
+
+def kv4_smooth_scales(k_bits):
+    """Calibration keys [T, H, d] FP16 bits -> lambda [H, d] FP16 bits."""
+    k = _c(k_bits, np.uint16)
+    T, H, d = k.shape
+    lam = np.empty((H, d), np.uint16)
+    _check(_load().orc_kv4_smooth_scales(_p(k), T, H, d, _p(lam)), "kv4_smooth_scales")
+    return lam
+
+
+def kv4_quantize(k_bits, v_bits, lambda_bits, Tcap=None):
+    """Keys and values [B, T, H, d] FP16 bits -> cache dict: kq, vq uint8 [B, H, Tcap, d]
+    (one code per byte), ks, vs FP16 bits [B, H, Tcap], kz, vz uint8 [B, H, Tcap]."""
+    k = _c(k_bits, np.uint16)
+    v = _c(v_bits, np.uint16)
+    B, T, H, d = k.shape
+    Tcap = T if Tcap is None else Tcap
+    out = {"kq": np.zeros((B, H, Tcap, d), np.uint8), "vq": np.zeros((B, H, Tcap, d), np.uint8),
+           "ks": np.zeros((B, H, Tcap), np.uint16), "vs": np.zeros((B, H, Tcap), np.uint16),
+           "kz": np.zeros((B, H, Tcap), np.uint8), "vz": np.zeros((B, H, Tcap), np.uint8)}
+    _check(_load().orc_kv4_quantize(_p(k), _p(v), _p(_c(lambda_bits, np.uint16)), B, T, H, d, Tcap,
+                                    _p(out["kq"]), _p(out["ks"]), _p(out["kz"]), _p(out["vq"]),
+                                    _p(out["vs"]), _p(out["vz"])), "kv4_quantize")
+    return out
+
+
+def kv4_decode_attention(q_bits, lambda_bits, cache, lens):
+    """q [B, Hq, d] FP16 bits, lambda [H, d], the cache of kv4_quantize, lens int32 [B]
+    -> o float64 [B, Hq, d]."""
+    q = _c(q_bits, np.uint16)
+    B, Hq, d = q.shape
+    H = cache["kq"].shape[1]
+    Tcap = cache["kq"].shape[2]
+    lens = _c(np.asarray(lens, np.int32), np.int32)
+    o = np.empty((B, Hq, d), np.float64)
+    c = {k: np.ascontiguousarray(v) for k, v in cache.items()}
+    _check(_load().orc_kv4_decode_attention(_p(q), _p(_c(lambda_bits, np.uint16)), _p(c["kq"]),
+                                            _p(c["ks"]), _p(c["kz"]), _p(c["vq"]), _p(c["vs"]),
+                                            _p(c["vz"]), _p(lens), B, Hq, H, d, Tcap, _p(o)),
+           "kv4_decode_attention")
+    return o

@@ -58,7 +58,10 @@
  *       precision;
  *   R15 the fused producer of the down projection's input rounds
  *       SiLU(gate) * up to FP16 before quantizing it, with the exponential
- *       defined step by step below (orc_exp_f32).
+ *       defined step by step below (orc_exp_f32);
+ *   R16 KV4 attention: SmoothAttention scales per (KV head, channel) from
+ *       calibration keys, FP16 queries multiplied by them, one asymmetric
+ *       UINT4 range per (token, head) vector for keys and values.
  *
  * Inputs must be finite FP16 (passed as raw binary16 bits).
  */
@@ -719,6 +722,140 @@ int orc_silu_mul(const uint16_t* gate_up, int64_t M, int64_t I, uint16_t* h) {
             const float s = g / t;
             h[m * I + k] = orc_f32_to_f16(s * u);
         }
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* KV4 decode attention with SmoothAttention (reading R16).                 */
+/*                                                                          */
+/* SmoothAttention ("QServe: Low Bit Width Does Not Guarantee High          */
+/* Throughput", section 4, the SmoothAttention paragraph; "QServe Guide",   */
+/* part 3): a per-channel scale lambda_j moves key outliers into the        */
+/* queries, K'_j = K_j / lambda_j and Q'_j = Q_j * lambda_j, which leaves    */
+/* Q K^T unchanged; lambda_j = max_t |K_{t,j}|^alpha with alpha = 0.5,       */
+/* estimated on calibration keys. Here per (KV head, channel):              */
+/*   lambda[h,j] = f16( sqrt( max_t |K[t,h,j]| ) )   (1 if the maximum is 0)  */
+/* KV4: every token's key (after smoothing) and value vector of one head is   */
+/* quantized to asymmetric UINT4 over its d channels, with an FP16 scale and */
+/* a UINT4 zero (the per-channel W4 formulas of reading R7, one range per    */
+/* (token, head)):                                                          */
+/*   x = K[t,h,:] / lambda[h,:]  (fp32 division)   or   x = V[t,h,:]         */
+/*   mn = min(0, min x), mx = max(0, max x), s = f16((mx - mn) / 15)          */
+/*   z = clip(round(-mn / s), 0, 15), q = clip(round(x / s) + z, 0, 15)      */
+/*   (s = 0: q = z = 0)                                                     */
+/* Layouts: keys and values in [B][T][H][d] FP16; caches [B][H][Tcap][d]     */
+/* codes (one per byte here; the GPU packs two per byte), scales and zeros   */
+/* [B][H][Tcap].                                                            */
+/* ------------------------------------------------------------------------ */
+int orc_kv4_smooth_scales(const uint16_t* k, int64_t T, int64_t H, int64_t d, uint16_t* lambda) {
+    if (T < 0 || H < 1 || d < 1) return ORC_ERR_SHAPE;
+    for (int64_t h = 0; h < H; ++h)
+        for (int64_t j = 0; j < d; ++j) {
+            float mx = 0.0f;
+            for (int64_t t = 0; t < T; ++t) {
+                const float a = fabsf(f16_to_f32(k[(t * H + h) * d + j]));
+                if (a > mx) mx = a;
+            }
+            lambda[h * d + j] = mx > 0.0f ? orc_f32_to_f16(sqrtf(mx)) : orc_f32_to_f16(1.0f);
+        }
+    return ORC_OK;
+}
+
+/* One (token, head) vector -> codes, FP16 scale, zero. */
+static void kv4_quant_vec(const float* x, int64_t d, uint8_t* q, uint16_t* s_out, uint8_t* z_out) {
+    float mn = 0.0f, mx = 0.0f;
+    for (int64_t j = 0; j < d; ++j) {
+        if (x[j] < mn) mn = x[j];
+        if (x[j] > mx) mx = x[j];
+    }
+    const uint16_t sb = orc_f32_to_f16((mx - mn) / 15.0f);
+    const float sf = f16_to_f32(sb);
+    int64_t zz = 0;
+    if (sf != 0.0f) zz = clamp64(rne_f32(-mn / sf), 0, 15);
+    for (int64_t j = 0; j < d; ++j)
+        q[j] = (uint8_t)(sf != 0.0f ? clamp64(rne_f32(x[j] / sf) + zz, 0, 15) : 0);
+    *s_out = sb;
+    *z_out = (uint8_t)zz;
+}
+
+int orc_kv4_quantize(const uint16_t* k, const uint16_t* v, const uint16_t* lambda, int64_t B,
+                     int64_t T, int64_t H, int64_t d, int64_t Tcap, uint8_t* kq, uint16_t* ks,
+                     uint8_t* kz, uint8_t* vq, uint16_t* vs, uint8_t* vz) {
+    if (B < 0 || T < 0 || H < 1 || d < 1 || Tcap < T) return ORC_ERR_SHAPE;
+#pragma omp parallel
+    {
+        float* x = (float*)malloc((size_t)d * sizeof(float));
+#pragma omp for schedule(static) collapse(2)
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t h = 0; h < H; ++h)
+                for (int64_t t = 0; t < T; ++t) {
+                    const int64_t src = ((b * T + t) * H + h) * d;
+                    const int64_t row = (b * H + h) * Tcap + t;
+                    for (int64_t j = 0; j < d; ++j)
+                        x[j] = f16_to_f32(k[src + j]) / f16_to_f32(lambda[h * d + j]);
+                    kv4_quant_vec(x, d, kq + row * d, ks + row, kz + row);
+                    for (int64_t j = 0; j < d; ++j) x[j] = f16_to_f32(v[src + j]);
+                    kv4_quant_vec(x, d, vq + row * d, vs + row, vz + row);
+                }
+        free(x);
+    }
+    return ORC_OK;
+}
+
+/* Decode attention of one query token per sequence, in fp64 from the cache:
+ *   q'[j]   = f16( q[b,hq,j] * lambda[h,j] )   (h = hq / (Hq / H), FP16 queries)
+ *   k^[t,j] = s_t * (q_t,j - z_t)   (exact), the same for v^
+ *   score_t = sum_j q'[j] k^[t,j] / sqrt(d),  p = softmax(score over t < len[b])
+ *   o[b,hq,:] = sum_t p_t v^[t,:]        (fp64, not rounded) */
+int orc_kv4_decode_attention(const uint16_t* q, const uint16_t* lambda, const uint8_t* kq,
+                             const uint16_t* ks, const uint8_t* kz, const uint8_t* vq,
+                             const uint16_t* vs, const uint8_t* vz, const int32_t* lens,
+                             int64_t B, int64_t Hq, int64_t H, int64_t d, int64_t Tcap,
+                             double* o) {
+    if (B < 0 || H < 1 || Hq < H || Hq % H || d < 1) return ORC_ERR_SHAPE;
+    for (int64_t b = 0; b < B; ++b)
+        if (lens[b] < 1 || lens[b] > Tcap) return ORC_ERR_SHAPE;
+    const int64_t group = Hq / H;
+#pragma omp parallel
+    {
+        double* qs = (double*)malloc((size_t)d * sizeof(double));
+        double* sc = (double*)malloc((size_t)Tcap * sizeof(double));
+#pragma omp for schedule(static) collapse(2)
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t hq = 0; hq < Hq; ++hq) {
+                const int64_t h = hq / group;
+                for (int64_t j = 0; j < d; ++j)
+                    qs[j] = orc_f16_to_f64(orc_f32_to_f16(f16_to_f32(q[(b * Hq + hq) * d + j]) *
+                                                          f16_to_f32(lambda[h * d + j])));
+                const int64_t L = lens[b];
+                double mx = -INFINITY;
+                for (int64_t t = 0; t < L; ++t) {
+                    const int64_t row = (b * H + h) * Tcap + t;
+                    const double s = orc_f16_to_f64(ks[row]);
+                    double acc = 0.0;
+                    for (int64_t j = 0; j < d; ++j)
+                        acc += qs[j] * (s * ((double)kq[row * d + j] - (double)kz[row]));
+                    sc[t] = acc / sqrt((double)d);
+                    if (sc[t] > mx) mx = sc[t];
+                }
+                double den = 0.0;
+                for (int64_t t = 0; t < L; ++t) {
+                    sc[t] = exp(sc[t] - mx);
+                    den += sc[t];
+                }
+                for (int64_t j = 0; j < d; ++j) {
+                    double acc = 0.0;
+                    for (int64_t t = 0; t < L; ++t) {
+                        const int64_t row = (b * H + h) * Tcap + t;
+                        acc += sc[t] * (orc_f16_to_f64(vs[row]) *
+                                        ((double)vq[row * d + j] - (double)vz[row]));
+                    }
+                    o[(b * Hq + hq) * d + j] = acc / den;
+                }
+            }
+        free(qs);
+        free(sc);
     }
     return ORC_OK;
 }

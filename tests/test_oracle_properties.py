@@ -519,3 +519,144 @@ def test_silu_mul_quantize_is_the_composition():
     np.testing.assert_array_equal(xq, xq2)
     np.testing.assert_array_equal(s_x, s_x2)
     np.testing.assert_array_equal(rowsum, rs2)
+
+
+# ------------------------------------------- KV4 attention + SmoothAttention ----
+def _kv_inputs(B, T, H, d, seed, k_outliers=()):
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((B, T, H, d)).astype(np.float32)
+    for ch, f in k_outliers:
+        k[..., ch] *= f
+    v = rng.standard_normal((B, T, H, d)).astype(np.float32)
+    return k.astype(np.float16), v.astype(np.float16)
+
+
+def _dequant(cache, which):
+    q = cache[which + "q"].astype(np.float64)
+    s = cache[which + "s"].view(np.float16).astype(np.float64)[..., None]
+    z = cache[which + "z"].astype(np.float64)[..., None]
+    return s * (q - z)
+
+
+def test_smooth_scales_definition_and_effect():
+    """lambda^2 recovers each channel's largest |K| to FP16 precision, the
+    smoothed keys' channel maxima are sqrt of the originals (the outlier
+    channel shrinks toward the rest), and q' . k' equals q . k."""
+    B, T, H, d = 1, 64, 2, 128
+    k, _ = _kv_inputs(B, T, H, d, 5, k_outliers=[(7, 20.0), (40, 12.0)])
+    lam = oracle.kv4_smooth_scales(k.reshape(T, H, d).view(np.uint16))
+    lf = lam.view(np.float16).astype(np.float64)
+    amax = np.abs(k.astype(np.float64)).max(axis=(0, 1))  # [H, d]
+    assert np.all(np.abs(lf**2 - amax) <= amax * 2.0**-9)
+    ks = k.astype(np.float64) / lf
+    smax = np.abs(ks).max(axis=(0, 1))
+    assert np.all(np.abs(smax - np.sqrt(amax)) <= np.sqrt(amax) * 2.0**-9)
+    spread_before = amax.max(axis=1) / np.median(amax, axis=1)
+    spread_after = smax.max(axis=1) / np.median(smax, axis=1)
+    assert np.all(spread_after < spread_before / 2)
+    q = np.random.default_rng(6).standard_normal((H, d))
+    np.testing.assert_allclose(((q * lf)[None, None] * ks).sum(-1),
+                               (q[None, None] * k.astype(np.float64)).sum(-1), rtol=1e-12, atol=1e-12)
+    zero = np.zeros((3, 1, 128), np.uint16)
+    assert np.all(oracle.kv4_smooth_scales(zero) == np.float16(1.0).view(np.uint16))
+
+
+def test_kv4_quantize_matches_per_channel_w4_rows_and_bounds():
+    """Each cached (token, head) vector is quantized like a per-channel W4 row
+    (two functions written separately from the same formulas), with codes
+    within half a step of the value."""
+    B, T, H, d = 2, 9, 3, 128
+    k, v = _kv_inputs(B, T, H, d, 7, k_outliers=[(3, 10.0)])
+    lam = oracle.kv4_smooth_scales(k.reshape(B * T, H, d).view(np.uint16))
+    c = oracle.kv4_quantize(k.view(np.uint16), v.view(np.uint16), lam, Tcap=12)
+    vrows = np.transpose(v, (0, 2, 1, 3)).reshape(-1, d)  # [B*H*T, d]
+    pc = oracle.quantize_weights(PC, vrows.view(np.uint16))
+    np.testing.assert_array_equal(c["vq"][:, :, :T].reshape(-1, d), pc["q"])
+    np.testing.assert_array_equal(c["vs"][:, :, :T].reshape(-1), pc["s_c"])
+    np.testing.assert_array_equal(c["vz"][:, :, :T].reshape(-1), pc["z"])
+    assert not c["kq"][:, :, T:].any() and not c["ks"][:, :, T:].any()  # capacity untouched
+    kd = _dequant(c, "k")[:, :, :T]
+    ks = (k.astype(np.float32) / lam.view(np.float16).astype(np.float32)).astype(np.float64)
+    ks = np.transpose(ks, (0, 2, 1, 3))
+    step = c["ks"][:, :, :T].view(np.float16).astype(np.float64)[..., None]
+    assert np.all(np.abs(kd - ks) <= step * 0.5 + 1e-6 * step)
+    assert c["kq"].max() <= 15 and c["kz"].max() <= 15
+
+
+def test_kv4_attention_against_library_softmax():
+    """The attention over the dequantized cache equals numpy matmuls and a
+    softmax written with numpy (library steps, independent of the C loops),
+    for ragged lengths and grouped-query heads."""
+    B, T, H, Hq, d = 3, 20, 2, 8, 128
+    k, v = _kv_inputs(B, T, H, d, 8, k_outliers=[(11, 15.0)])
+    lam = oracle.kv4_smooth_scales(k.reshape(B * T, H, d).view(np.uint16))
+    c = oracle.kv4_quantize(k.view(np.uint16), v.view(np.uint16), lam, Tcap=24)
+    q = np.random.default_rng(9).standard_normal((B, Hq, d)).astype(np.float16)
+    lens = np.array([20, 1, 13], np.int32)
+    o = oracle.kv4_decode_attention(q.view(np.uint16), lam, c, lens)
+    kd, vd = _dequant(c, "k"), _dequant(c, "v")
+    lf = lam.view(np.float16).astype(np.float32)
+    for b in range(B):
+        for hq in range(Hq):
+            h = hq // (Hq // H)
+            qs = (q[b, hq].astype(np.float32) * lf[h]).astype(np.float16).astype(np.float64)
+            L = lens[b]
+            sc = np.matmul(kd[b, h, :L], qs) / np.sqrt(d)
+            p = np.exp(sc - sc.max())
+            p /= p.sum()
+            np.testing.assert_allclose(o[b, hq], np.matmul(p, vd[b, h, :L]), rtol=1e-10, atol=1e-12)
+    # one token: the output is that token's dequantized value vector
+    np.testing.assert_allclose(o[1, 0], vd[1, 0, 0], rtol=0, atol=1e-15)
+
+
+def test_kv4_attention_two_token_closed_form():
+    """Two tokens whose keys sit exactly on the 4-bit grid: the output is the
+    logistic weighting of the two value vectors, in closed form."""
+    import math
+    d = 128
+    k = np.zeros((1, 2, 1, d), np.float16)
+    v = np.zeros((1, 2, 1, d), np.float16)
+    k[0, 0, 0, 0], k[0, 1, 0, 0] = 0.9375, -0.9375  # 15/16: scale 1/16, codes 15 / 0
+    v[0, 0, 0, 1] = 1.875                         # 15/8: scale 1/8, code 15
+    calib = np.ones((1, 1, d), np.float16)        # lambda = sqrt(1) = 1
+    lam = oracle.kv4_smooth_scales(calib.view(np.uint16))
+    c = oracle.kv4_quantize(k.view(np.uint16), v.view(np.uint16), lam)
+    assert c["ks"][0, 0, 0] == np.float16(0.0625).view(np.uint16) and c["kq"][0, 0, 0, 0] == 15
+    assert c["kz"][0, 0, 1] == 15 and c["kq"][0, 0, 1, 0] == 0
+    q = np.zeros((1, 1, d), np.float16)
+    q[0, 0, 0] = 1.0
+    o = oracle.kv4_decode_attention(q.view(np.uint16), lam, c, [2])
+    want = 1.875 / (1.0 + math.exp(-2 * 0.9375 / math.sqrt(d)))
+    assert abs(o[0, 0, 1] - want) <= 1e-15 * want
+    assert np.all(o[0, 0, [0] + list(range(2, d))] == 0)
+
+
+def test_smoothing_reduces_kv4_attention_error_with_key_outliers():
+    """The pages' claim for SmoothAttention on synthetic keys with outlier
+    channels: with the scales the KV4 attention is closer to the FP16 attention
+    than without them (lambda = 1)."""
+    for outliers, ratio in (([(5, 10.0)], 0.6), ([(5, 25.0), (77, 18.0), (100, 30.0)], 0.8)):
+        errs = _kv4_errors_with_and_without_smoothing(outliers)
+        assert errs[0] < errs[1] * ratio, (outliers, errs)
+
+
+def _kv4_errors_with_and_without_smoothing(outliers):
+    B, T, H, Hq, d = 2, 256, 2, 4, 128
+    k, v = _kv_inputs(B, T, H, d, 10, k_outliers=outliers)
+    q = np.random.default_rng(11).standard_normal((B, Hq, d)).astype(np.float16)
+    lens = np.array([T, T], np.int32)
+    kf, vf = k.astype(np.float64), v.astype(np.float64)
+    ref = np.zeros((B, Hq, d))
+    for b in range(B):
+        for hq in range(Hq):
+            h = hq // (Hq // H)
+            sc = kf[b, :, h] @ q[b, hq].astype(np.float64) / np.sqrt(d)
+            p = np.exp(sc - sc.max())
+            ref[b, hq] = (p / p.sum()) @ vf[b, :, h]
+    errs = []
+    for lam in (oracle.kv4_smooth_scales(k.reshape(B * T, H, d).view(np.uint16)),
+                np.full((H, d), np.float16(1.0).view(np.uint16), np.uint16)):
+        c = oracle.kv4_quantize(k.view(np.uint16), v.view(np.uint16), lam)
+        o = oracle.kv4_decode_attention(q.view(np.uint16), lam, c, lens)
+        errs.append(np.linalg.norm(o - ref) / np.linalg.norm(ref))
+    return errs
