@@ -285,6 +285,63 @@ qoq_status qoq_silu_mul_quantize_act(const uint16_t* gate_up, int64_t M, int64_t
                                      uint16_t* s_x, int32_t* rowsum, uint16_t* h, void* stream);
 
 /*
+ * ---- KV4 decode attention with SmoothAttention -----------------------------
+ * ([EN] section 4, the SmoothAttention paragraph; [GUIDE] part 3, SmoothAttention
+ * and the 4-bit KV cache; [EN] section 3, judgment C: KV4 needs the attention
+ * kernel's support, FP16 QK/SV.) Head dimension d = 128; H KV heads, Hq query
+ * heads with Hq / H in {1, 2, 4, 8} (grouped-query attention: query head hq uses
+ * KV head hq / (Hq / H)).
+ *
+ * qoq_kv4_smooth_scales: calibration keys k [T][H][128] FP16 ->
+ *   lambda[h][j] = f16(sqrt(max_t |k[t][h][j]|))  (alpha = 0.5), 1 where the
+ *   maximum is 0. Keys are cached as K / lambda; queries are multiplied by
+ *   lambda, which leaves every q . k unchanged.
+ *
+ * qoq_kv4_append: quantize T new tokens k, v [B][T][H][128] FP16 into positions
+ *   t0 .. t0+T-1 of the cache (t0 + T <= Tcap, Tcap a multiple of 16). For each
+ *   (b, t, h) vector x = k / lambda (fp32 division) or x = v:
+ *     mn = min(0, min x), mx = max(0, max x), s = f16((mx - mn) / 15),
+ *     z = clip(round(-mn / s), 0, 15), c = clip(round(x / s) + z, 0, 15)
+ *     (s = 0 gives c = z = 0), the per-channel W4 formulas applied per vector.
+ *   Cache layout (all caller-allocated, device memory):
+ *     kq [B][H][Tcap][64] bytes: byte j of a token holds channel 2j (low nibble)
+ *                         and 2j + 1 (high nibble);
+ *     vq [B][H][Tcap/16][64][16] bytes: blocks of 16 tokens; byte (blk, j, i) is
+ *                         byte j of token 16*blk + i, nibbles as for kq;
+ *     ks, vs [B][H][Tcap] FP16 scales; kz, vz [B][H][Tcap] uint8 zeros.
+ *
+ * qoq_kv4_decode_attention: one query token per sequence, q [B][Hq][128] FP16,
+ *   lens [B] int32 device array of cached lengths (values are clamped to
+ *   [0, Tcap]; a length of 0 gives a zero output). With q' = f16(q * lambda)
+ *   (fp32 product) and k^ = s (c - z), v^ likewise:
+ *     score_t = (q' . k^_t) / sqrt(128), p = softmax over t < len,
+ *     o[b][hq] = f16(sum_t p_t v^_t)           o [B][Hq][128] FP16
+ *   computed with FP16 products and FP32 sums in an order of the kernel's
+ *   own (the result is not bit-specified; it is within the rounding of
+ *   those operations of the exact value). workspace: device memory of at least
+ *   qoq_kv4_attention_workspace_bytes() bytes (per-chunk partial results; no
+ *   initialisation needed); calls that overlap in time must not share one.
+ */
+qoq_status qoq_kv4_smooth_scales(const uint16_t* k, int64_t T, int64_t H, int64_t d,
+                                 uint16_t* lambda, void* stream);
+
+qoq_status qoq_kv4_append(const uint16_t* k, const uint16_t* v, const uint16_t* lambda,
+                          int64_t B, int64_t T, int64_t H, int64_t d, int64_t Tcap, int64_t t0,
+                          uint8_t* kq, uint16_t* ks, uint8_t* kz, uint8_t* vq, uint16_t* vs,
+                          uint8_t* vz, void* stream);
+
+/* -1 for an unsupported shape. */
+int64_t qoq_kv4_attention_workspace_bytes(int64_t B, int64_t Hq, int64_t H, int64_t d,
+                                          int64_t Tcap);
+
+qoq_status qoq_kv4_decode_attention(const uint16_t* q, const uint16_t* lambda, const uint8_t* kq,
+                                    const uint16_t* ks, const uint8_t* kz, const uint8_t* vq,
+                                    const uint16_t* vs, const uint8_t* vz, const int32_t* lens,
+                                    int64_t B, int64_t Hq, int64_t H, int64_t d, int64_t Tcap,
+                                    uint16_t* o, void* workspace, int64_t workspace_bytes,
+                                    void* stream);
+
+/*
  * ---- W4A16 sibling ([W4A16]) ----------------------------------------------
  * FP16 activations against the same QoQ 4-bit weights (the blob and s_c of
  * qoq_quantize_weights / qoq_pack_weights, either mode), so that it differs

@@ -45,6 +45,10 @@ EXPORTED = (
     "qoq_w8a8_gemm",
     "qoq_w4a16_gemm",
     "qoq_silu_mul_quantize_act",
+    "qoq_kv4_smooth_scales",
+    "qoq_kv4_append",
+    "qoq_kv4_attention_workspace_bytes",
+    "qoq_kv4_decode_attention",
 )
 
 
@@ -86,6 +90,11 @@ def load_library():
             "qoq_w8a8_gemm": (I, [P, P, P, P, I64, I64, I64, P, P, P, I64, P]),
             "qoq_w4a16_gemm": (I, [I, P, P, P, I64, I64, I64, P, P, P]),
             "qoq_silu_mul_quantize_act": (I, [P, I64, I64, P, P, P, P, P]),
+            "qoq_kv4_smooth_scales": (I, [P, I64, I64, I64, P, P]),
+            "qoq_kv4_append": (I, [P, P, P, I64, I64, I64, I64, I64, I64, P, P, P, P, P, P, P]),
+            "qoq_kv4_attention_workspace_bytes": (I64, [I64, I64, I64, I64, I64]),
+            "qoq_kv4_decode_attention": (I, [P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64,
+                                             P, P, I64, P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(lib, name)
@@ -436,6 +445,68 @@ def qoq_w4a16_gemm(mode, x: torch.Tensor, blob: torch.Tensor, s_c: torch.Tensor,
                                        _ptr(acc_out), _stream(x))
     _check(st, "qoq_w4a16_gemm")
     return y
+
+
+# ---- KV4 decode attention with SmoothAttention ------------------------------
+
+HEAD_DIM = 128
+
+
+def qoq_kv4_smooth_scales(k_calib: torch.Tensor) -> torch.Tensor:
+    """Calibration keys [T, H, 128] fp16 -> lambda [H, 128] fp16 (alpha = 0.5)."""
+    _need(k_calib, torch.float16, "k_calib")
+    T, H, d = k_calib.shape
+    lam = torch.empty((H, d), dtype=torch.float16, device=k_calib.device)
+    st = load_library().qoq_kv4_smooth_scales(_ptr(k_calib), T, H, d, _ptr(lam), _stream(k_calib))
+    _check(st, "qoq_kv4_smooth_scales")
+    return lam
+
+
+class KV4Cache:
+    """A KV4 cache of B sequences x H heads x Tcap tokens (layout in include/qoq.h)."""
+
+    def __init__(self, B: int, H: int, Tcap: int, device, lam: torch.Tensor):
+        if Tcap % 16:
+            raise QoQError("Tcap must be a multiple of 16")
+        self.B, self.H, self.Tcap = B, H, Tcap
+        self.lam = _need(lam, torch.float16, "lambda", (H, HEAD_DIM))
+        dev = torch.device(device)
+        self.kq = torch.zeros((B, H, Tcap, HEAD_DIM // 2), dtype=torch.uint8, device=dev)
+        self.vq = torch.zeros((B, H, Tcap // 16, HEAD_DIM // 2, 16), dtype=torch.uint8, device=dev)
+        self.ks = torch.zeros((B, H, Tcap), dtype=torch.float16, device=dev)
+        self.vs = torch.zeros((B, H, Tcap), dtype=torch.float16, device=dev)
+        self.kz = torch.zeros((B, H, Tcap), dtype=torch.uint8, device=dev)
+        self.vz = torch.zeros((B, H, Tcap), dtype=torch.uint8, device=dev)
+
+    def append(self, k: torch.Tensor, v: torch.Tensor, t0: int):
+        """Quantize k, v [B, T, H, 128] fp16 into positions t0 .. t0+T-1."""
+        _need(k, torch.float16, "k")
+        _need(v, torch.float16, "v", tuple(k.shape))
+        B, T, H, d = k.shape
+        st = load_library().qoq_kv4_append(_ptr(k), _ptr(v), _ptr(self.lam), B, T, H, d, self.Tcap,
+                                           t0, _ptr(self.kq), _ptr(self.ks), _ptr(self.kz),
+                                           _ptr(self.vq), _ptr(self.vs), _ptr(self.vz), _stream(k))
+        _check(st, "qoq_kv4_append")
+
+    def attention(self, q: torch.Tensor, lens: torch.Tensor, o=None, workspace=None):
+        """One query token per sequence: q [B, Hq, 128] fp16, lens int32 [B] (device)
+        -> o [B, Hq, 128] fp16."""
+        _need(q, torch.float16, "q")
+        _need(lens, torch.int32, "lens", (self.B,))
+        B, Hq, d = q.shape
+        need = int(load_library().qoq_kv4_attention_workspace_bytes(B, Hq, self.H, d, self.Tcap))
+        if need < 0:
+            raise QoQError(f"qoq_kv4_decode_attention: unsupported shape B={B} Hq={Hq} H={self.H}")
+        if workspace is None:
+            workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+        o = o if o is not None else torch.empty((B, Hq, d), dtype=torch.float16, device=q.device)
+        _need(o, torch.float16, "o", (B, Hq, d))
+        st = load_library().qoq_kv4_decode_attention(
+            _ptr(q), _ptr(self.lam), _ptr(self.kq), _ptr(self.ks), _ptr(self.kz), _ptr(self.vq),
+            _ptr(self.vs), _ptr(self.vz), _ptr(lens), B, Hq, self.H, d, self.Tcap, _ptr(o),
+            _ptr(workspace), workspace.numel(), _stream(q))
+        _check(st, "qoq_kv4_decode_attention")
+        return o
 
 
 class PackedWeight:

@@ -199,6 +199,68 @@ qoq_status qoq_silu_mul_quantize_act(const uint16_t* gate_up, int64_t M, int64_t
     });
 }
 
+namespace {
+bool valid_kv_shape(int64_t B, int64_t H, int64_t d, int64_t Tcap) {
+    return B >= 0 && B <= INT32_MAX && H >= 1 && H <= 1024 && d == 128 && Tcap >= 16 &&
+           Tcap % 16 == 0 && Tcap <= (int64_t(1) << 24);
+}
+}  // namespace
+
+qoq_status qoq_kv4_smooth_scales(const uint16_t* k, int64_t T, int64_t H, int64_t d,
+                                 uint16_t* lambda, void* stream) {
+    if (T < 0 || T > INT32_MAX || H < 1 || H > 1024 || d != 128) return QOQ_ERR_SHAPE;
+    if (!lambda || (T > 0 && !k)) return QOQ_ERR_NULL;
+    if ((k && !aligned16(k)) || !aligned16(lambda)) return QOQ_ERR_ALIGN;
+    return launch_checked([&] { qoq::launch_kv4_smooth_scales(k, T, H, lambda, as_stream(stream)); });
+}
+
+qoq_status qoq_kv4_append(const uint16_t* k, const uint16_t* v, const uint16_t* lambda,
+                          int64_t B, int64_t T, int64_t H, int64_t d, int64_t Tcap, int64_t t0,
+                          uint8_t* kq, uint16_t* ks, uint8_t* kz, uint8_t* vq, uint16_t* vs,
+                          uint8_t* vz, void* stream) {
+    if (!valid_kv_shape(B, H, d, Tcap) || T < 0 || t0 < 0 || t0 + T > Tcap ||
+        B * T * H > INT32_MAX)
+        return QOQ_ERR_SHAPE;
+    if (B == 0 || T == 0) return QOQ_OK;
+    if (!k || !v || !lambda || !kq || !ks || !kz || !vq || !vs || !vz) return QOQ_ERR_NULL;
+    if (!aligned16(k) || !aligned16(v) || !aligned16(lambda) || !aligned16(kq) || !aligned16(ks) ||
+        !aligned16(kz) || !aligned16(vq) || !aligned16(vs) || !aligned16(vz))
+        return QOQ_ERR_ALIGN;
+    return launch_checked([&] {
+        qoq::launch_kv4_append(k, v, lambda, B, T, H, Tcap, t0, kq, ks, kz, vq, vs, vz,
+                               as_stream(stream));
+    });
+}
+
+int64_t qoq_kv4_attention_workspace_bytes(int64_t B, int64_t Hq, int64_t H, int64_t d,
+                                          int64_t Tcap) {
+    if (!valid_kv_shape(B, H, d, Tcap) || Hq < H || Hq % H || Hq / H > 8 || (Hq / H) & (Hq / H - 1))
+        return -1;
+    return qoq::kv4_workspace_bytes(B, Hq, H, Tcap);
+}
+
+qoq_status qoq_kv4_decode_attention(const uint16_t* q, const uint16_t* lambda, const uint8_t* kq,
+                                    const uint16_t* ks, const uint8_t* kz, const uint8_t* vq,
+                                    const uint16_t* vs, const uint8_t* vz, const int32_t* lens,
+                                    int64_t B, int64_t Hq, int64_t H, int64_t d, int64_t Tcap,
+                                    uint16_t* o, void* workspace, int64_t workspace_bytes,
+                                    void* stream) {
+    const int64_t need = qoq_kv4_attention_workspace_bytes(B, Hq, H, d, Tcap);
+    if (need < 0) return QOQ_ERR_SHAPE;
+    if (B == 0) return QOQ_OK;
+    if (!q || !lambda || !kq || !ks || !kz || !vq || !vs || !vz || !lens || !o || !workspace)
+        return QOQ_ERR_NULL;
+    if (!aligned16(q) || !aligned16(lambda) || !aligned16(kq) || !aligned16(ks) || !aligned16(kz) ||
+        !aligned16(vq) || !aligned16(vs) || !aligned16(vz) || !aligned16(lens) || !aligned16(o) ||
+        !aligned16(workspace))
+        return QOQ_ERR_ALIGN;
+    if (workspace_bytes < need) return QOQ_ERR_WORKSPACE;
+    return launch_checked([&] {
+        qoq::launch_kv4_decode_attention(q, lambda, kq, ks, kz, vq, vs, vz, lens, B, Hq, H, Tcap, o,
+                                         workspace, as_stream(stream));
+    });
+}
+
 qoq_status qoq_w4a16_gemm(int mode, const uint16_t* x, const void* blob, const uint16_t* s_c,
                           int64_t M, int64_t N, int64_t K, uint16_t* y, float* acc_out,
                           void* stream) {

@@ -53,4 +53,18 @@ void launch_gemm_w4a16(int mode, const uint16_t* x, const uint8_t* blob, const u
                        int64_t M, int64_t N, int64_t K, uint16_t* y, float* acc_out,
                        hipStream_t stream);
 
+// KV4 decode attention with SmoothAttention (head dimension 128).
+void launch_kv4_smooth_scales(const uint16_t* k, int64_t T, int64_t H, uint16_t* lambda,
+                              hipStream_t stream);
+void launch_kv4_append(const uint16_t* k, const uint16_t* v, const uint16_t* lambda, int64_t B,
+                       int64_t T, int64_t H, int64_t Tcap, int64_t t0, uint8_t* kq, uint16_t* ks,
+                       uint8_t* kz, uint8_t* vq, uint16_t* vs, uint8_t* vz, hipStream_t stream);
+int64_t kv4_chunk(int64_t B, int64_t H, int64_t Tcap);
+int64_t kv4_workspace_bytes(int64_t B, int64_t Hq, int64_t H, int64_t Tcap);
+void launch_kv4_decode_attention(const uint16_t* q, const uint16_t* lambda, const uint8_t* kq,
+                                 const uint16_t* ks, const uint8_t* kz, const uint8_t* vq,
+                                 const uint16_t* vs, const uint8_t* vz, const int32_t* lens,
+                                 int64_t B, int64_t Hq, int64_t H, int64_t Tcap, uint16_t* o,
+                                 void* ws, hipStream_t stream);
+
 }  // namespace qoq

@@ -191,3 +191,29 @@ def test_silu_mul_quantize_validation(lib):
     assert f(U, 4, 128, A, A, A, NUL, NUL) == ERR_ALIGN
     assert f(A, 4, 128, A, A, A, U, NUL) == ERR_ALIGN
 
+
+def test_kv4_validation(lib):
+    f = lib.qoq_kv4_smooth_scales
+    assert f(A, 4, 8, 64, A, NUL) == ERR_SHAPE  # head dimension must be 128
+    assert f(A, 4, 8, 128, NUL, NUL) == ERR_NULL
+    assert f(U, 4, 8, 128, A, NUL) == ERR_ALIGN
+    ap = lib.qoq_kv4_append
+    def app(B=2, T=1, H=8, d=128, Tcap=32, t0=0, k=A):
+        return ap(k, A, A, B, T, H, d, Tcap, t0, A, A, A, A, A, A, NUL)
+    assert app(Tcap=30) == ERR_SHAPE  # Tcap a multiple of 16
+    assert app(t0=32) == ERR_SHAPE  # past the capacity
+    assert app(T=0) == OK
+    assert app(k=NUL) == ERR_NULL
+    assert app(k=U) == ERR_ALIGN
+    w = lib.qoq_kv4_attention_workspace_bytes
+    assert w(2, 32, 8, 128, 1536) > 0
+    assert w(2, 24, 8, 128, 1536) == -1  # group of 3
+    assert w(2, 128, 8, 128, 1536) == -1  # group of 16
+    at = lib.qoq_kv4_decode_attention
+    need = w(2, 32, 8, 128, 1536)
+    def att(ws=A, wsb=need, lens=A):
+        return at(A, A, A, A, A, A, A, A, lens, 2, 32, 8, 128, 1536, A, ws, wsb, NUL)
+    assert att(ws=NUL) == ERR_NULL
+    assert att(lens=NUL) == ERR_NULL
+    assert att(wsb=need - 1) == ERR_WORKSPACE
+
