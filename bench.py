@@ -64,6 +64,10 @@ def parse_args(argv=None):
                    help="instead of the one-line result: time the fused SiLU(gate)*up + "
                         "per-token quantization against the unfused path (torch SiLU*up "
                         "writing h, then qoq_quantize_act) for every down-projection layer")
+    p.add_argument("--kv4", action="store_true",
+                   help="instead of the one-line result: time KV4 decode attention (4-bit "
+                        "cache, SmoothAttention) at the serving shapes next to torch's FP16 "
+                        "attention on an FP16 cache of the same shape")
     p.add_argument("--pmc-summary", nargs="+", default=None, metavar="DIR",
                    help="instead of timing: read rocprofv3 counter CSVs (FETCH_SIZE run, "
                         "WRITE_SIZE run) of a --profile-launches run and write the traffic "
@@ -401,6 +405,13 @@ def main(argv=None) -> int:
     if args.pmc_summary:
         return pmc_summary(args, wl, layer)
 
+    if args.kv4:
+        for name, B, Hq, H, T in KV4_SHAPES:
+            out = kv4_compare(args, name, B, Hq, H, T)
+            if isinstance(out, int):
+                return out
+            print(json.dumps(out), flush=True)
+        return 0
     if args.producer:
         for wl2 in workloads.WORKLOADS.values():
             for layer2 in wl2.layers:
@@ -435,6 +446,82 @@ def main(argv=None) -> int:
         return out
     print(json.dumps(out))
     return 0
+
+
+# Decode attention at the pages' serving point (1024 input + 512 output tokens:
+# 1536 cached tokens at the last step), head dimension 128.
+KV4_SHAPES = (("llama3_8b_b64", 64, 32, 8, 1536), ("llama3_8b_b16", 16, 32, 8, 1536),
+              ("qwen15_72b_b16", 16, 64, 8, 1536))
+
+
+def kv4_compare(args, name, B, Hq, H, T):
+    """KV4 decode attention vs torch FP16 attention, cold caches (rotating copies)."""
+    import torch
+
+    import quantized_gemm_qoq_amd as qoq
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 3
+    dev = torch.device("cuda:0")
+    d = qoq.HEAD_DIM
+    g = torch.Generator(device="cpu")
+    g.manual_seed(8000 + B + Hq)
+    k = torch.randn(B, T, H, d, generator=g).to(torch.float16).to(dev)
+    v = torch.randn(B, T, H, d, generator=g).to(torch.float16).to(dev)
+    q = torch.randn(B, Hq, d, generator=g).to(torch.float16).to(dev)
+    lam = qoq.qoq_kv4_smooth_scales(k[0])
+    lens = torch.full((B,), T, dtype=torch.int32, device=dev)
+    kv4_bytes = B * H * T * (2 * d // 2 + 2 * 3)  # codes, scales, zeros of K and V
+    R = max(2, math.ceil(args.rotate_mib * 2**20 / kv4_bytes))
+    caches = []
+    for _ in range(R):
+        c = qoq.KV4Cache(B, H, T, dev, lam)
+        c.append(k, v, 0)
+        caches.append(c)
+    ws = torch.empty((max(16, qoq.load_library().qoq_kv4_attention_workspace_bytes(B, Hq, H, d, T)),),
+                     dtype=torch.uint8, device=dev)
+    outs = [torch.empty((B, Hq, d), dtype=torch.float16, device=dev) for _ in range(R)]
+    fp16_bytes = 2 * B * H * T * d * 2
+    R16 = max(2, math.ceil(args.rotate_mib * 2**20 / fp16_bytes))
+    kvs = [(k.permute(0, 2, 1, 3).contiguous(), v.permute(0, 2, 1, 3).contiguous()) for _ in range(R16)]
+    q4 = q.view(B, Hq, 1, d)
+    del k, v
+
+    def avg_us(fns, launches):
+        for f in fns[:2]:
+            f()
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for i in range(launches):
+                fns[i % len(fns)]()
+        gr.replay()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        gr.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / launches
+
+    L = max(R, args.kernel_launches // R * R)
+    us4 = avg_us([lambda i=i: caches[i].attention(q, lens, o=outs[i], workspace=ws) for i in range(R)], L)
+    sdpa = torch.nn.functional.scaled_dot_product_attention
+    try:
+        L16 = max(R16, args.kernel_launches // R16 * R16)
+        us16 = avg_us([lambda i=i: sdpa(q4, kvs[i][0], kvs[i][1], enable_gqa=True) for i in range(R16)], L16)
+    except Exception as e:  # an FP16 attention path torch lacks here: report without it
+        print(f"bench.py: torch FP16 attention not timed ({e})", file=sys.stderr)
+        us16 = None
+    alg = kv4_bytes + 2 * 2 * B * Hq * d + 4 * B + 2 * H * d
+    return {"shape": name, "B": B, "Hq": Hq, "H": H, "T": T, "kv4_us": round(us4, 3),
+            "kv4_GBs": round(alg / us4 / 1e3, 1), "kv4_frac_of_hbm": round(alg / us4 / 1e3 / HBM_PEAK_GBS, 3),
+            "kv4_bytes": alg, "fp16_torch_us": None if us16 is None else round(us16, 3),
+            "fp16_cache_bytes": fp16_bytes,
+            "speedup_vs_fp16": None if us16 is None else round(us16 / us4, 2)}
 
 
 def producer_compare(args, layer):

@@ -318,7 +318,8 @@ qoq_status qoq_silu_mul_quantize_act(const uint16_t* gate_up, int64_t M, int64_t
  *     o[b][hq] = f16(sum_t p_t v^_t)           o [B][Hq][128] FP16
  *   computed with FP16 products and FP32 sums in an order of the kernel's
  *   own (the result is not bit-specified; it is within the rounding of
- *   those operations of the exact value). workspace: device memory of at least
+ *   those operations of the exact value). Query heads per KV head: 1, 2, 4
+ *   or 8. workspace: device memory of at least
  *   qoq_kv4_attention_workspace_bytes() bytes (per-chunk partial results; no
  *   initialisation needed); calls that overlap in time must not share one.
  */

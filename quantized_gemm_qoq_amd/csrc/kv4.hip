@@ -22,8 +22,9 @@
 // the way the W4A8 GEMM keeps the zero point out of its: with k^ = s (c - z),
 //   q' . k^ = s (q' . c - z sum(q')),   sum_t w_t v^_t = sum_t (w_t s_t) c_t - sum_t w_t s_t z_t
 // so the codes c are converted to FP16 integers and multiplied as they are
-// (products on the FP16 dot-product instruction with FP32 accumulation, the
-// FP16 QK of the pages), and each token's scale and zero are applied once.
+// (QK on the FP16 matrix cores with FP32 accumulation, the FP16 QK of the
+// pages; SV in FP32 on the vector units), and each token's scale and zero are
+// applied once.
 #include <math.h>
 
 #include "qoq_device.hpp"
@@ -110,26 +111,32 @@ __global__ __launch_bounds__(kKvThreads) void k_kv4_append(
 
 // ---------------------------------------------------------------------------
 // Decode attention, part 1: one workgroup per (b, KV head h, chunk of C
-// tokens) for all G query heads of the group. Each wave takes C/4 tokens of the
-// chunk in steps of 16 and keeps its own online-softmax state:
-//   keys: lane = 8 * (token in the step's half) + slice; a lane reads 8 bytes
-//     (16 channels) of its token, dots them with its 16 channels of each of
-//     the G queries, and the 8 lanes of a token add their sums;
-//   values: lane l owns channels 2l, 2l + 1 and reads the 16-byte block of its
-//     byte for the step's 16 tokens, weighted by p * s_v from LDS.
+// tokens) for all G query heads of the group; wave w takes C/4 of the chunk's
+// tokens (at most 128) in steps of 16, in two passes.
+//   Pass 1, scores on the matrix cores: S[g][t] = q'_g . c_t for 16 tokens is
+//   four v_mfma_f32_16x16x32_f16 with the G queries as A (rows g, padded with
+//   zeros to 16) and the raw codes as B. Lane l reads 16 bytes of token l % 16
+//   (channels 32(l/16) .. +31, the four lanes of a token cover its 64 bytes,
+//   the wave reads 1 KB in one instruction); operation f uses channels
+//   32(l/16) + 8f .. +7 of A and B alike. Scores s = s_k (S - z_k sum q') /
+//   sqrt(128) go to LDS, and the chunk maximum of each query is taken once.
+//   Pass 2: p = exp(s - m) and u = p s_v per (query, token) into LDS; then lane
+//   l owns channels 2l, 2l + 1 of the values and reads the 16-byte block of its
+//   byte for each step's 16 tokens, acc += u * c, with sum(u z_v) subtracted
+//   at the end. All key and value loads of a wave are issued at the start of
+//   their pass.
 // The four waves' states are merged through LDS; the chunk's (max, sum,
 // output) go to the workspace for part 2.
-__device__ __forceinline__ float lane8_sum(float x) {
-    x += __shfl_xor(x, 1, kWave);
-    x += __shfl_xor(x, 2, kWave);
-    x += __shfl_xor(x, 4, kWave);
-    return x;
-}
+constexpr int kMaxSteps = 8;  // 16-token steps per wave (C <= 512)
 
-// Codes of one 32-bit word (8 channels 2j..2j+7 of bytes j..j+3) as four FP16
-// pairs of exact integers 0..15, channel order.
-__device__ __forceinline__ void codes8_to_f16(uint32_t w, uint32_t (&out)[4]) {
+typedef _Float16 half8v __attribute__((ext_vector_type(8)));
+typedef float float4t __attribute__((ext_vector_type(4)));
+
+// Codes of one 32-bit word (8 channels of bytes j..j+3) as four FP16 pairs of
+// exact integers 0..15, channel order.
+__device__ __forceinline__ u32x4 codes8_to_f16(uint32_t w) {
     const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    u32x4 out;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
         // bytes [lo_b, 0, hi_b, 0] | 0x6400 in each half = 1024 + code
@@ -138,6 +145,13 @@ __device__ __forceinline__ void codes8_to_f16(uint32_t w, uint32_t (&out)[4]) {
         const half2v hv = __builtin_bit_cast(half2v, p) - half2v{(_Float16)1024.0f, (_Float16)1024.0f};
         out[b] = __builtin_bit_cast(uint32_t, hv);
     }
+    return out;
+}
+
+__device__ __forceinline__ float wave_sum_f(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
 }
 
 template <int G>
@@ -147,7 +161,8 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_kv4_attn_chunk(
     const uint8_t* __restrict__ vq, const uint16_t* __restrict__ vs, const uint8_t* __restrict__ vz,
     const int32_t* __restrict__ lens, int H, int Tcap, int C, int nchunks,
     float* __restrict__ part_o, float* __restrict__ part_ml) {
-    __shared__ float u_lds[kAttnWaves][G][16];
+    __shared__ float sc_lds[kAttnWaves][G][16 * kMaxSteps];  // scores, then p * s_v
+    __shared__ float qs_lds[kAttnWaves][16];
     __shared__ float mrg_m[kAttnWaves][G], mrg_l[kAttnWaves][G], mrg_z[kAttnWaves][G];
     __shared__ float mrg_o[kAttnWaves][G][kD];
 
@@ -162,138 +177,172 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_kv4_attn_chunk(
     // Part 2 reads a chunk's record only when the chunk starts before len.
     if (c0 >= len) return;
 
-    // This lane's 16 channels (slice) of each query, times lambda, rounded to
-    // FP16 as the queries are kept; and sum(q') per query (for the zeros).
-    const int slice = lane % 8;
-    uint32_t qv[G][8];
-    float qsum[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const uint16_t* qrow = q + ((size_t)b * Hq + h * G + g) * kD + 16 * slice;
-        const uint16_t* lrow = lambda + (size_t)h * kD + 16 * slice;
-        float s = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t qw = *reinterpret_cast<const uint32_t*>(qrow + 2 * i);
-            const uint32_t lw = *reinterpret_cast<const uint32_t*>(lrow + 2 * i);
-            // FP32 products rounded to FP16 (the barriers keep the backend from
-            // forming one mixed-precision multiply that would round once)
-            float pa = h2f(qw & 0xFFFFu) * h2f(lw & 0xFFFFu);
-            float pc = h2f(qw >> 16) * h2f(lw >> 16);
-            asm("" : "+v"(pa), "+v"(pc));
-            const uint16_t a = f2h(pa);
-            const uint16_t c = f2h(pc);
-            qv[g][i] = (uint32_t)a | ((uint32_t)c << 16);
-            s += h2f(a) + h2f(c);
-        }
-        qsum[g] = lane8_sum(s);
-    }
-
-    const float inv_sqrt_d = 0.08838834764831845f;  // 1 / sqrt(128)
-    float m[G], l[G], zs[G], acc[G][2];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        m[g] = -INFINITY;
-        l[g] = 0.0f;
-        zs[g] = 0.0f;
-        acc[g][0] = acc[g][1] = 0.0f;
-    }
-
     const size_t rowbase = (size_t)bh * Tcap;
     const int wstart = c0 + wave * (C / kAttnWaves);
     const int wend = min(wstart + C / kAttnWaves, len);
-    for (int t0 = wstart; t0 < wend; t0 += 16) {
-        // ---- scores of the step's 16 tokens (two halves of 8)
-        float sc[2][G];
+    const int nsteps = wend > wstart ? (wend - wstart + 15) / 16 : 0;
+    const int r16 = lane % 16, jg = lane / 16;
+
+    // ---- keys of every step in flight first
+    u32x4 kb[kMaxSteps];
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int t = t0 + 8 * half + lane / 8;
+    for (int s = 0; s < kMaxSteps; ++s) {
+        if (s < nsteps) {
+            const int t = min(wstart + 16 * s + r16, wend - 1);  // masked tokens read a valid row
+            kb[s] = *reinterpret_cast<const u32x4*>(kq + (rowbase + t) * 64 + 16 * jg);
+        }
+    }
+
+    // ---- A operands: query g = r16 (zeros for r16 >= G), channels 32 jg + 8f + 0..7,
+    // q' = f16(q * lambda) from an FP32 product (the barrier keeps the backend
+    // from forming one mixed-precision multiply that rounds once)
+    half8v qa[4];
+    float qpart = 0.0f;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (r16 < G) {
+            const int ch = 32 * jg + 8 * f;
+            const u32x4 qw = *reinterpret_cast<const u32x4*>(q + ((size_t)b * Hq + h * G + r16) * kD + ch);
+            const u32x4 lw = *reinterpret_cast<const u32x4*>(lambda + (size_t)h * kD + ch);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float pa = h2f(qw[e] & 0xFFFFu) * h2f(lw[e] & 0xFFFFu);
+                float pb = h2f(qw[e] >> 16) * h2f(lw[e] >> 16);
+                asm("" : "+v"(pa), "+v"(pb));
+                const uint16_t a = f2h(pa), c = f2h(pb);
+                w[e] = (uint32_t)a | ((uint32_t)c << 16);
+                qpart += h2f(a) + h2f(c);
+            }
+        }
+        qa[f] = __builtin_bit_cast(half8v, w);
+    }
+    // sum(q') of query r16: add the four lanes of the row (jg = 0..3)
+    qpart += __shfl_xor(qpart, 16, kWave);
+    qpart += __shfl_xor(qpart, 32, kWave);
+    if (lane < 16) qs_lds[wave][lane] = qpart;
+    __builtin_amdgcn_wave_barrier();
+    float qsum[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) qsum[v] = qs_lds[wave][4 * jg + v];
+
+    // ---- pass 1: scores. Output lane l holds rows (queries) 4 jg + v, column
+    // (token) r16 of the step.
+    const float inv_sqrt_d = 0.08838834764831845f;  // 1 / sqrt(128)
+    float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int s = 0; s < kMaxSteps; ++s) {
+        if (s < nsteps) {
+            float4t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int f = 0; f < 4; ++f)
+                d = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    qa[f], __builtin_bit_cast(half8v, codes8_to_f16(kb[s][f])), d, 0, 0, 0);
+            const int t = wstart + 16 * s + r16;
             const bool valid = t < wend;
-            const int tt = valid ? t : wstart;  // in-bounds row for masked lanes
-            const uint2 kw = *reinterpret_cast<const uint2*>(kq + (rowbase + tt) * 64 + 8 * slice);
-            uint32_t ka[4], kb[4];
-            codes8_to_f16(kw.x, ka);
-            codes8_to_f16(kw.y, kb);
-            const uint32_t kc[8] = {ka[0], ka[1], ka[2], ka[3], kb[0], kb[1], kb[2], kb[3]};
+            const int tt = valid ? t : wstart;
             const float sk = h2f(ks[rowbase + tt]);
             const float zk = (float)kz[rowbase + tt];
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                float d = 0.0f;
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    d = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, qv[g][i]),
-                                               __builtin_bit_cast(half2v, kc[i]), d, false);
-                d = lane8_sum(d);
-                const float s = (sk * (d - zk * qsum[g])) * inv_sqrt_d;
-                sc[half][g] = valid ? s : -INFINITY;
-            }
-        }
-        // ---- online softmax over the 16 tokens (all lanes end with the same m, l)
-        const int tA = t0 + lane / 8, tB = t0 + 8 + lane / 8;
-        const float svA = tA < wend ? h2f(vs[rowbase + tA]) : 0.0f;
-        const float svB = tB < wend ? h2f(vs[rowbase + tB]) : 0.0f;
-        const float zvA = tA < wend ? (float)vz[rowbase + tA] : 0.0f;
-        const float zvB = tB < wend ? (float)vz[rowbase + tB] : 0.0f;
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            float tm = fmaxf(sc[0][g], sc[1][g]);
-            tm = fmaxf(tm, __shfl_xor(tm, 8, kWave));
-            tm = fmaxf(tm, __shfl_xor(tm, 16, kWave));
-            tm = fmaxf(tm, __shfl_xor(tm, 32, kWave));
-            const float mn = fmaxf(m[g], tm);  // finite: the step has a valid token
-            const float r = __expf(m[g] - mn);
-            const float pA = __expf(sc[0][g] - mn), pB = __expf(sc[1][g] - mn);
-            // one lane per token carries the token's terms into the sums
-            const bool lead = slice == 0;
-            float ps = lead ? pA + pB : 0.0f;
-            float zsum = lead ? pA * svA * zvA + pB * svB * zvB : 0.0f;
-            ps += __shfl_xor(ps, 8, kWave);
-            ps += __shfl_xor(ps, 16, kWave);
-            ps += __shfl_xor(ps, 32, kWave);
-            zsum += __shfl_xor(zsum, 8, kWave);
-            zsum += __shfl_xor(zsum, 16, kWave);
-            zsum += __shfl_xor(zsum, 32, kWave);
-            l[g] = l[g] * r + ps;
-            zs[g] = zs[g] * r + zsum;
-            acc[g][0] *= r;
-            acc[g][1] *= r;
-            m[g] = mn;
-            if (lead) {
-                u_lds[wave][g][lane / 8] = pA * svA;
-                u_lds[wave][g][8 + lane / 8] = pB * svB;
-            }
-        }
-        // ---- values: lane owns channels 2*lane, 2*lane + 1 of the 16 tokens
-        const int blk = t0 / 16;  // steps start on 16-token boundaries
-        const u32x4 vb = *reinterpret_cast<const u32x4*>(
-            vq + ((size_t)bh * (Tcap / 16) + blk) * 1024 + (size_t)lane * 16);
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int w4 = 0; w4 < 4; ++w4) {
-            const uint32_t word = vb[w4];
-            const uint32_t lo = word & 0x0F0F0F0Fu, hi = (word >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 4 * w4 + e;  // token t0 + i (weight 0 past the end)
-                const float vlo = (float)((lo >> (8 * e)) & 0xFFu);
-                const float vhi = (float)((hi >> (8 * e)) & 0xFFu);
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    const float u = u_lds[wave][g][i];
-                    acc[g][0] += u * vlo;
-                    acc[g][1] += u * vhi;
+            for (int v = 0; v < 4; ++v) {
+                const int g = 4 * jg + v;
+                if (g < G) {
+                    const float sv = valid ? (sk * (d[v] - zk * qsum[v])) * inv_sqrt_d : -INFINITY;
+                    sc_lds[wave][g][16 * s + r16] = sv;
+                    mx[v] = fmaxf(mx[v], sv);
                 }
             }
         }
-        __builtin_amdgcn_wave_barrier();
+    }
+    // chunk maximum of each query: the 16 lanes of a row group hold its tokens
+    float m[G];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        float x = mx[v];
+        x = fmaxf(x, __shfl_xor(x, 1, kWave));
+        x = fmaxf(x, __shfl_xor(x, 2, kWave));
+        x = fmaxf(x, __shfl_xor(x, 4, kWave));
+        x = fmaxf(x, __shfl_xor(x, 8, kWave));
+        mx[v] = x;
+    }
+    if (r16 == 0) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            if (4 * jg + v < G) mrg_m[wave][4 * jg + v] = mx[v];
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int g = 0; g < G; ++g) m[g] = mrg_m[wave][g];
+
+    // ---- values of every step in flight
+    u32x4 vb[kMaxSteps];
+#pragma unroll
+    for (int s = 0; s < kMaxSteps; ++s)
+        if (s < nsteps)
+            vb[s] = *reinterpret_cast<const u32x4*>(
+                vq + ((size_t)bh * (Tcap / 16) + (wstart / 16 + s)) * 1024 + (size_t)lane * 16);
+
+    // ---- pass 2a: u = exp(s - m) * s_v in place; the lane's shares of
+    // sum(p) and sum(u z_v)
+    const int ntok = 16 * nsteps;
+    float l[G], zs[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        l[g] = 0.0f;
+        zs[g] = 0.0f;
+        for (int i = lane; i < ntok; i += kWave) {
+            const int t = wstart + i;
+            const float sv = sc_lds[wave][g][i];
+            float u = 0.0f;
+            if (t < wend) {
+                const float p = __expf(sv - m[g]);
+                u = p * h2f(vs[rowbase + t]);
+                l[g] += p;
+                zs[g] += u * (float)vz[rowbase + t];
+            }
+            sc_lds[wave][g][i] = u;
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    // ---- pass 2b: values
+    float acc[G][2];
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[g][0] = acc[g][1] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < kMaxSteps; ++s) {
+        if (s < nsteps) {
+#pragma unroll
+            for (int w4 = 0; w4 < 4; ++w4) {
+                const uint32_t word = vb[s][w4];
+                const uint32_t lo = word & 0x0F0F0F0Fu, hi = (word >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 16 * s + 4 * w4 + e;
+                    const float vlo = (float)((lo >> (8 * e)) & 0xFFu);
+                    const float vhi = (float)((hi >> (8 * e)) & 0xFFu);
+#pragma unroll
+                    for (int g = 0; g < G; ++g) {
+                        const float u = sc_lds[wave][g][i];
+                        acc[g][0] += u * vlo;
+                        acc[g][1] += u * vhi;
+                    }
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        l[g] = wave_sum_f(l[g]);
+        zs[g] = wave_sum_f(zs[g]);
     }
 
-    // ---- merge the waves' states; a wave without tokens has m = -inf, l = 0
+    // ---- merge the waves' states; a wave without tokens has l = 0
+    __syncthreads();
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         if (lane == 0) {
-            mrg_m[wave][g] = m[g];
+            mrg_m[wave][g] = nsteps > 0 ? m[g] : -INFINITY;
             mrg_l[wave][g] = l[g];
             mrg_z[wave][g] = zs[g];
         }
@@ -304,7 +353,8 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_kv4_attn_chunk(
     // wave w finishes query heads g = w, w + 4, ...
     for (int g = wave; g < G; g += kAttnWaves) {
         float M = -INFINITY;
-        for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, mrg_m[w][g]);
+        for (int w = 0; w < kAttnWaves; ++w)
+            if (mrg_l[w][g] > 0.0f) M = fmaxf(M, mrg_m[w][g]);
         float L = 0.0f, Z = 0.0f, o0 = 0.0f, o1 = 0.0f;
         for (int w = 0; w < kAttnWaves; ++w) {
             const float e = mrg_l[w][g] > 0.0f ? __expf(mrg_m[w][g] - M) : 0.0f;
