@@ -27,6 +27,8 @@
 // applied once.
 #include <math.h>
 
+#include <algorithm>
+
 #include "qoq_device.hpp"
 #include "qoq_launch.hpp"
 
@@ -112,269 +114,415 @@ __global__ __launch_bounds__(kKvThreads) void k_kv4_append(
 // ---------------------------------------------------------------------------
 // Decode attention, part 1: one workgroup per (b, KV head h, chunk of C
 // tokens) for all G query heads of the group; wave w takes C/4 of the chunk's
-// tokens (at most 128) in steps of 16, in two passes.
-//   Pass 1, scores on the matrix cores: S[g][t] = q'_g . c_t for 16 tokens is
-//   four v_mfma_f32_16x16x32_f16 with the G queries as A (rows g, padded with
-//   zeros to 16) and the raw codes as B. Lane l reads 16 bytes of token l % 16
-//   (channels 32(l/16) .. +31, the four lanes of a token cover its 64 bytes,
-//   the wave reads 1 KB in one instruction); operation f uses channels
-//   32(l/16) + 8f .. +7 of A and B alike. Scores s = s_k (S - z_k sum q') /
-//   sqrt(128) go to LDS, and the chunk maximum of each query is taken once.
-//   Pass 2: p = exp(s - m) and u = p s_v per (query, token) into LDS; then lane
-//   l owns channels 2l, 2l + 1 of the values and reads the 16-byte block of its
-//   byte for each step's 16 tokens, acc += u * c, with sum(u z_v) subtracted
-//   at the end. All key and value loads of a wave are issued at the start of
-//   their pass.
+// tokens in steps of 32, the loads of a step issued while the step before is
+// computed, with an online softmax across steps. Scores are kept in log2
+// units (the 1/sqrt(128) and log2(e) factors folded into s_k), p = 2^(s - m).
+// Both contractions run on v_mfma_f32_16x16x32_f16 (16 x 16 output, K = 32):
+//   Key codes enter the matrix cores as FP16 subnormals: the bit pattern c is
+//   the value c 2^-24, exact, so a code needs only a mask and a shift; the
+//   2^24 is folded into the scales, and the queries are scaled by a power of
+//   two so that the largest of a row lies in [2^14, 2^15). The K order of each
+//   lane's 8 elements is permuted to what the masks give, and the queries use
+//   the same order. Value codes are normal FP16 integers (1024 + c - 1024):
+//   with the much smaller weights as the other operand, subnormal codes lose
+//   bits of the products on the matrix cores.
+//   Rows: query g sits on MFMA row 4 j + v (j = (g / NV) 4 / GR, v = g % NV,
+//   GR = min(G, 4) row groups of NV = G / GR queries), so that every lane of a
+//   row group holds its queries' results in registers v < NV and the softmax
+//   work is not repeated on padding rows.
+//   Scores: S[g][t] = q'_g . c_t for 16 tokens is four MFMAs with the queries as
+//   A and the key codes as B. Lane l reads 16 bytes of token l % 16 (channels
+//   32(l/16) .. +31: the four lanes of a token cover its 64 bytes, the wave
+//   reads 1 KB in one instruction). s = s_k (S - z_k sum q').
+//   Values: with w = p s_v, O[g][ch] = sum_t w_t c_t[ch] is P (16 x 32 tokens)
+//   times the codes (32 tokens x 16 channels) per MFMA. The weights are scaled
+//   by 2^E and split as w 2^E = hi + lo, both FP16 (hi: w 2^E cut to 11
+//   significant bits, lo: the remainder rounded toward zero); two MFMAs with
+//   exact products carry w to about 22 bits; each step is summed from zero on
+//   the matrix cores and added to FP32 running sums. E only decreases,
+//   from the step maxima of s_v, so that max(s_v) 2^E < 2^7; the running
+//   maximum m moves only when a step's maximum exceeds it by more than 8, so
+//   p <= 2^8 and w 2^E < 2^15 stays finite in FP16. hi and lo pass through LDS
+//   to the A layout (row 4 j + v, 8 tokens per lane); lane l reads bytes j =
+//   16m + l % 16 of the same 8 tokens from one 16-token value block (low
+//   nibbles: channel 2j, high: 2j + 1) for m = 0..3: eight output blocks of 16
+//   channels. sum_t w_t z_t is subtracted at the end.
 // The four waves' states are merged through LDS; the chunk's (max, sum,
-// output) go to the workspace for part 2.
-constexpr int kMaxSteps = 8;  // 16-token steps per wave (C <= 512)
-
+// output) go to the workspace for part 2, or, when the sequence is a single
+// chunk, the normalised FP16 output is written directly and part 2 is skipped.
 typedef _Float16 half8v __attribute__((ext_vector_type(8)));
 typedef float float4t __attribute__((ext_vector_type(4)));
 
-// Codes of one 32-bit word (8 channels of bytes j..j+3) as four FP16 pairs of
-// exact integers 0..15, channel order.
-__device__ __forceinline__ u32x4 codes8_to_f16(uint32_t w) {
-    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-    u32x4 out;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        // bytes [lo_b, 0, hi_b, 0] | 0x6400 in each half = 1024 + code
-        const uint32_t sel = (uint32_t)b | (0x0Cu << 8) | ((uint32_t)(4 + b) << 16) | (0x0Cu << 24);
-        const uint32_t p = __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u;
-        const half2v hv = __builtin_bit_cast(half2v, p) - half2v{(_Float16)1024.0f, (_Float16)1024.0f};
-        out[b] = __builtin_bit_cast(uint32_t, hv);
-    }
-    return out;
+constexpr float kLog2eRsqrtD = 0.12751743082459868f;  // log2(e) / sqrt(128)
+constexpr float kLazyMax = 8.0f;  // log2 units the running maximum may lag
+constexpr int kPrefetch = 1;      // steps whose loads are in flight ahead of the one computed
+
+// One DPP move within rows of 16 lanes.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, false));
+}
+// Maximum and sum over the 16 lanes of a row (the same value on all of them):
+// swap neighbours, swap pairs, mirror the half rows, mirror the row.
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, dpp_f<0xB1>(x));
+    x = fmaxf(x, dpp_f<0x4E>(x));
+    x = fmaxf(x, dpp_f<0x141>(x));
+    return fmaxf(x, dpp_f<0x140>(x));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_f<0xB1>(x);
+    x += dpp_f<0x4E>(x);
+    x += dpp_f<0x141>(x);
+    return x + dpp_f<0x140>(x);
 }
 
-__device__ __forceinline__ float wave_sum_f(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+__device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(127 + e) << 23); }
+
+// One 32-bit word of key codes (bytes i = 0..3: channels 2i low, 2i + 1 high)
+// as an 8-element FP16 operand in channel order 0, 4, 2, 6, 1, 5, 3, 7.
+__device__ __forceinline__ half8v key_word_f16(uint32_t w) {
+    const uint32_t m = 0x000F000Fu;
+    return __builtin_bit_cast(half8v, u32x4{w & m, (w >> 8) & m, (w >> 4) & m, (w >> 12) & m});
+}
+// Bytes of 8 tokens (x0: tokens 0..3, x1: 4..7) -> two 8-element FP16
+// operands in token order: the low nibbles c and the high nibbles as 16 c, both
+// as normal FP16 integers (bytes [n, 0x64] are 1024 + n; 1024 is subtracted).
+__device__ __forceinline__ void value_bytes_f16(uint32_t x0, uint32_t x1, half8v& lo, half8v& hi) {
+    const uint32_t k64 = 0x64646464u;
+    const half2v off = half2v{(_Float16)1024.0f, (_Float16)1024.0f};
+    auto cv = [&](uint32_t nib, uint32_t sel) {
+        return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, __builtin_amdgcn_perm(k64, nib, sel)) - off);
+    };
+    const uint32_t l0 = x0 & 0x0F0F0F0Fu, l1 = x1 & 0x0F0F0F0Fu;
+    const uint32_t h0 = x0 & 0xF0F0F0F0u, h1 = x1 & 0xF0F0F0F0u;
+    lo = __builtin_bit_cast(half8v, u32x4{cv(l0, 0x04010400u), cv(l0, 0x04030402u), cv(l1, 0x04010400u),
+                                          cv(l1, 0x04030402u)});
+    hi = __builtin_bit_cast(half8v, u32x4{cv(h0, 0x04010400u), cv(h0, 0x04030402u), cv(h1, 0x04010400u),
+                                          cv(h1, 0x04030402u)});
 }
 
 template <int G>
-__global__ __launch_bounds__(kAttnWaves * 64) void k_kv4_attn_chunk(
+__global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu(3))) void k_kv4_attn_chunk(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ lambda,
     const uint8_t* __restrict__ kq, const uint16_t* __restrict__ ks, const uint8_t* __restrict__ kz,
     const uint8_t* __restrict__ vq, const uint16_t* __restrict__ vs, const uint8_t* __restrict__ vz,
     const int32_t* __restrict__ lens, int H, int Tcap, int C, int nchunks,
-    float* __restrict__ part_o, float* __restrict__ part_ml) {
-    __shared__ float sc_lds[kAttnWaves][G][16 * kMaxSteps];  // scores, then p * s_v
-    __shared__ float qs_lds[kAttnWaves][16];
+    float* __restrict__ part_o, float* __restrict__ part_ml, uint16_t* __restrict__ out) {
+    constexpr int GR = G < 4 ? G : 4;  // row groups that hold queries
+    constexpr int NV = G / GR;         // queries per row group
+    constexpr int JS = 4 / GR;         // stride between those row groups
+    __shared__ __align__(16) uint16_t wh_lds[kAttnWaves][16][32];  // hi parts of w 2^E, by row
+    __shared__ __align__(16) uint16_t wl_lds[kAttnWaves][16][32];  // lo parts
+    __shared__ float qs_lds[kAttnWaves][16], qf_lds[kAttnWaves][16];
     __shared__ float mrg_m[kAttnWaves][G], mrg_l[kAttnWaves][G], mrg_z[kAttnWaves][G];
     __shared__ float mrg_o[kAttnWaves][G][kD];
 
     const int lane = threadIdx.x % kWave;
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: scalar branches
     const int chunk = blockIdx.x % nchunks;
     const int bh = blockIdx.x / nchunks;  // b * H + h
     const int h = bh % H, b = bh / H;
     const int Hq = H * G;
     const int len = min(max(lens[b], 0), Tcap);
     const int c0 = chunk * C;
-    // Part 2 reads a chunk's record only when the chunk starts before len.
-    if (c0 >= len) return;
+    // Part 2 reads a chunk's record only when the chunk starts before len; a
+    // sequence of length 0 that is one chunk gets its zeros here.
+    if (c0 >= len) {
+        if (nchunks == 1)
+            for (int g = wave; g < G; g += kAttnWaves)
+                reinterpret_cast<uint32_t*>(out + ((size_t)b * Hq + h * G + g) * kD)[lane] = 0u;
+        return;
+    }
 
     const size_t rowbase = (size_t)bh * Tcap;
-    const int wstart = c0 + wave * (C / kAttnWaves);
+    const int wstart = c0 + wave * (C / kAttnWaves);  // a multiple of 32
     const int wend = min(wstart + C / kAttnWaves, len);
-    const int nsteps = wend > wstart ? (wend - wstart + 15) / 16 : 0;
+    const int ntotal = wend > wstart ? (wend - wstart + 31) / 32 : 0;  // steps of this wave
     const int r16 = lane % 16, jg = lane / 16;
+    const uint8_t* vbase = vq + (size_t)bh * (Tcap / 16) * 1024;
+    const int vlast = (wend - 1) / 16;  // last value block with a valid token
+    const bool lane_q = jg % JS == 0;   // rows 4 jg + v (v < NV) of this lane are queries
+    const int gbase = (jg / JS) * NV;   // the query on row 4 jg
 
-    // ---- keys of every step in flight first
-    u32x4 kb[kMaxSteps];
-#pragma unroll
-    for (int s = 0; s < kMaxSteps; ++s) {
-        if (s < nsteps) {
-            const int t = min(wstart + 16 * s + r16, wend - 1);  // masked tokens read a valid row
-            kb[s] = *reinterpret_cast<const u32x4*>(kq + (rowbase + t) * 64 + 16 * jg);
-        }
-    }
-
-    // ---- A operands: query g = r16 (zeros for r16 >= G), channels 32 jg + 8f + 0..7,
-    // q' = f16(q * lambda) from an FP32 product (the barrier keeps the backend
-    // from forming one mixed-precision multiply that rounds once)
+    // ---- A operands of the scores: row r16 (zeros where it holds no query),
+    // channels 32 jg + 8f + {0, 4, 2, 6, 1, 5, 3, 7}; q' = f16(q * lambda) from
+    // an FP32 product (the barrier keeps the backend from forming one
+    // mixed-precision multiply that rounds once), times 2^s_r per row so that
+    // the row's largest |q'| 2^s_r lies in [2^14, 2^15) (s_r >= 0, exact): the
+    // products with the subnormal codes then stay far above the smallest FP16
+    // magnitudes, where the matrix cores lose bits of such products.
     half8v qa[4];
-    float qpart = 0.0f;
+    {
+        const int rj = r16 / 4, rv = r16 % 4;
+        const bool row_q = rj % JS == 0 && rv < NV;
+        const int rg = (rj / JS) * NV + rv;
+        // all query and lambda loads in flight together (rows without a query
+        // read row 0 and give zeros)
+        const size_t qoff = ((size_t)b * Hq + h * G + (row_q ? rg : 0)) * kD + 32 * jg;
+        u32x4 qw[4], lw[4];
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (r16 < G) {
-            const int ch = 32 * jg + 8 * f;
-            const u32x4 qw = *reinterpret_cast<const u32x4*>(q + ((size_t)b * Hq + h * G + r16) * kD + ch);
-            const u32x4 lw = *reinterpret_cast<const u32x4*>(lambda + (size_t)h * kD + ch);
+        for (int f = 0; f < 4; ++f) {
+            qw[f] = *reinterpret_cast<const u32x4*>(q + qoff + 8 * f);
+            lw[f] = *reinterpret_cast<const u32x4*>(lambda + (size_t)h * kD + 32 * jg + 8 * f);
+        }
+        uint16_t e8[4][8];
+        float qpart = 0.0f, qmax = 0.0f;
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                float pa = h2f(qw[e] & 0xFFFFu) * h2f(lw[e] & 0xFFFFu);
-                float pb = h2f(qw[e] >> 16) * h2f(lw[e] >> 16);
+                float pa = h2f(qw[f][e] & 0xFFFFu) * h2f(lw[f][e] & 0xFFFFu);
+                float pb = h2f(qw[f][e] >> 16) * h2f(lw[f][e] >> 16);
                 asm("" : "+v"(pa), "+v"(pb));
-                const uint16_t a = f2h(pa), c = f2h(pb);
-                w[e] = (uint32_t)a | ((uint32_t)c << 16);
-                qpart += h2f(a) + h2f(c);
+                e8[f][2 * e] = row_q ? f2h(pa) : (uint16_t)0;
+                e8[f][2 * e + 1] = row_q ? f2h(pb) : (uint16_t)0;
+                const float a = h2f(e8[f][2 * e]), c = h2f(e8[f][2 * e + 1]);
+                qpart += a + c;
+                qmax = fmaxf(qmax, fmaxf(fabsf(a), fabsf(c)));
             }
         }
-        qa[f] = __builtin_bit_cast(half8v, w);
+        // sum(q') and max|q'| of row r16 over the four lanes of the row (jg = 0..3)
+        qpart += __shfl_xor(qpart, 16, kWave);
+        qpart += __shfl_xor(qpart, 32, kWave);
+        qmax = fmaxf(qmax, __shfl_xor(qmax, 16, kWave));
+        qmax = fmaxf(qmax, __shfl_xor(qmax, 32, kWave));
+        const int srow = qmax > 0.0f ? max(0, 141 - (int)((__float_as_uint(qmax) >> 23) & 0xFF)) : 0;
+        const float qscale = pow2f(srow);
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+            uint32_t e2[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) e2[e] = f2h(h2f(e8[f][e]) * qscale);
+            qa[f] = __builtin_bit_cast(half8v, u32x4{e2[0] | (e2[4] << 16), e2[2] | (e2[6] << 16),
+                                                     e2[1] | (e2[5] << 16), e2[3] | (e2[7] << 16)});
+        }
+        if (lane < 16) {
+            qs_lds[wave][lane] = qpart;
+            qf_lds[wave][lane] = pow2f(24 - srow);  // undoes 2^s_r and the codes' 2^-24
+        }
     }
-    // sum(q') of query r16: add the four lanes of the row (jg = 0..3)
-    qpart += __shfl_xor(qpart, 16, kWave);
-    qpart += __shfl_xor(qpart, 32, kWave);
-    if (lane < 16) qs_lds[wave][lane] = qpart;
     __builtin_amdgcn_wave_barrier();
-    float qsum[4];
+    float qsum[NV], qfac[NV];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) qsum[v] = qs_lds[wave][4 * jg + v];
+    for (int v = 0; v < NV; ++v) {
+        qsum[v] = qs_lds[wave][4 * jg + v];
+        qfac[v] = qf_lds[wave][4 * jg + v];
+    }
 
-    // ---- pass 1: scores. Output lane l holds rows (queries) 4 jg + v, column
-    // (token) r16 of the step.
-    const float inv_sqrt_d = 0.08838834764831845f;  // 1 / sqrt(128)
-    float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    float mrun[NV], lp[NV], zp[NV];  // running maximum (log2 units), sum of p, sum of w z_v
 #pragma unroll
-    for (int s = 0; s < kMaxSteps; ++s) {
-        if (s < nsteps) {
-            float4t d = {0.f, 0.f, 0.f, 0.f};
+    for (int v = 0; v < NV; ++v) {
+        mrun[v] = -INFINITY;
+        lp[v] = zp[v] = 0.0f;
+    }
+    float acc[8][NV];  // output block 2m + n: channels 2(16m + r16) + n, rows 4 jg + v
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int v = 0; v < NV; ++v) acc[i][v] = 0.0f;
+    int ecur = 64;  // the exponent E the accumulators carry (64: none yet)
+
+    // One step: 32 tokens.
+    struct StepData {
+        u32x4 kb[2];  // key bytes of token 16 hs + r16, channels 32 jg ..
+        uint2 vb[4];  // value bytes j = 16m + r16 of tokens 8 jg .. +7
+        // raw scales and zeros: converted only when the step is computed, so
+        // that no use waits for a load of the step ahead
+        uint16_t sk[2], sv[2];
+        uint8_t zk[2], zv[2];
+    };
+    auto load_step = [&](int st, StepData& d) {
+        const int bstart = wstart + 32 * st;
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+            const int t = min(bstart + 16 * hs + r16, wend - 1);  // masked tokens read a valid row
+            d.kb[hs] = *reinterpret_cast<const u32x4*>(kq + (rowbase + t) * 64 + 16 * jg);
+        }
+        const int blk = min(bstart / 16 + jg / 2, vlast);
+        const uint8_t* vp = vbase + (size_t)blk * 1024 + r16 * 16 + 8 * (jg % 2);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) d.vb[m] = *reinterpret_cast<const uint2*>(vp + 256 * m);
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+            const int t = min(bstart + 16 * hs + r16, wend - 1);
+            d.sk[hs] = ks[rowbase + t];
+            d.zk[hs] = kz[rowbase + t];
+            d.sv[hs] = vs[rowbase + t];
+            d.zv[hs] = vz[rowbase + t];
+        }
+    };
+    auto compute_step = [&](int st, const StepData& d) {
+        const int bstart = wstart + 32 * st;
+        float sk[2], zk[2], sv[2], zv[2];
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+            sk[hs] = h2f(d.sk[hs]) * kLog2eRsqrtD;
+            zk[hs] = (float)d.zk[hs];
+            sv[hs] = h2f(d.sv[hs]);
+            zv[hs] = (float)d.zv[hs];
+        }
+        // ---- scores of 16 tokens per half step: lane l holds token l % 16
+        float sc[2][NV];
+        float bmx[NV];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) bmx[v] = -INFINITY;
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+            float4t s4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int f = 0; f < 4; ++f)
-                d = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                    qa[f], __builtin_bit_cast(half8v, codes8_to_f16(kb[s][f])), d, 0, 0, 0);
-            const int t = wstart + 16 * s + r16;
-            const bool valid = t < wend;
-            const int tt = valid ? t : wstart;
-            const float sk = h2f(ks[rowbase + tt]);
-            const float zk = (float)kz[rowbase + tt];
+                s4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[f], key_word_f16(d.kb[hs][f]), s4, 0, 0, 0);
+            const bool valid = bstart + 16 * hs + r16 < wend;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int g = 4 * jg + v;
-                if (g < G) {
-                    const float sv = valid ? (sk * (d[v] - zk * qsum[v])) * inv_sqrt_d : -INFINITY;
-                    sc_lds[wave][g][16 * s + r16] = sv;
-                    mx[v] = fmaxf(mx[v], sv);
-                }
+            for (int v = 0; v < NV; ++v) {
+                sc[hs][v] = valid ? sk[hs] * __builtin_fmaf(-zk[hs], qsum[v], s4[v] * qfac[v]) : -INFINITY;
+                bmx[v] = fmaxf(bmx[v], sc[hs][v]);
+            }
+        }
+        float msv = row16_max(fmaxf(sv[0], sv[1]));
+        // E: max(s_v) 2^E < 2^7 with s_v an FP16 value (at least 2^-24 when
+        // not 0); the same on every lane, never increased
+        const int ebits = __builtin_amdgcn_readfirstlane((int)((__float_as_uint(msv) >> 23) & 0xFF));
+        const int enew = min(ecur, 133 - max(ebits, 103));
+        bool need = enew != ecur;
+        const float erescale = pow2f(enew - ecur);
+        float rs[NV];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            bmx[v] = row16_max(bmx[v]);  // finite: the step has a valid token
+            const float mn = bmx[v] > mrun[v] + kLazyMax ? bmx[v] : mrun[v];
+            const float r = __builtin_amdgcn_exp2f(mrun[v] - mn);  // 0 on the first step
+            need |= mn != mrun[v];
+            lp[v] *= r;
+            zp[v] *= r;
+            rs[v] = r * erescale;
+            mrun[v] = mn;
+        }
+        ecur = enew;
+        if (__builtin_amdgcn_ballot_w64(need)) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int v = 0; v < NV; ++v) acc[i][v] *= rs[v];
+        }
+
+        // ---- p = 2^(s - m); sums of p and of w z_v; w 2^E = hi + lo into LDS
+        const float wscale = pow2f(enew);
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+            const float svs = sv[hs] * wscale, svz = sv[hs] * zv[hs];
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const float p = __builtin_amdgcn_exp2f(sc[hs][v] - mrun[v]);  // 0 for masked tokens
+                lp[v] += p;
+                zp[v] = __builtin_fmaf(p, svz, zp[v]);
+                const float w = p * svs;
+                const float whi = __uint_as_float(__float_as_uint(w) & 0xFFFFE000u);
+                const uint32_t pk = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(whi, w - whi));
+                wh_lds[wave][4 * jg + v][16 * hs + r16] = (uint16_t)pk;
+                wl_lds[wave][4 * jg + v][16 * hs + r16] = (uint16_t)(pk >> 16);
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+
+        // ---- values: O += (hi + lo) x codes. Each step's products are summed
+        // on the matrix cores from zero (the lo products first, so that their
+        // small sum is the addend of the hi ones), then added to the running
+        // sums in FP32 on the vector units: the matrix cores align their
+        // addends to the largest one, which would cut the bits of a step's
+        // contribution against a long running sum.
+        const half8v ah = *reinterpret_cast<const half8v*>(&wh_lds[wave][r16][8 * jg]);
+        const half8v al = *reinterpret_cast<const half8v*>(&wl_lds[wave][r16][8 * jg]);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            half8v blo, bhi;
+            value_bytes_f16(d.vb[m].x, d.vb[m].y, blo, bhi);
+            const float4t zero = {0.f, 0.f, 0.f, 0.f};
+            float4t t0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, blo, zero, 0, 0, 0);
+            float4t t1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bhi, zero, 0, 0, 0);
+            t0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, blo, t0, 0, 0, 0);
+            t1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bhi, t1, 0, 0, 0);
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                acc[2 * m][v] += t0[v];
+                acc[2 * m + 1][v] += t1[v];
+            }
+        }
+        __builtin_amdgcn_wave_barrier();  // the next step rewrites the LDS weights
+    };
+
+    // Loads run kPrefetch steps ahead of their use; a load beyond the last
+    // step repeats the last step (cached, unused), so that the count of loads
+    // in flight, and with it each wait, is the same at every step.
+    if (ntotal > 0) {
+        StepData d[kPrefetch + 1];
+#pragma unroll
+        for (int i = 0; i < kPrefetch; ++i) load_step(min(i, ntotal - 1), d[i]);
+        for (int st = 0;; st += kPrefetch + 1) {
+#pragma unroll
+            for (int ph = 0; ph <= kPrefetch; ++ph) {
+                load_step(min(st + ph + kPrefetch, ntotal - 1), d[(ph + kPrefetch) % (kPrefetch + 1)]);
+                compute_step(st + ph, d[ph]);
+                if (st + ph + 1 >= ntotal) goto steps_done;
             }
         }
     }
-    // chunk maximum of each query: the 16 lanes of a row group hold its tokens
-    float m[G];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        float x = mx[v];
-        x = fmaxf(x, __shfl_xor(x, 1, kWave));
-        x = fmaxf(x, __shfl_xor(x, 2, kWave));
-        x = fmaxf(x, __shfl_xor(x, 4, kWave));
-        x = fmaxf(x, __shfl_xor(x, 8, kWave));
-        mx[v] = x;
-    }
-    if (r16 == 0) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-            if (4 * jg + v < G) mrg_m[wave][4 * jg + v] = mx[v];
-    }
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int g = 0; g < G; ++g) m[g] = mrg_m[wave][g];
-
-    // ---- values of every step in flight
-    u32x4 vb[kMaxSteps];
-#pragma unroll
-    for (int s = 0; s < kMaxSteps; ++s)
-        if (s < nsteps)
-            vb[s] = *reinterpret_cast<const u32x4*>(
-                vq + ((size_t)bh * (Tcap / 16) + (wstart / 16 + s)) * 1024 + (size_t)lane * 16);
-
-    // ---- pass 2a: u = exp(s - m) * s_v in place; the lane's shares of
-    // sum(p) and sum(u z_v)
-    const int ntok = 16 * nsteps;
-    float l[G], zs[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        l[g] = 0.0f;
-        zs[g] = 0.0f;
-        for (int i = lane; i < ntok; i += kWave) {
-            const int t = wstart + i;
-            const float sv = sc_lds[wave][g][i];
-            float u = 0.0f;
-            if (t < wend) {
-                const float p = __expf(sv - m[g]);
-                u = p * h2f(vs[rowbase + t]);
-                l[g] += p;
-                zs[g] += u * (float)vz[rowbase + t];
-            }
-            sc_lds[wave][g][i] = u;
-        }
-    }
-    __builtin_amdgcn_wave_barrier();
-
-    // ---- pass 2b: values
-    float acc[G][2];
-#pragma unroll
-    for (int g = 0; g < G; ++g) acc[g][0] = acc[g][1] = 0.0f;
-#pragma unroll
-    for (int s = 0; s < kMaxSteps; ++s) {
-        if (s < nsteps) {
-#pragma unroll
-            for (int w4 = 0; w4 < 4; ++w4) {
-                const uint32_t word = vb[s][w4];
-                const uint32_t lo = word & 0x0F0F0F0Fu, hi = (word >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = 16 * s + 4 * w4 + e;
-                    const float vlo = (float)((lo >> (8 * e)) & 0xFFu);
-                    const float vhi = (float)((hi >> (8 * e)) & 0xFFu);
-#pragma unroll
-                    for (int g = 0; g < G; ++g) {
-                        const float u = sc_lds[wave][g][i];
-                        acc[g][0] += u * vlo;
-                        acc[g][1] += u * vhi;
-                    }
-                }
-            }
-        }
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        l[g] = wave_sum_f(l[g]);
-        zs[g] = wave_sum_f(zs[g]);
-    }
+steps_done:
 
     // ---- merge the waves' states; a wave without tokens has l = 0
-    __syncthreads();
+    // undo 2^E (and the 16 of the high-nibble codes)
+    const float unscale_lo = ntotal > 0 ? pow2f(-ecur) : 1.0f, unscale_hi = unscale_lo * 0.0625f;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        if (lane == 0) {
-            mrg_m[wave][g] = nsteps > 0 ? m[g] : -INFINITY;
-            mrg_l[wave][g] = l[g];
-            mrg_z[wave][g] = zs[g];
+    for (int v = 0; v < NV; ++v) {
+        const float l = row16_sum(lp[v]), z = row16_sum(zp[v]);
+        if (lane_q) {
+            const int g = gbase + v;
+            if (r16 == 0) {
+                mrg_m[wave][g] = ntotal > 0 ? mrun[v] : -INFINITY;
+                mrg_l[wave][g] = l;
+                mrg_z[wave][g] = z;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                mrg_o[wave][g][2 * (16 * (i / 2) + r16) + (i % 2)] = acc[i][v] * (i % 2 ? unscale_hi : unscale_lo);
         }
-        mrg_o[wave][g][2 * lane] = acc[g][0];
-        mrg_o[wave][g][2 * lane + 1] = acc[g][1];
     }
     __syncthreads();
-    // wave w finishes query heads g = w, w + 4, ...
+    // wave w finishes query heads g = w, w + 4, ...; a sequence that is one
+    // chunk writes its FP16 output here, otherwise the chunk's record for part 2
     for (int g = wave; g < G; g += kAttnWaves) {
         float M = -INFINITY;
         for (int w = 0; w < kAttnWaves; ++w)
             if (mrg_l[w][g] > 0.0f) M = fmaxf(M, mrg_m[w][g]);
         float L = 0.0f, Z = 0.0f, o0 = 0.0f, o1 = 0.0f;
         for (int w = 0; w < kAttnWaves; ++w) {
-            const float e = mrg_l[w][g] > 0.0f ? __expf(mrg_m[w][g] - M) : 0.0f;
+            const float e = mrg_l[w][g] > 0.0f ? __builtin_amdgcn_exp2f(mrg_m[w][g] - M) : 0.0f;
             L += e * mrg_l[w][g];
             Z += e * mrg_z[w][g];
             o0 += e * mrg_o[w][g][2 * lane];
             o1 += e * mrg_o[w][g][2 * lane + 1];
         }
-        const size_t rec = ((size_t)b * Hq + h * G + g) * nchunks + chunk;
-        part_o[rec * kD + 2 * lane] = o0 - Z;
-        part_o[rec * kD + 2 * lane + 1] = o1 - Z;
-        if (lane == 0) {
-            part_ml[rec * 2] = M;
-            part_ml[rec * 2 + 1] = L;
+        const size_t qrow = (size_t)b * Hq + h * G + g;
+        if (nchunks == 1) {
+            const float inv = 1.0f / L;  // L > 0: the chunk has a valid token
+            reinterpret_cast<uint32_t*>(out + qrow * kD)[lane] =
+                (uint32_t)f2h((o0 - Z) * inv) | ((uint32_t)f2h((o1 - Z) * inv) << 16);
+        } else {
+            const size_t rec = qrow * nchunks + chunk;
+            part_o[rec * kD + 2 * lane] = o0 - Z;
+            part_o[rec * kD + 2 * lane + 1] = o1 - Z;
+            if (lane == 0) {
+                part_ml[rec * 2] = M;
+                part_ml[rec * 2 + 1] = L;
+            }
         }
     }
 }
 
 // Part 2: one wave per (b, query head): combine the chunks that start before
-// len[b]; o = sum_c e^(M_c - M) O_c / sum_c e^(M_c - M) L_c, rounded to FP16
+// len[b]; o = sum_c 2^(M_c - M) O_c / sum_c 2^(M_c - M) L_c (maxima in log2
+// units), rounded to FP16
 // (a sequence of length 0 gives zeros).
 __global__ __launch_bounds__(kKvThreads) void k_kv4_attn_combine(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
@@ -391,7 +539,7 @@ __global__ __launch_bounds__(kKvThreads) void k_kv4_attn_combine(
     float L = 0.0f, o0 = 0.0f, o1 = 0.0f;
     for (int c = 0; c < used; ++c) {
         const size_t rec = (size_t)w * nchunks + c;
-        const float e = __expf(part_ml[rec * 2] - M);
+        const float e = __builtin_amdgcn_exp2f(part_ml[rec * 2] - M);
         L += e * part_ml[rec * 2 + 1];
         o0 += e * part_o[rec * kD + 2 * lane];
         o1 += e * part_o[rec * kD + 2 * lane + 1];
@@ -420,14 +568,22 @@ void launch_kv4_append(const uint16_t* k, const uint16_t* v, const uint16_t* lam
                        vq, vs, vz);
 }
 
-// Chunk length: the smallest of 64, 128, 256, 512 tokens (at least 16 per
-// wave) that keeps the number of chunks per sequence at or below 64 and still
-// gives at least 1024 workgroups when that is possible.
+// Chunk length: the sequence is cut into n = ceil(256 / (B H)) chunks (at
+// least one workgroup per compute unit; one chunk when B H >= 256, which
+// skips the combine kernel), each a multiple of 128 tokens so that every wave
+// takes whole 32-token steps.
+#ifdef QOQ_TUNING
+int64_t g_kv4_chunk = 0;
+extern "C" void qoq_tuning_force_kv4_chunk(int c) { g_kv4_chunk = c; }
+#endif
+
 int64_t kv4_chunk(int64_t B, int64_t H, int64_t Tcap) {
-    int64_t C = 64;
-    while (C < 512 && (B * H * ((Tcap + 2 * C - 1) / (2 * C)) >= 1024 || (Tcap + C - 1) / C > 64))
-        C *= 2;
-    return C;
+#ifdef QOQ_TUNING
+    if (g_kv4_chunk) return g_kv4_chunk;
+#endif
+    const int64_t bh = std::max<int64_t>(B * H, 1);
+    const int64_t n = std::min<int64_t>((256 + bh - 1) / bh, std::max<int64_t>((Tcap + 127) / 128, 1));
+    return std::max<int64_t>(((Tcap + n - 1) / n + 127) / 128 * 128, 128);
 }
 
 int64_t kv4_workspace_bytes(int64_t B, int64_t Hq, int64_t H, int64_t Tcap) {
@@ -449,12 +605,13 @@ void launch_kv4_decode_attention(const uint16_t* q, const uint16_t* lambda, cons
 #define QOQ_ATTN(GV)                                                                                 \
     hipLaunchKernelGGL((k_kv4_attn_chunk<GV>), dim3(grid), dim3(kAttnWaves * 64), 0, stream, q,     \
                        lambda, kq, ks, kz, vq, vs, vz, lens, (int)H, (int)Tcap, (int)C, (int)n, part_o, \
-                       part_ml)
+                       part_ml, o)
     if (G == 1) QOQ_ATTN(1);
     else if (G == 2) QOQ_ATTN(2);
     else if (G == 4) QOQ_ATTN(4);
     else QOQ_ATTN(8);
 #undef QOQ_ATTN
+    if (n == 1) return;  // part 1 wrote the output
     hipLaunchKernelGGL(k_kv4_attn_combine, dim3(blocks_of(B * Hq, kKvThreads / kWave)),
                        dim3(kKvThreads), 0, stream, part_o, part_ml, lens, (int)B, (int)Hq, (int)Tcap,
                        (int)C, (int)n, o);

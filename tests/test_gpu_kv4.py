@@ -136,6 +136,30 @@ def test_decode_attention_matches_oracle(B, Hq, H, Tcap, lens):
             assert not ob[b].any()
 
 
+def test_decode_attention_magnitudes():
+    """Queries from 1e-4 to 30 times unit size (flat to one-hot attention) and
+    value vectors whose ranges span four decades along the sequence, large ones
+    late: the kernel's power-of-two scalings of queries and weights and its
+    running maximum all move."""
+    B, Hq, H, Tcap = 2, 16, 4, 1024
+    lens = [1024, 700]
+    k, v = _kv(B, Tcap, H, 810)
+    rng = np.random.default_rng(811)
+    vf = 10.0 ** np.linspace(-3.0, 1.0, Tcap) * rng.uniform(0.5, 1.0, Tcap)
+    v = (v.astype(np.float32) * vf[None, :, None, None].astype(np.float32)).astype(np.float16)
+    qf = np.array([1e-4, 1e-2, 1.0, 3.0, 10.0, 30.0, 0.3, 1.0] * 2, np.float32)
+    q = (rng.standard_normal((B, Hq, D)).astype(np.float32) * qf[None, :, None]).astype(np.float16)
+    lam_w = oracle.kv4_smooth_scales(k.reshape(B * Tcap, H, D).view(np.uint16))
+    cache_w = oracle.kv4_quantize(k.view(np.uint16), v.view(np.uint16), lam_w)
+    print("kv4 attention magnitudes", flush=True)
+    cache = qoq.KV4Cache(B, H, Tcap, DEV, to_dev(lam_w, torch.float16))
+    cache.append(f16_dev(k.view(np.uint16)), f16_dev(v.view(np.uint16)), 0)
+    o = cache.attention(f16_dev(q.view(np.uint16)), torch.tensor(lens, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    ref = oracle.kv4_decode_attention(q.view(np.uint16), lam_w, cache_w, np.array(lens, np.int32))
+    _assert_attn_close(host_bits(o), ref, "magnitudes")
+
+
 def test_decode_attention_serving_shape():
     """Llama-3-8B decode at the pages' serving point (1024 input + 512 output
     tokens: the cache holds 1536 at the last step), 64 sequences, 32 query and 8
