@@ -451,7 +451,8 @@ def main(argv=None) -> int:
 # Decode attention at the pages' serving point (1024 input + 512 output tokens:
 # 1536 cached tokens at the last step), head dimension 128.
 KV4_SHAPES = (("llama3_8b_b64", 64, 32, 8, 1536), ("llama3_8b_b16", 16, 32, 8, 1536),
-              ("qwen15_72b_b16", 16, 64, 8, 1536))
+              ("qwen15_72b_b16", 16, 64, 64, 1536), ("hq64_h8_b16", 16, 64, 8, 1536),
+              ("llama3_8b_b16_t8192", 16, 32, 8, 8192))
 
 
 def kv4_compare(args, name, B, Hq, H, T):
