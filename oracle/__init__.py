@@ -81,6 +81,7 @@ def _load():
                 "orc_kv4_quantize": (I, [P, P, P, I64, I64, I64, I64, I64, P, P, P, P, P, P]),
                 "orc_kv4_decode_attention": (I, [P, P, P, P, P, P, P, P, P, I64, I64, I64, I64,
                                                  I64, P]),
+                "orc_rmsnorm": (I, [P, P, ctypes.c_float, I64, I64, P, P]),
             }
             for name, (res, args) in sigs.items():
                 fn = getattr(lib, name)
@@ -394,6 +395,28 @@ def silu_mul_quantize_act(gate_up_bits):
     h = silu_mul(gate_up_bits)
     xq, s_x, rowsum = quantize_act(h)
     return h, xq, s_x, rowsum
+
+
+# --- RMSNorm producer (reading R17) -------------------------------------------
+
+def rmsnorm(x_bits, gamma_bits, eps, want_r=False):
+    """x [M, K] FP16 bits, gamma [K] FP16 bits, eps > 0 -> y [M, K] FP16 bits
+    (and r [M] float32 when want_r)."""
+    x = _c(x_bits, np.uint16)
+    M, K = x.shape
+    y = np.empty((M, K), np.uint16)
+    r = np.empty((M,), np.float32)
+    _check(_load().orc_rmsnorm(_p(x), _p(_c(gamma_bits, np.uint16)), eps, M, K, _p(y), _p(r)),
+           "rmsnorm")
+    return (y, r) if want_r else y
+
+
+def rmsnorm_quantize_act(x_bits, gamma_bits, eps):
+    """The fused producer: (y, xq, s_x, rowsum) with y = rmsnorm(x) and
+    (xq, s_x, rowsum) = quantize_act(y)."""
+    y = rmsnorm(x_bits, gamma_bits, eps)
+    xq, s_x, rowsum = quantize_act(y)
+    return y, xq, s_x, rowsum
 
 
 # --- KV4 decode attention with SmoothAttention (reading R16) ---------------

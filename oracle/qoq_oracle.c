@@ -62,6 +62,8 @@
  *   R16 KV4 attention: SmoothAttention scales per (KV head, channel) from
  *       calibration keys, FP16 queries multiplied by them, one asymmetric
  *       UINT4 range per (token, head) vector for keys and values.
+ *   R17 the RMSNorm producer of a GEMM input: the exact sum of squares,
+ *       each later step one IEEE operation (orc_rmsnorm below).
  *
  * Inputs must be finite FP16 (passed as raw binary16 bits).
  */
@@ -856,6 +858,48 @@ int orc_kv4_decode_attention(const uint16_t* q, const uint16_t* lambda, const ui
             }
         free(qs);
         free(sc);
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* RMSNorm producer of a GEMM input (reading R17). The GEMM's FP16 outputs  */
+/* feed the next layer's norm, whose output is quantized per token to INT8  */
+/* for the next GEMM ("QServe Guide: W4A8KV4 Quantization for LLM Serving", */
+/* "High-Throughput Native INT8 Tensor Core GEMMs" and "Deep Dive" part 1). */
+/* The pages do not give the norm; the models they serve use RMSNorm,       */
+/*   y_k = x_k / sqrt(mean_k(x_k^2) + eps) * gamma_k,                        */
+/* made exact here so that the INT8 codes downstream are unique:           */
+/*   S  = sum_k x_k^2, exactly (each FP16 x_k = M 2^(e - 24) squares to an   */
+/*        integer multiple of 2^-48; the sum is kept in 128 bits)           */
+/*   ms = f32( f64(S) / K )      S rounded to fp64, fp64 division, to fp32  */
+/*   r  = 1 / sqrt(ms + eps)     fp32 add, fp32 sqrt, fp32 division         */
+/*   y_k = f16( (x_k * r) * gamma_k )   two fp32 products, then FP16        */
+/* with every rounding to nearest even. r is returned per row when r_out is */
+/* not NULL. eps > 0.                                                       */
+/* ------------------------------------------------------------------------ */
+int orc_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, int64_t M, int64_t K,
+                uint16_t* y, float* r_out) {
+    if (M < 0 || K < 1 || !(eps > 0.0f) || isinf(eps)) return ORC_ERR_SHAPE;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t* row = x + m * K;
+        unsigned __int128 S = 0;  /* in units of 2^-48 */
+        for (int64_t k = 0; k < K; ++k) {
+            const unsigned e = (row[k] >> 10) & 31u, f = row[k] & 1023u;
+            const uint64_t mant = e ? (1024u | f) : f;   /* |x| = mant * 2^(max(e,1) - 25) */
+            const unsigned shift = 2u * (e ? e - 1u : 0u); /* x^2 = mant^2 * 2^(shift - 48) */
+            S += (unsigned __int128)(mant * mant) << shift;
+        }
+        const double s64 = (double)S * 0x1p-48;
+        const float ms = (float)(s64 / (double)K);
+        const float v = ms + eps;
+        const float r = 1.0f / sqrtf(v);
+        if (r_out) r_out[m] = r;
+        for (int64_t k = 0; k < K; ++k) {
+            const float t = f16_to_f32(row[k]) * r;
+            y[m * K + k] = orc_f32_to_f16(t * f16_to_f32(gamma[k]));
+        }
     }
     return ORC_OK;
 }

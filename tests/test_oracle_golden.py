@@ -263,3 +263,26 @@ def test_silu_mul_golden():
         want[int(k)] = v
     np.testing.assert_array_equal(xq[-1], want)
     assert rowsum[-1] == qr["rowsum"]
+
+
+def _row(spec, K, dtype):
+    v = np.full(K, spec.get("default", 0), dtype)
+    if "even" in spec:
+        v[0::2] = spec["even"]
+        v[1::2] = spec["odd"]
+    for k, val in spec.get("at", {}).items():
+        v[int(k)] = val
+    return v
+
+
+def test_rmsnorm_golden():
+    """RMSNorm rows whose sums of squares and means are exact, with the fp32
+    square root, reciprocal and products rounded by hand (rmsnorm.json)."""
+    d = _load("rmsnorm.json")
+    K = d["K"]
+    for c in d["cases"]:
+        x = _row(c["x"], K, np.float16).view(np.uint16)[None]
+        g = _row(c["gamma"], K, np.float16).view(np.uint16)
+        y, r = oracle.rmsnorm(x, g, c["eps"], want_r=True)
+        assert r.view(np.uint32)[0] == c["r_bits"], (c["name"], r.view(np.uint32)[0])
+        np.testing.assert_array_equal(y[0], _row(c["y_bits"], K, np.uint16), err_msg=c["name"])

@@ -660,3 +660,84 @@ def _kv4_errors_with_and_without_smoothing(outliers):
         o = oracle.kv4_decode_attention(q.view(np.uint16), lam, c, lens)
         errs.append(np.linalg.norm(o - ref) / np.linalg.norm(ref))
     return errs
+
+
+# --- RMSNorm producer (reading R17) ------------------------------------------
+
+def _rms_rows(rng, M, K, wide=True):
+    """FP16 rows; with wide=True they mix subnormals, ordinary values, zeros and
+    values near the FP16 maximum, so the exact sum of squares spans its range."""
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    if wide:
+        e = rng.integers(-24, 16, size=(M, K)).astype(np.float32)
+        x = np.sign(x) * np.exp2(e) * rng.uniform(1.0, 1.99, size=(M, K)).astype(np.float32)
+        x[rng.random((M, K)) < 0.1] = 0.0
+        x = np.clip(x, -65504, 65504)
+    return x.astype(np.float16)
+
+
+def _exact_r(x16, eps):
+    """1 / sqrt(S/K + eps) from the exact sum of squares S (Python fractions)."""
+    from fractions import Fraction
+    out = []
+    for row in x16.astype(np.float64):
+        S = sum(Fraction(float(v)) ** 2 for v in row)
+        out.append(1.0 / np.sqrt(float(S / len(row)) + float(eps)))
+    return np.array(out)
+
+
+@pytest.mark.parametrize("K,wide", [(1, True), (3, True), (128, True), (4096, True), (4096, False)])
+def test_rmsnorm_scale_and_outputs_within_rounding_of_exact(K, wide):
+    """r is within a few fp32 roundings of 1/sqrt(mean(x^2) + eps) computed from
+    the exact sum of squares (which pins the 128-bit sum over subnormals and
+    values near 65504 alike), and each y within half an FP16 step of
+    x * gamma * r_exact plus those roundings."""
+    rng = np.random.default_rng(900 + K)
+    M = 6
+    x = _rms_rows(rng, M, K, wide)
+    gamma = rng.uniform(0.25, 2.0, size=K).astype(np.float16)
+    eps = np.float32(1e-5)
+    y, r = oracle.rmsnorm(x.view(np.uint16), gamma.view(np.uint16), float(eps), want_r=True)
+    r_ex = _exact_r(x, eps)
+    assert np.all(np.abs(r.astype(np.float64) - r_ex) <= r_ex * 2.0**-21)
+    want = x.astype(np.float64) * gamma.astype(np.float64)[None] * r_ex[:, None]
+    got = y.view(np.float16).astype(np.float64)
+    half_step = 0.5 * np.spacing(np.abs(want).astype(np.float16)).astype(np.float64)
+    assert np.all(np.abs(got - want) <= half_step + np.abs(want) * 2.0**-20)
+
+
+def test_rmsnorm_power_of_two_invariance():
+    """Scaling a row by 2^j scales S by 4^j and r by 2^-j exactly (every step
+    rounds the same way at another exponent), so y does not change at all."""
+    rng = np.random.default_rng(910)
+    x = rng.uniform(0.05, 50.0, size=(5, 512)).astype(np.float32)
+    x *= np.where(rng.random(x.shape) < 0.5, -1.0, 1.0)
+    x16 = x.astype(np.float16)
+    gamma = rng.uniform(0.5, 1.5, size=512).astype(np.float16).view(np.uint16)
+    y0 = oracle.rmsnorm(x16.view(np.uint16), gamma, 1e-30)
+    for j in (-3, 4):
+        xs = (x16.astype(np.float32) * np.float32(2.0**j)).astype(np.float16)
+        assert np.array_equal(xs.astype(np.float32), x16.astype(np.float32) * np.float32(2.0**j))
+        np.testing.assert_array_equal(oracle.rmsnorm(xs.view(np.uint16), gamma, 1e-30), y0)
+
+
+@pytest.mark.parametrize("K", [128, 4096, 14336])
+def test_rmsnorm_single_input_closed_form(K):
+    """One nonzero input a: mean(x^2) = a^2 / K, so y = sign(a) sqrt(K) gamma at
+    that position (to FP16 and fp32 rounding) and 0 elsewhere."""
+    x = np.zeros((3, K), np.float16)
+    x[0, 5], x[1, K - 1], x[2, 0] = 3.5, -0.001, 1000.0
+    gamma = np.full(K, np.float16(0.5))
+    y = oracle.rmsnorm(x.view(np.uint16), gamma.view(np.uint16), 1e-30).view(np.float16)
+    for m, (pos, sgn) in enumerate([(5, 1), (K - 1, -1), (0, 1)]):
+        want = sgn * np.sqrt(K) * 0.5
+        assert abs(float(y[m, pos]) - want) <= abs(want) * 2.0**-10
+        assert np.count_nonzero(y[m].astype(np.float32)) == 1
+
+
+def test_rmsnorm_rejects_bad_eps():
+    x = np.zeros((1, 128), np.uint16)
+    g = np.zeros(128, np.uint16)
+    for eps in (0.0, -1.0, float("inf"), float("nan")):
+        with pytest.raises(Exception):
+            oracle.rmsnorm(x, g, eps)
