@@ -69,9 +69,10 @@
 extern "C" {
 #endif
 
-#define QOQ_ABI_VERSION 3
+#define QOQ_ABI_VERSION 4
 #define QOQ_GROUP 128
 #define QOQ_MAX_K 132096
+#define QOQ_RMSNORM_MAX_K 32768 /* row length of qoq_rmsnorm_quantize_act */
 
 typedef enum {
     QOQ_MODE_G128 = 0,        /* progressive: INT8 [-119,119] per channel, then g128 UINT4 */
@@ -283,6 +284,27 @@ qoq_status qoq_w8a8_gemm(const int8_t* xq, const uint16_t* s_x, const void* blob
  */
 qoq_status qoq_silu_mul_quantize_act(const uint16_t* gate_up, int64_t M, int64_t I, int8_t* xq,
                                      uint16_t* s_x, int32_t* rowsum, uint16_t* h, void* stream);
+
+/*
+ * qoq_rmsnorm_quantize_act: the other producer of a GEMM input. ([GUIDE]
+ * "High-Throughput Native INT8 Tensor Core GEMMs": the GEMM's FP16 output goes
+ * on to the next layer norm; Deep Dive part 1: the GEMM input is quantized per
+ * token.) The pages do not write the norm out; this is the RMSNorm of the
+ * models they serve, made exact so that the codes are unique:
+ *   x [M, K] FP16 row-major, gamma [K] FP16, eps > 0 (finite fp32)
+ *   S    = sum_k x[m,k]^2, exactly (every FP16 square is a multiple of 2^-48)
+ *   ms   = f32( f64(S) / K )            S rounded to fp64, fp64 division
+ *   r    = 1 / sqrt(ms + eps)           fp32 add, square root, division
+ *   y[m,k] = f16( (x[m,k] * r) * gamma[k] )   two fp32 products
+ *   then xq, s_x, rowsum exactly as qoq_quantize_act(y, M, K, ...), every
+ *   rounding to nearest even. y [M, K] FP16 receives y when not NULL.
+ *   K follows the K rules and is at most QOQ_RMSNORM_MAX_K; x, gamma finite,
+ *   with |gamma| small enough that y stays finite (|y| <= |gamma| sqrt(K)).
+ *   eps <= 0, infinite or NaN gives QOQ_ERR_SHAPE.
+ */
+qoq_status qoq_rmsnorm_quantize_act(const uint16_t* x, const uint16_t* gamma, float eps, int64_t M,
+                                   int64_t K, int8_t* xq, uint16_t* s_x, int32_t* rowsum,
+                                   uint16_t* y, void* stream);
 
 /*
  * ---- KV4 decode attention with SmoothAttention -----------------------------

@@ -45,6 +45,7 @@ EXPORTED = (
     "qoq_w8a8_gemm",
     "qoq_w4a16_gemm",
     "qoq_silu_mul_quantize_act",
+    "qoq_rmsnorm_quantize_act",
     "qoq_kv4_smooth_scales",
     "qoq_kv4_append",
     "qoq_kv4_attention_workspace_bytes",
@@ -90,6 +91,7 @@ def load_library():
             "qoq_w8a8_gemm": (I, [P, P, P, P, I64, I64, I64, P, P, P, I64, P]),
             "qoq_w4a16_gemm": (I, [I, P, P, P, I64, I64, I64, P, P, P]),
             "qoq_silu_mul_quantize_act": (I, [P, I64, I64, P, P, P, P, P]),
+            "qoq_rmsnorm_quantize_act": (I, [P, P, ctypes.c_float, I64, I64, P, P, P, P, P]),
             "qoq_kv4_smooth_scales": (I, [P, I64, I64, I64, P, P]),
             "qoq_kv4_append": (I, [P, P, P, I64, I64, I64, I64, I64, I64, P, P, P, P, P, P, P]),
             "qoq_kv4_attention_workspace_bytes": (I64, [I64, I64, I64, I64, I64]),
@@ -268,6 +270,35 @@ def qoq_silu_mul_quantize_act(gate_up: torch.Tensor, xq=None, s_x=None, rowsum=N
     st = load_library().qoq_silu_mul_quantize_act(_ptr(gate_up), M, I, _ptr(xq), _ptr(s_x),
                                                   _ptr(rowsum), _ptr(h), _stream(gate_up))
     _check(st, "qoq_silu_mul_quantize_act")
+    return xq, s_x, rowsum
+
+
+def qoq_rmsnorm_quantize_act(x: torch.Tensor, gamma: torch.Tensor, eps: float, xq=None, s_x=None,
+                             rowsum=None, want_rowsum: bool = True, y=None):
+    """x [M, K] fp16, gamma [K] fp16, eps > 0 -> (xq, s_x, rowsum | None) of
+    y = f16((x * r) * gamma), r = 1 / sqrt(mean(x^2) + eps) (the exact sum of
+    squares); the same outputs as qoq_quantize_act(y). y (fp16 [M, K]) is
+    written too when given."""
+    _need(x, torch.float16, "x")
+    M, K = x.shape
+    _need(gamma, torch.float16, "gamma", (K,))
+    dev = x.device
+    nbytes = qoq_act_bytes(M, K)
+    if nbytes < 0:
+        raise QoQError(f"qoq_rmsnorm_quantize_act: unsupported shape M={M} K={K}")
+    xq = xq if xq is not None else torch.empty((nbytes,), dtype=torch.int8, device=dev)
+    s_x = s_x if s_x is not None else torch.empty((M,), dtype=torch.float16, device=dev)
+    if rowsum is None and want_rowsum:
+        rowsum = torch.empty((M,), dtype=torch.int32, device=dev)
+    _need(xq, torch.int8, "xq", (nbytes,))
+    _need(s_x, torch.float16, "s_x", (M,))
+    if rowsum is not None:
+        _need(rowsum, torch.int32, "rowsum", (M,))
+    if y is not None:
+        _need(y, torch.float16, "y", (M, K))
+    st = load_library().qoq_rmsnorm_quantize_act(_ptr(x), _ptr(gamma), float(eps), M, K, _ptr(xq),
+                                                 _ptr(s_x), _ptr(rowsum), _ptr(y), _stream(x))
+    _check(st, "qoq_rmsnorm_quantize_act")
     return xq, s_x, rowsum
 
 

@@ -6,6 +6,8 @@
 #include "qoq.h"
 #include "qoq_launch.hpp"
 
+#include <cmath>
+
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -196,6 +198,21 @@ qoq_status qoq_silu_mul_quantize_act(const uint16_t* gate_up, int64_t M, int64_t
         return QOQ_ERR_ALIGN;
     return launch_checked([&] {
         qoq::launch_silu_mul_quantize_act(gate_up, M, I, xq, s_x, rowsum, h, as_stream(stream));
+    });
+}
+
+qoq_status qoq_rmsnorm_quantize_act(const uint16_t* x, const uint16_t* gamma, float eps, int64_t M,
+                                   int64_t K, int8_t* xq, uint16_t* s_x, int32_t* rowsum,
+                                   uint16_t* y, void* stream) {
+    if (M < 0 || M > INT32_MAX - 15 || !valid_k(K) || K > QOQ_RMSNORM_MAX_K) return QOQ_ERR_SHAPE;
+    if (!(eps > 0.0f) || !std::isfinite(eps)) return QOQ_ERR_SHAPE;
+    if (M == 0) return QOQ_OK;
+    if (!x || !gamma || !xq || !s_x) return QOQ_ERR_NULL;
+    if (!aligned16(x) || !aligned16(gamma) || !aligned16(xq) || !aligned16(s_x) ||
+        (rowsum && !aligned16(rowsum)) || (y && !aligned16(y)))
+        return QOQ_ERR_ALIGN;
+    return launch_checked([&] {
+        qoq::launch_rmsnorm_quantize_act(x, gamma, eps, M, K, xq, s_x, rowsum, y, as_stream(stream));
     });
 }
 

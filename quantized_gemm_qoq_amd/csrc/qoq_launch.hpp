@@ -24,6 +24,9 @@ void launch_unpack(int mode, const uint8_t* blob, int64_t N, int64_t K, uint8_t*
 // Fused producer of the down projection's input: h = f16(SiLU(gate) * up)
 // from gate_up [M, 2I], then the per-token quantization of launch_quantize_act
 // (same outputs); h [M, I] is written when not null.
+void launch_rmsnorm_quantize_act(const uint16_t* x, const uint16_t* gamma, float eps, int64_t M,
+                                 int64_t K, int8_t* xq, uint16_t* s_x, int32_t* rowsum,
+                                 uint16_t* y, hipStream_t stream);
 void launch_silu_mul_quantize_act(const uint16_t* gate_up, int64_t M, int64_t I, int8_t* xq,
                                   uint16_t* s_x, int32_t* rowsum, uint16_t* h,
                                   hipStream_t stream);

@@ -1,4 +1,5 @@
-// quantize.hip -- per-token INT8 activation quantization and the offline
+// quantize.hip -- per-token INT8 activation quantization, its fused producers
+// (SiLU(gate) * up and RMSNorm in front of the quantization), and the offline
 // weight quantizers (progressive g128 and per-channel UINT4, and the INT8
 // weights of the W8A8 sibling), for gfx950.
 //
@@ -433,6 +434,154 @@ __global__ __launch_bounds__(THR) void k_silu_quant_reg(const uint16_t* __restri
     }
 }
 
+// ---------------------------------------------------------------------------
+// RMSNorm producer of a GEMM input: y = f16((x * r) * gamma) with
+// r = 1 / sqrt(f32(f64(S) / K) + eps), S the exact sum of squares of the
+// row, then the per-token INT8 quantization of y exactly as
+// k_quantize_act_reg does it. Each FP16 x = M 2^(e - 24) squares to an
+// integer multiple of 2^-48, so S is kept exactly as a 128-bit integer
+// (K <= 32768 values below 2^80) and the rounding of the mean is unique,
+// which makes y, and with it every code, independent of the summation order.
+// The fp64 division, the fp32 square root and the fp32 reciprocal are
+// correctly rounded, the products separate fp32 multiplies.
+__device__ __forceinline__ unsigned __int128 square_fp16(uint32_t bits) {
+    const uint32_t e = (bits >> 10) & 31u, f = bits & 1023u;
+    const uint32_t mant = e ? (f | 1024u) : f;  // |x| = mant 2^(max(e, 1) - 25)
+    const uint32_t shift = e ? 2u * (e - 1u) : 0u;
+    return (unsigned __int128)(mant * mant) << shift;  // x^2 in units of 2^-48
+}
+
+struct SumU128 {
+    __device__ unsigned __int128 operator()(unsigned __int128 v) const {
+        uint64_t lo = (uint64_t)v, hi = (uint64_t)(v >> 64);
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            const uint64_t olo = __shfl_xor(lo, o, kWave), ohi = __shfl_xor(hi, o, kWave);
+            const uint64_t nlo = lo + olo;
+            hi += ohi + (nlo < lo ? 1u : 0u);
+            lo = nlo;
+        }
+        return ((unsigned __int128)hi << 64) | lo;
+    }
+    __device__ unsigned __int128 combine(unsigned __int128 a, unsigned __int128 b) const { return a + b; }
+};
+
+// y of 8 inputs (one 16-byte vector of x and of gamma)
+__device__ __forceinline__ u32x4 rms_scale8(u32x4 xv, u32x4 gv, float r) {
+    u32x4 out;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        float lo = (h2f(xv[e] & 0xFFFFu) * r) * h2f(gv[e] & 0xFFFFu);
+        float hi = (h2f(xv[e] >> 16) * r) * h2f(gv[e] >> 16);
+        // keep the fp32 product: the backend would otherwise form one
+        // mixed-precision multiply rounding straight to FP16
+        asm("" : "+v"(lo), "+v"(hi));
+        out[e] = (uint32_t)f2h(lo) | ((uint32_t)f2h(hi) << 16);
+    }
+    return out;
+}
+
+// Row held in registers (CH runs of 16 inputs per thread, THR threads per
+// row), K <= 16 * THR * CH; y (FP16 [M, K]) is written too when asked for.
+template <int THR, int CH>
+__global__ __launch_bounds__(THR) void k_rmsnorm_quant_reg(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ gamma,
+                                                          float eps, int M, int K,
+                                                          int8_t* __restrict__ xq,
+                                                          uint16_t* __restrict__ s_x,
+                                                          int32_t* __restrict__ rowsum,
+                                                          uint16_t* __restrict__ y_out) {
+    constexpr int kNW = THR / kWave;
+    __shared__ unsigned __int128 red_s[kNW];
+    __shared__ unsigned red_u[kNW];
+    __shared__ int red_i[kNW];
+    const int m = blockIdx.x;
+    const int U = gridDim.x / 16;
+    const int u = m / 16, rr = m % 16;
+    const int nchunk = K / 16;
+    u32x4* out = reinterpret_cast<u32x4*>(xq);
+    auto slot = [&](int c) {
+        const int g = c / 8, s = (c / 4) % 2, j = c % 4;
+        return ((size_t)g * U + u) * 128 + 64 * s + 16 * j + rr;
+    };
+    if (m >= M) {
+        for (int c = threadIdx.x; c < nchunk; c += THR) out[slot(c)] = u32x4{0u, 0u, 0u, 0u};
+        return;
+    }
+    const u32x4* xrow = reinterpret_cast<const u32x4*>(x + (size_t)m * K);
+    const u32x4* grow = reinterpret_cast<const u32x4*>(gamma);
+    u32x4* yrow = y_out ? reinterpret_cast<u32x4*>(y_out + (size_t)m * K) : nullptr;
+    u32x4 v0[CH], v1[CH];
+    unsigned __int128 S = 0;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int c = threadIdx.x + THR * i;
+        v0[i] = u32x4{0u, 0u, 0u, 0u};
+        v1[i] = u32x4{0u, 0u, 0u, 0u};
+        if (c < nchunk) {
+            v0[i] = xrow[2 * c];
+            v1[i] = xrow[2 * c + 1];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            S += square_fp16(v0[i][e] & 0xFFFFu) + square_fp16(v0[i][e] >> 16);
+            S += square_fp16(v1[i][e] & 0xFFFFu) + square_fp16(v1[i][e] >> 16);
+        }
+    }
+    S = block_reduce<unsigned __int128, SumU128, kNW>(S, red_s, SumU128{});
+    const double s64 = (double)S * 0x1p-48;
+    const float ms = (float)(s64 / (double)K);
+    const float r = 1.0f / sqrtf(ms + eps);
+
+    unsigned amax = 0;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int c = threadIdx.x + THR * i;
+        if (c < nchunk) {
+            v0[i] = rms_scale8(v0[i], grow[2 * c], r);
+            v1[i] = rms_scale8(v1[i], grow[2 * c + 1], r);
+            if (yrow) {
+                yrow[2 * c] = v0[i];
+                yrow[2 * c + 1] = v1[i];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            amax = max(amax, max(absmax_bits2(v0[i][e]), absmax_bits2(v1[i][e])));
+    }
+    amax = block_reduce<unsigned, MaxU, kNW>(amax, red_u, MaxU{});
+    const uint16_t sbits = f2h(h2f(amax) / 127.0f);
+    const float sf = h2f(sbits);
+
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int c = threadIdx.x + THR * i;
+        if (c < nchunk) {
+            u32x4 o = u32x4{0u, 0u, 0u, 0u};
+            if (sf != 0.0f) {
+                const uint32_t w[8] = {v0[i][0], v0[i][1], v0[i][2], v0[i][3],
+                                       v1[i][0], v1[i][1], v1[i][2], v1[i][3]};
+                uint32_t packed[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const uint32_t hb = (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu);
+                    const int q = quant_act1(hb, sf);
+                    sum += q;
+                    packed[e >> 2] |= (uint32_t)(q & 0xFF) << (8 * (e & 3));
+                }
+                o = u32x4{packed[0], packed[1], packed[2], packed[3]};
+            }
+            out[slot(c)] = o;
+        }
+    }
+    if (rowsum) sum = block_reduce<int, SumI, kNW>(sum, red_i, SumI{});
+    if (threadIdx.x == 0) {
+        s_x[m] = sbits;
+        if (rowsum) rowsum[m] = sum;
+    }
+}
+
 // Larger I: two passes over the gate_up row (the second recomputes h).
 __global__ __launch_bounds__(kThreads) void k_silu_quant(const uint16_t* __restrict__ gu, int M,
                                                          int I, int8_t* __restrict__ xq,
@@ -553,6 +702,21 @@ void launch_silu_mul_quantize_act(const uint16_t* gate_up, int64_t M, int64_t I,
         hipLaunchKernelGGL(k_silu_quant, dim3(mp), dim3(kThreads), 0, stream, gate_up, (int)M,
                            (int)I, xq, s_x, rowsum, h);
 #undef QOQ_SQ
+}
+
+void launch_rmsnorm_quantize_act(const uint16_t* x, const uint16_t* gamma, float eps, int64_t M,
+                                 int64_t K, int8_t* xq, uint16_t* s_x, int32_t* rowsum,
+                                 uint16_t* y, hipStream_t stream) {
+    const unsigned mp = (unsigned)((M + 15) / 16 * 16);
+    const int64_t runs = K / 16;
+#define QOQ_RQ(THRV, CHV)                                                                      \
+    hipLaunchKernelGGL((k_rmsnorm_quant_reg<THRV, CHV>), dim3(mp), dim3(THRV), 0, stream, x,      \
+                       gamma, eps, (int)M, (int)K, xq, s_x, rowsum, y)
+    if (runs <= 256) QOQ_RQ(256, 1);
+    else if (runs <= 512) QOQ_RQ(256, 2);
+    else if (runs <= 1024) QOQ_RQ(1024, 1);
+    else QOQ_RQ(1024, 2);  // K <= 32768, checked by the caller
+#undef QOQ_RQ
 }
 
 void launch_quantize_weights_w8(const uint16_t* w, int64_t N, int64_t K, int8_t* q, uint16_t* s_c,

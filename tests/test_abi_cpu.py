@@ -192,6 +192,20 @@ def test_silu_mul_quantize_validation(lib):
     assert f(A, 4, 128, A, A, A, U, NUL) == ERR_ALIGN
 
 
+def test_rmsnorm_quantize_validation(lib):
+    f = lib.qoq_rmsnorm_quantize_act
+    assert f(A, A, 1e-5, 0, 128, A, A, A, NUL, NUL) == OK
+    assert f(A, A, 1e-5, -1, 128, A, A, A, NUL, NUL) == ERR_SHAPE
+    assert f(A, A, 1e-5, 4, 100, A, A, A, NUL, NUL) == ERR_SHAPE
+    assert f(A, A, 1e-5, 4, 32768 + 128, A, A, A, NUL, NUL) == ERR_SHAPE  # row longer than the limit
+    for eps in (0.0, -1e-5, float("inf"), float("nan")):
+        assert f(A, A, eps, 4, 128, A, A, A, NUL, NUL) == ERR_SHAPE
+    assert f(NUL, A, 1e-5, 4, 128, A, A, A, NUL, NUL) == ERR_NULL
+    assert f(A, NUL, 1e-5, 4, 128, A, A, A, NUL, NUL) == ERR_NULL
+    assert f(A, U, 1e-5, 4, 128, A, A, A, NUL, NUL) == ERR_ALIGN
+    assert f(A, A, 1e-5, 4, 128, A, A, A, U, NUL) == ERR_ALIGN
+
+
 def test_kv4_validation(lib):
     f = lib.qoq_kv4_smooth_scales
     assert f(A, 4, 8, 64, A, NUL) == ERR_SHAPE  # head dimension must be 128
