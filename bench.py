@@ -420,6 +420,15 @@ def main(argv=None) -> int:
                     if isinstance(out, int):
                         return out
                     print(json.dumps(out), flush=True)
+        seen = set()
+        for wl2 in workloads.WORKLOADS.values():
+            for layer2 in wl2.layers:
+                if ("qkv" in layer2.name or "gate_up" in layer2.name) and (layer2.M, layer2.K) not in seen:
+                    seen.add((layer2.M, layer2.K))
+                    out = rmsnorm_compare(args, layer2)
+                    if isinstance(out, int):
+                        return out
+                    print(json.dumps(out), flush=True)
         return 0
     if args.formats:
         todo = [(w, l) for w in (workloads.WORKLOADS.values() if args.all_layers else [wl])
@@ -579,6 +588,66 @@ def producer_compare(args, layer):
     f_bytes = 4 * M * I + M * I + 6 * M  # read gate_up, write codes, scale, row sum
     return {"layer": layer.name, "M": M, "I": I, "fused_us": round(f_us, 3),
             "unfused_us": round(u_us, 3), "speedup": round(u_us / f_us, 2),
+            "fused_GBs": round(f_bytes / f_us / 1e3, 1),
+            "fused_frac_of_hbm": round(f_bytes / f_us / 1e3 / HBM_PEAK_GBS, 3)}
+
+
+def rmsnorm_compare(args, layer, eps=1e-5):
+    """Fused RMSNorm + per-token quantization vs torch's FP16 rms_norm writing
+    y and then qoq_quantize_act, for the input [M, K] of a qkv or gate_up
+    layer (x synthetic N(0,1) FP16, gamma U(0.5, 1.5)). HBM figures over
+    rotating copies."""
+    import torch
+
+    import quantized_gemm_qoq_amd as qoq
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 3
+    dev = torch.device("cuda:0")
+    M, K = layer.M, layer.K
+    g = torch.Generator(device="cpu")
+    g.manual_seed(layer.seed + 77)
+    x = torch.randn(M, K, generator=g).to(torch.float16).to(dev)
+    gamma = (torch.rand(K, generator=g) + 0.5).to(torch.float16).to(dev)
+    per = 2 * M * K * 2 + M * K
+    R = max(2, math.ceil(args.rotate_mib * 2**20 / per))
+    sets = [{"x": x.clone(), "y": torch.empty((M, K), dtype=torch.float16, device=dev),
+             "xq": torch.empty((qoq.qoq_act_bytes(M, K),), dtype=torch.int8, device=dev),
+             "s_x": torch.empty((M,), dtype=torch.float16, device=dev),
+             "rs": torch.empty((M,), dtype=torch.int32, device=dev)} for _ in range(R)]
+    L = max(R, args.kernel_launches // R * R)
+
+    def fused(st):
+        qoq.qoq_rmsnorm_quantize_act(st["x"], gamma, eps, st["xq"], st["s_x"], st["rs"])
+
+    def unfused(st):
+        st["y"].copy_(torch.nn.functional.rms_norm(st["x"], (K,), gamma, eps))
+        qoq.qoq_quantize_act(st["y"], st["xq"], st["s_x"], st["rs"])
+
+    def avg_us(fn):
+        for st in sets[:2]:
+            fn(st)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for i in range(L):
+                fn(sets[i % R])
+        gr.replay()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        gr.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / L
+
+    f_us, u_us = avg_us(fused), avg_us(unfused)
+    f_bytes = 2 * M * K + 2 * K + M * K + 6 * M  # read x and gamma, write codes, scale, row sum
+    return {"producer": "rmsnorm", "layer_input_of": layer.name, "M": M, "K": K,
+            "fused_us": round(f_us, 3), "unfused_us": round(u_us, 3), "speedup": round(u_us / f_us, 2),
             "fused_GBs": round(f_bytes / f_us / 1e3, 1),
             "fused_frac_of_hbm": round(f_bytes / f_us / 1e3 / HBM_PEAK_GBS, 3)}
 
