@@ -713,11 +713,6 @@ __global__ __launch_bounds__(W * 64) void k_gemm_stream(
 
     constexpr bool kG128 = Fmt<F>::kG128;
     constexpr int kV = Fmt<F>::kVec;
-    for (int i = threadIdx.x; i < kPairs * 4 * kWave; i += kThr) red[i] = 0;
-    if (kG128)
-        for (int i = threadIdx.x; i < 256; i += kThr) lut[i] = group_word((uint32_t)i);
-    __syncthreads();
-
     const int g0 = G * wave / W;
     const int count = G * (wave + 1) / W - g0;
 
@@ -753,10 +748,36 @@ __global__ __launch_bounds__(W * 64) void k_gemm_stream(
     uint32_t pq[R][NT];
     int32x4 aq[R][MB][2];
     const int main_count = count / R * R;
+    // The ring's first loads go out before anything else: the LDS set-up and
+    // the epilogue's scale loads then overlap their latency.
 #pragma unroll
     for (int r = 0; r < R - 1; ++r)
         stream_load<F, MB, NT>(bq[r], pq[r], aq[r], rb, rp, ra, b_off, p_off, a_off, r,
-                                   r < main_count, a_step);
+                               r < main_count, a_step);
+    // Operands of this wave's epilogue pairs (p = wave + e W), read now so
+    // that the stores at the end wait on no global load.
+    constexpr int kEp = (kPairs + W - 1) / W;
+    float ep_sc[kEp], ep_sx[kEp][4];
+    int ep_z[kEp], ep_rs[kEp][4];
+#pragma unroll
+    for (int e = 0; e < kEp; ++e) {
+        const int p = wave + e * W;
+        const int t = min(nb * NT + min(p, kPairs - 1) / MB, tiles - 1);
+        const int n = 16 * t + c;
+        const int mrow = 16 * (u0 + min(p, kPairs - 1) % MB) + 4 * j;
+        ep_sc[e] = h2f(s_c[n]);
+        ep_z[e] = Fmt<F>::kZp ? (int)blob[code_bytes + n] : 0;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int m = min(mrow + v, M - 1);
+            ep_sx[e][v] = h2f(s_x[m]);
+            ep_rs[e][v] = Fmt<F>::kZp ? rowsum[m] : 0;
+        }
+    }
+    for (int i = threadIdx.x; i < kPairs * 4 * kWave; i += kThr) red[i] = 0;
+    if (kG128)
+        for (int i = threadIdx.x; i < 256; i += kThr) lut[i] = group_word((uint32_t)i);
+    __syncthreads();
     for (int h = 0; h < main_count; h += R) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -783,18 +804,26 @@ __global__ __launch_bounds__(W * 64) void k_gemm_stream(
                 atomicAdd(&red[((i * MB + mb) * 4 + v) * kWave + lane], acc[i][mb][v]);
     __syncthreads();
 
-    const uint8_t* pc_z = blob + code_bytes;
-    for (int p = wave; p < kPairs; p += W) {
+#pragma unroll
+    for (int e = 0; e < kEp; ++e) {
+        const int p = wave + e * W;
+        if (p >= kPairs) break;
         const int i = p / MB, mb = p % MB;
         const int t = nb * NT + i;
         if (t >= tiles) continue;
         const int n = 16 * t + c;
-        int32x4 a;
+        const int m_first = 16 * (u0 + mb) + 4 * j;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) a[v] = red[(p * 4 + v) * kWave + lane];
-        const int zpc = Fmt<F>::kZp ? (int)pc_z[n] : 0;
-        store_outputs<F>(a, 16 * (u0 + mb) + 4 * j, n, M, N, s_x, rowsum, h2f(s_c[n]), zpc,
-                             y, acc_out);
+        for (int v = 0; v < 4; ++v) {
+            const int m = m_first + v;
+            if (m < M) {
+                int r = red[(p * 4 + v) * kWave + lane];
+                if (Fmt<F>::kZp) r -= ep_z[e] * ep_rs[e][v];
+                const size_t o = (size_t)m * N + n;
+                if (acc_out) acc_out[o] = r;
+                y[o] = output_value(r, ep_sx[e][v], ep_sc[e]);
+            }
+        }
     }
 }
 
