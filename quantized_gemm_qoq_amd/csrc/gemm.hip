@@ -669,10 +669,12 @@ template <int F, int MB, int NT>
 __device__ __forceinline__ void stream_compute(int32x4 (&acc)[NT][MB],
                                                const u32x4 (&bq)[NT][Fmt<F>::kVec],
                                                const uint32_t (&pq)[NT],
-                                               const int32x4 (&aq)[MB][2], const uint32_t* lut) {
+                                               const int32x4 (&aq)[MB][2]) {
+    // the group word from the parameter byte in a few integer operations (a
+    // table in LDS would need a barrier before the first group)
     uint32_t gw[NT];
 #pragma unroll
-    for (int i = 0; i < NT; ++i) gw[i] = Fmt<F>::kG128 ? lut[pq[i] & 0xFFu] : 0u;
+    for (int i = 0; i < NT; ++i) gw[i] = Fmt<F>::kG128 ? group_word(pq[i] & 0xFFu) : 0u;
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
         const int32x4 b0 = b_operand<F, 0>(bq[i], gw[i]);
@@ -692,9 +694,14 @@ __global__ __launch_bounds__(W * 64) void k_gemm_stream(
     int32_t* __restrict__ acc_out) {
     constexpr int kPairs = NT * MB;
     constexpr int kThr = W * 64;
-    // red[(p * 4 + v) * 64 + lane]: row v of pair p in lane order (conflict-free).
-    __shared__ int32_t red[kPairs * 4 * kWave];
-    __shared__ uint32_t lut[256];
+    // The waves' partial tiles are summed through LDS: each wave writes its
+    // own slice and the epilogue adds the slices in wave order when they fit
+    // in 96 KB (then nothing needs zeroing and no barrier precedes the first
+    // loads); otherwise the waves add into one zeroed copy.
+    // red[((s * kPairs + p) * 4 + v) * 64 + lane]: row v of pair p in lane
+    // order (conflict-free), slice s.
+    constexpr bool kSlices = W * kPairs * 4 * kWave * 4 <= 96 * 1024;
+    __shared__ int32_t red[(kSlices ? W : 1) * kPairs * 4 * kWave];
 
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -748,8 +755,8 @@ __global__ __launch_bounds__(W * 64) void k_gemm_stream(
     uint32_t pq[R][NT];
     int32x4 aq[R][MB][2];
     const int main_count = count / R * R;
-    // The ring's first loads go out before anything else: the LDS set-up and
-    // the epilogue's scale loads then overlap their latency.
+    // The ring's first loads go out before anything else: the epilogue's
+    // scale loads (and the LDS set-up, if any) then overlap their latency.
 #pragma unroll
     for (int r = 0; r < R - 1; ++r)
         stream_load<F, MB, NT>(bq[r], pq[r], aq[r], rb, rp, ra, b_off, p_off, a_off, r,
@@ -774,10 +781,10 @@ __global__ __launch_bounds__(W * 64) void k_gemm_stream(
             ep_rs[e][v] = Fmt<F>::kZp ? rowsum[m] : 0;
         }
     }
-    for (int i = threadIdx.x; i < kPairs * 4 * kWave; i += kThr) red[i] = 0;
-    if (kG128)
-        for (int i = threadIdx.x; i < 256; i += kThr) lut[i] = group_word((uint32_t)i);
-    __syncthreads();
+    if (!kSlices) {
+        for (int i = threadIdx.x; i < kPairs * 4 * kWave; i += kThr) red[i] = 0;
+        __syncthreads();
+    }
     for (int h = 0; h < main_count; h += R) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -785,13 +792,13 @@ __global__ __launch_bounds__(W * 64) void k_gemm_stream(
             stream_load<F, MB, NT>(bq[(r + R - 1) % R], pq[(r + R - 1) % R],
                                        aq[(r + R - 1) % R], rb, rp, ra, b_off, p_off, a_off, nxt,
                                        nxt < main_count, a_step);
-            stream_compute<F, MB, NT>(acc, bq[r], pq[r], aq[r], lut);
+            stream_compute<F, MB, NT>(acc, bq[r], pq[r], aq[r]);
         }
     }
     for (int h = main_count; h < count; ++h) {
         stream_load<F, MB, NT>(bq[0], pq[0], aq[0], rb, rp, ra, b_off, p_off, a_off, h, true,
                                    a_step);
-        stream_compute<F, MB, NT>(acc, bq[0], pq[0], aq[0], lut);
+        stream_compute<F, MB, NT>(acc, bq[0], pq[0], aq[0]);
     }
 
     // Sum the waves' partial tiles in LDS.
@@ -800,8 +807,11 @@ __global__ __launch_bounds__(W * 64) void k_gemm_stream(
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-                atomicAdd(&red[((i * MB + mb) * 4 + v) * kWave + lane], acc[i][mb][v]);
+            for (int v = 0; v < 4; ++v) {
+                const int idx = ((i * MB + mb) * 4 + v) * kWave + lane;
+                if (kSlices) red[wave * kPairs * 4 * kWave + idx] = acc[i][mb][v];
+                else atomicAdd(&red[idx], acc[i][mb][v]);
+            }
     __syncthreads();
 
 #pragma unroll
@@ -817,7 +827,12 @@ __global__ __launch_bounds__(W * 64) void k_gemm_stream(
         for (int v = 0; v < 4; ++v) {
             const int m = m_first + v;
             if (m < M) {
-                int r = red[(p * 4 + v) * kWave + lane];
+                int r = 0;
+                if (kSlices) {
+                    for (int w2 = 0; w2 < W; ++w2) r += red[((w2 * kPairs + p) * 4 + v) * kWave + lane];
+                } else {
+                    r = red[(p * 4 + v) * kWave + lane];
+                }
                 if (Fmt<F>::kZp) r -= ep_z[e] * ep_rs[e][v];
                 const size_t o = (size_t)m * N + n;
                 if (acc_out) acc_out[o] = r;
