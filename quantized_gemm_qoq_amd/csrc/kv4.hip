@@ -245,6 +245,37 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
     const bool lane_q = jg % JS == 0;   // rows 4 jg + v (v < NV) of this lane are queries
     const int gbase = (jg / JS) * NV;   // the query on row 4 jg
 
+    // One step: 32 tokens.
+    struct StepData {
+        u32x4 kb[2];  // key bytes of token 16 hs + r16, channels 32 jg ..
+        uint2 vb[4];  // value bytes j = 16m + r16 of tokens 8 jg .. +7
+        // raw scales and zeros: converted only when the step is computed, so
+        // that no use waits for a load of the step ahead
+        uint16_t sk[2], sv[2];
+        uint8_t zk[2], zv[2];
+    };
+    auto load_step = [&](int st, StepData& d) {
+        const int bstart = wstart + 32 * st;
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+            const int t = min(bstart + 16 * hs + r16, wend - 1);  // masked tokens read a valid row
+            d.kb[hs] = *reinterpret_cast<const u32x4*>(kq + (rowbase + t) * 64 + 16 * jg);
+        }
+        const int blk = min(bstart / 16 + jg / 2, vlast);
+        const uint8_t* vp = vbase + (size_t)blk * 1024 + r16 * 16 + 8 * (jg % 2);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) d.vb[m] = *reinterpret_cast<const uint2*>(vp + 256 * m);
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+            const int t = min(bstart + 16 * hs + r16, wend - 1);
+            d.sk[hs] = ks[rowbase + t];
+            d.zk[hs] = kz[rowbase + t];
+            d.sv[hs] = vs[rowbase + t];
+            d.zv[hs] = vz[rowbase + t];
+        }
+    };
+    StepData d[kPrefetch + 1];
+
     // ---- A operands of the scores: row r16 (zeros where it holds no query),
     // channels 32 jg + 8f + {0, 4, 2, 6, 1, 5, 3, 7}; q' = f16(q * lambda) from
     // an FP32 product (the barrier keeps the backend from forming one
@@ -323,35 +354,6 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
         for (int v = 0; v < NV; ++v) acc[i][v] = 0.0f;
     int ecur = 64;  // the exponent E the accumulators carry (64: none yet)
 
-    // One step: 32 tokens.
-    struct StepData {
-        u32x4 kb[2];  // key bytes of token 16 hs + r16, channels 32 jg ..
-        uint2 vb[4];  // value bytes j = 16m + r16 of tokens 8 jg .. +7
-        // raw scales and zeros: converted only when the step is computed, so
-        // that no use waits for a load of the step ahead
-        uint16_t sk[2], sv[2];
-        uint8_t zk[2], zv[2];
-    };
-    auto load_step = [&](int st, StepData& d) {
-        const int bstart = wstart + 32 * st;
-#pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {
-            const int t = min(bstart + 16 * hs + r16, wend - 1);  // masked tokens read a valid row
-            d.kb[hs] = *reinterpret_cast<const u32x4*>(kq + (rowbase + t) * 64 + 16 * jg);
-        }
-        const int blk = min(bstart / 16 + jg / 2, vlast);
-        const uint8_t* vp = vbase + (size_t)blk * 1024 + r16 * 16 + 8 * (jg % 2);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) d.vb[m] = *reinterpret_cast<const uint2*>(vp + 256 * m);
-#pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {
-            const int t = min(bstart + 16 * hs + r16, wend - 1);
-            d.sk[hs] = ks[rowbase + t];
-            d.zk[hs] = kz[rowbase + t];
-            d.sv[hs] = vs[rowbase + t];
-            d.zv[hs] = vz[rowbase + t];
-        }
-    };
     auto compute_step = [&](int st, const StepData& d) {
         const int bstart = wstart + 32 * st;
         float sk[2], zk[2], sv[2], zv[2];
@@ -456,7 +458,6 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
     // step repeats the last step (cached, unused), so that the count of loads
     // in flight, and with it each wait, is the same at every step.
     if (ntotal > 0) {
-        StepData d[kPrefetch + 1];
 #pragma unroll
         for (int i = 0; i < kPrefetch; ++i) load_step(min(i, ntotal - 1), d[i]);
         for (int st = 0;; st += kPrefetch + 1) {
@@ -522,8 +523,8 @@ steps_done:
 
 // Part 2: one wave per (b, query head): combine the chunks that start before
 // len[b]; o = sum_c 2^(M_c - M) O_c / sum_c 2^(M_c - M) L_c (maxima in log2
-// units), rounded to FP16
-// (a sequence of length 0 gives zeros).
+// units, M their maximum, taken as a running maximum), rounded to FP16 (a
+// sequence of length 0 gives zeros).
 __global__ __launch_bounds__(kKvThreads) void k_kv4_attn_combine(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
     const int32_t* __restrict__ lens, int B, int Hq, int Tcap, int C, int nchunks,
@@ -534,15 +535,33 @@ __global__ __launch_bounds__(kKvThreads) void k_kv4_attn_combine(
     const int b = (int)(w / Hq);
     const int len = min(max(lens[b], 0), Tcap);
     const int used = (len + C - 1) / C;
-    float M = -INFINITY;
-    for (int c = 0; c < used; ++c) M = fmaxf(M, part_ml[(w * nchunks + c) * 2]);
-    float L = 0.0f, o0 = 0.0f, o1 = 0.0f;
-    for (int c = 0; c < used; ++c) {
-        const size_t rec = (size_t)w * nchunks + c;
-        const float e = __builtin_amdgcn_exp2f(part_ml[rec * 2] - M);
-        L += e * part_ml[rec * 2 + 1];
-        o0 += e * part_o[rec * kD + 2 * lane];
-        o1 += e * part_o[rec * kD + 2 * lane + 1];
+    // One pass with a running maximum; the records of four chunks are read
+    // together, independently of len (chunks past it are read but not used),
+    // so the loads of a batch overlap each other and the load of len.
+    float M = -INFINITY, L = 0.0f, o0 = 0.0f, o1 = 0.0f;
+    for (int cb = 0; cb < nchunks; cb += 4) {
+        float mc[4], lc[4];
+        float2 oc[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const size_t rec = (size_t)w * nchunks + min(cb + k, nchunks - 1);
+            mc[k] = part_ml[rec * 2];
+            lc[k] = part_ml[rec * 2 + 1];
+            oc[k] = *reinterpret_cast<const float2*>(part_o + rec * kD + 2 * lane);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (cb + k < used) {
+                const float mn = fmaxf(M, mc[k]);
+                const float r = __builtin_amdgcn_exp2f(M - mn);  // 0 for the first chunk
+                const float e = __builtin_amdgcn_exp2f(mc[k] - mn);
+                L = L * r + e * lc[k];
+                o0 = o0 * r + e * oc[k].x;
+                o1 = o1 * r + e * oc[k].y;
+                M = mn;
+            }
+        }
+        if (cb + 4 >= used) break;
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     reinterpret_cast<uint32_t*>(o + (size_t)w * kD)[lane] =
