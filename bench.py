@@ -420,6 +420,12 @@ def main(argv=None) -> int:
                     if isinstance(out, int):
                         return out
                     print(json.dumps(out), flush=True)
+        for M2, I2 in SILU_SPLIT_SHAPES:
+            layer2 = workloads.Layer(f"silu_m{M2}_i{I2}", M=M2, K=I2, N=16, seed=3100 + M2)
+            out = producer_compare(args, layer2)
+            if isinstance(out, int):
+                return out
+            print(json.dumps(out), flush=True)
         seen = set()
         for wl2 in workloads.WORKLOADS.values():
             for layer2 in wl2.layers:
@@ -459,6 +465,10 @@ def main(argv=None) -> int:
 
 # Decode attention at the pages' serving point (1024 input + 512 output tokens:
 # 1536 cached tokens at the last step), head dimension 128.
+# Few-row inputs of a down projection (Llama-2-7B's 11008, Llama-3-8B's 14336,
+# Qwen1.5-72B's 24576 inputs) around the split-row policy's edges.
+SILU_SPLIT_SHAPES = ((1, 24576), (16, 14336), (32, 14336), (16, 11008), (64, 14336))
+
 KV4_SHAPES = (("llama3_8b_b64", 64, 32, 8, 1536), ("llama3_8b_b16", 16, 32, 8, 1536),
               ("qwen15_72b_b16", 16, 64, 64, 1536), ("hq64_h8_b16", 16, 64, 8, 1536),
               ("llama3_8b_b16_t8192", 16, 32, 8, 8192))
@@ -561,6 +571,9 @@ def producer_compare(args, layer):
     def fused(st):
         qoq.qoq_silu_mul_quantize_act(st["gu"], st["xq"], st["s_x"], st["rs"])
 
+    def one_pass(st):
+        qoq.qoq_silu_mul_quantize_act(st["gu"], st["xq"], st["s_x"], st["rs"], workspace=None)
+
     def unfused(st):
         torch.mul(torch.nn.functional.silu(st["gu"][:, :I]), st["gu"][:, I:], out=st["h"])
         qoq.qoq_quantize_act(st["h"], st["xq"], st["s_x"], st["rs"])
@@ -586,10 +599,14 @@ def producer_compare(args, layer):
 
     f_us, u_us = avg_us(fused), avg_us(unfused)
     f_bytes = 4 * M * I + M * I + 6 * M  # read gate_up, write codes, scale, row sum
-    return {"layer": layer.name, "M": M, "I": I, "fused_us": round(f_us, 3),
-            "unfused_us": round(u_us, 3), "speedup": round(u_us / f_us, 2),
-            "fused_GBs": round(f_bytes / f_us / 1e3, 1),
-            "fused_frac_of_hbm": round(f_bytes / f_us / 1e3 / HBM_PEAK_GBS, 3)}
+    out = {"layer": layer.name, "M": M, "I": I, "fused_us": round(f_us, 3),
+           "unfused_us": round(u_us, 3), "speedup": round(u_us / f_us, 2),
+           "fused_GBs": round(f_bytes / f_us / 1e3, 1),
+           "fused_frac_of_hbm": round(f_bytes / f_us / 1e3 / HBM_PEAK_GBS, 3)}
+    if qoq.load_library().qoq_silu_mul_workspace_bytes(M, I) > 0:
+        out["split_rows"] = True  # fused_us is the split-row path; the one-pass kernel beside it
+        out["one_pass_us"] = round(avg_us(one_pass), 3)
+    return out
 
 
 def rmsnorm_compare(args, layer, eps=1e-5):

@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define QOQ_ABI_VERSION 4
+#define QOQ_ABI_VERSION 5
 #define QOQ_GROUP 128
 #define QOQ_MAX_K 132096
 #define QOQ_RMSNORM_MAX_K 32768 /* row length of qoq_rmsnorm_quantize_act */
@@ -284,6 +284,24 @@ qoq_status qoq_w8a8_gemm(const int8_t* xq, const uint16_t* s_x, const void* blob
  */
 qoq_status qoq_silu_mul_quantize_act(const uint16_t* gate_up, int64_t M, int64_t I, int8_t* xq,
                                      uint16_t* s_x, int32_t* rowsum, uint16_t* h, void* stream);
+
+/*
+ * The same call for few rows: with a workspace of
+ * qoq_silu_mul_workspace_bytes(M, I) bytes (device memory, 16-byte aligned,
+ * no initialisation needed), each row is shared by several workgroups in two
+ * passes (the largest |h| of each share, then the codes, the row sum gathered
+ * in a per-row 64-bit tally in the workspace), so that rows use more than one
+ * compute unit. The size is 0 where the one-pass kernels are as fast (more
+ * than 32 rows, or I < 12288). The outputs are those of
+ * qoq_silu_mul_quantize_act bit for bit. A NULL workspace (or a size 0 one)
+ * runs the one-pass kernels; a workspace smaller than needed gives
+ * QOQ_ERR_SHAPE. Calls that overlap in time must not share a workspace.
+ * qoq_silu_mul_workspace_bytes returns -1 for an unsupported shape.
+ */
+int64_t qoq_silu_mul_workspace_bytes(int64_t M, int64_t I);
+qoq_status qoq_silu_mul_quantize_act_ws(const uint16_t* gate_up, int64_t M, int64_t I, int8_t* xq,
+                                        uint16_t* s_x, int32_t* rowsum, uint16_t* h,
+                                        void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
  * qoq_rmsnorm_quantize_act: the other producer of a GEMM input. ([GUIDE]

@@ -46,6 +46,8 @@ EXPORTED = (
     "qoq_w4a16_gemm",
     "qoq_silu_mul_quantize_act",
     "qoq_rmsnorm_quantize_act",
+    "qoq_silu_mul_workspace_bytes",
+    "qoq_silu_mul_quantize_act_ws",
     "qoq_kv4_smooth_scales",
     "qoq_kv4_append",
     "qoq_kv4_attention_workspace_bytes",
@@ -92,6 +94,8 @@ def load_library():
             "qoq_w4a16_gemm": (I, [I, P, P, P, I64, I64, I64, P, P, P]),
             "qoq_silu_mul_quantize_act": (I, [P, I64, I64, P, P, P, P, P]),
             "qoq_rmsnorm_quantize_act": (I, [P, P, ctypes.c_float, I64, I64, P, P, P, P, P]),
+            "qoq_silu_mul_workspace_bytes": (I64, [I64, I64]),
+            "qoq_silu_mul_quantize_act_ws": (I, [P, I64, I64, P, P, P, P, P, I64, P]),
             "qoq_kv4_smooth_scales": (I, [P, I64, I64, I64, P, P]),
             "qoq_kv4_append": (I, [P, P, P, I64, I64, I64, I64, I64, I64, P, P, P, P, P, P, P]),
             "qoq_kv4_attention_workspace_bytes": (I64, [I64, I64, I64, I64, I64]),
@@ -244,10 +248,12 @@ def qoq_quantize_act(x: torch.Tensor, xq=None, s_x=None, rowsum=None, want_rowsu
 
 
 def qoq_silu_mul_quantize_act(gate_up: torch.Tensor, xq=None, s_x=None, rowsum=None,
-                              want_rowsum: bool = True, h=None):
+                              want_rowsum: bool = True, h=None, workspace="auto"):
     """gate_up [M, 2I] fp16 -> (xq, s_x, rowsum | None) of h = f16(SiLU(gate) * up),
     gate = columns 0..I-1, up = columns I..2I-1; the same outputs as
-    qoq_quantize_act(h). h (fp16 [M, I]) is written too when given."""
+    qoq_quantize_act(h). h (fp16 [M, I]) is written too when given.
+    workspace: "auto" allocates the split-row workspace when the shape uses one,
+    None runs the one-pass kernels, or a uint8 device tensor."""
     _need(gate_up, torch.float16, "gate_up")
     M, I2 = gate_up.shape
     if I2 % 2:
@@ -267,8 +273,13 @@ def qoq_silu_mul_quantize_act(gate_up: torch.Tensor, xq=None, s_x=None, rowsum=N
         _need(rowsum, torch.int32, "rowsum", (M,))
     if h is not None:
         _need(h, torch.float16, "h", (M, I))
-    st = load_library().qoq_silu_mul_quantize_act(_ptr(gate_up), M, I, _ptr(xq), _ptr(s_x),
-                                                  _ptr(rowsum), _ptr(h), _stream(gate_up))
+    lib = load_library()
+    if isinstance(workspace, str):
+        need = int(lib.qoq_silu_mul_workspace_bytes(M, I))
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev) if need > 0 else None
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    st = lib.qoq_silu_mul_quantize_act_ws(_ptr(gate_up), M, I, _ptr(xq), _ptr(s_x), _ptr(rowsum),
+                                          _ptr(h), _ptr(workspace), ws_bytes, _stream(gate_up))
     _check(st, "qoq_silu_mul_quantize_act")
     return xq, s_x, rowsum
 

@@ -201,6 +201,28 @@ qoq_status qoq_silu_mul_quantize_act(const uint16_t* gate_up, int64_t M, int64_t
     });
 }
 
+int64_t qoq_silu_mul_workspace_bytes(int64_t M, int64_t I) {
+    if (M < 0 || M > INT32_MAX - 15 || !valid_k(I)) return -1;
+    return qoq::silu_mul_workspace_bytes(M, I);
+}
+
+qoq_status qoq_silu_mul_quantize_act_ws(const uint16_t* gate_up, int64_t M, int64_t I, int8_t* xq,
+                                        uint16_t* s_x, int32_t* rowsum, uint16_t* h,
+                                        void* workspace, int64_t workspace_bytes, void* stream) {
+    if (M < 0 || M > INT32_MAX - 15 || !valid_k(I)) return QOQ_ERR_SHAPE;
+    if (M == 0) return QOQ_OK;
+    if (!gate_up || !xq || !s_x) return QOQ_ERR_NULL;
+    if (!aligned16(gate_up) || !aligned16(xq) || !aligned16(s_x) || (rowsum && !aligned16(rowsum)) ||
+        (h && !aligned16(h)) || (workspace && !aligned16(workspace)))
+        return QOQ_ERR_ALIGN;
+    const int64_t need = qoq::silu_mul_workspace_bytes(M, I);
+    if (workspace && workspace_bytes < need) return QOQ_ERR_SHAPE;
+    return launch_checked([&] {
+        qoq::launch_silu_mul_quantize_act_ws(gate_up, M, I, xq, s_x, rowsum, h, need > 0 ? workspace : nullptr,
+                                             as_stream(stream));
+    });
+}
+
 qoq_status qoq_rmsnorm_quantize_act(const uint16_t* x, const uint16_t* gamma, float eps, int64_t M,
                                    int64_t K, int8_t* xq, uint16_t* s_x, int32_t* rowsum,
                                    uint16_t* y, void* stream) {

@@ -27,6 +27,10 @@ void launch_unpack(int mode, const uint8_t* blob, int64_t N, int64_t K, uint8_t*
 void launch_rmsnorm_quantize_act(const uint16_t* x, const uint16_t* gamma, float eps, int64_t M,
                                  int64_t K, int8_t* xq, uint16_t* s_x, int32_t* rowsum,
                                  uint16_t* y, hipStream_t stream);
+int64_t silu_mul_workspace_bytes(int64_t M, int64_t I);
+void launch_silu_mul_quantize_act_ws(const uint16_t* gate_up, int64_t M, int64_t I, int8_t* xq,
+                                     uint16_t* s_x, int32_t* rowsum, uint16_t* h, void* ws,
+                                     hipStream_t stream);
 void launch_silu_mul_quantize_act(const uint16_t* gate_up, int64_t M, int64_t I, int8_t* xq,
                                   uint16_t* s_x, int32_t* rowsum, uint16_t* h,
                                   hipStream_t stream);

@@ -12,7 +12,10 @@
 // Rounding follows the library contract in qoq.h: round half to even, scales
 // computed in IEEE fp32 with correctly rounded division, stored as FP16, and
 // the stored FP16 scale is the one used to quantize.
+#include <algorithm>
+
 #include "qoq_device.hpp"
+#include "qoq.h"
 #include "qoq_launch.hpp"
 
 namespace qoq {
@@ -582,6 +585,131 @@ __global__ __launch_bounds__(THR) void k_rmsnorm_quant_reg(const uint16_t* __res
     }
 }
 
+// Split rows, for few rows: S workgroups share a row (grid Mp x S, the
+// row's quads of 4 inputs split evenly, one quad per thread and step, so a
+// thread's chain of exponentials and divisions stays short). Part 1 computes
+// h for its share and writes its largest magnitude (FP16 bits) to the
+// workspace, and the share-0 workgroup clears the row's tally; part 2 takes
+// the row's maximum over the S shares, computes h again and writes the codes
+// of its share (4 bytes of a 16-byte run slot per thread). The row sum is
+// gathered without a separate pass: each part-2 workgroup adds (1 << 32) plus
+// its share's sum biased by 128 per input to the row's 64-bit tally (one
+// atomic per workgroup, each row's tally on its own 256-byte line, so rows do
+// not queue on one line), and the workgroup that finds S - 1 shares already
+// counted writes the row sum, the tally's low word less 128 I. Integer adds:
+// exact in any order. h, codes, scale and row sum are the single-pass
+// kernel's bit for bit.
+constexpr int kTallyStride = 32;  // 64-bit words: 256 bytes per row
+static_assert(255LL * QOQ_MAX_K < (1LL << 32), "the biased row tally must fit its low word");
+
+__device__ __forceinline__ void split_range(int n, int S, int s, int& q0, int& q1) {
+    q0 = (int)((int64_t)n * s / S);
+    q1 = (int)((int64_t)n * (s + 1) / S);
+}
+
+// h of 4 inputs: two words of gate and two of up
+__device__ __forceinline__ uint2 silu_mul4(uint2 g, uint2 u) {
+    return uint2{silu_mul1(g.x & 0xFFFFu, u.x & 0xFFFFu) | (silu_mul1(g.x >> 16, u.x >> 16) << 16),
+                 silu_mul1(g.y & 0xFFFFu, u.y & 0xFFFFu) | (silu_mul1(g.y >> 16, u.y >> 16) << 16)};
+}
+
+__global__ __launch_bounds__(kThreads) void k_silu_max_part(const uint16_t* __restrict__ gu, int M,
+                                                            int I, int S,
+                                                            uint32_t* __restrict__ part_max,
+                                                            unsigned long long* __restrict__ tally) {
+    __shared__ unsigned red_u[kWaves];
+    const int m = blockIdx.x / S, s = blockIdx.x % S;
+    if (m >= M) return;
+    int q0, q1;
+    split_range(I / 4, S, s, q0, q1);
+    const uint2* grow = reinterpret_cast<const uint2*>(gu + (size_t)m * 2 * I);
+    const uint2* urow = reinterpret_cast<const uint2*>(gu + (size_t)m * 2 * I + I);
+    unsigned amax = 0;
+    for (int q = q0 + threadIdx.x; q < q1; q += kThreads) {
+        const uint2 h = silu_mul4(grow[q], urow[q]);
+        amax = max(amax, max(absmax_bits2(h.x), absmax_bits2(h.y)));
+    }
+    amax = block_reduce(amax, red_u, MaxU{});
+    if (threadIdx.x == 0) {
+        part_max[blockIdx.x] = amax;
+        if (s == 0) tally[(size_t)m * kTallyStride] = 0ull;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_silu_quant_part(const uint16_t* __restrict__ gu, int M,
+                                                              int I, int S,
+                                                              const uint32_t* __restrict__ part_max,
+                                                              unsigned long long* __restrict__ tally,
+                                                              int8_t* __restrict__ xq,
+                                                              uint16_t* __restrict__ s_x,
+                                                              int32_t* __restrict__ rowsum,
+                                                              uint16_t* __restrict__ h_out) {
+    __shared__ int red_i[kWaves];
+    const int m = blockIdx.x / S, s = blockIdx.x % S;
+    const int U = gridDim.x / S / 16;
+    const int u = m / 16, r = m % 16;
+    int q0, q1;
+    split_range(I / 4, S, s, q0, q1);
+    // byte offset of quad q's 4 codes: its run's 16-byte slot in the packed
+    // tile order, plus 4 bytes per quad within the run
+    auto dst = [&](int q) {
+        const int c = q / 4, g = c / 8, sl = (c / 4) % 2, j = c % 4;
+        return ((((size_t)g * U + u) * 128 + 64 * sl + 16 * j + r) << 4) + 4 * (q % 4);
+    };
+    if (m >= M) {
+        for (int q = q0 + threadIdx.x; q < q1; q += kThreads)
+            *reinterpret_cast<uint32_t*>(xq + dst(q)) = 0u;
+        return;
+    }
+    const uint2* grow = reinterpret_cast<const uint2*>(gu + (size_t)m * 2 * I);
+    const uint2* urow = reinterpret_cast<const uint2*>(gu + (size_t)m * 2 * I + I);
+    uint2* hrow = h_out ? reinterpret_cast<uint2*>(h_out + (size_t)m * I) : nullptr;
+    // h of the first quad is computed while the shares' maxima are read (each
+    // wave reads them across its lanes)
+    int q = q0 + threadIdx.x;
+    uint2 h = uint2{0u, 0u};
+    if (q < q1) h = silu_mul4(grow[q], urow[q]);
+    unsigned amax = 0;
+    for (int i = threadIdx.x % kWave; i < S; i += kWave) amax = max(amax, part_max[(size_t)m * S + i]);
+    amax = wave_max_u(amax);
+    const uint16_t sbits = f2h(h2f(amax) / 127.0f);
+    const float sf = h2f(sbits);
+    int sum = 0;
+    // the last quad's codes are stored after the row-sum reduction, so its
+    // barriers do not wait on them
+    uint32_t held = 0u;
+    int held_q = -1;
+    for (; q < q1; q += kThreads) {
+        if (q != q0 + (int)threadIdx.x) h = silu_mul4(grow[q], urow[q]);
+        if (hrow) hrow[q] = h;
+        uint32_t packed = 0u;
+        if (sf != 0.0f) {
+            const uint32_t w[4] = {h.x & 0xFFFFu, h.x >> 16, h.y & 0xFFFFu, h.y >> 16};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int qv = quant_act1(w[e], sf);
+                sum += qv;
+                packed |= (uint32_t)(qv & 0xFF) << (8 * e);
+            }
+        }
+        if (held_q >= 0) *reinterpret_cast<uint32_t*>(xq + dst(held_q)) = held;
+        held = packed;
+        held_q = q;
+    }
+    if (rowsum) {
+        sum = block_reduce(sum, red_i, SumI{});
+        if (threadIdx.x == 0) {
+            const unsigned long long add =
+                (1ull << 32) + (unsigned long long)(uint32_t)(sum + 128 * 4 * (q1 - q0));
+            const unsigned long long old = atomicAdd(&tally[(size_t)m * kTallyStride], add);
+            if ((int)(old >> 32) == S - 1)
+                rowsum[m] = (int32_t)((uint32_t)(old + add) - (uint32_t)(128 * I));
+        }
+    }
+    if (held_q >= 0) *reinterpret_cast<uint32_t*>(xq + dst(held_q)) = held;
+    if (threadIdx.x == 0 && s == 0) s_x[m] = sbits;
+}
+
 // Larger I: two passes over the gate_up row (the second recomputes h).
 __global__ __launch_bounds__(kThreads) void k_silu_quant(const uint16_t* __restrict__ gu, int M,
                                                          int I, int8_t* __restrict__ xq,
@@ -717,6 +845,45 @@ void launch_rmsnorm_quantize_act(const uint16_t* x, const uint16_t* gamma, float
     else if (runs <= 1024) QOQ_RQ(1024, 1);
     else QOQ_RQ(1024, 2);  // K <= 32768, checked by the caller
 #undef QOQ_RQ
+}
+
+// Shares per row of the split path: about 512 workgroups in all, each share
+// at least 1024 inputs (one quad per thread); 1 means the one-pass kernels
+// are used. The split pays its second launch back only where the one-pass
+// kernel leaves most compute units idle (at most 32 rows) and its threads
+// carry long chains (rows of 12288 inputs or more).
+int64_t silu_split_shares(int64_t M, int64_t I) {
+    const int64_t mp = (M + 15) / 16 * 16;
+    if (M <= 0 || mp > 32 || I < 12288) return 1;
+    return std::max<int64_t>(1, std::min<int64_t>((512 + mp - 1) / mp, I / 1024));
+}
+
+// Workspace of the split path: the shares' maxima, then one 256-byte line
+// per row for its tally.
+static int64_t silu_tally_offset(int64_t mp, int64_t S) { return (mp * S * 4 + 255) / 256 * 256; }
+
+int64_t silu_mul_workspace_bytes(int64_t M, int64_t I) {
+    const int64_t S = silu_split_shares(M, I);
+    const int64_t mp = (M + 15) / 16 * 16;
+    return S > 1 ? silu_tally_offset(mp, S) + mp * kTallyStride * 8 : 0;
+}
+
+void launch_silu_mul_quantize_act_ws(const uint16_t* gate_up, int64_t M, int64_t I, int8_t* xq,
+                                     uint16_t* s_x, int32_t* rowsum, uint16_t* h, void* ws,
+                                     hipStream_t stream) {
+    const int64_t S = silu_split_shares(M, I);
+    if (S <= 1 || !ws) {
+        launch_silu_mul_quantize_act(gate_up, M, I, xq, s_x, rowsum, h, stream);
+        return;
+    }
+    const unsigned mp = (unsigned)((M + 15) / 16 * 16);
+    uint32_t* part = static_cast<uint32_t*>(ws);
+    auto* tally = reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) +
+                                                        silu_tally_offset(mp, S));
+    hipLaunchKernelGGL(k_silu_max_part, dim3(mp * (unsigned)S), dim3(kThreads), 0, stream, gate_up,
+                       (int)M, (int)I, (int)S, part, tally);
+    hipLaunchKernelGGL(k_silu_quant_part, dim3(mp * (unsigned)S), dim3(kThreads), 0, stream, gate_up,
+                       (int)M, (int)I, (int)S, part, tally, xq, s_x, rowsum, h);
 }
 
 void launch_quantize_weights_w8(const uint16_t* w, int64_t N, int64_t K, int8_t* q, uint16_t* s_c,

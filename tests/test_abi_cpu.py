@@ -192,6 +192,24 @@ def test_silu_mul_quantize_validation(lib):
     assert f(A, 4, 128, A, A, A, U, NUL) == ERR_ALIGN
 
 
+def test_silu_mul_split_workspace(lib):
+    w = lib.qoq_silu_mul_workspace_bytes
+    # 24 shares of 1024 inputs per row: their maxima, then a 256-byte tally line per row
+    assert w(16, 24576) == 16 * 24 * 4 + 16 * 256
+    assert w(32, 14336) == 32 * 14 * 4 + 32 * 256
+    assert w(64, 14336) == 0                # enough rows for the one-pass kernel
+    assert w(16, 11008) == 0                # rows short enough for it
+    assert w(16, 12288) == 16 * 12 * 4 + 16 * 256
+    assert w(512, 14336) == 0               # enough rows: one pass
+    assert w(16, 512) == 0                  # rows too short to share
+    assert w(16, 100) == -1
+    f = lib.qoq_silu_mul_quantize_act_ws
+    assert f(A, 16, 24576, A, A, A, NUL, A, 5631, NUL) == ERR_SHAPE  # workspace too small
+    assert f(A, 16, 24576, A, A, A, NUL, U, 5632, NUL) == ERR_ALIGN
+    assert f(A, 0, 24576, A, A, A, NUL, NUL, 0, NUL) == OK
+    assert f(NUL, 16, 24576, A, A, A, NUL, A, 5632, NUL) == ERR_NULL
+
+
 def test_rmsnorm_quantize_validation(lib):
     f = lib.qoq_rmsnorm_quantize_act
     assert f(A, A, 1e-5, 0, 128, A, A, A, NUL, NUL) == OK
