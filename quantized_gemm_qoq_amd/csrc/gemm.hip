@@ -620,6 +620,218 @@ __global__ __launch_bounds__(WN * 64, 2) void k_gemm_wide(
 }
 
 // ---------------------------------------------------------------------------
+// LDS-pipelined kernel (large M). One workgroup of 8 waves per compute unit
+// owns a BM x 256 block; wave (wm, wn) computes 128 rows x 256/WN channels
+// (8 row tiles x TN channel tiles), so every weight tile is unpacked by WM
+// waves. Both operands reach LDS by direct buffer-to-LDS loads (no staging
+// registers), three groups deep: the loads of group g+2 are issued at the
+// start of step g into the buffer that step g-1 has just finished reading, and
+// step g waits only for its own group's loads (the load counter is in order,
+// so the wait leaves the next group's loads in flight), then one barrier
+// publishes the group to all waves. The three buffers are separate arrays
+// named by fixed code (three steps per loop iteration), so that the compiler
+// can tell the loads into one buffer from the reads of another.
+template <int F, int TM, int TN>
+__device__ __forceinline__ void lds_compute(int32x4 (&acc)[TM][TN], const u32x4* la,
+                                            const u32x4* lb, const uint8_t* lp) {
+    constexpr bool kG128 = Fmt<F>::kG128;
+    constexpr int kV = Fmt<F>::kVec;
+    u32x4 bq[TN][kV];
+    uint32_t gw[TN];
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+#pragma unroll
+        for (int v = 0; v < kV; ++v) bq[i][v] = lb[(i * kV + v) * 64];
+        gw[i] = kG128 ? group_word(lp[i * 16]) : 0u;
+    }
+    int32x4 b0[TN], b1[TN];
+#pragma unroll
+    for (int i = 0; i < TN; ++i) b0[i] = b_operand<F, 0>(bq[i], gw[i]);
+#pragma unroll
+    for (int i = 0; i < TN; ++i) b1[i] = b_operand<F, 1>(bq[i], gw[i]);
+#pragma unroll
+    for (int a = 0; a < TM; ++a) {
+        const int32x4 af = __builtin_bit_cast(int32x4, la[a * 128]);
+#pragma unroll
+        for (int i = 0; i < TN; ++i) acc[a][i] = mfma16x16x64(af, b0[i], acc[a][i]);
+    }
+#pragma unroll
+    for (int a = 0; a < TM; ++a) {
+        const int32x4 af = __builtin_bit_cast(int32x4, la[a * 128 + 64]);
+#pragma unroll
+        for (int i = 0; i < TN; ++i) acc[a][i] = mfma16x16x64(af, b1[i], acc[a][i]);
+    }
+    // Scheduling pattern (masks: 0x2 VALU, 0x8 MFMA, 0x100 LDS read): the
+    // weight reads first, the k-step-0 unpack, then the k-step-1 unpack spread
+    // over the k-step-0 matrix-core operations.
+    constexpr int kUnpackHalf = (F == kFmtG128 ? 14 : F == kFmtPC ? 6 : 0) * TN;
+    constexpr int kGroupWord = kG128 ? 7 * TN : 0;
+    constexpr int kValuPerRow = (kUnpackHalf + TM - 1) / TM;
+    __builtin_amdgcn_sched_group_barrier(0x100, TN * (kV + (kG128 ? 1 : 0)), 0);
+    if (kUnpackHalf > 0) __builtin_amdgcn_sched_group_barrier(0x002, kGroupWord + kUnpackHalf, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int a = 0; a < TM; ++a) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);
+        if (kValuPerRow > 0) __builtin_amdgcn_sched_group_barrier(0x002, kValuPerRow, 0);
+    }
+#pragma unroll
+    for (int a = 0; a < TM; ++a) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);
+    }
+}
+
+#define QOQ_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+template <int F, int BM, int WM>
+__global__ __launch_bounds__(512, 1) void k_gemm_lds(
+    const int8_t* __restrict__ xq, const uint16_t* __restrict__ s_x,
+    const int32_t* __restrict__ rowsum, const uint8_t* __restrict__ blob,
+    const uint16_t* __restrict__ s_c, int M, int N, int K, uint16_t* __restrict__ y,
+    int32_t* __restrict__ acc_out, int group_m) {
+    constexpr int kThr = 512, kW = 8, BN = 256;
+    constexpr int WN = kW / WM;
+    constexpr int TM = BM / 16 / WM, TN = BN / WN / 16;
+    constexpr bool kG128 = Fmt<F>::kG128;
+    constexpr int kV = Fmt<F>::kVec;
+    constexpr int kAVec = BM * 128 / 16;         // 16-byte vectors of A per group
+    constexpr int kBVec = (BN / 16) * 64 * kV;   // of B
+    constexpr int kPVec = kG128 ? 16 : 0;        // 256 parameter bytes
+    constexpr int kStageVec = kAVec + kBVec + kPVec;
+    constexpr int kADma = kAVec / kThr;          // loads per wave per group
+    constexpr int kBDma = kBVec / kThr;
+    static_assert(kAVec % kThr == 0 && kBVec % kThr == 0, "loads must divide evenly");
+    static_assert(3 * kStageVec * 16 <= 160 * 1024, "three stages must fit the LDS");
+    // Wait for all but the next group's loads (wave 0's parameter load of the
+    // next group may be waited for too), and for this wave's LDS reads.
+    constexpr int kD = kADma + kBDma;
+    constexpr int kWaitStep = (kD & 15) | ((kD >> 4) << 14) | (7 << 4);  // vmcnt(kD) lgkmcnt(0)
+    constexpr int kWaitAll = (7 << 4);                                   // vmcnt(0) lgkmcnt(0)
+    __shared__ u32x4 st0[kStageVec];
+    __shared__ u32x4 st1[kStageVec];
+    __shared__ u32x4 st2[kStageVec];
+
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int wm = wave / WN, wn = wave % WN;
+    const int c = lane % 16, j = lane / 16;
+    const int G = K / kGroup;
+    const int U = (M + 15) / 16;
+    const int tiles = N / 16;
+    const int grid_m = (M + BM - 1) / BM, grid_n = (N + BN - 1) / BN;
+
+    // Block renumbering: contiguous range per XCD, then groups of group_m
+    // block rows.
+    int pid = blockIdx.x;
+    const int nblocks = grid_m * grid_n;
+    if (nblocks % 8 == 0) pid = (pid % 8) * (nblocks / 8) + pid / 8;
+    const int per_group = group_m * grid_n;
+    const int first_m = (pid / per_group) * group_m;
+    const int gsz = min(grid_m - first_m, group_m);
+    const int bm = first_m + (pid % per_group) % gsz;
+    const int bn = (pid % per_group) / gsz;
+
+    const size_t code_bytes = code_bytes_of(F, N, K);
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)xq, (short)0, (int)((uint32_t)G * (uint32_t)U * 2048u), kBufferConfig);
+    const __amdgpu_buffer_rsrc_t rb =
+        __builtin_amdgcn_make_buffer_rsrc((void*)blob, (short)0, (int)(uint32_t)code_bytes, kBufferConfig);
+    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(blob + code_bytes), (short)0, (int)(uint32_t)(kG128 ? N * G : N), kBufferConfig);
+
+    // Load v of this wave moves 16-byte vectors (v * 8 + wave) * 64 + lane of
+    // the group's A run (BM/16 packed 2 KB row tiles, clamped past the last
+    // one) and of its B run (16 channel tiles of kV KB, clamped past the last
+    // one) to the same LDS vector index. Wave 0 also moves the 256 parameter
+    // bytes, 4 per lane (tile lane/4, channels 4*(lane%4) .. +3).
+    const int u0 = bm * (BM / 16);
+    uint32_t a_off[kADma], b_off[kBDma];
+#pragma unroll
+    for (int v = 0; v < kADma; ++v) {
+        const int idx = (v * kW + wave) * 64 + lane;
+        const int u = min(u0 + idx / 128, U - 1);
+        a_off[v] = (uint32_t)(u * 128 + idx % 128) * 16u;
+    }
+#pragma unroll
+    for (int v = 0; v < kBDma; ++v) {
+        const int idx = (v * kW + wave) * 64 + lane;
+        const int t = min(bn * (BN / 16) + idx / (64 * kV), tiles - 1);
+        b_off[v] = ((uint32_t)t * (uint32_t)G * 64u * kV + (uint32_t)(idx % (64 * kV))) * 16u;
+    }
+    const uint32_t p_off =
+        (uint32_t)min(bn * (BN / 16) + lane / 4, tiles - 1) * (uint32_t)G * 16u + 4u * (lane % 4);
+    const uint32_t a_step = (uint32_t)U * 2048u;  // bytes per group
+
+    auto issue = [&](u32x4* st, int g) {
+#pragma unroll
+        for (int v = 0; v < kADma; ++v)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, QOQ_LDS_PTR(st + (v * kW + wave) * 64), 16,
+                                                     (int)a_off[v], (int)((uint32_t)g * a_step), 0, 0);
+#pragma unroll
+        for (int v = 0; v < kBDma; ++v)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, QOQ_LDS_PTR(st + kAVec + (v * kW + wave) * 64),
+                                                     16, (int)b_off[v], g * kV * 1024, 0, 0);
+        if (kG128 && wave == 0)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, QOQ_LDS_PTR(st + kAVec + kBVec), 4, (int)p_off,
+                                                     g * 16, 0, 0);
+    };
+
+    int32x4 acc[TM][TN];
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TN; ++b) acc[a][b] = int32x4{0, 0, 0, 0};
+
+    const int la = (wm * TM) * 128 + lane;
+    const int lb = kAVec + (wn * TN) * 64 * kV + lane;
+    const int lp = (kAVec + kBVec) * 16 + (wn * TN) * 16 + c;  // byte index
+
+    // Step g: wait for group g, publish it, refill the buffer step g-1 read
+    // with group g+2 (clamped at the end: those loads are never read), run g.
+    auto step = [&](const u32x4* cur, u32x4* refill, int g) {
+        __builtin_amdgcn_s_waitcnt(kWaitStep);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        issue(refill, min(g + 2, G - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        lds_compute<F, TM, TN>(acc, cur + la, cur + lb, reinterpret_cast<const uint8_t*>(cur) + lp);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    issue(st0, 0);
+    issue(st1, min(1, G - 1));
+    int h = 0;
+    for (; h + 2 < G; h += 3) {
+        step(st0, st2, h);
+        step(st1, st0, h + 1);
+        step(st2, st1, h + 2);
+    }
+    if (h < G) step(st0, st2, h);
+    if (h + 1 < G) step(st1, st0, h + 1);
+    // No load may still be writing this workgroup's LDS when it exits.
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
+
+    // Epilogue.
+    const uint8_t* pc_z = blob + code_bytes;
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+        const int t = bn * (BN / 16) + wn * TN + i;
+        if (t >= tiles) continue;
+        const int n = 16 * t + c;
+        const float sc = h2f(s_c[n]);
+        const int zpc = Fmt<F>::kZp ? (int)pc_z[n] : 0;
+#pragma unroll
+        for (int a = 0; a < TM; ++a) {
+            const int m_first = bm * BM + (wm * TM + a) * 16 + 4 * j;
+            store_outputs<F>(acc[a][i], m_first, n, M, N, s_x, rowsum, sc, zpc, y, acc_out);
+        }
+    }
+}
+#undef QOQ_LDS_PTR
+
+// ---------------------------------------------------------------------------
 // Pipelined decode kernel (M <= 64): weight streaming at HBM rate.
 //
 // A workgroup of W waves owns NT 16-channel tiles and the whole K; wave w takes
@@ -847,7 +1059,7 @@ __global__ __launch_bounds__(W * 64) void k_gemm_stream(
 
 constexpr int kCUs = 256;
 
-enum Kind { kSimple = 0, kTile = 2, kWide = 3, kStream = 4 };
+enum Kind { kSimple = 0, kTile = 2, kWide = 3, kStream = 4, kLds = 5 };
 
 struct Plan {
     int kind = kSimple;
@@ -856,7 +1068,8 @@ struct Plan {
     int bn = 256;                      // 16-row-wave tiled kernel: 128 x bn blocks
     int s = 1;                         //   and its K splits (partial sums in the workspace)
     int64_t ws_bytes = 0;
-    int group_m = 4;                   // wide kernel: block rows per XCD raster group
+    int group_m = 4;                   // wide and LDS-pipelined kernels: block rows per XCD raster group
+    int lds_bm = 128;                  // LDS-pipelined kernel: block rows (128 or 256)
     int64_t nblk = 0;
 };
 
@@ -880,16 +1093,25 @@ bool fits_buffer_offsets(int fmt, int64_t M, int64_t N, int64_t K) {
 //     fewer groups each beat a deeper ring, which would not fit the registers
 //     of 16 waves); for 33..64 rows two 32-row workgroups per band of three
 //     channel tiles.
-//   M >= 512: the wide-wave tiled kernel with 128 x 256 blocks.
-//   64 < M < 512: fewer than two 128 x 256 blocks per compute unit exist; the
-//     16-row-wave tiled kernel, split over K when its blocks do not cover the
-//     compute units and a workspace is given.
+//   M > 64, counting 128 x 256 blocks (nb128):
+//     nb128 <= 256 (and at least 128, or M >= 512): the LDS-pipelined kernel
+//       with 128-row blocks, one 8-wave workgroup per compute unit;
+//     nb128 > 256 but 256 x 256 blocks fit one round of the compute units
+//       (M a multiple of 256, UINT4 weights): the same kernel with 256-row
+//       blocks;
+//     otherwise more than 256 blocks, M >= 512: the wide-wave tiled kernel,
+//       two 4-wave workgroups of 128 x 256 per compute unit; M < 512: the
+//       LDS-pipelined kernel with 128-row blocks;
+//     nb128 < 128 and M < 512: the 16-row-wave tiled kernel, split over K
+//       when its blocks do not cover the compute units and a workspace is
+//       given.
 // Shapes whose offsets do not fit the buffer-load kernels take the reference
 // kernel (M <= 64) or the 16-row-wave tiled kernel (M > 64).
 Plan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, bool have_ws) {
     Plan p;
     const int64_t tiles = N / 16;
     const bool fits = fits_buffer_offsets(fmt, M, N, K);
+    const int64_t nb128 = ((M + 127) / 128) * ((N + 255) / 256);  // 128 x 256 blocks
     if (M <= 64) {
         if (fits) {
             p.kind = kStream;
@@ -912,8 +1134,15 @@ Plan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, bool have_ws) {
                 p.w = 2 * ((tiles + 2) / 3) <= kCUs ? 16 : 8;
             }
         }
-    } else if (M >= 512 && fits) {
-        p.kind = kWide;
+    } else if (fits && (M >= 512 || nb128 >= kCUs / 2)) {
+        // 128 x 256 blocks that fill at most one round of the compute units
+        // run as one 8-wave workgroup per CU (two waves per SIMD even then);
+        // with more, 256-row blocks when they fit one round, else the wide
+        // kernel's two 4-wave workgroups per CU.
+        const int64_t nb256 = ((M + 255) / 256) * ((N + 255) / 256);
+        p.kind = kLds;
+        if (nb128 > kCUs && nb256 <= kCUs && M % 256 == 0 && fmt != kFmtW8) p.lds_bm = 256;
+        else if (nb128 > kCUs && M >= 512) p.kind = kWide;
     } else {
         p.kind = kTile;
         const int64_t gm128 = (M + 127) / 128, gn256 = (N + 255) / 256, gn128 = (N + 127) / 128;
@@ -933,7 +1162,7 @@ Plan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, bool have_ws) {
         p.kind = g_force_kind < 0 ? kSimple : g_force_kind;
         if (p.kind == kStream && p.mb == 0) p.mb = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
         if (p.kind == kStream && (M > 64 || !fits)) p.kind = kSimple;
-        if (p.kind == kWide && !fits) p.kind = kTile;
+        if ((p.kind == kWide || p.kind == kLds) && !fits) p.kind = kTile;
     }
     if (g_force_nt) p.nt = g_force_nt;
     if (g_force_r) p.r = g_force_r;
@@ -942,6 +1171,7 @@ Plan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, bool have_ws) {
     if (g_force_gm) p.group_m = g_force_gm;
     if (p.kind == kTile && g_force_nt) p.s = std::max(1, std::min<int>(g_force_nt, (int)(K / kGroup)));
     if (p.kind == kStream && g_force_bn) p.mb = g_force_bn;  // row tiles per workgroup
+    if (p.kind == kLds && g_force_bn) p.lds_bm = g_force_bn;  // block rows
 #endif
     if (p.kind == kStream) {
         const int64_t U = (M + 15) / 16;
@@ -1027,6 +1257,13 @@ void launch_wide_t(const GemmArgs& a) {
                        a.group_m);
 }
 
+template <int F, int BM, int WM>
+void launch_lds_t(const GemmArgs& a) {
+    const unsigned blocks = (unsigned)(((a.M + BM - 1) / BM) * ((a.N + 255) / 256));
+    hipLaunchKernelGGL((k_gemm_lds<F, BM, WM>), dim3(blocks), dim3(512), 0, a.stream, a.xq, a.s_x,
+                       a.rowsum, a.blob, a.s_c, a.M, a.N, a.K, a.y, a.acc_out, a.group_m);
+}
+
 template <int F>
 void launch_simple(const GemmArgs& a) {
     const dim3 grid((unsigned)((a.N / 16 + 3) / 4), (unsigned)((a.M + 63) / 64));
@@ -1042,6 +1279,10 @@ void launch_plan(const Plan& p, const GemmArgs& a) {
             break;
         case kWide:
             launch_wide_t<F, 128, 256, 4>(a);
+            break;
+        case kLds:
+            if (F != kFmtW8 && p.lds_bm == 256) launch_lds_t<F, F == kFmtW8 ? 128 : 256, 2>(a);
+            else launch_lds_t<F, 128, 1>(a);
             break;
         case kTile:
             if (p.bn == 256) launch_tile_t<F, 128, 256, 2, 4>(p, a);

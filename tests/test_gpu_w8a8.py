@@ -88,6 +88,7 @@ GEMM_SHAPES = [
     (129, 32, 640), (257, 80, 128), (512, 512, 1024), (520, 272, 640), (3, 16, 132096),
     (9, 32, 128 * 21), (30, 48, 128 * 67), (48, 64, 128 * 70),
     (200, 272, 128 * 13),
+    (600, 528, 128 * 9), (700, 400, 128 * 10), (200, 16400, 128 * 3), (1024, 8208, 128 * 13),
 ]
 
 
