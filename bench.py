@@ -59,7 +59,8 @@ def parse_args(argv=None):
                    help="instead of the one-line result: per layer (of --workload, or of every "
                         "workload with --all-layers), time the per-call path in each weight/"
                         "activation format -- W4A8 g128 and per-channel, W8A8, W4A16 -- and "
-                        "print one line per layer")
+                        "print one line per layer (for M > 64 also the vendor library's plain "
+                        "INT8 GEMM on the same shape)")
     p.add_argument("--producer", action="store_true",
                    help="instead of the one-line result: time the fused SiLU(gate)*up + "
                         "per-token quantization against the unfused path (torch SiLU*up "
@@ -756,6 +757,27 @@ def format_compare(args, wl, layer):
         torch.cuda.empty_cache()
     best = min(res["formats"], key=lambda f: res["formats"][f]["call_us"])
     res["fastest_call"] = best
+    if M > 64:
+        # Context for the matrix-core ceiling: the vendor library's plain INT8
+        # GEMM (torch._int_mm: INT8 [M,K] x INT8 [K,N] -> INT32, no rescale)
+        # on random INT8 operands of the same shape, over rotating copies.
+        per = M * K + N * K + 4 * M * N
+        R = max(2, math.ceil(args.rotate_mib * 2**20 / per))
+        L = max(R, args.kernel_launches // R * R)
+        g = torch.Generator(device="cpu")
+        g.manual_seed(layer.seed)
+        a = torch.randint(-127, 128, (M, K), dtype=torch.int8, generator=g).to(dev)
+        b = torch.randint(-127, 128, (N, K), dtype=torch.int8, generator=g).to(dev)
+        sets = [(a.clone(), b.clone(), torch.empty((M, N), dtype=torch.int32, device=dev))
+                for _ in range(R)]
+        for st in sets[:2]:
+            torch._int_mm(st[0], st[1].t(), out=st[2])
+        torch.cuda.synchronize()
+        v_us = avg_us([lambda st=st: torch._int_mm(st[0], st[1].t(), out=st[2]) for st in sets], L)
+        res["vendor_int8_gemm"] = {"gemm_us": round(v_us, 3),
+                                   "gemm_TOPS": round(2 * M * N * K / v_us / 1e6, 1)}
+        del sets
+        torch.cuda.empty_cache()
     return res
 
 

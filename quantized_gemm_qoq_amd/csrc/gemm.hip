@@ -1069,7 +1069,6 @@ struct Plan {
     int s = 1;                         //   and its K splits (partial sums in the workspace)
     int64_t ws_bytes = 0;
     int group_m = 4;                   // wide and LDS-pipelined kernels: block rows per XCD raster group
-    int lds_bm = 128;                  // LDS-pipelined kernel: block rows (128 or 256)
     int64_t nblk = 0;
 };
 
@@ -1096,12 +1095,10 @@ bool fits_buffer_offsets(int fmt, int64_t M, int64_t N, int64_t K) {
 //   M > 64, counting 128 x 256 blocks (nb128):
 //     nb128 <= 256 (and at least 128, or M >= 512): the LDS-pipelined kernel
 //       with 128-row blocks, one 8-wave workgroup per compute unit;
-//     nb128 > 256 but 256 x 256 blocks fit one round of the compute units
-//       (M a multiple of 256, UINT4 weights): the same kernel with 256-row
-//       blocks;
-//     otherwise more than 256 blocks, M >= 512: the wide-wave tiled kernel,
-//       two 4-wave workgroups of 128 x 256 per compute unit; M < 512: the
-//       LDS-pipelined kernel with 128-row blocks;
+//     nb128 > 256, M >= 512: the wide-wave tiled kernel, two 4-wave
+//       workgroups of 128 x 256 per compute unit (256-row blocks of the
+//       LDS-pipelined kernel were within 5% of it either way, depending on
+//       the data); M < 512: the LDS-pipelined kernel with 128-row blocks;
 //     nb128 < 128 and M < 512: the 16-row-wave tiled kernel, split over K
 //       when its blocks do not cover the compute units and a workspace is
 //       given.
@@ -1137,12 +1134,8 @@ Plan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, bool have_ws) {
     } else if (fits && (M >= 512 || nb128 >= kCUs / 2)) {
         // 128 x 256 blocks that fill at most one round of the compute units
         // run as one 8-wave workgroup per CU (two waves per SIMD even then);
-        // with more, 256-row blocks when they fit one round, else the wide
-        // kernel's two 4-wave workgroups per CU.
-        const int64_t nb256 = ((M + 255) / 256) * ((N + 255) / 256);
-        p.kind = kLds;
-        if (nb128 > kCUs && nb256 <= kCUs && M % 256 == 0 && fmt != kFmtW8) p.lds_bm = 256;
-        else if (nb128 > kCUs && M >= 512) p.kind = kWide;
+        // with more, the wide kernel's two 4-wave workgroups per CU.
+        p.kind = nb128 > kCUs && M >= 512 ? kWide : kLds;
     } else {
         p.kind = kTile;
         const int64_t gm128 = (M + 127) / 128, gn256 = (N + 255) / 256, gn128 = (N + 127) / 128;
@@ -1171,7 +1164,6 @@ Plan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, bool have_ws) {
     if (g_force_gm) p.group_m = g_force_gm;
     if (p.kind == kTile && g_force_nt) p.s = std::max(1, std::min<int>(g_force_nt, (int)(K / kGroup)));
     if (p.kind == kStream && g_force_bn) p.mb = g_force_bn;  // row tiles per workgroup
-    if (p.kind == kLds && g_force_bn) p.lds_bm = g_force_bn;  // block rows
 #endif
     if (p.kind == kStream) {
         const int64_t U = (M + 15) / 16;
@@ -1281,8 +1273,7 @@ void launch_plan(const Plan& p, const GemmArgs& a) {
             launch_wide_t<F, 128, 256, 4>(a);
             break;
         case kLds:
-            if (F != kFmtW8 && p.lds_bm == 256) launch_lds_t<F, F == kFmtW8 ? 128 : 256, 2>(a);
-            else launch_lds_t<F, 128, 1>(a);
+            launch_lds_t<F, 128, 1>(a);
             break;
         case kTile:
             if (p.bn == 256) launch_tile_t<F, 128, 256, 2, 4>(p, a);
