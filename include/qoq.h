@@ -295,7 +295,7 @@ qoq_status qoq_silu_mul_quantize_act(const uint16_t* gate_up, int64_t M, int64_t
  * than 32 rows, or I < 12288). The outputs are those of
  * qoq_silu_mul_quantize_act bit for bit. A NULL workspace (or a size 0 one)
  * runs the one-pass kernels; a workspace smaller than needed gives
- * QOQ_ERR_SHAPE. Calls that overlap in time must not share a workspace.
+ * QOQ_ERR_WORKSPACE. Calls that overlap in time must not share a workspace.
  * qoq_silu_mul_workspace_bytes returns -1 for an unsupported shape.
  */
 int64_t qoq_silu_mul_workspace_bytes(int64_t M, int64_t I);

@@ -41,7 +41,7 @@ const char* qoq_status_str(int status) {
         case QOQ_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         case QOQ_ERR_MODE: return "unknown quantization mode";
         case QOQ_ERR_HIP: return "HIP runtime error at launch";
-        case QOQ_ERR_WORKSPACE: return "workspace smaller than the GEMM plan needs";
+        case QOQ_ERR_WORKSPACE: return "workspace smaller than the call needs";
         default: return "unknown status";
     }
 }
@@ -216,7 +216,7 @@ qoq_status qoq_silu_mul_quantize_act_ws(const uint16_t* gate_up, int64_t M, int6
         (h && !aligned16(h)) || (workspace && !aligned16(workspace)))
         return QOQ_ERR_ALIGN;
     const int64_t need = qoq::silu_mul_workspace_bytes(M, I);
-    if (workspace && workspace_bytes < need) return QOQ_ERR_SHAPE;
+    if (workspace && workspace_bytes < need) return QOQ_ERR_WORKSPACE;
     return launch_checked([&] {
         qoq::launch_silu_mul_quantize_act_ws(gate_up, M, I, xq, s_x, rowsum, h, need > 0 ? workspace : nullptr,
                                              as_stream(stream));

@@ -204,7 +204,7 @@ def test_silu_mul_split_workspace(lib):
     assert w(16, 512) == 0                  # rows too short to share
     assert w(16, 100) == -1
     f = lib.qoq_silu_mul_quantize_act_ws
-    assert f(A, 16, 24576, A, A, A, NUL, A, 5631, NUL) == ERR_SHAPE  # workspace too small
+    assert f(A, 16, 24576, A, A, A, NUL, A, 5631, NUL) == ERR_WORKSPACE  # workspace too small
     assert f(A, 16, 24576, A, A, A, NUL, U, 5632, NUL) == ERR_ALIGN
     assert f(A, 0, 24576, A, A, A, NUL, NUL, 0, NUL) == OK
     assert f(NUL, 16, 24576, A, A, A, NUL, A, 5632, NUL) == ERR_NULL
