@@ -390,6 +390,71 @@ __global__ __launch_bounds__(kThreads) void k_splitk_reduce(
                                                 out[2] | ((uint32_t)out[3] << 16));
 }
 
+// Epilogue of one wave's TM x TN accumulator tiles (rows m0 .. m0 + 16 TM - 1,
+// channels n0 .. n0 + 16 TN - 1) with the FP16 outputs staged through a
+// wave-private LDS region, 32 rows at a time: each output is written to LDS
+// as it is computed (an accumulator lane holds four rows of one channel), then
+// the rows are stored as 16-byte segments, so each row of the strip leaves in
+// whole 32 TN-byte runs instead of 2-byte pieces. The row stride is padded by
+// 16 bytes so that the four row groups of a write fall in different banks.
+// acc_out, when given, receives the INT32 sums element by element.
+template <int F, int TM, int TN>
+__device__ __forceinline__ void staged_epilogue(const int32x4 (&acc)[TM][TN], uint8_t* region,
+                                                int m0, int n0, int M, int N,
+                                                const uint16_t* __restrict__ s_x,
+                                                const int32_t* __restrict__ rowsum,
+                                                const uint16_t* __restrict__ s_c,
+                                                const uint8_t* __restrict__ pc_z,
+                                                uint16_t* __restrict__ y,
+                                                int32_t* __restrict__ acc_out) {
+    constexpr int kRowBytes = TN * 32;
+    constexpr int kStride = kRowBytes + 16;
+    constexpr int kPass = 2;  // row tiles per pass
+    constexpr int kChunks = kPass * 16 * kRowBytes / 16;
+    static_assert(TM % kPass == 0 && kChunks % kWave == 0, "passes must cover the tiles evenly");
+    // The lane index taken afresh, so that nothing lane-derived from before
+    // the main loop has to stay live through it.
+    const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int c = lane % 16, j = lane / 16;
+    float sc[TN];
+    int zpc[TN];
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+        const int n = n0 + 16 * i + c;
+        sc[i] = n < N ? h2f(s_c[n]) : 0.0f;
+        zpc[i] = Fmt<F>::kZp && n < N ? (int)pc_z[n] : 0;
+    }
+#pragma unroll
+    for (int p = 0; p < TM; p += kPass) {
+#pragma unroll
+        for (int a = p; a < p + kPass; ++a) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int m = m0 + a * 16 + 4 * j + v;
+                const float sx = m < M ? h2f(s_x[m]) : 0.0f;
+                const int rs = Fmt<F>::kZp && m < M ? rowsum[m] : 0;
+#pragma unroll
+                for (int i = 0; i < TN; ++i) {
+                    int r = acc[a][i][v];
+                    if (Fmt<F>::kZp) r -= zpc[i] * rs;
+                    const int n = n0 + 16 * i + c;
+                    if (acc_out && m < M && n < N) acc_out[(size_t)m * N + n] = r;
+                    *reinterpret_cast<uint16_t*>(region + ((a - p) * 16 + 4 * j + v) * kStride +
+                                                 (16 * i + c) * 2) = output_value(r, sx, sc[i]);
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kChunks / kWave; ++k) {
+            const int q = lane + k * kWave;
+            const int row = q / (kRowBytes / 16), col = q % (kRowBytes / 16);
+            const u32x4 out = *reinterpret_cast<const u32x4*>(region + row * kStride + col * 16);
+            const int m = m0 + p * 16 + row, n = n0 + col * 8;
+            if (m < M && n < N) *reinterpret_cast<u32x4*>(y + (size_t)m * N + n) = out;
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Wide-wave tiled kernel (M > 64). The waves of a workgroup sit side by side
 // in N and each one spans all BM rows of the block (TM = BM/16 row tiles, TN
@@ -602,21 +667,15 @@ __global__ __launch_bounds__(WN * 64, 2) void k_gemm_wide(
     }
     if (h < G) wide_compute<F, TM, TN>(acc, lw0, b0q, p0q, lut);
 
-    // Epilogue.
-    const uint8_t* pc_z = blob + code_bytes;
-#pragma unroll
-    for (int i = 0; i < TN; ++i) {
-        const int t = bn * (BN / 16) + wave * TN + i;
-        if (t >= tiles) continue;
-        const int n = 16 * t + c;
-        const float sc = h2f(s_c[n]);
-        const int zpc = Fmt<F>::kZp ? (int)pc_z[n] : 0;
-#pragma unroll
-        for (int a = 0; a < TM; ++a) {
-            const int m_first = bm * BM + a * 16 + 4 * j;
-            store_outputs<F>(acc[a][i], m_first, n, M, N, s_x, rowsum, sc, zpc, y, acc_out);
-        }
-    }
+    // Epilogue through LDS (the activation buffers, free once every wave is
+    // past its last group).
+    static_assert(WN == 4 && 2 * 2 * 16 * (TN * 32 + 16) <= kAVec * 16,
+                  "two epilogue regions must fit each activation buffer");
+    __syncthreads();
+    uint8_t* region = reinterpret_cast<uint8_t*>(wave < 2 ? lds_a0 : lds_a1) +
+                      (wave % 2) * (2 * 16 * (TN * 32 + 16));
+    staged_epilogue<F, TM, TN>(acc, region, bm * BM, (bn * (BN / 16) + wave * TN) * 16, M, N, s_x,
+                               rowsum, s_c, blob + code_bytes, y, acc_out);
 }
 
 // ---------------------------------------------------------------------------
@@ -813,21 +872,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm_lds(
     // No load may still be writing this workgroup's LDS when it exits.
     __builtin_amdgcn_s_waitcnt(kWaitAll);
 
-    // Epilogue.
-    const uint8_t* pc_z = blob + code_bytes;
-#pragma unroll
-    for (int i = 0; i < TN; ++i) {
-        const int t = bn * (BN / 16) + wn * TN + i;
-        if (t >= tiles) continue;
-        const int n = 16 * t + c;
-        const float sc = h2f(s_c[n]);
-        const int zpc = Fmt<F>::kZp ? (int)pc_z[n] : 0;
-#pragma unroll
-        for (int a = 0; a < TM; ++a) {
-            const int m_first = bm * BM + (wm * TM + a) * 16 + 4 * j;
-            store_outputs<F>(acc[a][i], m_first, n, M, N, s_x, rowsum, sc, zpc, y, acc_out);
-        }
-    }
+    // Epilogue through LDS (buffer 0, free once every wave's loads have landed
+    // and every wave is past its last group).
+    static_assert(kW * 2 * 16 * (TN * 32 + 16) <= kStageVec * 16, "epilogue regions must fit buffer 0");
+    __syncthreads();
+    uint8_t* region = reinterpret_cast<uint8_t*>(st0) + wave * (2 * 16 * (TN * 32 + 16));
+    staged_epilogue<F, TM, TN>(acc, region, bm * BM + wm * TM * 16, (bn * (BN / 16) + wn * TN) * 16, M,
+                               N, s_x, rowsum, s_c, blob + code_bytes, y, acc_out);
 }
 #undef QOQ_LDS_PTR
 
