@@ -100,6 +100,60 @@ __device__ __forceinline__ void store4(float4v a, int m_first, int n, int M, int
     }
 }
 
+// Epilogue of one wave's TM x TN accumulator tiles (rows m0 .. m0 + 16 TM - 1,
+// channels n0 .. n0 + 16 TN - 1) with the FP16 outputs staged through a
+// wave-private LDS region, 32 rows at a time, so that they leave as 16-byte
+// row segments (an accumulator lane holds four rows of one channel). The row
+// stride is padded by 16 bytes so that the four row groups of a write fall in
+// different banks. acc_out, when given, receives the FP32 sums on the way.
+template <int TM, int TN>
+__device__ __forceinline__ void w16_staged_epilogue(const float4v (&acc)[TM][TN], uint8_t* region,
+                                                    int m0, int n0, int M, int N,
+                                                    const uint16_t* __restrict__ s_c,
+                                                    uint16_t* __restrict__ y,
+                                                    float* __restrict__ acc_out) {
+    constexpr int kRowBytes = TN * 32;
+    constexpr int kStride = kRowBytes + 16;
+    constexpr int kPass = 2;  // row tiles per pass
+    constexpr int kChunks = kPass * 16 * kRowBytes / 16;
+    static_assert(TM % kPass == 0 && kChunks % kWave == 0, "passes must cover the tiles evenly");
+    // The lane index taken afresh, so that nothing lane-derived from before
+    // the main loop has to stay live through it.
+    const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int c = lane % 16, j = lane / 16;
+    float sc[TN];
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+        const int n = n0 + 16 * i + c;
+        sc[i] = n < N ? h2f(s_c[n]) : 0.0f;
+    }
+#pragma unroll
+    for (int p = 0; p < TM; p += kPass) {
+#pragma unroll
+        for (int a = p; a < p + kPass; ++a) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int m = m0 + a * 16 + 4 * j + v;
+#pragma unroll
+                for (int i = 0; i < TN; ++i) {
+                    const int n = n0 + 16 * i + c;
+                    if (acc_out && m < M && n < N) acc_out[(size_t)m * N + n] = acc[a][i][v];
+                    *reinterpret_cast<uint16_t*>(region + ((a - p) * 16 + 4 * j + v) * kStride +
+                                                 (16 * i + c) * 2) = out_f16(acc[a][i][v], sc[i]);
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kChunks / kWave; ++k) {
+            const int q = lane + k * kWave;
+            const int row = q / (kRowBytes / 16), col = q % (kRowBytes / 16);
+            const u32x4 out = *reinterpret_cast<const u32x4*>(region + row * kStride + col * 16);
+            const int m = m0 + p * 16 + row, n = n0 + col * 8;
+            if (m < M && n < N) *reinterpret_cast<u32x4*>(y + (size_t)m * N + n) = out;
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Streaming kernel (decode, and up to 256 rows on narrow layers): the
 // structure of the W4A8 streaming kernel. A
@@ -331,7 +385,7 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void k_w4a16_tile(
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int wm = wave / WN, wn = wave % WN;
-    const int c = lane % 16, j = lane / 16;
+    const int c = lane % 16;
     const int G = K / kGroup;
     const int tiles = N / 16;
     const int grid_m = (M + BM - 1) / BM, grid_n = (N + BN - 1) / BN;
@@ -416,16 +470,15 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void k_w4a16_tile(
     }
     if (h < G) w16_tile_compute<kG128, TM, TN>(acc, lw0, b0q, p0q, lut, gw_pc);
 
-#pragma unroll
-    for (int i = 0; i < TN; ++i) {
-        const int t = bn * (BN / 16) + wn * TN + i;
-        if (t >= tiles) continue;
-        const int n = 16 * t + c;
-        const float sc = h2f(s_c[n]);
-#pragma unroll
-        for (int a = 0; a < TM; ++a)
-            store4(acc[a][i], bm * BM + (wm * TM + a) * 16 + 4 * j, n, M, N, sc, y, acc_out);
-    }
+    // Epilogue through LDS (the activation buffers, free once every wave is
+    // past its last group; half the waves in each).
+    constexpr int kRegion = 2 * 16 * (TN * 32 + 16);
+    static_assert(WM * WN / 2 * kRegion <= kAVec * 16, "epilogue regions must fit the buffers");
+    __syncthreads();
+    uint8_t* region = reinterpret_cast<uint8_t*>(wave < WM * WN / 2 ? lds_a0 : lds_a1) +
+                      (wave % (WM * WN / 2)) * kRegion;
+    w16_staged_epilogue<TM, TN>(acc, region, bm * BM + wm * TM * 16, (bn * (BN / 16) + wn * TN) * 16, M,
+                                N, s_c, y, acc_out);
 }
 
 // ---------------------------------------------------------------------------
