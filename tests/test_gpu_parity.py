@@ -124,6 +124,8 @@ GEMM_SHAPES = [
     # LDS-pipelined kernel, 128-row blocks: group counts 0, 1 and 2 past a
     # multiple of its three-buffer loop, ragged rows and channels
     (600, 528, 128 * 9), (700, 400, 128 * 10), (200, 16400, 128 * 3),
+    # ... one and two groups, one and three channel tiles
+    (520, 16, 128), (1024, 48, 256),
     # the wide kernel: too many blocks for one round, ragged rows and channels
     (1024, 8208, 128 * 13), (640, 16400, 128 * 5),
 ]
