@@ -568,7 +568,7 @@ __global__ __launch_bounds__(WN * 64, 2) void k_gemm_wide(
 
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int c = lane % 16, j = lane / 16;
+    const int c = lane % 16;
     const int G = K / kGroup;
     const int U = (M + 15) / 16;
     const int tiles = N / 16;
@@ -775,7 +775,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_lds(
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int wm = wave / WN, wn = wave % WN;
-    const int c = lane % 16, j = lane / 16;
+    const int c = lane % 16;
     const int G = K / kGroup;
     const int U = (M + 15) / 16;
     const int tiles = N / 16;
