@@ -455,6 +455,36 @@ __device__ __forceinline__ void staged_epilogue(const int32x4 (&acc)[TM][TN], ui
     }
 }
 
+// The INT32 partial sums of one wave's TM x TN accumulator tiles, staged
+// through a wave-private LDS region one row tile (16 rows) at a time and
+// stored as 16-byte row segments of dst (an [M, N] slice of the workspace).
+template <int TM, int TN>
+__device__ __forceinline__ void staged_partials(const int32x4 (&acc)[TM][TN], uint8_t* region,
+                                                int m0, int n0, int M, int N,
+                                                int32_t* __restrict__ dst) {
+    constexpr int kRowBytes = TN * 64;
+    constexpr int kChunks = 16 * kRowBytes / 16;
+    static_assert(kChunks % kWave == 0, "a row tile must split evenly over the lanes");
+    const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int c = lane % 16, j = lane / 16;
+#pragma unroll
+    for (int a = 0; a < TM; ++a) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+            for (int i = 0; i < TN; ++i)
+                *reinterpret_cast<int32_t*>(region + (4 * j + v) * kRowBytes + (16 * i + c) * 4) = acc[a][i][v];
+#pragma unroll
+        for (int k = 0; k < kChunks / kWave; ++k) {
+            const int q = lane + k * kWave;
+            const int row = q / (kRowBytes / 16), col = q % (kRowBytes / 16);
+            const int32x4 out = *reinterpret_cast<const int32x4*>(region + row * kRowBytes + col * 16);
+            const int m = m0 + a * 16 + row, n = n0 + col * 4;
+            if (m < M && n < N) *reinterpret_cast<int32x4*>(dst + (size_t)m * N + n) = out;
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Wide-wave tiled kernel (M > 64). The waves of a workgroup sit side by side
 // in N and each one spans all BM rows of the block (TM = BM/16 row tiles, TN
@@ -749,7 +779,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_lds(
     const int8_t* __restrict__ xq, const uint16_t* __restrict__ s_x,
     const int32_t* __restrict__ rowsum, const uint8_t* __restrict__ blob,
     const uint16_t* __restrict__ s_c, int M, int N, int K, uint16_t* __restrict__ y,
-    int32_t* __restrict__ acc_out, int group_m) {
+    int32_t* __restrict__ acc_out, int group_m, int S, int32_t* __restrict__ part) {
     constexpr int kThr = 512, kW = 8, BN = 256;
     constexpr int WN = kW / WM;
     constexpr int TM = BM / 16 / WM, TN = BN / WN / 16;
@@ -781,10 +811,16 @@ __global__ __launch_bounds__(512, 1) void k_gemm_lds(
     const int tiles = N / 16;
     const int grid_m = (M + BM - 1) / BM, grid_n = (N + BN - 1) / BN;
 
+    // With S > 1 the grid holds S copies of the block grid, copy s taking the
+    // groups [G*s/S, G*(s+1)/S) and writing its INT32 partial sums to part[s].
+    const int nblocks = grid_m * grid_n;
+    const int split = blockIdx.x / nblocks;
+    const int g0 = (int)((int64_t)G * split / S);
+    const int Gc = (int)((int64_t)G * (split + 1) / S) - g0;  // >= 1: the plan keeps S <= G
+
     // Block renumbering: contiguous range per XCD, then groups of group_m
     // block rows.
-    int pid = blockIdx.x;
-    const int nblocks = grid_m * grid_n;
+    int pid = blockIdx.x - split * nblocks;
     if (nblocks % 8 == 0) pid = (pid % 8) * (nblocks / 8) + pid / 8;
     const int per_group = group_m * grid_n;
     const int first_m = (pid / per_group) * group_m;
@@ -853,32 +889,39 @@ __global__ __launch_bounds__(512, 1) void k_gemm_lds(
         __builtin_amdgcn_s_waitcnt(kWaitStep);
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        issue(refill, min(g + 2, G - 1));
+        issue(refill, g0 + min(g + 2, Gc - 1));
         __builtin_amdgcn_sched_barrier(0);
         lds_compute<F, TM, TN>(acc, cur + la, cur + lb, reinterpret_cast<const uint8_t*>(cur) + lp);
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    issue(st0, 0);
-    issue(st1, min(1, G - 1));
+    issue(st0, g0);
+    issue(st1, g0 + min(1, Gc - 1));
     int h = 0;
-    for (; h + 2 < G; h += 3) {
+    for (; h + 2 < Gc; h += 3) {
         step(st0, st2, h);
         step(st1, st0, h + 1);
         step(st2, st1, h + 2);
     }
-    if (h < G) step(st0, st2, h);
-    if (h + 1 < G) step(st1, st0, h + 1);
+    if (h < Gc) step(st0, st2, h);
+    if (h + 1 < Gc) step(st1, st0, h + 1);
     // No load may still be writing this workgroup's LDS when it exits.
     __builtin_amdgcn_s_waitcnt(kWaitAll);
 
     // Epilogue through LDS (buffer 0, free once every wave's loads have landed
-    // and every wave is past its last group).
-    static_assert(kW * 2 * 16 * (TN * 32 + 16) <= kStageVec * 16, "epilogue regions must fit buffer 0");
+    // and every wave is past its last group): with S > 1 the raw partial sums
+    // (the reduction kernel adds them and applies the zero-point compensation
+    // and the rescale once), else the outputs.
+    static_assert(kW * 2 * 16 * (TN * 32 + 16) <= kStageVec * 16 && kW * 16 * TN * 64 <= kStageVec * 16,
+                  "epilogue regions must fit buffer 0");
     __syncthreads();
-    uint8_t* region = reinterpret_cast<uint8_t*>(st0) + wave * (2 * 16 * (TN * 32 + 16));
-    staged_epilogue<F, TM, TN>(acc, region, bm * BM + wm * TM * 16, (bn * (BN / 16) + wn * TN) * 16, M,
-                               N, s_x, rowsum, s_c, blob + code_bytes, y, acc_out);
+    const int m0 = bm * BM + wm * TM * 16, n0 = (bn * (BN / 16) + wn * TN) * 16;
+    if (part)
+        staged_partials<TM, TN>(acc, reinterpret_cast<uint8_t*>(st0) + wave * (16 * TN * 64), m0, n0, M,
+                                N, part + (size_t)split * M * N);
+    else
+        staged_epilogue<F, TM, TN>(acc, reinterpret_cast<uint8_t*>(st0) + wave * (2 * 16 * (TN * 32 + 16)),
+                                   m0, n0, M, N, s_x, rowsum, s_c, blob + code_bytes, y, acc_out);
 }
 #undef QOQ_LDS_PTR
 
@@ -1144,17 +1187,17 @@ bool fits_buffer_offsets(int fmt, int64_t M, int64_t N, int64_t K) {
 //     of 16 waves); for 33..64 rows two 32-row workgroups per band of three
 //     channel tiles.
 //   M > 64, counting 128 x 256 blocks (nb128):
-//     nb128 <= 256 (and at least 128, or M >= 512): the LDS-pipelined kernel
-//       with 128-row blocks, one 8-wave workgroup per compute unit;
+//     nb128 <= 256: the LDS-pipelined kernel with 128-row blocks, one 8-wave
+//       workgroup per compute unit; below 128 blocks, with a workspace, split
+//       over K into min(8, 256 / nb128) ranges (the split sums are added by
+//       the reduction kernel); without one, M >= 512 runs unsplit and
+//       M < 512 takes the 16-row-wave tiled kernel;
 //     nb128 > 256, M >= 512: the wide-wave tiled kernel, two 4-wave
 //       workgroups of 128 x 256 per compute unit (256-row blocks of the
 //       LDS-pipelined kernel were within 5% of it either way, depending on
-//       the data); M < 512: the LDS-pipelined kernel with 128-row blocks;
-//     nb128 < 128 and M < 512: the 16-row-wave tiled kernel, split over K
-//       when its blocks do not cover the compute units and a workspace is
-//       given.
+//       the data); M < 512: the LDS-pipelined kernel with 128-row blocks.
 // Shapes whose offsets do not fit the buffer-load kernels take the reference
-// kernel (M <= 64) or the 16-row-wave tiled kernel (M > 64).
+// kernel (M <= 64) or the 16-row-wave tiled kernel, split over K (M > 64).
 Plan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, bool have_ws) {
     Plan p;
     const int64_t tiles = N / 16;
@@ -1182,11 +1225,15 @@ Plan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, bool have_ws) {
                 p.w = 2 * ((tiles + 2) / 3) <= kCUs ? 16 : 8;
             }
         }
-    } else if (fits && (M >= 512 || nb128 >= kCUs / 2)) {
+    } else if (fits && (M >= 512 || nb128 >= kCUs / 2 || have_ws)) {
         // 128 x 256 blocks that fill at most one round of the compute units
-        // run as one 8-wave workgroup per CU (two waves per SIMD even then);
-        // with more, the wide kernel's two 4-wave workgroups per CU.
+        // run as one 8-wave workgroup per CU (two waves per SIMD even then),
+        // split over K (at least two groups per split, at most 8 splits) until
+        // they fill about one round; with more blocks, the wide kernel's two
+        // 4-wave workgroups per CU.
         p.kind = nb128 > kCUs && M >= 512 ? kWide : kLds;
+        if (p.kind == kLds && nb128 < kCUs / 2)
+            p.s = (int)std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(8, kCUs / nb128), K / kGroup / 2));
     } else {
         p.kind = kTile;
         const int64_t gm128 = (M + 127) / 128, gn256 = (N + 255) / 256, gn128 = (N + 127) / 128;
@@ -1213,7 +1260,8 @@ Plan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, bool have_ws) {
     if (g_force_w) p.w = g_force_w;
     if (g_force_bn) p.bn = g_force_bn;
     if (g_force_gm) p.group_m = g_force_gm;
-    if (p.kind == kTile && g_force_nt) p.s = std::max(1, std::min<int>(g_force_nt, (int)(K / kGroup)));
+    if ((p.kind == kTile || p.kind == kLds) && g_force_nt)
+        p.s = std::max(1, std::min<int>(g_force_nt, (int)(K / kGroup)));
     if (p.kind == kStream && g_force_bn) p.mb = g_force_bn;  // row tiles per workgroup
 #endif
     if (p.kind == kStream) {
@@ -1221,7 +1269,7 @@ Plan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, bool have_ws) {
         p.mgrid = (int)((U + p.mb - 1) / p.mb);
         p.nblk = (tiles + p.nt - 1) / p.nt;
     }
-    if (p.kind != kTile) p.s = 1;
+    if (p.kind != kTile && p.kind != kLds) p.s = 1;
     p.ws_bytes = p.s > 1 ? (int64_t)p.s * M * N * 4 : 0;
     if (!have_ws) p.s = 1;
     return p;
@@ -1301,10 +1349,17 @@ void launch_wide_t(const GemmArgs& a) {
 }
 
 template <int F, int BM, int WM>
-void launch_lds_t(const GemmArgs& a) {
-    const unsigned blocks = (unsigned)(((a.M + BM - 1) / BM) * ((a.N + 255) / 256));
+void launch_lds_t(const Plan& p, const GemmArgs& a) {
+    const unsigned blocks = (unsigned)(((a.M + BM - 1) / BM) * ((a.N + 255) / 256) * p.s);
+    int32_t* part = p.s > 1 ? a.part : nullptr;
     hipLaunchKernelGGL((k_gemm_lds<F, BM, WM>), dim3(blocks), dim3(512), 0, a.stream, a.xq, a.s_x,
-                       a.rowsum, a.blob, a.s_c, a.M, a.N, a.K, a.y, a.acc_out, a.group_m);
+                       a.rowsum, a.blob, a.s_c, a.M, a.N, a.K, a.y, a.acc_out, a.group_m, p.s, part);
+    if (part) {
+        const int64_t quads = (int64_t)a.M * a.N / 4;
+        hipLaunchKernelGGL(k_splitk_reduce<F>, dim3((unsigned)((quads + kThreads - 1) / kThreads)),
+                           dim3(kThreads), 0, a.stream, part, p.s, a.s_x, a.rowsum,
+                           a.blob + code_bytes_of(F, a.N, a.K), a.s_c, a.M, a.N, a.y, a.acc_out);
+    }
 }
 
 template <int F>
@@ -1324,7 +1379,7 @@ void launch_plan(const Plan& p, const GemmArgs& a) {
             launch_wide_t<F, 128, 256, 4>(a);
             break;
         case kLds:
-            launch_lds_t<F, 128, 1>(a);
+            launch_lds_t<F, 128, 1>(p, a);
             break;
         case kTile:
             if (p.bn == 256) launch_tile_t<F, 128, 256, 2, 4>(p, a);
