@@ -383,8 +383,8 @@ def run_layer(args, wl, layer):
 def main(argv=None) -> int:
     args = parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the path is single-GPU and no multi-GPU figure is produced.", file=sys.stderr)
+        print(f"bench.py: the path runs on one GPU only (asked for --gpus {args.gpus}); "
+              "no multi-GPU figure is produced.", file=sys.stderr)
         return 2
     if args.steps < 1:
         print("bench.py: --steps must be >= 1", file=sys.stderr)
