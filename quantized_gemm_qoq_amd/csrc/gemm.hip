@@ -719,7 +719,9 @@ __global__ __launch_bounds__(WN * 64, 2) void k_gemm_wide(
 // so the wait leaves the next group's loads in flight), then one barrier
 // publishes the group to all waves. The three buffers are separate arrays
 // named by fixed code (three steps per loop iteration), so that the compiler
-// can tell the loads into one buffer from the reads of another.
+// can tell the loads into one buffer from the reads of another. Small grids
+// split K over S copies of the block grid; each copy writes its exact INT32
+// partial sums and the split-K reduction kernel finishes them.
 template <int F, int TM, int TN>
 __device__ __forceinline__ void lds_compute(int32x4 (&acc)[TM][TN], const u32x4* la,
                                             const u32x4* lb, const uint8_t* lp) {
