@@ -200,6 +200,7 @@ def test_silu_mul_split_workspace(lib):
     assert w(64, 14336) == 0                # enough rows for the one-pass kernel
     assert w(16, 11008) == 0                # rows short enough for it
     assert w(16, 12288) == 16 * 12 * 4 + 16 * 256
+    assert w(32, 12288) > 0 and w(33, 24576) == 0  # at most 32 rows (two row tiles) split
     assert w(512, 14336) == 0               # enough rows: one pass
     assert w(16, 512) == 0                  # rows too short to share
     assert w(16, 100) == -1
