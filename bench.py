@@ -152,6 +152,8 @@ def pmc_summary(args, wl, layer) -> int:
                         if mode is None:
                             continue
                         key = ("w4a8_gemm_" + mode) if mode != "w8a8" else "w8a8_gemm"
+                        if "k_splitk_reduce" in name:
+                            key += "+reduce"  # the split-K plan's second launch, added below
                     elif "k_quantize_act" in name:
                         key = "quantize_act"
                     elif "copyBuffer" in name:
@@ -176,14 +178,19 @@ def pmc_summary(args, wl, layer) -> int:
                f"python3 bench.py --workload {wl.name} --layer {layer.name} --profile-launches 3",
                f"python3 bench.py --workload {wl.name} --layer {layer.name} --pmc-summary <dir1> <dir2>"],
            "kernels": {}}
-    for key in sorted({k for k, _ in med if k != "copy"}):
+    for key in sorted({k for k, _ in med if k != "copy" and not k.endswith("+reduce")}):
         fk, wk = med.get((key, "FETCH_SIZE")), med.get((key, "WRITE_SIZE"))
         if fk is None or wk is None:
             continue
-        fb, wb = fk * 1024 * fs, wk * 1024 * ws
+        # a GEMM call of a split-K plan is two launches: both count
+        rf, rw = med.get((key + "+reduce", "FETCH_SIZE"), 0.0), med.get((key + "+reduce", "WRITE_SIZE"), 0.0)
+        fb, wb = (fk + rf) * 1024 * fs, (wk + rw) * 1024 * ws
         out["kernels"][key] = {"FETCH_SIZE_KiB": fk, "WRITE_SIZE_KiB": wk,
                                "hbm_read_bytes": round(fb), "hbm_write_bytes": round(wb),
                                "hbm_bytes": round(fb + wb)}
+        if rf or rw:
+            out["kernels"][key]["reduce_FETCH_SIZE_KiB"] = rf
+            out["kernels"][key]["reduce_WRITE_SIZE_KiB"] = rw
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     with open(traffic_path(wl.name, layer.name), "w") as f:
         json.dump(out, f, indent=1)
