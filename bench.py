@@ -34,13 +34,18 @@ import time
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0  # MI355X dense INT8 MFMA (5.0 POPS)
 
+# The default run: the decode layer of the one-line result, and the prefill
+# layer of the metric's large-M half (reported in the same line as "large_m").
+DEFAULT_WORKLOAD = "llama3_8b_qkv_decode"
+LARGE_M_WORKLOAD, LARGE_M_LAYER = "llama3_8b_prefill", "llama3_8b_gate_up_m4096"
+
 
 def parse_args(argv=None):
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=2000)
     p.add_argument("--warmup", type=int, default=100)
-    p.add_argument("--workload", default="llama3_8b_qkv_decode")
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--rotate-mib", type=int, default=1536,
                    help="total size of the rotating buffer copies")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -69,6 +74,9 @@ def parse_args(argv=None):
                    help="instead of the one-line result: time KV4 decode attention (4-bit "
                         "cache, SmoothAttention) at the serving shapes next to torch's FP16 "
                         "attention on an FP16 cache of the same shape")
+    p.add_argument("--no-large-m", action="store_true",
+                   help="leave the large-M half (Llama-3-8B prefill gate_up, M=4096) out of the "
+                        "default run's line")
     p.add_argument("--pmc-summary", nargs="+", default=None, metavar="DIR",
                    help="instead of timing: read rocprofv3 counter CSVs (FETCH_SIZE run, "
                         "WRITE_SIZE run) of a --profile-launches run and write the traffic "
@@ -353,7 +361,8 @@ def run_layer(args, wl, layer):
     else:
         roofline = {"bound": "mfma", "achieved": dk["TOPS"], "peak": INT8_PEAK_TOPS,
                     "unit": "TOPS", "frac": round(dk["TOPS"] / INT8_PEAK_TOPS, 4),
-                    "traffic": traffic, "kernel": dominant, "algorithmic_bytes": dk["bytes"]}
+                    "traffic": traffic, "kernel": dominant, "algorithmic_ops": 2 * M * N * K,
+                    "algorithmic_bytes": dk["bytes"]}
 
     # ---- CPU baseline: the oracle on the host cores, same step, bounded sample
     cpu = None
@@ -467,6 +476,16 @@ def main(argv=None) -> int:
     out = run_layer(args, wl, layer)
     if isinstance(out, int):
         return out
+    if args.workload == DEFAULT_WORKLOAD and args.layer is None and not args.no_large_m:
+        # The metric's large-M half: TOPS and % of INT8 peak on a prefill layer.
+        wl2 = workloads.WORKLOADS[LARGE_M_WORKLOAD]
+        layer2 = [l for l in wl2.layers if l.name == LARGE_M_LAYER][0]
+        big = run_layer(args, wl2, layer2)
+        if isinstance(big, int):
+            return big
+        out["large_m"] = {k: big[k] for k in ("metric", "value", "unit", "ms_per_step", "dtype",
+                                              "data", "config", "step_TOPS", "kernels", "roofline",
+                                              "cpu_baseline")}
     print(json.dumps(out))
     return 0
 
@@ -826,6 +845,18 @@ def profile_launches(args, qoq, torch, dev, x_dev, packed, modes, M, N, K) -> in
     return 0
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(layer, modes, s, bound, seconds):
     """Time the oracle (the plain C reference, as it stands) on the host cores
     over the same step on the first `rows` token rows of the workload, with
@@ -878,7 +909,7 @@ def cpu_baseline(layer, modes, s, bound, seconds):
         work = sum(2 * rows * N * K for _ in modes)
         value, unit = work / dt / 1e12, "TOPS"
     return {"value": round(value, 4), "unit": unit,
-            "cores": oracle.num_threads(), "kind": "oracle",
+            "cores": oracle.num_threads(), "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{reps} step(s) on the first {rows} of {M} token rows (per-token "
                       f"quantization + {len(modes)} GEMM(s) + epilogue over all N={N} "
                       f"channels), {dt * 1e3:.1f} ms each; rate = the sample's algorithmic "

@@ -238,6 +238,57 @@ def gemm_points(mode, xq, q, s_g, z, ms, ns):
     return acc
 
 
+def weights_int(mode, q, s_g, z):
+    """The integer weights the accumulator contracts, [N, K] int32: g128
+    (q - z[n, k/128]) * s_g[n, k/128], per-channel q - z[n] (the same values
+    orc_gemm forms row by row)."""
+    q = _c(q, np.uint8).astype(np.int32)
+    if mode == MODE_G128:
+        zz = np.repeat(_c(z, np.uint8).astype(np.int32), GROUP, axis=1)
+        ss = np.repeat(_c(s_g, np.uint8).astype(np.int32), GROUP, axis=1)
+        return (q - zz) * ss
+    if mode == MODE_PER_CHANNEL:
+        return q - _c(z, np.uint8).astype(np.int32)[:, None]
+    raise ValueError("bad mode")
+
+
+# Output channels per library product in the matmul forms below (bounds the
+# float64 copy of the weights to a few hundred MB).
+_CHANNEL_SLICE = 2048
+
+
+def _exact_int_matmul(xf, wf):
+    """xf [M,K] @ wf [n,K]^T in float64 for integer-valued operands, returned
+    as int32 (an error if a sum leaves the int32 range, as in orc_gemm). Exact:
+    every product and every partial sum is an integer of magnitude at most
+    max_m sum_k |x[m,k]| * max |w|, checked below 2^53, so float64 holds every
+    intermediate exactly whatever order the library adds them in."""
+    if xf.size and wf.size and np.abs(xf).sum(axis=1).max() * np.abs(wf).max() >= 2.0**53:
+        raise OverflowError("partial sums could exceed 2^53")
+    r = xf @ wf.T
+    if r.size and (r.max() > 2.0**31 - 1 or r.min() < -(2.0**31)):
+        raise OverflowError("accumulator outside int32")
+    return r.astype(np.int32)
+
+
+def gemm_matmul(mode, xq, q, s_g, z):
+    """The accumulator of gemm() [M, N] int32, computed as library matrix
+    products (numpy float64, one per slice of output channels) of Xq and the
+    integer weights of weights_int(): the definition acc = Xq . W8^T with a
+    matmul as its one step, exact as _exact_int_matmul states. For shapes the C
+    loops of gemm() take minutes over."""
+    xf = _c(xq, np.int8).astype(np.float64)
+    q = _c(q, np.uint8)
+    M, N = xf.shape[0], q.shape[0]
+    acc = np.empty((M, N), np.int32)
+    for n0 in range(0, N, _CHANNEL_SLICE):
+        n1 = min(N, n0 + _CHANNEL_SLICE)
+        sg = None if s_g is None else np.asarray(s_g)[n0:n1]
+        zz = np.asarray(z)[n0:n1]
+        acc[:, n0:n1] = _exact_int_matmul(xf, weights_int(mode, q[n0:n1], sg, zz).astype(np.float64))
+    return acc
+
+
 def epilogue(acc, s_x, s_c):
     """Y = acc * s_x * s_c in fp64 (exact), shape [M,N]."""
     acc = _c(acc, np.int32)
@@ -318,6 +369,19 @@ def gemm_w8_points(xq, q, ms, ns):
     return acc
 
 
+def gemm_w8_matmul(xq, q):
+    """The accumulator of gemm_w8() [M, N] int32 as library matrix products in
+    float64 (exact, as for gemm_matmul)."""
+    xf = _c(xq, np.int8).astype(np.float64)
+    q = _c(q, np.int8)
+    M, N = xf.shape[0], q.shape[0]
+    acc = np.empty((M, N), np.int32)
+    for n0 in range(0, N, _CHANNEL_SLICE):
+        n1 = min(N, n0 + _CHANNEL_SLICE)
+        acc[:, n0:n1] = _exact_int_matmul(xf, q[n0:n1].astype(np.float64))
+    return acc
+
+
 def forward_w8(x_bits, w_bits):
     """The W8A8 path on the host: quantize both sides, contract, rescale."""
     xq, s_x, rowsum = quantize_act(x_bits)
@@ -357,6 +421,28 @@ def gemm_w4a16_points(mode, x_bits, s_c, q, s_g, z, ms, ns):
     _check(_load().orc_gemm_w4a16_points(mode, _p(x), _p(_c(s_c, np.uint16)), _p(q), _p(sg),
                                          _p(_c(z, np.uint8)), M, N, K, len(ms), _p(ms), _p(ns),
                                          _p(y), _p(a)), "gemm_w4a16_points")
+    return y, a
+
+
+def gemm_w4a16_matmul(mode, x_bits, s_c, q, s_g, z):
+    """(y, absum) of gemm_w4a16() as library matrix products in float64: y =
+    (X . W8^T) * s_c[n] and absum = (|X| . |W8|^T) * s_c[n], with X the exact
+    FP16 values and W8 the integer weights of weights_int(). The float64 sums
+    are not exact here (X is not integral); their rounding, at most about
+    K * 2^-53 * absum, is many orders below any FP32 accumulation bound."""
+    x = f16_bits_to_f64(_c(x_bits, np.uint16)).reshape(np.shape(x_bits))
+    xa = np.abs(x)
+    q = _c(q, np.uint8)
+    sc = f16_bits_to_f64(_c(s_c, np.uint16))
+    M, N = x.shape[0], q.shape[0]
+    y = np.empty((M, N), np.float64)
+    a = np.empty((M, N), np.float64)
+    for n0 in range(0, N, _CHANNEL_SLICE):
+        n1 = min(N, n0 + _CHANNEL_SLICE)
+        sg = None if s_g is None else np.asarray(s_g)[n0:n1]
+        w = weights_int(mode, q[n0:n1], sg, np.asarray(z)[n0:n1]).astype(np.float64)
+        y[:, n0:n1] = (x @ w.T) * sc[None, n0:n1]
+        a[:, n0:n1] = (xa @ np.abs(w).T) * sc[None, n0:n1]
     return y, a
 
 

@@ -318,14 +318,18 @@ def qoq_gemm_workspace_bytes(mode, M: int, N: int, K: int) -> int:
 
 
 _workspaces = {}
+_retired = []  # superseded workspaces: kept alive, a captured graph may still use them
 
 
 def gemm_workspace(mode, M: int, N: int, K: int, device) -> Optional[torch.Tensor]:
-    """The device's shared workspace when the plan for this shape uses one
-    (split-K partial sums), else None. ``mode`` is a W4 mode or ``"w8a8"``.
+    """The shared workspace of the device's current stream when the plan for
+    this shape uses one (split-K partial sums), else None. ``mode`` is a W4
+    mode or ``"w8a8"``.
 
-    One workspace per device is shared by every call that does not bring its
-    own, so calls issued concurrently on different streams must pass their own."""
+    One workspace per (device, stream) serves every call on that stream that
+    does not bring its own; calls on different streams never share one. It
+    only grows: a workspace replaced by a larger one is kept alive until the
+    process ends, so a HIP graph captured with it replays on valid memory."""
     if mode == W8A8:
         need = qoq_w8a8_gemm_workspace_bytes(M, N, K)
     else:
@@ -333,10 +337,13 @@ def gemm_workspace(mode, M: int, N: int, K: int, device) -> Optional[torch.Tenso
     if need <= 0:
         return None
     dev = torch.device(device)
-    key = (dev.type, dev.index if dev.index is not None else torch.cuda.current_device())
+    index = dev.index if dev.index is not None else torch.cuda.current_device()
+    key = (index, torch.cuda.current_stream(index).cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < need:
-        ws = torch.zeros((max(need, 1 << 20),), dtype=torch.uint8, device=dev)
+        if ws is not None:
+            _retired.append(ws)
+        ws = torch.zeros((max(need, 1 << 20),), dtype=torch.uint8, device=torch.device("cuda", index))
         _workspaces[key] = ws
     return ws
 
@@ -347,8 +354,8 @@ def qoq_w4a8_gemm(mode, xq: torch.Tensor, s_x: torch.Tensor, rowsum: Optional[to
     """Y [M,N] fp16 = rescale(sum_k xq * unpack(blob)); acc_out (int32 [M,N]) optional.
 
     xq: packed activations from qoq_quantize_act (M is the length of s_x).
-    workspace: "auto" (the device's shared workspace), None (a plan that needs
-    none) or a zero-initialised uint8 tensor of qoq_gemm_workspace_bytes()."""
+    workspace: "auto" (the shared workspace of the current stream), None (a
+    plan that needs none) or a uint8 tensor of qoq_gemm_workspace_bytes()."""
     mode = _mode(mode)
     _need(xq, torch.int8, "xq")
     _need(s_x, torch.float16, "s_x")

@@ -1006,10 +1006,10 @@ __global__ __launch_bounds__(W * 64) void k_gemm_stream(
     // own slice and the epilogue adds the slices in wave order when they fit
     // in 96 KB (then nothing needs zeroing and no barrier precedes the first
     // loads); otherwise the waves add into one zeroed copy.
-    // red[((s * kPairs + p) * 4 + v) * 64 + lane]: row v of pair p in lane
-    // order (conflict-free), slice s.
-    constexpr bool kSlices = W * kPairs * 4 * kWave * 4 <= 96 * 1024;
-    __shared__ int32_t red[(kSlices ? W : 1) * kPairs * 4 * kWave];
+    // red[(s * kPairs + p) * 64 + lane]: the four accumulator rows of pair p
+    // held by a lane, one 16-byte LDS access per lane and pair, slice s.
+    constexpr bool kSlices = W * kPairs * kWave * 16 <= 96 * 1024;
+    __shared__ int32x4 red[(kSlices ? W : 1) * kPairs * kWave];
 
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -1090,7 +1090,7 @@ __global__ __launch_bounds__(W * 64) void k_gemm_stream(
         }
     }
     if (!kSlices) {
-        for (int i = threadIdx.x; i < kPairs * 4 * kWave; i += kThr) red[i] = 0;
+        for (int i = threadIdx.x; i < kPairs * kWave; i += kThr) red[i] = int32x4{0, 0, 0, 0};
         __syncthreads();
     }
     for (int h = 0; h < main_count; h += R) {
@@ -1113,13 +1113,15 @@ __global__ __launch_bounds__(W * 64) void k_gemm_stream(
 #pragma unroll
     for (int i = 0; i < NT; ++i)
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+        for (int mb = 0; mb < MB; ++mb) {
+            const int idx = (i * MB + mb) * kWave + lane;
+            if (kSlices) {
+                red[wave * kPairs * kWave + idx] = acc[i][mb];
+            } else {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int idx = ((i * MB + mb) * 4 + v) * kWave + lane;
-                if (kSlices) red[wave * kPairs * 4 * kWave + idx] = acc[i][mb][v];
-                else atomicAdd(&red[idx], acc[i][mb][v]);
+                for (int v = 0; v < 4; ++v) atomicAdd(reinterpret_cast<int*>(red + idx) + v, acc[i][mb][v]);
             }
+        }
     __syncthreads();
 
 #pragma unroll
@@ -1131,22 +1133,224 @@ __global__ __launch_bounds__(W * 64) void k_gemm_stream(
         if (t >= tiles) continue;
         const int n = 16 * t + c;
         const int m_first = 16 * (u0 + mb) + 4 * j;
+        // all slices' reads issued together, then added in wave order
+        int32x4 r4;
+        if (kSlices) {
+            int32x4 part[W];
+#pragma unroll
+            for (int w2 = 0; w2 < W; ++w2) part[w2] = red[(w2 * kPairs + p) * kWave + lane];
+            r4 = part[0];
+#pragma unroll
+            for (int w2 = 1; w2 < W; ++w2) r4 += part[w2];
+        } else {
+            r4 = red[p * kWave + lane];
+        }
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int m = m_first + v;
             if (m < M) {
-                int r = 0;
-                if (kSlices) {
-                    for (int w2 = 0; w2 < W; ++w2) r += red[((w2 * kPairs + p) * 4 + v) * kWave + lane];
-                } else {
-                    r = red[(p * 4 + v) * kWave + lane];
-                }
+                int r = r4[v];
                 if (Fmt<F>::kZp) r -= ep_z[e] * ep_rs[e][v];
                 const size_t o = (size_t)m * N + n;
                 if (acc_out) acc_out[o] = r;
                 y[o] = output_value(r, ep_sx[e][v], ep_sc[e]);
             }
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Split-K decode kernel (M <= 64): weight streaming at HBM rate with every
+// weight byte requested once.
+//
+// Workgroup b owns a band of NT 16-channel tiles, every row tile of the call
+// (MB of them) and one of S contiguous K-slices; its W waves split the slice's
+// groups and stream them through a ring of R register sets exactly as in
+// k_gemm_stream. The waves' partial tiles are added in LDS (one 16-byte slot
+// per lane and tile pair, added in wave order). With S > 1 the slices of a
+// band meet in the workspace: each workgroup stores its sums in its own slot,
+// publishes them (agent-scope release), and takes a ticket from the band's
+// counter; the workgroup that draws the last ticket acquires the other slots,
+// adds them, writes the outputs and resets the counter to zero for the next
+// call. INT32 addition is exact, so the outputs do not depend on which slice
+// arrives last. The S slices of a band are given block indices that the
+// round-robin dispatch places on one XCD, so their partial sums meet in that
+// XCD's L2. The FP16 outputs of the band are staged in LDS and leave as
+// 16-byte row segments.
+template <int F, int MB, int NT, int S, int W, int R>
+__global__ __launch_bounds__(W * 64) void k_gemm_dec(
+    const int8_t* __restrict__ xq, const uint16_t* __restrict__ s_x,
+    const int32_t* __restrict__ rowsum, const uint8_t* __restrict__ blob,
+    const uint16_t* __restrict__ s_c, int M, int N, int K, uint16_t* __restrict__ y,
+    int32_t* __restrict__ acc_out, int32x4* part, uint32_t* cnt) {
+    constexpr int kPairs = NT * MB;
+    constexpr int kThr = W * 64;
+    constexpr int kEp = (kPairs + W - 1) / W;  // tile pairs each wave finishes
+    constexpr int kRowHalves = 16 * NT + 8;     // output staging row: 16 NT values + 16 bytes
+    static_assert(W * kPairs * kWave * 16 <= 128 * 1024, "the waves' partial tiles must fit the LDS");
+    __shared__ int32x4 red[W * kPairs * kWave];
+    __shared__ __attribute__((aligned(16))) uint16_t ostage[16 * MB * kRowHalves];
+    __shared__ uint32_t ticket;
+
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int G = K / kGroup;
+    const int tiles = N / 16;
+    const int U = (M + 15) / 16;
+    const int c = lane % 16, j = lane / 16;
+    const int nblk = (tiles + NT - 1) / NT;
+    int nb, s;
+    if (S > 1 && nblk % 8 == 0) {
+        const int hi = blockIdx.x / (8 * S), rem = blockIdx.x % (8 * S);
+        s = rem / 8;
+        nb = hi * 8 + rem % 8;
+    } else {
+        nb = blockIdx.x / S;
+        s = blockIdx.x % S;
+    }
+    const int gs0 = G * s / S;
+    const int Gs = G * (s + 1) / S - gs0;
+    const int g0 = gs0 + Gs * wave / W;
+    const int count = gs0 + Gs * (wave + 1) / W - g0;
+
+    constexpr bool kG128 = Fmt<F>::kG128;
+    constexpr int kV = Fmt<F>::kVec;
+    const size_t code_bytes = code_bytes_of(F, N, K);
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)xq, (short)0, (int)((uint32_t)G * (uint32_t)U * 2048u), kBufferConfig);
+    const __amdgpu_buffer_rsrc_t rb =
+        __builtin_amdgcn_make_buffer_rsrc((void*)blob, (short)0, (int)(uint32_t)code_bytes, kBufferConfig);
+    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(blob + code_bytes), (short)0, (int)(uint32_t)(kG128 ? N * G : N), kBufferConfig);
+
+    uint32_t b_off[NT], p_off[NT], a_off[MB];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        const int t = min(nb * NT + i, tiles - 1);
+        b_off[i] = ((uint32_t)t * (uint32_t)G + (uint32_t)g0) * (1024u * kV) + (uint32_t)lane * 16u;
+        p_off[i] = ((uint32_t)t * (uint32_t)G + (uint32_t)g0) * 16u + (uint32_t)c;
+    }
+    const uint32_t a_step = (uint32_t)U * 2048u;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+        a_off[mb] = (uint32_t)g0 * a_step + (uint32_t)min(mb, U - 1) * 2048u + (uint32_t)lane * 16u;
+
+    int32x4 acc[NT][MB];
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[i][mb] = int32x4{0, 0, 0, 0};
+
+    u32x4 bq[R][NT][kV];
+    uint32_t pq[R][NT];
+    int32x4 aq[R][MB][2];
+    const int main_count = count / R * R;
+#pragma unroll
+    for (int r = 0; r < R - 1; ++r)
+        stream_load<F, MB, NT>(bq[r], pq[r], aq[r], rb, rp, ra, b_off, p_off, a_off, r,
+                               r < main_count, a_step);
+    // Operands of this wave's epilogue pairs (p = wave + e W), read now so
+    // that the stores at the end wait on no global load.
+    float ep_sc[kEp], ep_sx[kEp][4];
+    int ep_z[kEp], ep_rs[kEp][4];
+#pragma unroll
+    for (int e = 0; e < kEp; ++e) {
+        const int p = min(wave + e * W, kPairs - 1);
+        const int t = min(nb * NT + p / MB, tiles - 1);
+        const int n = 16 * t + c;
+        const int mrow = 16 * (p % MB) + 4 * j;
+        ep_sc[e] = h2f(s_c[n]);
+        ep_z[e] = Fmt<F>::kZp ? (int)blob[code_bytes + n] : 0;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int m = min(mrow + v, M - 1);
+            ep_sx[e][v] = h2f(s_x[m]);
+            ep_rs[e][v] = Fmt<F>::kZp ? rowsum[m] : 0;
+        }
+    }
+    for (int h = 0; h < main_count; h += R) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int nxt = h + r + R - 1;
+            stream_load<F, MB, NT>(bq[(r + R - 1) % R], pq[(r + R - 1) % R], aq[(r + R - 1) % R], rb,
+                                   rp, ra, b_off, p_off, a_off, nxt, nxt < main_count, a_step);
+            stream_compute<F, MB, NT>(acc, bq[r], pq[r], aq[r]);
+        }
+    }
+    for (int h = main_count; h < count; ++h) {
+        stream_load<F, MB, NT>(bq[0], pq[0], aq[0], rb, rp, ra, b_off, p_off, a_off, h, true, a_step);
+        stream_compute<F, MB, NT>(acc, bq[0], pq[0], aq[0]);
+    }
+
+    // The waves' partial tiles, added in LDS in wave order.
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) red[(wave * kPairs + i * MB + mb) * kWave + lane] = acc[i][mb];
+    __syncthreads();
+    int32x4 r4[kEp];
+#pragma unroll
+    for (int e = 0; e < kEp; ++e) {
+        const int p = min(wave + e * W, kPairs - 1);
+        int32x4 sl[W];
+#pragma unroll
+        for (int w2 = 0; w2 < W; ++w2) sl[w2] = red[(w2 * kPairs + p) * kWave + lane];
+        r4[e] = sl[0];
+#pragma unroll
+        for (int w2 = 1; w2 < W; ++w2) r4[e] += sl[w2];
+    }
+
+    if constexpr (S > 1) {
+        // This slice's sums into its slot, then the ticket.
+#pragma unroll
+        for (int e = 0; e < kEp; ++e) {
+            const int p = wave + e * W;
+            if (p < kPairs) part[((size_t)(nb * S + s) * kPairs + p) * kWave + lane] = r4[e];
+        }
+        __threadfence();
+        __syncthreads();
+        if (threadIdx.x == 0) ticket = atomicAdd(&cnt[nb], 1u);
+        __syncthreads();
+        if (ticket != (uint32_t)(S - 1)) return;
+        __threadfence();
+#pragma unroll
+        for (int e = 0; e < kEp; ++e) {
+            const int p = wave + e * W;
+            if (p >= kPairs) continue;
+            int32x4 other[S];
+#pragma unroll
+            for (int s2 = 0; s2 < S; ++s2)
+                other[s2] = s2 == s ? int32x4{0, 0, 0, 0} : part[((size_t)(nb * S + s2) * kPairs + p) * kWave + lane];
+#pragma unroll
+            for (int s2 = 0; s2 < S; ++s2) r4[e] += other[s2];
+        }
+        if (threadIdx.x == 0) cnt[nb] = 0u;
+    }
+
+    // Epilogue: outputs into the staging rows, then 16-byte row segments.
+#pragma unroll
+    for (int e = 0; e < kEp; ++e) {
+        const int p = wave + e * W;
+        if (p >= kPairs) break;
+        const int i = p / MB, mb = p % MB;
+        const int t = nb * NT + i;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int row = 16 * mb + 4 * j + v;
+            int r = r4[e][v];
+            if (Fmt<F>::kZp) r -= ep_z[e] * ep_rs[e][v];
+            if (acc_out && t < tiles && row < M) acc_out[(size_t)row * N + 16 * t + c] = r;
+            ostage[row * kRowHalves + 16 * i + c] = output_value(r, ep_sx[e][v], ep_sc[e]);
+        }
+    }
+    __syncthreads();
+    constexpr int kChunks = 2 * NT;  // 16-byte segments per staged row
+    for (int q = threadIdx.x; q < 16 * MB * kChunks; q += kThr) {
+        const int row = q / kChunks, ch = q % kChunks;
+        const int n = (nb * NT) * 16 + ch * 8;
+        if (row < M && n < N)
+            *reinterpret_cast<u32x4*>(y + (size_t)row * N + n) =
+                *reinterpret_cast<const u32x4*>(ostage + row * kRowHalves + ch * 8);
     }
 }
 
@@ -1167,10 +1371,6 @@ struct Plan {
     int group_m = 4;                   // wide and LDS-pipelined kernels: block rows per XCD raster group
     int64_t nblk = 0;
 };
-
-#ifdef QOQ_TUNING
-int g_force_kind = 0, g_force_nt = 0, g_force_r = 0, g_force_w = 0, g_force_bn = 0, g_force_gm = 0;
-#endif
 
 // The buffer-load kernels form 32-bit byte offsets, and mark prefetches past
 // the end with offset 2^31: every real offset must stay below that.
@@ -1250,22 +1450,6 @@ Plan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, bool have_ws) {
             p.s = (int)std::min<int64_t>(std::min<int64_t>(8, (kCUs + nblk - 1) / nblk), K / kGroup / 2);
         if (p.s < 1) p.s = 1;
     }
-#ifdef QOQ_TUNING
-    if (g_force_kind) {
-        p.kind = g_force_kind < 0 ? kSimple : g_force_kind;
-        if (p.kind == kStream && p.mb == 0) p.mb = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-        if (p.kind == kStream && (M > 64 || !fits)) p.kind = kSimple;
-        if ((p.kind == kWide || p.kind == kLds) && !fits) p.kind = kTile;
-    }
-    if (g_force_nt) p.nt = g_force_nt;
-    if (g_force_r) p.r = g_force_r;
-    if (g_force_w) p.w = g_force_w;
-    if (g_force_bn) p.bn = g_force_bn;
-    if (g_force_gm) p.group_m = g_force_gm;
-    if ((p.kind == kTile || p.kind == kLds) && g_force_nt)
-        p.s = std::max(1, std::min<int>(g_force_nt, (int)(K / kGroup)));
-    if (p.kind == kStream && g_force_bn) p.mb = g_force_bn;  // row tiles per workgroup
-#endif
     if (p.kind == kStream) {
         const int64_t U = (M + 15) / 16;
         p.mgrid = (int)((U + p.mb - 1) / p.mb);
@@ -1300,22 +1484,12 @@ void launch_stream_t(const Plan& p, const GemmArgs& a) {
 
 template <int F, int MB, int NT>
 void launch_stream_rw(const Plan& p, const GemmArgs& a) {
-#ifdef QOQ_TUNING
-    if (p.r == 4 && p.w == 4) { launch_stream_t<F, MB, NT, 4, 4>(p, a); return; }
-    if (p.r == 2 && p.w == 4) { launch_stream_t<F, MB, NT, 2, 4>(p, a); return; }
-    if (p.r == 4 && p.w == 8) { launch_stream_t<F, MB, NT, 4, 8>(p, a); return; }
-    if (p.r == 2 && p.w == 16) { launch_stream_t<F, MB, NT, 2, 16>(p, a); return; }
-    if (p.r == 1 && p.w == 8) { launch_stream_t<F, MB, NT, 1, 8>(p, a); return; }
-#endif
     if (p.r == 1) launch_stream_t<F, MB, NT, 1, 16>(p, a);
     else launch_stream_t<F, MB, NT, 2, 8>(p, a);
 }
 
 template <int F, int MB>
 void launch_stream_nt(const Plan& p, const GemmArgs& a) {
-#ifdef QOQ_TUNING
-    if (p.nt == 1) { launch_stream_rw<F, MB, 1>(p, a); return; }
-#endif
     if (p.nt == 3) launch_stream_rw<F, MB, 3>(p, a);
     else launch_stream_rw<F, MB, 2>(p, a);
 }
@@ -1412,19 +1586,5 @@ void launch_gemm(int fmt, const int8_t* xq, const uint16_t* s_x, const int32_t* 
     else
         launch_plan<kFmtW8>(p, a);
 }
-
-#ifdef QOQ_TUNING
-// Plan overrides for measurement builds: kind (-1 reference, 2 tiled, 3 wide,
-// 4 streaming; 0 keeps the plan), then the kind's own parameters (0 keeps).
-// gm: block rows per XCD raster group of the wide kernel.
-extern "C" void qoq_tuning_force(int kind, int nt, int r, int w, int bn, int gm) {
-    g_force_gm = gm;
-    g_force_kind = kind;
-    g_force_nt = nt;
-    g_force_r = r;
-    g_force_w = w;
-    g_force_bn = bn;
-}
-#endif
 
 }  // namespace qoq

@@ -491,44 +491,6 @@ void launch_w16_stream(int64_t M, int64_t N, int64_t K, const uint16_t* x, const
                        stream, x, blob, s_c, (int)M, (int)N, (int)K, y, acc_out);
 }
 
-#ifdef QOQ_TUNING
-int g_w16_mb = 0, g_w16_nt = 0, g_w16_w = 0, g_w16_r = 0;
-
-template <bool kG128, int MB, int NT>
-bool tune_w16_rw(int64_t M, int64_t N, int64_t K, const uint16_t* x, const uint8_t* blob,
-                 const uint16_t* s_c, uint16_t* y, float* acc_out, hipStream_t stream) {
-#define QOQ_W16(RV, WV)                                                                        \
-    if (g_w16_r == RV && g_w16_w == WV) {                                                     \
-        if constexpr (WV * NT * MB <= 64)                                                     \
-            launch_w16_stream<kG128, MB, NT, RV, WV>(M, N, K, x, blob, s_c, y, acc_out, stream); \
-        return WV * NT * MB <= 64;                                                            \
-    }
-    QOQ_W16(2, 8) QOQ_W16(1, 16) QOQ_W16(2, 4) QOQ_W16(1, 8) QOQ_W16(2, 16) QOQ_W16(1, 4)
-#undef QOQ_W16
-    return false;
-}
-
-template <bool kG128, int MB>
-bool tune_w16_nt(int64_t M, int64_t N, int64_t K, const uint16_t* x, const uint8_t* blob,
-                 const uint16_t* s_c, uint16_t* y, float* acc_out, hipStream_t stream) {
-    if (g_w16_nt == 1) return tune_w16_rw<kG128, MB, 1>(M, N, K, x, blob, s_c, y, acc_out, stream);
-    if (g_w16_nt == 2) return tune_w16_rw<kG128, MB, 2>(M, N, K, x, blob, s_c, y, acc_out, stream);
-    if (g_w16_nt == 3) return tune_w16_rw<kG128, MB, 3>(M, N, K, x, blob, s_c, y, acc_out, stream);
-    if (g_w16_nt == 4) return tune_w16_rw<kG128, MB, 4>(M, N, K, x, blob, s_c, y, acc_out, stream);
-    return false;
-}
-
-template <bool kG128>
-bool tune_w16(int64_t M, int64_t N, int64_t K, const uint16_t* x, const uint8_t* blob,
-              const uint16_t* s_c, uint16_t* y, float* acc_out, hipStream_t stream) {
-    if (!g_w16_mb || M > 256) return false;
-    if (g_w16_mb == 1) return tune_w16_nt<kG128, 1>(M, N, K, x, blob, s_c, y, acc_out, stream);
-    if (g_w16_mb == 2) return tune_w16_nt<kG128, 2>(M, N, K, x, blob, s_c, y, acc_out, stream);
-    if (g_w16_mb == 4) return tune_w16_nt<kG128, 4>(M, N, K, x, blob, s_c, y, acc_out, stream);
-    return false;
-}
-#endif
-
 template <bool kG128, int BN, int WN>
 void launch_w16_tile(int64_t M, int64_t N, int64_t K, const uint16_t* x, const uint8_t* blob,
                      const uint16_t* s_c, uint16_t* y, float* acc_out, hipStream_t stream) {
@@ -541,9 +503,6 @@ template <bool kG128>
 void launch_w16(int64_t M, int64_t N, int64_t K, const uint16_t* x, const uint8_t* blob,
                 const uint16_t* s_c, uint16_t* y, float* acc_out, hipStream_t stream) {
     const int64_t tiles = N / 16;
-#ifdef QOQ_TUNING
-    if (kG128 && tune_w16<kG128>(M, N, K, x, blob, s_c, y, acc_out, stream)) return;
-#endif
     // The streaming kernel forms 32-bit byte offsets into the codes and the rows.
     const bool fits = N * K / 2 < (int64_t(1) << 31) && N * (K / kGroup) < (int64_t(1) << 31);
     if (M <= 64 && fits) {
@@ -585,17 +544,6 @@ void launch_w16(int64_t M, int64_t N, int64_t K, const uint16_t* x, const uint8_
 }
 
 }  // namespace
-
-#ifdef QOQ_TUNING
-// Decode-kernel overrides for measurement builds (g128 only): row tiles and
-// channel tiles per workgroup, waves, ring depth; mb = 0 restores the plan.
-extern "C" void qoq_tuning_force_w16(int mb, int nt, int w, int r) {
-    g_w16_mb = mb;
-    g_w16_nt = nt;
-    g_w16_w = w;
-    g_w16_r = r;
-}
-#endif
 
 void launch_gemm_w4a16(int mode, const uint16_t* x, const uint8_t* blob, const uint16_t* s_c,
                        int64_t M, int64_t N, int64_t K, uint16_t* y, float* acc_out,

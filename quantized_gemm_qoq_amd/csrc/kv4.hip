@@ -43,15 +43,45 @@ constexpr int kAttnWaves = 4;  // waves per attention workgroup
 
 // ---------------------------------------------------------------------------
 // lambda[h, j] = f16(sqrt(max_t |k[t, h, j]|)), 1 where the maximum is 0.
-__global__ __launch_bounds__(kKvThreads) void k_kv4_smooth_scales(const uint16_t* __restrict__ k,
-                                                                  int T, int H,
-                                                                  uint16_t* __restrict__ lambda) {
-    const int i = blockIdx.x * kKvThreads + threadIdx.x;  // h * kD + j
-    if (i >= H * kD) return;
-    unsigned mx = 0;  // magnitude bits of FP16 values order like the values
-    for (int t = 0; t < T; ++t) mx = max(mx, (unsigned)(k[(size_t)t * H * kD + i] & 0x7FFFu));
-    const float m = h2f(mx);
-    lambda[i] = m > 0.0f ? f2h(sqrtf(m)) : f2h(1.0f);
+// One workgroup of 16 waves per 64 consecutive (head, channel) indices: lane l
+// of a wave reads the 8 channels 8 (l % 8) .. +7 (one 16-byte load) of token
+// 8 w + l / 8 + 128 s at step s, so every step of the workgroup covers 128
+// tokens with 128-byte runs; the magnitudes are maximised on their FP16 bit
+// patterns (which order like the values), across the token lanes of a wave
+// with shuffles and across the waves in LDS.
+constexpr int kSmoothWaves = 16;
+__global__ __launch_bounds__(kSmoothWaves * kWave) void k_kv4_smooth_scales(
+    const uint16_t* __restrict__ k, int T, int H, uint16_t* __restrict__ lambda) {
+    __shared__ uint32_t part[kSmoothWaves][64];
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int c8 = lane % 8;
+    const int i0 = blockIdx.x * 64 + c8 * 8;  // first (head, channel) index of this lane
+    const size_t row = (size_t)H * kD;         // elements per token
+    uint32_t m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int t = wave * 8 + lane / 8; t < T; t += 8 * kSmoothWaves) {
+        const uint4 v = *reinterpret_cast<const uint4*>(k + (size_t)t * row + i0);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            m[2 * q] = max(m[2 * q], w[q] & 0x7FFFu);
+            m[2 * q + 1] = max(m[2 * q + 1], (w[q] >> 16) & 0x7FFFu);
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int o = 8; o < kWave; o <<= 1) m[q] = max(m[q], (uint32_t)__shfl_xor((int)m[q], o, kWave));
+    if (lane < 8)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) part[wave][c8 * 8 + q] = m[q];
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        uint32_t mx = 0;
+#pragma unroll
+        for (int w2 = 0; w2 < kSmoothWaves; ++w2) mx = max(mx, part[w2][threadIdx.x]);
+        const float mf = h2f(mx);
+        lambda[blockIdx.x * 64 + threadIdx.x] = mf > 0.0f ? f2h(sqrtf(mf)) : f2h(1.0f);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -574,7 +604,7 @@ unsigned blocks_of(int64_t n, int per) { return (unsigned)((n + per - 1) / per);
 
 void launch_kv4_smooth_scales(const uint16_t* k, int64_t T, int64_t H, uint16_t* lambda,
                               hipStream_t stream) {
-    hipLaunchKernelGGL(k_kv4_smooth_scales, dim3(blocks_of(H * kD, kKvThreads)), dim3(kKvThreads), 0,
+    hipLaunchKernelGGL(k_kv4_smooth_scales, dim3((unsigned)(H * kD / 64)), dim3(kSmoothWaves * kWave), 0,
                        stream, k, (int)T, (int)H, lambda);
 }
 
@@ -591,15 +621,8 @@ void launch_kv4_append(const uint16_t* k, const uint16_t* v, const uint16_t* lam
 // least one workgroup per compute unit; one chunk when B H >= 256, which
 // skips the combine kernel), each a multiple of 128 tokens so that every wave
 // takes whole 32-token steps.
-#ifdef QOQ_TUNING
-int64_t g_kv4_chunk = 0;
-extern "C" void qoq_tuning_force_kv4_chunk(int c) { g_kv4_chunk = c; }
-#endif
 
 int64_t kv4_chunk(int64_t B, int64_t H, int64_t Tcap) {
-#ifdef QOQ_TUNING
-    if (g_kv4_chunk) return g_kv4_chunk;
-#endif
     const int64_t bh = std::max<int64_t>(B * H, 1);
     const int64_t n = std::min<int64_t>((256 + bh - 1) / bh, std::max<int64_t>((Tcap + 127) / 128, 1));
     return std::max<int64_t>(((Tcap + n - 1) / n + 127) / 128 * 128, 128);

@@ -52,16 +52,3 @@ def quantize_all(mode, x_bits, w_bits):
     wq = oracle.quantize_weights(mode, w_bits)
     blob = oracle.pack(mode, wq["q"], wq["s_g"], wq["z"])
     return xq, s_x, rowsum, wq, blob
-
-
-def sample_points(M: int, N: int, count: int, seed: int):
-    """Random (m, n) pairs plus the four corners and the last row and column
-    (the ragged tails)."""
-    rng = np.random.default_rng(seed)
-    ms = rng.integers(0, M, size=count)
-    ns = rng.integers(0, N, size=count)
-    edge_m = np.concatenate([[0, 0, M - 1, M - 1], np.full(min(N, 64), M - 1),
-                             rng.integers(0, M, size=min(M, 64))])
-    edge_n = np.concatenate([[0, N - 1, 0, N - 1], rng.integers(0, N, size=min(N, 64)),
-                             np.full(min(M, 64), N - 1)])
-    return np.concatenate([ms, edge_m]).astype(np.int64), np.concatenate([ns, edge_n]).astype(np.int64)

@@ -102,3 +102,42 @@ def test_graph_replays_match_eager_calls():
         assert not torch.equal(captured["att"], before_att), r
         for k in packed:
             assert not torch.equal(captured["y"][k], before[k]), (r, k)
+
+
+def test_captured_split_call_survives_workspace_growth():
+    """A graph that captured a split-K call on its stream's shared workspace
+    still replays correctly after a later call on the same stream needed a
+    larger workspace: the smaller one stays allocated, so tensors allocated
+    afterwards neither receive the replay's partial sums nor feed it."""
+    small, large = (200, 1664, 272), (128, 8192, 8192)
+    assert 0 < qoq.qoq_gemm_workspace_bytes("g128", *small) < qoq.qoq_gemm_workspace_bytes("g128", *large)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        (M, K, N) = small
+        pw = qoq.PackedWeight("g128", _f16((N, K), 970, 0.02))
+        x = _f16((M, K), 971, 1.0)
+        xq, s_x, _ = qoq.qoq_quantize_act(x, want_rowsum=False)
+        want = qoq.qoq_w4a8_gemm("g128", xq, s_x, None, pw.blob, pw.s_c, N)
+        y = torch.empty_like(want)
+        qoq.qoq_w4a8_gemm("g128", xq, s_x, None, pw.blob, pw.s_c, N, y=y)  # warm-up on this stream
+        s.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            qoq.qoq_w4a8_gemm("g128", xq, s_x, None, pw.blob, pw.s_c, N, y=y)
+        (M2, K2, N2) = large
+        pw2 = qoq.PackedWeight("g128", _f16((N2, K2), 972, 0.02))
+        xq2, s_x2, _ = qoq.qoq_quantize_act(_f16((M2, K2), 973, 1.0), want_rowsum=False)
+        qoq.qoq_w4a8_gemm("g128", xq2, s_x2, None, pw2.blob, pw2.s_c, N2)  # grows the workspace
+        s.synchronize()
+        del pw2, xq2, s_x2
+        torch.cuda.empty_cache()
+        need = qoq.qoq_gemm_workspace_bytes("g128", *small)
+        fillers = [torch.full((max(need, 1 << 20),), 0x55, dtype=torch.uint8, device=DEV) for _ in range(8)]
+        for r in range(3):
+            y.fill_(0)
+            g.replay()
+            s.synchronize()
+            assert torch.equal(y, want), r
+        s.synchronize()
+        for f in fillers:
+            assert bool((f == 0x55).all())

@@ -276,6 +276,81 @@ def test_gemm_matches_library_matmul(mode):
         np.testing.assert_array_equal(acc, factored)
 
 
+MATMUL_SHAPES = [(1, 16, 128), (7, 48, 384), (33, 272, 1024), (130, 2064, 256), (3, 16, 132096)]
+
+
+@pytest.mark.parametrize("mode", [G128, PC])
+@pytest.mark.parametrize("M,N,K", MATMUL_SHAPES)
+def test_gemm_matmul_equals_the_c_loops(mode, M, N, K):
+    """The library-product form of the accumulator (used on full-size layers)
+    equals the C oracle's int64 loops element by element, on ragged shapes
+    (M != N, a channel count past one slice of the product) and at the largest
+    K; activations include the extreme codes -128 and 127."""
+    x = workloads.random_fp16((M, K), 600 + M, 1.0).numpy().view(np.uint16)
+    w = workloads.random_fp16((N, K), 700 + N, 0.02).numpy().view(np.uint16)
+    xq, _, _ = oracle.quantize_act(x)
+    xq = xq.copy()
+    xq[0, :3] = [-128, 127, -127]
+    wq = oracle.quantize_weights(mode, w)
+    want = oracle.gemm(mode, xq, wq["q"], wq["s_g"], wq["z"])
+    np.testing.assert_array_equal(oracle.gemm_matmul(mode, xq, wq["q"], wq["s_g"], wq["z"]), want)
+
+
+def test_gemm_matmul_refuses_int32_overflow():
+    K = 132096
+    xq = np.full((1, K), -128, np.int8)
+    q = np.zeros((16, K), np.uint8)
+    s_g = np.full((16, K // 128), 16, np.uint8)
+    z = np.full((16, K // 128), 8, np.uint8)
+    with pytest.raises(OverflowError):
+        oracle.gemm_matmul(G128, xq, q, s_g, z)
+
+
+@pytest.mark.parametrize("M,N,K", MATMUL_SHAPES[:4])
+def test_gemm_w8_matmul_equals_the_c_loops(M, N, K):
+    x = workloads.random_fp16((M, K), 800 + M, 1.0).numpy().view(np.uint16)
+    w = workloads.random_fp16((N, K), 900 + N, 0.02).numpy().view(np.uint16)
+    xq, _, _ = oracle.quantize_act(x)
+    _, q = oracle.quantize_weights_w8(w)
+    np.testing.assert_array_equal(oracle.gemm_w8_matmul(xq, q), oracle.gemm_w8(xq, q))
+
+
+@pytest.mark.parametrize("mode", [G128, PC])
+@pytest.mark.parametrize("M,N,K", MATMUL_SHAPES[:4])
+def test_gemm_w4a16_matmul_matches_the_c_loops(mode, M, N, K):
+    """Both forms sum in fp64 in different orders: they agree far inside the
+    rounding of a float64 sum (K * 2^-52 of the absolute sum)."""
+    x = workloads.random_fp16((M, K), 1000 + M, 1.0).numpy().view(np.uint16)
+    w = workloads.random_fp16((N, K), 1100 + N, 0.02).numpy().view(np.uint16)
+    wq = oracle.quantize_weights(mode, w)
+    y0, a0 = oracle.gemm_w4a16(mode, x, wq["s_c"], wq["q"], wq["s_g"], wq["z"])
+    y1, a1 = oracle.gemm_w4a16_matmul(mode, x, wq["s_c"], wq["q"], wq["s_g"], wq["z"])
+    tol = K * 2.0**-52 * a0
+    assert np.all(np.abs(y1 - y0) <= tol)
+    assert np.all(np.abs(a1 - a0) <= tol)
+
+
+def test_epilogue_points_equals_epilogue_everywhere():
+    """orc_epilogue_points, at every (m, n) of a non-square shape in shuffled
+    order, equals orc_epilogue; the scales are distinct per row and per channel
+    (and the two vectors have different lengths), so a swapped or transposed
+    index fails."""
+    M, N = 37, 80
+    rng = np.random.default_rng(77)
+    acc = rng.integers(-(2**31), 2**31, size=(M, N), dtype=np.int64).astype(np.int32)
+    s_x = rng.permutation(np.arange(M, dtype=np.uint16) * 7 + 0x3000)  # distinct FP16 scales
+    s_c = rng.permutation(np.arange(N, dtype=np.uint16) * 3 + 0x1000)
+    y = oracle.epilogue(acc, s_x, s_c)
+    order = rng.permutation(M * N)
+    ms, ns = order // N, order % N
+    yp = oracle.epilogue_points(acc[ms, ns], s_x, s_c, ms, ns)
+    np.testing.assert_array_equal(yp, y[ms, ns])
+    # and against the definition at a few points, in exact arithmetic
+    sx, sc = oracle.f16_bits_to_f64(s_x), oracle.f16_bits_to_f64(s_c)
+    for p in range(0, M * N, 97):
+        assert yp[p] == float(acc[ms[p], ns[p]]) * sx[ms[p]] * sc[ns[p]]
+
+
 def test_gemm_int32_range_at_max_k():
     """At K = 132096 the largest reachable products stay inside INT32, and the
     oracle refuses a sum that would not (|xq| = 128 with |W8^| = 128 is outside
