@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define QOQ_ABI_VERSION 5
+#define QOQ_ABI_VERSION 6
 #define QOQ_GROUP 128
 #define QOQ_MAX_K 132096
 #define QOQ_RMSNORM_MAX_K 32768 /* row length of qoq_rmsnorm_quantize_act */
@@ -86,7 +86,8 @@ typedef enum {
     QOQ_ERR_ALIGN = 3,  /* a pointer is not 16-byte aligned */
     QOQ_ERR_MODE = 4,   /* mode is neither QOQ_MODE_G128 nor QOQ_MODE_PER_CHANNEL */
     QOQ_ERR_HIP = 5,    /* the HIP runtime reported an error at launch */
-    QOQ_ERR_WORKSPACE = 6 /* workspace given but smaller than the *_workspace_bytes() value */
+    QOQ_ERR_WORKSPACE = 6, /* workspace given but smaller than the *_workspace_bytes() value */
+    QOQ_ERR_HEADER = 7     /* a checkpoint header that does not describe the expected blob */
 } qoq_status;
 
 /* QOQ_ABI_VERSION of the loaded library. */
@@ -401,6 +402,44 @@ qoq_status qoq_kv4_decode_attention(const uint16_t* q, const uint16_t* lambda, c
 qoq_status qoq_w4a16_gemm(int mode, const uint16_t* x, const void* blob, const uint16_t* s_c,
                           int64_t M, int64_t N, int64_t K, uint16_t* y, float* acc_out,
                           void* stream);
+
+/*
+ * ---- Checkpoint header ------------------------------------------------------
+ * [EN] section 4, evaluation pseudocode, output: the quantized (W4A8KV4)
+ * checkpoint. A packed weight matrix is stored as this 64-byte header, then the
+ * blob of the pack call (blob_bytes bytes), then the FP16 per-channel scales
+ * s_c (scale_bytes = 2 N bytes). The header is host memory: the GEMMs take
+ * device pointers and never read it; a loader checks it with
+ * qoq_blob_header_check before it copies the blob to the device, so that a
+ * checkpoint written by a library with another blob layout, for another
+ * format, group size or shape, is refused instead of being misread.
+ * Little-endian fields, no padding.
+ */
+#define QOQ_BLOB_MAGIC 0x314B5051u /* the bytes "QPK1" */
+#define QOQ_FORMAT_W8A8 2          /* format code of the W8A8 sibling's blob */
+
+typedef struct {
+    uint32_t magic;       /* QOQ_BLOB_MAGIC */
+    uint32_t abi_version; /* QOQ_ABI_VERSION of the library that packed the blob */
+    uint32_t format;      /* QOQ_MODE_G128, QOQ_MODE_PER_CHANNEL or QOQ_FORMAT_W8A8 */
+    uint32_t group;       /* QOQ_GROUP */
+    int64_t n;            /* output channels N */
+    int64_t k;            /* input channels K */
+    int64_t blob_bytes;   /* qoq_packed_bytes(format, N, K) or qoq_w8a8_packed_bytes(N, K) */
+    int64_t scale_bytes;  /* 2 * N */
+    uint8_t reserved[16]; /* zero */
+} qoq_blob_header;
+
+/* Fills *h for a blob of this format and shape (host memory). QOQ_ERR_NULL
+ * for a NULL h, QOQ_ERR_MODE for an unknown format, QOQ_ERR_SHAPE for a shape
+ * the pack calls reject; *h is written only on QOQ_OK. */
+qoq_status qoq_blob_header_init(int format, int64_t N, int64_t K, qoq_blob_header* h);
+
+/* QOQ_OK if *h is exactly what qoq_blob_header_init(format, N, K) writes;
+ * QOQ_ERR_HEADER if any field differs (magic, ABI version, format, group,
+ * shape, byte counts or a non-zero reserved byte); QOQ_ERR_NULL, QOQ_ERR_MODE
+ * or QOQ_ERR_SHAPE as for qoq_blob_header_init. Reads nothing but *h. */
+qoq_status qoq_blob_header_check(const qoq_blob_header* h, int format, int64_t N, int64_t K);
 
 #ifdef __cplusplus
 }

@@ -3,7 +3,9 @@
 TEST INFRASTRUCTURE. Only the test suite, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package. The product path (the
 HIP library under ``quantized_gemm_qoq_amd``) never imports it, and the two share
-no code: the oracle is plain C in ``qoq_oracle.c``, loaded here through ctypes.
+no code: the oracle is plain C in ``qoq_oracle.c``, loaded here through ctypes,
+plus numpy library-product forms of its contractions for full-size shapes
+(``gemm_matmul`` and its siblings), each pinned against the C loops.
 
 Every function takes and returns numpy arrays. FP16 values travel as their raw
 binary16 bits (``uint16``). What each function computes, and the passage of the
@@ -25,6 +27,9 @@ GROUP = 128
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "qoq_oracle.c")
 _LIB = os.path.join(_HERE, "libqoq_oracle.so")
+# A prebuilt copy of the same source to load instead (the sanitizer test
+# builds one with AddressSanitizer and UndefinedBehaviorSanitizer).
+_LIB_OVERRIDE = os.environ.get("QOQ_ORACLE_LIB")
 _lock = threading.Lock()
 _lib = None
 
@@ -45,8 +50,11 @@ def _load():
     global _lib
     with _lock:
         if _lib is None:
-            build()
-            lib = ctypes.CDLL(_LIB)
+            if _LIB_OVERRIDE:
+                lib = ctypes.CDLL(_LIB_OVERRIDE)
+            else:
+                build()
+                lib = ctypes.CDLL(_LIB)
             P = ctypes.c_void_p
             I64 = ctypes.c_int64
             I = ctypes.c_int

@@ -52,7 +52,22 @@ EXPORTED = (
     "qoq_kv4_append",
     "qoq_kv4_attention_workspace_bytes",
     "qoq_kv4_decode_attention",
+    "qoq_blob_header_init",
+    "qoq_blob_header_check",
+
 )
+
+FORMAT_W8A8 = 2  # format code of the W8A8 blob in a checkpoint header
+BLOB_MAGIC = 0x314B5051
+
+
+class BlobHeader(ctypes.Structure):
+    """qoq_blob_header of include/qoq.h (64 bytes, little-endian, no padding)."""
+    _fields_ = [("magic", ctypes.c_uint32), ("abi_version", ctypes.c_uint32),
+                ("format", ctypes.c_uint32), ("group", ctypes.c_uint32),
+                ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("blob_bytes", ctypes.c_int64), ("scale_bytes", ctypes.c_int64),
+                ("reserved", ctypes.c_uint8 * 16)]
 
 
 class QoQError(RuntimeError):
@@ -101,6 +116,8 @@ def load_library():
             "qoq_kv4_attention_workspace_bytes": (I64, [I64, I64, I64, I64, I64]),
             "qoq_kv4_decode_attention": (I, [P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64,
                                              P, P, I64, P]),
+            "qoq_blob_header_init": (I, [I, I64, I64, ctypes.POINTER(BlobHeader)]),
+            "qoq_blob_header_check": (I, [ctypes.POINTER(BlobHeader), I, I64, I64]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(lib, name)
@@ -580,6 +597,45 @@ class PackedWeight:
             return qoq_w8a8_gemm(xq, s_x, self.blob, self.s_c, self.N, y=y, K=self.K)
         return qoq_w4a8_gemm(self.mode, xq, s_x, rowsum, self.blob, self.s_c, self.N, y=y,
                              K=self.K)
+
+    def _format(self) -> int:
+        return FORMAT_W8A8 if self.mode == W8A8 else int(self.mode)
+
+    def save(self, path: str) -> None:
+        """Write the checkpoint: the 64-byte qoq_blob_header, the blob, then s_c."""
+        h = BlobHeader()
+        _check(load_library().qoq_blob_header_init(self._format(), self.N, self.K, ctypes.byref(h)),
+               "qoq_blob_header_init")
+        with open(path, "wb") as f:
+            f.write(bytes(h))
+            f.write(self.blob.cpu().numpy().tobytes())
+            f.write(self.s_c.cpu().view(torch.int16).numpy().tobytes())
+
+    @classmethod
+    def load(cls, path: str, mode, N: int, K: int, device) -> "PackedWeight":
+        """Read a checkpoint written by save(), refusing (QoQError) one whose
+        header does not describe a blob of this format and shape, or whose
+        length does not match the header."""
+        fmt = FORMAT_W8A8 if mode == W8A8 else _mode(mode)
+        with open(path, "rb") as f:
+            raw = f.read()
+        if len(raw) < ctypes.sizeof(BlobHeader):
+            raise QoQError(f"{path}: shorter than a checkpoint header")
+        h = BlobHeader.from_buffer_copy(raw[:ctypes.sizeof(BlobHeader)])
+        _check(load_library().qoq_blob_header_check(ctypes.byref(h), fmt, int(N), int(K)),
+               f"checkpoint {path}")
+        off = ctypes.sizeof(BlobHeader)
+        if len(raw) != off + h.blob_bytes + h.scale_bytes:
+            raise QoQError(f"{path}: {len(raw)} bytes, the header describes "
+                           f"{off + h.blob_bytes + h.scale_bytes}")
+        self = cls.__new__(cls)
+        self.mode = W8A8 if mode == W8A8 else fmt
+        self.N, self.K = int(N), int(K)
+        blob = torch.frombuffer(bytearray(raw[off:off + h.blob_bytes]), dtype=torch.uint8)
+        sc = torch.frombuffer(bytearray(raw[off + h.blob_bytes:]), dtype=torch.int16)
+        self.blob = blob.to(device)
+        self.s_c = sc.view(torch.float16).to(device)
+        return self
 
     def forward_fp16(self, x: torch.Tensor, y=None) -> torch.Tensor:
         """The W4A16 sibling on the same 4-bit weights: FP16 x, no quantization."""

@@ -42,6 +42,7 @@ const char* qoq_status_str(int status) {
         case QOQ_ERR_MODE: return "unknown quantization mode";
         case QOQ_ERR_HIP: return "HIP runtime error at launch";
         case QOQ_ERR_WORKSPACE: return "workspace smaller than the call needs";
+        case QOQ_ERR_HEADER: return "checkpoint header does not describe the expected blob";
         default: return "unknown status";
     }
 }
@@ -315,6 +316,46 @@ qoq_status qoq_w4a16_gemm(int mode, const uint16_t* x, const void* blob, const u
         qoq::launch_gemm_w4a16(mode, x, static_cast<const uint8_t*>(blob), s_c, M, N, K, y, acc_out,
                                as_stream(stream));
     });
+}
+
+namespace {
+int64_t blob_bytes_of(int format, int64_t N, int64_t K) {
+    if (format == QOQ_FORMAT_W8A8) return qoq_w8a8_packed_bytes(N, K);
+    return qoq_packed_bytes(format, N, K);
+}
+}  // namespace
+
+static_assert(sizeof(qoq_blob_header) == 64, "the checkpoint header is 64 bytes");
+
+qoq_status qoq_blob_header_init(int format, int64_t N, int64_t K, qoq_blob_header* h) {
+    if (!h) return QOQ_ERR_NULL;
+    if (!valid_mode(format) && format != QOQ_FORMAT_W8A8) return QOQ_ERR_MODE;
+    const int64_t bytes = blob_bytes_of(format, N, K);
+    if (bytes < 0) return QOQ_ERR_SHAPE;
+    qoq_blob_header t{};
+    t.magic = QOQ_BLOB_MAGIC;
+    t.abi_version = QOQ_ABI_VERSION;
+    t.format = (uint32_t)format;
+    t.group = QOQ_GROUP;
+    t.n = N;
+    t.k = K;
+    t.blob_bytes = bytes;
+    t.scale_bytes = 2 * N;
+    *h = t;
+    return QOQ_OK;
+}
+
+qoq_status qoq_blob_header_check(const qoq_blob_header* h, int format, int64_t N, int64_t K) {
+    if (!h) return QOQ_ERR_NULL;
+    qoq_blob_header want;
+    const qoq_status st = qoq_blob_header_init(format, N, K, &want);
+    if (st != QOQ_OK) return st;
+    bool same = h->magic == want.magic && h->abi_version == want.abi_version &&
+                h->format == want.format && h->group == want.group && h->n == want.n &&
+                h->k == want.k && h->blob_bytes == want.blob_bytes &&
+                h->scale_bytes == want.scale_bytes;
+    for (int i = 0; i < 16; ++i) same = same && h->reserved[i] == 0;
+    return same ? QOQ_OK : QOQ_ERR_HEADER;
 }
 
 }  // extern "C"

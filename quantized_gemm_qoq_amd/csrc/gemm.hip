@@ -503,6 +503,11 @@ __device__ __forceinline__ void staged_partials(const int32x4 (&acc)[TM][TN], ui
 //     address arithmetic.
 // The plan selects this kernel only when every byte offset fits in 32 bits.
 constexpr int kBufferConfig = 0x00020000;  // gfx9 buffer resource word 3: 32-bit dwords
+// Cache policy of a buffer access that is coherent across the whole device
+// (sc1; what an agent-scope atomic load or store compiles to on gfx950).
+constexpr int kCoherent = 16;
+// s_waitcnt vmcnt(0) lgkmcnt(0): every issued memory access has completed.
+constexpr int kWaitAllMem = 7 << 4;
 
 template <int N>
 __device__ __forceinline__ void wide_load_a(u32x4 (&stage)[N], __amdgpu_buffer_rsrc_t ra,
@@ -1301,18 +1306,26 @@ __global__ __launch_bounds__(W * 64) void k_gemm_dec(
     }
 
     if constexpr (S > 1) {
-        // This slice's sums into its slot, then the ticket.
+        // This slice's sums into its slot with device-coherent stores (sc1:
+        // the same access as an agent-scope atomic store), acknowledged before
+        // the ticket is drawn; the last slice reads the other slots with
+        // device-coherent loads. No cache-wide write-back or invalidation is
+        // needed, since only these accesses cross workgroups.
+        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)part, (short)0, (int)((uint32_t)nblk * (uint32_t)(S * kPairs) * 1024u), kBufferConfig);
 #pragma unroll
         for (int e = 0; e < kEp; ++e) {
             const int p = wave + e * W;
-            if (p < kPairs) part[((size_t)(nb * S + s) * kPairs + p) * kWave + lane] = r4[e];
+            if (p < kPairs)
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(u32x4, r4[e]), rw,
+                    (int)((((uint32_t)(nb * S + s) * kPairs + p) * kWave + lane) * 16u), 0, kCoherent);
         }
-        __threadfence();
+        __builtin_amdgcn_s_waitcnt(kWaitAllMem);
         __syncthreads();
-        if (threadIdx.x == 0) ticket = atomicAdd(&cnt[nb], 1u);
+        if (threadIdx.x == 0) ticket = __hip_atomic_fetch_add(&cnt[nb], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
         if (ticket != (uint32_t)(S - 1)) return;
-        __threadfence();
 #pragma unroll
         for (int e = 0; e < kEp; ++e) {
             const int p = wave + e * W;
@@ -1320,11 +1333,14 @@ __global__ __launch_bounds__(W * 64) void k_gemm_dec(
             int32x4 other[S];
 #pragma unroll
             for (int s2 = 0; s2 < S; ++s2)
-                other[s2] = s2 == s ? int32x4{0, 0, 0, 0} : part[((size_t)(nb * S + s2) * kPairs + p) * kWave + lane];
+                other[s2] = s2 == s ? int32x4{0, 0, 0, 0}
+                                    : __builtin_bit_cast(int32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                          rw, (int)((((uint32_t)(nb * S + s2) * kPairs + p) * kWave + lane) * 16u), 0,
+                                          kCoherent));
 #pragma unroll
             for (int s2 = 0; s2 < S; ++s2) r4[e] += other[s2];
         }
-        if (threadIdx.x == 0) cnt[nb] = 0u;
+        if (threadIdx.x == 0) __hip_atomic_store(&cnt[nb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
     // Epilogue: outputs into the staging rows, then 16-byte row segments.

@@ -12,7 +12,7 @@ import quantized_gemm_qoq_amd as qoq
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "qoq.h")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_MODE, ERR_HIP, ERR_WORKSPACE = range(7)
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_MODE, ERR_HIP, ERR_WORKSPACE, ERR_HEADER = range(8)
 A = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: every call below fails validation
 U = ctypes.c_void_p(0x10004)  # misaligned
 NUL = None
@@ -40,7 +40,7 @@ def test_version_and_status_strings(lib):
     hdr = open(HEADER).read()
     ver = int(re.search(r"#define QOQ_ABI_VERSION (\d+)", hdr).group(1))
     assert lib.qoq_abi_version() == ver == qoq.qoq_abi_version()
-    for s in range(7):
+    for s in range(8):
         assert lib.qoq_status_str(s) and lib.qoq_status_str(s) != b"unknown status"
     assert lib.qoq_status_str(99) == b"unknown status"
 
@@ -250,3 +250,73 @@ def test_kv4_validation(lib):
     assert att(lens=NUL) == ERR_NULL
     assert att(wsb=need - 1) == ERR_WORKSPACE
 
+
+
+# ---- checkpoint header ------------------------------------------------------
+def _header(lib, fmt, N, K):
+    h = qoq.BlobHeader()
+    assert lib.qoq_blob_header_init(fmt, N, K, ctypes.byref(h)) == OK
+    return h
+
+
+def test_blob_header_layout_and_fields(lib):
+    assert ctypes.sizeof(qoq.BlobHeader) == 64
+    hdr = open(HEADER).read()
+    ver = int(re.search(r"#define QOQ_ABI_VERSION (\d+)", hdr).group(1))
+    h = _header(lib, 0, 6144, 4096)
+    raw = bytes(h)
+    assert raw[:4] == b"QPK1"
+    assert (h.magic, h.abi_version, h.format, h.group) == (qoq.BLOB_MAGIC, ver, 0, 128)
+    assert (h.n, h.k, h.blob_bytes, h.scale_bytes) == (6144, 4096, 6144 * 2048 + 6144 * 32, 2 * 6144)
+    assert bytes(h.reserved) == bytes(16)
+    assert _header(lib, 1, 16, 128).blob_bytes == 16 * 64 + 16
+    assert _header(lib, qoq.FORMAT_W8A8, 32, 256).blob_bytes == 32 * 256
+    assert lib.qoq_blob_header_check(ctypes.byref(h), 0, 6144, 4096) == OK
+
+
+@pytest.mark.parametrize("field,value", [
+    ("magic", 0x314B5052), ("abi_version", 5), ("format", 1), ("group", 64), ("n", 6160),
+    ("k", 4224), ("blob_bytes", 6144 * 2048), ("scale_bytes", 6144)])
+def test_blob_header_rejects_any_mismatch(lib, field, value):
+    h = _header(lib, 0, 6144, 4096)
+    setattr(h, field, value)
+    assert lib.qoq_blob_header_check(ctypes.byref(h), 0, 6144, 4096) == ERR_HEADER
+
+
+def test_blob_header_rejects_wrong_expectation_and_reserved_bytes(lib):
+    h = _header(lib, 0, 6144, 4096)
+    assert lib.qoq_blob_header_check(ctypes.byref(h), 1, 6144, 4096) == ERR_HEADER  # other mode
+    assert lib.qoq_blob_header_check(ctypes.byref(h), 0, 6144, 8192) == ERR_HEADER  # other K
+    assert lib.qoq_blob_header_check(ctypes.byref(h), 0, 4096, 4096) == ERR_HEADER  # other N
+    h.reserved[7] = 1
+    assert lib.qoq_blob_header_check(ctypes.byref(h), 0, 6144, 4096) == ERR_HEADER
+    assert lib.qoq_blob_header_check(None, 0, 6144, 4096) == ERR_NULL
+    assert lib.qoq_blob_header_init(0, 6144, 4096, None) == ERR_NULL
+    assert lib.qoq_blob_header_init(3, 16, 128, ctypes.byref(h)) == ERR_MODE
+    assert lib.qoq_blob_header_init(0, 15, 128, ctypes.byref(h)) == ERR_SHAPE
+    assert lib.qoq_blob_header_init(0, 16, 100, ctypes.byref(h)) == ERR_SHAPE
+
+
+def test_checkpoint_loader_refuses_mismatches(lib, tmp_path):
+    """PackedWeight.load checks the header and the length before touching a
+    device: a checkpoint for another shape or format, a truncated one or one
+    from another ABI version is refused on the host."""
+    N, K = 32, 256
+    h = _header(lib, 0, N, K)
+    body = bytes(h.blob_bytes) + bytes(h.scale_bytes)
+    good = tmp_path / "w.qpk"
+    good.write_bytes(bytes(h) + body)
+    for mode, n, k in ((1, N, K), (0, N, 384), (0, 48, K), (qoq.W8A8, N, K)):
+        with pytest.raises(qoq.QoQError):
+            qoq.PackedWeight.load(str(good), mode, n, k, "cpu")
+    short = tmp_path / "short.qpk"
+    short.write_bytes(bytes(h) + body[:-1])
+    with pytest.raises(qoq.QoQError):
+        qoq.PackedWeight.load(str(short), 0, N, K, "cpu")
+    h.abi_version -= 1
+    old = tmp_path / "old.qpk"
+    old.write_bytes(bytes(h) + body)
+    with pytest.raises(qoq.QoQError):
+        qoq.PackedWeight.load(str(old), 0, N, K, "cpu")
+    pw = qoq.PackedWeight.load(str(good), 0, N, K, "cpu")  # a matching header loads
+    assert pw.blob.numel() == N * K // 2 + N * K // 128 and pw.s_c.numel() == N
