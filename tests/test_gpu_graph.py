@@ -109,8 +109,9 @@ def test_captured_split_call_survives_workspace_growth():
     still replays correctly after a later call on the same stream needed a
     larger workspace: the smaller one stays allocated, so tensors allocated
     afterwards neither receive the replay's partial sums nor feed it."""
-    small, large = (200, 1664, 272), (128, 8192, 8192)
-    assert 0 < qoq.qoq_gemm_workspace_bytes("g128", *small) < qoq.qoq_gemm_workspace_bytes("g128", *large)
+    small, large = (200, 1664, 272), (128, 8192, 8192)  # (M, K, N)
+    need_small = qoq.qoq_gemm_workspace_bytes("g128", small[0], small[2], small[1])
+    assert 0 < need_small < qoq.qoq_gemm_workspace_bytes("g128", large[0], large[2], large[1])
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         (M, K, N) = small
@@ -131,7 +132,7 @@ def test_captured_split_call_survives_workspace_growth():
         s.synchronize()
         del pw2, xq2, s_x2
         torch.cuda.empty_cache()
-        need = qoq.qoq_gemm_workspace_bytes("g128", *small)
+        need = need_small
         fillers = [torch.full((max(need, 1 << 20),), 0x55, dtype=torch.uint8, device=DEV) for _ in range(8)]
         for r in range(3):
             y.fill_(0)
