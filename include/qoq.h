@@ -57,8 +57,9 @@
  *   - Rounding: every "round" is round-half-to-even; scales are computed in IEEE
  *     fp32 (correctly rounded division) and stored as FP16 (round to nearest
  *     even), and the stored FP16 scale is the one used to quantize.
- *   - There is no global mutable state: calls on different streams or threads
- *     are independent.
+ *   - There is no global mutable state, except in qoq_w4a8_gemm_noalloc (its
+ *     fixed scratch array): calls on different streams or threads are
+ *     independent.
  */
 #ifndef QOQ_H_
 #define QOQ_H_
@@ -214,6 +215,29 @@ qoq_status qoq_w4a8_gemm(int mode, const int8_t* xq, const uint16_t* s_x, const 
                          const void* blob, const uint16_t* s_c, int64_t M, int64_t N, int64_t K,
                          uint16_t* y, int32_t* acc_out, void* workspace, int64_t workspace_bytes,
                          void* stream);
+
+/*
+ * W4A8 GEMM that allocates nothing, for callers that cannot allocate device
+ * memory: code under HIP graph capture, serving loops and harnesses that
+ * forbid hipMalloc. The same computation, arguments and errors as
+ * qoq_w4a8_gemm, without the workspace arguments: the split-K partial sums go
+ * to a fixed device array of QOQ_NOALLOC_SCRATCH_BYTES (32 MiB) inside the
+ * library, one per GPU, held from the library's load until the process ends.
+ * That is the most any plan needs (a split plan keeps its split count times
+ * its 128 x 256 output blocks at most 256, so at most 256 x 128 x 256 x 4
+ * bytes); a shape whose plan needed more would return QOQ_ERR_WORKSPACE and
+ * launch nothing. Every call on a GPU
+ * uses that GPU's one array: calls that overlap in time on one GPU (on
+ * different streams, or from different threads) race and must not be issued;
+ * no contents are carried from one call to the next. The first call on each
+ * GPU looks up the array's address (hipGetSymbolAddress) and keeps it, the one
+ * piece of global state of this entry point.
+ */
+#define QOQ_NOALLOC_SCRATCH_BYTES (32 * 1024 * 1024)
+qoq_status qoq_w4a8_gemm_noalloc(int mode, const int8_t* xq, const uint16_t* s_x,
+                                 const int32_t* rowsum, const void* blob, const uint16_t* s_c,
+                                 int64_t M, int64_t N, int64_t K, uint16_t* y, int32_t* acc_out,
+                                 void* stream);
 
 /*
  * ---- W8A8 sibling ([W8A8]) ------------------------------------------------

@@ -54,7 +54,7 @@ EXPORTED = (
     "qoq_kv4_decode_attention",
     "qoq_blob_header_init",
     "qoq_blob_header_check",
-
+    "qoq_w4a8_gemm_noalloc",
 )
 
 FORMAT_W8A8 = 2  # format code of the W8A8 blob in a checkpoint header
@@ -118,6 +118,7 @@ def load_library():
                                              P, P, I64, P]),
             "qoq_blob_header_init": (I, [I, I64, I64, ctypes.POINTER(BlobHeader)]),
             "qoq_blob_header_check": (I, [ctypes.POINTER(BlobHeader), I, I64, I64]),
+            "qoq_w4a8_gemm_noalloc": (I, [I, P, P, P, P, P, I64, I64, I64, P, P, P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(lib, name)
