@@ -77,6 +77,10 @@ def parse_args(argv=None):
     p.add_argument("--no-large-m", action="store_true",
                    help="leave the large-M half (Llama-3-8B prefill gate_up, M=4096) out of the "
                         "default run's line")
+    p.add_argument("--counter-summary", nargs="+", default=None, metavar="DIR",
+                   help="instead of timing: read the counter CSVs of rocprofv3 --pmc runs of "
+                        "--profile-launches (one directory per pass) and write a per-kernel "
+                        "median table for this workload and layer under profiles/")
     p.add_argument("--pmc-summary", nargs="+", default=None, metavar="DIR",
                    help="instead of timing: read rocprofv3 counter CSVs (FETCH_SIZE run, "
                         "WRITE_SIZE run) of a --profile-launches run and write the traffic "
@@ -136,6 +140,54 @@ def stored_traffic(workload: str, layer: str, kernel: str):
         return None
     k = d.get("kernels", {}).get(kernel)
     return None if k is None else k["hbm_bytes"]
+
+
+def counter_summary(args, wl, layer) -> int:
+    """Median of each hardware counter per kernel over the dispatches of a
+    --profile-launches run (one rocprofv3 --pmc pass per directory), written as
+    a markdown table to profiles/counters_<workload>_<layer>.md with the
+    commands that produced it."""
+    import csv
+    import glob
+    import re
+    import statistics
+
+    vals, passes = {}, []
+    for d in args.counter_summary:
+        names = set()
+        for f in glob.glob(os.path.join(d, "**", "*_counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    m = re.search(r"(k_[a-z0-9_]+(<[^>]*>)?)", r["Kernel_Name"])
+                    if not m or not m.group(1).startswith(("k_gemm", "k_quantize_act", "k_splitk")):
+                        continue
+                    names.add(r["Counter_Name"])
+                    vals.setdefault((m.group(1), r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+        passes.append(sorted(names))
+    kernels = sorted({k for k, _ in vals})
+    counters = list(dict.fromkeys(c for ps in passes for c in ps))
+    lines = [f"# Hardware counters: {wl.name} / {layer.name} (M={layer.M} K={layer.K} N={layer.N})", "",
+             "Median per dispatch over the cold-cache launches of `bench.py --profile-launches` "
+             "(caches flushed before each launch). SQ_* counters are summed over the shader engines "
+             "(SQ_WAVE_CYCLES and SQ_WAIT_* in units of 4 cycles); TCC_* are 128-byte L2 requests "
+             "summed over the L2 channels; TA_BUSY_avr averages the compute units' address units; "
+             "GRBM_GUI_ACTIVE counts GPU cycles of the dispatch.", "",
+             "Commands (one pass per counter set):", ""]
+    for ps in passes:
+        lines.append(f"    rocprofv3 --kernel-trace --pmc {' '.join(ps)} --output-format csv -d <dir> -- "
+                     f"python3 bench.py --workload {wl.name} --layer {layer.name} --profile-launches 3")
+    lines += [f"    python3 bench.py --workload {wl.name} --layer {layer.name} --counter-summary <dir> ...",
+              "", "| counter | " + " | ".join(f"`{k}`" for k in kernels) + " |",
+              "|---|" + "---|" * len(kernels)]
+    for c in counters:
+        row = [f"{statistics.median(vals[(k, c)]):.0f}" if (k, c) in vals else "" for k in kernels]
+        lines.append(f"| {c} | " + " | ".join(row) + " |")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    out = os.path.join(ROOT, "profiles", f"counters_{wl.name}_{layer.name}.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out)
+    return 0
 
 
 def pmc_summary(args, wl, layer) -> int:
@@ -421,6 +473,8 @@ def main(argv=None) -> int:
     layer = layers[0]
     if args.pmc_summary:
         return pmc_summary(args, wl, layer)
+    if args.counter_summary:
+        return counter_summary(args, wl, layer)
 
     if args.kv4:
         for name, B, Hq, H, T in KV4_SHAPES:

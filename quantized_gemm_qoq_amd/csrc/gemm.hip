@@ -503,11 +503,6 @@ __device__ __forceinline__ void staged_partials(const int32x4 (&acc)[TM][TN], ui
 //     address arithmetic.
 // The plan selects this kernel only when every byte offset fits in 32 bits.
 constexpr int kBufferConfig = 0x00020000;  // gfx9 buffer resource word 3: 32-bit dwords
-// Cache policy of a buffer access that is coherent across the whole device
-// (sc1; what an agent-scope atomic load or store compiles to on gfx950).
-constexpr int kCoherent = 16;
-// s_waitcnt vmcnt(0) lgkmcnt(0): every issued memory access has completed.
-constexpr int kWaitAllMem = 7 << 4;
 
 template <int N>
 __device__ __forceinline__ void wide_load_a(u32x4 (&stage)[N], __amdgpu_buffer_rsrc_t ra,
@@ -950,7 +945,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_lds(
 // runs the epilogue for a share of the (tile, row block) pairs.
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
-template <int F, int MB, int NT>
+template <int F, int MB, int NT, int PL>
 __device__ __forceinline__ void stream_load(u32x4 (&bq)[NT][Fmt<F>::kVec], uint32_t (&pq)[NT],
                                             int32x4 (&aq)[MB][2], __amdgpu_buffer_rsrc_t rb,
                                             __amdgpu_buffer_rsrc_t rp, __amdgpu_buffer_rsrc_t ra,
@@ -964,7 +959,7 @@ __device__ __forceinline__ void stream_load(u32x4 (&bq)[NT][Fmt<F>::kVec], uint3
         const uint32_t ob = valid ? b_off[i] + (uint32_t)gi * (1024u * kV) : kOutOfRange;
         bq[i][0] = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)ob, 0, 0);
         if constexpr (kV == 2) bq[i][1] = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)ob, 1024, 0);
-        if (Fmt<F>::kG128) {
+        if (Fmt<F>::kG128 && PL == 0) {
             const uint32_t op = valid ? p_off[i] + (uint32_t)gi * 16u : kOutOfRange;
             pq[i] = __builtin_amdgcn_raw_buffer_load_b8(rp, (int)op, 0, 0);
         }
@@ -978,16 +973,39 @@ __device__ __forceinline__ void stream_load(u32x4 (&bq)[NT][Fmt<F>::kVec], uint3
     }
 }
 
-template <int F, int MB, int NT>
+// The parameter byte of tile i and group h of a wave (h counted from the
+// wave's first group) from the wave's parameter dwords pd: dword d = (h NT +
+// i) 4 + q of the wave's run sits in lane d % 64 of pd[d / 64] and holds
+// channels 4q .. 4q + 3, so lane c takes it from lane (h NT + i) 4 + c / 4
+// with one cross-lane read (ds_bpermute, no memory access).
+template <int PL, int NT>
+__device__ __forceinline__ uint32_t param_byte(const uint32_t (&pd)[PL], int i, int h, int c) {
+    const int base = (h * NT + i) * 4;  // wave-uniform, a multiple of 4
+    const int blk = base >> 6;
+    uint32_t w = pd[0];
+#pragma unroll
+    for (int k = 1; k < PL; ++k) w = blk == k ? pd[k] : w;
+    const int src = (base & 63) + (c >> 2);
+    const uint32_t v = (uint32_t)__builtin_amdgcn_ds_bpermute(src * 4, (int)w);
+    return (v >> ((c & 3) * 8)) & 0xFFu;
+}
+
+template <int F, int MB, int NT, int PL>
 __device__ __forceinline__ void stream_compute(int32x4 (&acc)[NT][MB],
                                                const u32x4 (&bq)[NT][Fmt<F>::kVec],
                                                const uint32_t (&pq)[NT],
-                                               const int32x4 (&aq)[MB][2]) {
+                                               const int32x4 (&aq)[MB][2],
+                                               const uint32_t (&pd)[PL > 0 ? PL : 1], int h, int c) {
     // the group word from the parameter byte in a few integer operations (a
     // table in LDS would need a barrier before the first group)
     uint32_t gw[NT];
 #pragma unroll
-    for (int i = 0; i < NT; ++i) gw[i] = Fmt<F>::kG128 ? group_word(pq[i] & 0xFFu) : 0u;
+    for (int i = 0; i < NT; ++i) {
+        if constexpr (Fmt<F>::kG128 && PL > 0)
+            gw[i] = group_word(param_byte<PL, NT>(pd, i, h, c));
+        else
+            gw[i] = Fmt<F>::kG128 ? group_word(pq[i] & 0xFFu) : 0u;
+    }
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
         const int32x4 b0 = b_operand<F, 0>(bq[i], gw[i]);
@@ -999,7 +1017,7 @@ __device__ __forceinline__ void stream_compute(int32x4 (&acc)[NT][MB],
     }
 }
 
-template <int F, int MB, int NT, int R, int W>
+template <int F, int MB, int NT, int R, int W, int PL>
 __global__ __launch_bounds__(W * 64) void k_gemm_stream(
     const int8_t* __restrict__ xq, const uint16_t* __restrict__ s_x,
     const int32_t* __restrict__ rowsum, const uint8_t* __restrict__ blob,
@@ -1072,12 +1090,39 @@ __global__ __launch_bounds__(W * 64) void k_gemm_stream(
     // scale loads (and the LDS set-up, if any) then overlap their latency.
 #pragma unroll
     for (int r = 0; r < R - 1; ++r)
-        stream_load<F, MB, NT>(bq[r], pq[r], aq[r], rb, rp, ra, b_off, p_off, a_off, r,
-                               r < main_count, a_step);
-    // Operands of this wave's epilogue pairs (p = wave + e W), read now so
-    // that the stores at the end wait on no global load.
+        stream_load<F, MB, NT, PL>(bq[r], pq[r], aq[r], rb, rp, ra, b_off, p_off, a_off, r,
+                                   r < main_count, a_step);
+    // g128 parameters: with PL > 0 the wave's NT x count parameter bytes
+    // arrive as 4 bytes per lane per load (dword d = (h NT + i) 4 + q holds
+    // channels 4q .. 4q + 3 of group g0 + h of tile i), PL loads in all
+    // instead of one 1-byte load per tile and group; param_byte() hands each
+    // lane its byte. Dwords past the wave's groups get an out-of-range offset
+    // (no memory request).
+    uint32_t pd[PL > 0 ? PL : 1];
+    if constexpr (kG128 && PL > 0) {
+        uint32_t off[PL];
+#pragma unroll
+        for (int L = 0; L < PL; ++L) {
+            const int d = 64 * L + lane;
+            const int hh = d / (4 * NT), i = (d >> 2) % NT;
+            const int t = min(nb * NT + i, tiles - 1);
+            off[L] = hh < count ? ((uint32_t)t * (uint32_t)G + (uint32_t)(g0 + hh)) * 16u + 4u * (uint32_t)(d & 3)
+                                : kOutOfRange;
+        }
+        // all offsets first, then the loads back to back (interleaving them
+        // made the compiler reuse a load's destination as a temporary, which
+        // costs a wait for that load)
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int L = 0; L < PL; ++L) pd[L] = __builtin_amdgcn_raw_buffer_load_b32(rp, (int)off[L], 0, 0);
+    }
+    // Operands of this wave's epilogue pairs (p = wave + e W), read now (after
+    // the first weight loads, and kept as raw bits until the epilogue, so that
+    // nothing waits for them early) so that the stores at the end wait on no
+    // global load.
+    __builtin_amdgcn_sched_barrier(0);
     constexpr int kEp = (kPairs + W - 1) / W;
-    float ep_sc[kEp], ep_sx[kEp][4];
+    uint32_t ep_sc[kEp], ep_sx[kEp][4];
     int ep_z[kEp], ep_rs[kEp][4];
 #pragma unroll
     for (int e = 0; e < kEp; ++e) {
@@ -1085,15 +1130,16 @@ __global__ __launch_bounds__(W * 64) void k_gemm_stream(
         const int t = min(nb * NT + min(p, kPairs - 1) / MB, tiles - 1);
         const int n = 16 * t + c;
         const int mrow = 16 * (u0 + min(p, kPairs - 1) % MB) + 4 * j;
-        ep_sc[e] = h2f(s_c[n]);
+        ep_sc[e] = s_c[n];
         ep_z[e] = Fmt<F>::kZp ? (int)blob[code_bytes + n] : 0;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int m = min(mrow + v, M - 1);
-            ep_sx[e][v] = h2f(s_x[m]);
+            ep_sx[e][v] = s_x[m];
             ep_rs[e][v] = Fmt<F>::kZp ? rowsum[m] : 0;
         }
     }
+    __builtin_amdgcn_sched_barrier(0);
     if (!kSlices) {
         for (int i = threadIdx.x; i < kPairs * kWave; i += kThr) red[i] = int32x4{0, 0, 0, 0};
         __syncthreads();
@@ -1102,16 +1148,19 @@ __global__ __launch_bounds__(W * 64) void k_gemm_stream(
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int nxt = h + r + R - 1;
-            stream_load<F, MB, NT>(bq[(r + R - 1) % R], pq[(r + R - 1) % R],
+            stream_load<F, MB, NT, PL>(bq[(r + R - 1) % R], pq[(r + R - 1) % R],
                                        aq[(r + R - 1) % R], rb, rp, ra, b_off, p_off, a_off, nxt,
                                        nxt < main_count, a_step);
-            stream_compute<F, MB, NT>(acc, bq[r], pq[r], aq[r]);
+            // the look-ahead loads leave before this group's unpack, which
+            // would otherwise be scheduled first and wait for every load
+            __builtin_amdgcn_sched_barrier(0);
+            stream_compute<F, MB, NT, PL>(acc, bq[r], pq[r], aq[r], pd, h + r, c);
         }
     }
     for (int h = main_count; h < count; ++h) {
-        stream_load<F, MB, NT>(bq[0], pq[0], aq[0], rb, rp, ra, b_off, p_off, a_off, h, true,
+        stream_load<F, MB, NT, PL>(bq[0], pq[0], aq[0], rb, rp, ra, b_off, p_off, a_off, h, true,
                                    a_step);
-        stream_compute<F, MB, NT>(acc, bq[0], pq[0], aq[0]);
+        stream_compute<F, MB, NT, PL>(acc, bq[0], pq[0], aq[0], pd, h, c);
     }
 
     // Sum the waves' partial tiles in LDS.
@@ -1158,215 +1207,9 @@ __global__ __launch_bounds__(W * 64) void k_gemm_stream(
                 if (Fmt<F>::kZp) r -= ep_z[e] * ep_rs[e][v];
                 const size_t o = (size_t)m * N + n;
                 if (acc_out) acc_out[o] = r;
-                y[o] = output_value(r, ep_sx[e][v], ep_sc[e]);
+                y[o] = output_value(r, h2f(ep_sx[e][v]), h2f(ep_sc[e]));
             }
         }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Split-K decode kernel (M <= 64): weight streaming at HBM rate with every
-// weight byte requested once.
-//
-// Workgroup b owns a band of NT 16-channel tiles, every row tile of the call
-// (MB of them) and one of S contiguous K-slices; its W waves split the slice's
-// groups and stream them through a ring of R register sets exactly as in
-// k_gemm_stream. The waves' partial tiles are added in LDS (one 16-byte slot
-// per lane and tile pair, added in wave order). With S > 1 the slices of a
-// band meet in the workspace: each workgroup stores its sums in its own slot,
-// publishes them (agent-scope release), and takes a ticket from the band's
-// counter; the workgroup that draws the last ticket acquires the other slots,
-// adds them, writes the outputs and resets the counter to zero for the next
-// call. INT32 addition is exact, so the outputs do not depend on which slice
-// arrives last. The S slices of a band are given block indices that the
-// round-robin dispatch places on one XCD, so their partial sums meet in that
-// XCD's L2. The FP16 outputs of the band are staged in LDS and leave as
-// 16-byte row segments.
-template <int F, int MB, int NT, int S, int W, int R>
-__global__ __launch_bounds__(W * 64) void k_gemm_dec(
-    const int8_t* __restrict__ xq, const uint16_t* __restrict__ s_x,
-    const int32_t* __restrict__ rowsum, const uint8_t* __restrict__ blob,
-    const uint16_t* __restrict__ s_c, int M, int N, int K, uint16_t* __restrict__ y,
-    int32_t* __restrict__ acc_out, int32x4* part, uint32_t* cnt) {
-    constexpr int kPairs = NT * MB;
-    constexpr int kThr = W * 64;
-    constexpr int kEp = (kPairs + W - 1) / W;  // tile pairs each wave finishes
-    constexpr int kRowHalves = 16 * NT + 8;     // output staging row: 16 NT values + 16 bytes
-    static_assert(W * kPairs * kWave * 16 <= 128 * 1024, "the waves' partial tiles must fit the LDS");
-    __shared__ int32x4 red[W * kPairs * kWave];
-    __shared__ __attribute__((aligned(16))) uint16_t ostage[16 * MB * kRowHalves];
-    __shared__ uint32_t ticket;
-
-    const int lane = threadIdx.x % kWave;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int G = K / kGroup;
-    const int tiles = N / 16;
-    const int U = (M + 15) / 16;
-    const int c = lane % 16, j = lane / 16;
-    const int nblk = (tiles + NT - 1) / NT;
-    int nb, s;
-    if (S > 1 && nblk % 8 == 0) {
-        const int hi = blockIdx.x / (8 * S), rem = blockIdx.x % (8 * S);
-        s = rem / 8;
-        nb = hi * 8 + rem % 8;
-    } else {
-        nb = blockIdx.x / S;
-        s = blockIdx.x % S;
-    }
-    const int gs0 = G * s / S;
-    const int Gs = G * (s + 1) / S - gs0;
-    const int g0 = gs0 + Gs * wave / W;
-    const int count = gs0 + Gs * (wave + 1) / W - g0;
-
-    constexpr bool kG128 = Fmt<F>::kG128;
-    constexpr int kV = Fmt<F>::kVec;
-    const size_t code_bytes = code_bytes_of(F, N, K);
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)xq, (short)0, (int)((uint32_t)G * (uint32_t)U * 2048u), kBufferConfig);
-    const __amdgpu_buffer_rsrc_t rb =
-        __builtin_amdgcn_make_buffer_rsrc((void*)blob, (short)0, (int)(uint32_t)code_bytes, kBufferConfig);
-    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(blob + code_bytes), (short)0, (int)(uint32_t)(kG128 ? N * G : N), kBufferConfig);
-
-    uint32_t b_off[NT], p_off[NT], a_off[MB];
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-        const int t = min(nb * NT + i, tiles - 1);
-        b_off[i] = ((uint32_t)t * (uint32_t)G + (uint32_t)g0) * (1024u * kV) + (uint32_t)lane * 16u;
-        p_off[i] = ((uint32_t)t * (uint32_t)G + (uint32_t)g0) * 16u + (uint32_t)c;
-    }
-    const uint32_t a_step = (uint32_t)U * 2048u;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-        a_off[mb] = (uint32_t)g0 * a_step + (uint32_t)min(mb, U - 1) * 2048u + (uint32_t)lane * 16u;
-
-    int32x4 acc[NT][MB];
-#pragma unroll
-    for (int i = 0; i < NT; ++i)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[i][mb] = int32x4{0, 0, 0, 0};
-
-    u32x4 bq[R][NT][kV];
-    uint32_t pq[R][NT];
-    int32x4 aq[R][MB][2];
-    const int main_count = count / R * R;
-#pragma unroll
-    for (int r = 0; r < R - 1; ++r)
-        stream_load<F, MB, NT>(bq[r], pq[r], aq[r], rb, rp, ra, b_off, p_off, a_off, r,
-                               r < main_count, a_step);
-    // Operands of this wave's epilogue pairs (p = wave + e W), read now so
-    // that the stores at the end wait on no global load.
-    float ep_sc[kEp], ep_sx[kEp][4];
-    int ep_z[kEp], ep_rs[kEp][4];
-#pragma unroll
-    for (int e = 0; e < kEp; ++e) {
-        const int p = min(wave + e * W, kPairs - 1);
-        const int t = min(nb * NT + p / MB, tiles - 1);
-        const int n = 16 * t + c;
-        const int mrow = 16 * (p % MB) + 4 * j;
-        ep_sc[e] = h2f(s_c[n]);
-        ep_z[e] = Fmt<F>::kZp ? (int)blob[code_bytes + n] : 0;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int m = min(mrow + v, M - 1);
-            ep_sx[e][v] = h2f(s_x[m]);
-            ep_rs[e][v] = Fmt<F>::kZp ? rowsum[m] : 0;
-        }
-    }
-    for (int h = 0; h < main_count; h += R) {
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int nxt = h + r + R - 1;
-            stream_load<F, MB, NT>(bq[(r + R - 1) % R], pq[(r + R - 1) % R], aq[(r + R - 1) % R], rb,
-                                   rp, ra, b_off, p_off, a_off, nxt, nxt < main_count, a_step);
-            stream_compute<F, MB, NT>(acc, bq[r], pq[r], aq[r]);
-        }
-    }
-    for (int h = main_count; h < count; ++h) {
-        stream_load<F, MB, NT>(bq[0], pq[0], aq[0], rb, rp, ra, b_off, p_off, a_off, h, true, a_step);
-        stream_compute<F, MB, NT>(acc, bq[0], pq[0], aq[0]);
-    }
-
-    // The waves' partial tiles, added in LDS in wave order.
-#pragma unroll
-    for (int i = 0; i < NT; ++i)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) red[(wave * kPairs + i * MB + mb) * kWave + lane] = acc[i][mb];
-    __syncthreads();
-    int32x4 r4[kEp];
-#pragma unroll
-    for (int e = 0; e < kEp; ++e) {
-        const int p = min(wave + e * W, kPairs - 1);
-        int32x4 sl[W];
-#pragma unroll
-        for (int w2 = 0; w2 < W; ++w2) sl[w2] = red[(w2 * kPairs + p) * kWave + lane];
-        r4[e] = sl[0];
-#pragma unroll
-        for (int w2 = 1; w2 < W; ++w2) r4[e] += sl[w2];
-    }
-
-    if constexpr (S > 1) {
-        // This slice's sums into its slot with device-coherent stores (sc1:
-        // the same access as an agent-scope atomic store), acknowledged before
-        // the ticket is drawn; the last slice reads the other slots with
-        // device-coherent loads. No cache-wide write-back or invalidation is
-        // needed, since only these accesses cross workgroups.
-        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)part, (short)0, (int)((uint32_t)nblk * (uint32_t)(S * kPairs) * 1024u), kBufferConfig);
-#pragma unroll
-        for (int e = 0; e < kEp; ++e) {
-            const int p = wave + e * W;
-            if (p < kPairs)
-                __builtin_amdgcn_raw_buffer_store_b128(
-                    __builtin_bit_cast(u32x4, r4[e]), rw,
-                    (int)((((uint32_t)(nb * S + s) * kPairs + p) * kWave + lane) * 16u), 0, kCoherent);
-        }
-        __builtin_amdgcn_s_waitcnt(kWaitAllMem);
-        __syncthreads();
-        if (threadIdx.x == 0) ticket = __hip_atomic_fetch_add(&cnt[nb], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __syncthreads();
-        if (ticket != (uint32_t)(S - 1)) return;
-#pragma unroll
-        for (int e = 0; e < kEp; ++e) {
-            const int p = wave + e * W;
-            if (p >= kPairs) continue;
-            int32x4 other[S];
-#pragma unroll
-            for (int s2 = 0; s2 < S; ++s2)
-                other[s2] = s2 == s ? int32x4{0, 0, 0, 0}
-                                    : __builtin_bit_cast(int32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                          rw, (int)((((uint32_t)(nb * S + s2) * kPairs + p) * kWave + lane) * 16u), 0,
-                                          kCoherent));
-#pragma unroll
-            for (int s2 = 0; s2 < S; ++s2) r4[e] += other[s2];
-        }
-        if (threadIdx.x == 0) __hip_atomic_store(&cnt[nb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-
-    // Epilogue: outputs into the staging rows, then 16-byte row segments.
-#pragma unroll
-    for (int e = 0; e < kEp; ++e) {
-        const int p = wave + e * W;
-        if (p >= kPairs) break;
-        const int i = p / MB, mb = p % MB;
-        const int t = nb * NT + i;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int row = 16 * mb + 4 * j + v;
-            int r = r4[e][v];
-            if (Fmt<F>::kZp) r -= ep_z[e] * ep_rs[e][v];
-            if (acc_out && t < tiles && row < M) acc_out[(size_t)row * N + 16 * t + c] = r;
-            ostage[row * kRowHalves + 16 * i + c] = output_value(r, ep_sx[e][v], ep_sc[e]);
-        }
-    }
-    __syncthreads();
-    constexpr int kChunks = 2 * NT;  // 16-byte segments per staged row
-    for (int q = threadIdx.x; q < 16 * MB * kChunks; q += kThr) {
-        const int row = q / kChunks, ch = q % kChunks;
-        const int n = (nb * NT) * 16 + ch * 8;
-        if (row < M && n < N)
-            *reinterpret_cast<u32x4*>(y + (size_t)row * N + n) =
-                *reinterpret_cast<const u32x4*>(ostage + row * kRowHalves + ch * 8);
     }
 }
 
@@ -1379,12 +1222,14 @@ enum Kind { kSimple = 0, kTile = 2, kWide = 3, kStream = 4, kLds = 5 };
 
 struct Plan {
     int kind = kSimple;
-    int mb = 0, nt = 0, r = 2, w = 8;  // stream kernel: row tiles, channel tiles, ring depth, waves
-    int mgrid = 1;                     //   and workgroups along M
+    int mb = 0, nt = 0, r = 2, w = 8;  // stream kernel: row tiles, channel tiles, ring depth, waves,
+    int mgrid = 1;                     //   workgroups along M
+    int pl = 0;                        //   and g128 parameter loads per wave (0: one per tile and group)
     int bn = 256;                      // 16-row-wave tiled kernel: 128 x bn blocks
     int s = 1;                         //   and its K splits (partial sums in the workspace)
     int64_t ws_bytes = 0;
     int group_m = 4;                   // wide and LDS-pipelined kernels: block rows per XCD raster group
+    int bm = 128;                      // LDS-pipelined kernel: rows per block
     int64_t nblk = 0;
 };
 
@@ -1426,9 +1271,12 @@ Plan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, bool have_ws) {
             p.kind = kStream;
             p.nt = (tiles + 2) / 3 >= 2 * kCUs ? 3 : 2;
             if (M <= 16) {
+                // g128 keeps 8 waves (two groups in flight each), whose
+                // parameter bytes fit two 4-byte lane loads; the other formats
+                // stream with 4 waves, four groups in flight each
                 p.mb = 1;
-                p.r = 2;
-                p.w = 8;
+                p.r = fmt == kFmtG128 ? 2 : 4;
+                p.w = fmt == kFmtG128 ? 8 : 4;
             } else if (M <= 32) {
                 p.mb = 2;
                 p.r = 1;
@@ -1450,6 +1298,16 @@ Plan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, bool have_ws) {
         // they fill about one round; with more blocks, the wide kernel's two
         // 4-wave workgroups per CU.
         p.kind = nb128 > kCUs && M >= 512 ? kWide : kLds;
+        // 256-row blocks of the LDS-pipelined kernel (two rows of four 128 x
+        // 64 waves; each weight tile loaded once for 256 rows) in place of the
+        // wide kernel when they fill one to four rounds of the compute units
+        // (measured 4-7% faster there; equal beyond)
+        const int64_t nb256 = ((M + 255) / 256) * ((N + 255) / 256);
+        if (p.kind == kWide && nb256 >= kCUs && nb256 <= 4 * kCUs) {
+            p.kind = kLds;
+            p.bm = 256;
+            p.group_m = 8;
+        }
         if (p.kind == kLds && nb128 < kCUs / 2)
             p.s = (int)std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(8, kCUs / nb128), K / kGroup / 2));
     } else {
@@ -1470,6 +1328,12 @@ Plan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, bool have_ws) {
         const int64_t U = (M + 15) / 16;
         p.mgrid = (int)((U + p.mb - 1) / p.mb);
         p.nblk = (tiles + p.nt - 1) / p.nt;
+        // g128: a wave's NT x (groups per wave) parameter bytes in 4-byte lane
+        // loads, 64 lanes per load, when that takes at most 2 loads (a third
+        // load made the compiler wait for all of them before the first group)
+        const int64_t per_wave = (K / kGroup + p.w - 1) / p.w;
+        const int64_t loads = (p.nt * per_wave + 15) / 16;
+        p.pl = fmt != kFmtG128 || loads > 2 ? 0 : (int)loads;
     }
     if (p.kind != kTile && p.kind != kLds) p.s = 1;
     p.ws_bytes = p.s > 1 ? (int64_t)p.s * M * N * 4 : 0;
@@ -1491,17 +1355,27 @@ struct GemmArgs {
     int group_m;
 };
 
-template <int F, int MB, int NT, int R, int W>
+template <int F, int MB, int NT, int R, int W, int PL>
 void launch_stream_t(const Plan& p, const GemmArgs& a) {
-    hipLaunchKernelGGL((k_gemm_stream<F, MB, NT, R, W>), dim3((unsigned)(p.nblk * p.mgrid)), dim3(W * 64),
-                       0, a.stream, a.xq, a.s_x, a.rowsum, a.blob, a.s_c, a.M, a.N, a.K, a.y,
-                       a.acc_out);
+    hipLaunchKernelGGL((k_gemm_stream<F, MB, NT, R, W, PL>), dim3((unsigned)(p.nblk * p.mgrid)),
+                       dim3(W * 64), 0, a.stream, a.xq, a.s_x, a.rowsum, a.blob, a.s_c, a.M, a.N, a.K,
+                       a.y, a.acc_out);
+}
+
+template <int F, int MB, int NT, int R, int W>
+void launch_stream_pl(const Plan& p, const GemmArgs& a) {
+    if constexpr (F == kFmtG128) {
+        if (p.pl == 1) { launch_stream_t<F, MB, NT, R, W, 1>(p, a); return; }
+        if (p.pl == 2) { launch_stream_t<F, MB, NT, R, W, 2>(p, a); return; }
+    }
+    launch_stream_t<F, MB, NT, R, W, 0>(p, a);
 }
 
 template <int F, int MB, int NT>
 void launch_stream_rw(const Plan& p, const GemmArgs& a) {
-    if (p.r == 1) launch_stream_t<F, MB, NT, 1, 16>(p, a);
-    else launch_stream_t<F, MB, NT, 2, 8>(p, a);
+    if (p.r == 1) launch_stream_pl<F, MB, NT, 1, 16>(p, a);
+    else if (p.r == 4) launch_stream_pl<F, MB, NT, 4, 4>(p, a);
+    else launch_stream_pl<F, MB, NT, 2, 8>(p, a);
 }
 
 template <int F, int MB>
@@ -1513,8 +1387,7 @@ void launch_stream_nt(const Plan& p, const GemmArgs& a) {
 template <int F>
 void launch_stream(const Plan& p, const GemmArgs& a) {
     if (p.mb == 1) launch_stream_nt<F, 1>(p, a);
-    else if (p.mb == 2) launch_stream_nt<F, 2>(p, a);
-    else launch_stream_nt<F, 4>(p, a);
+    else launch_stream_nt<F, 2>(p, a);
 }
 
 template <int F, int BM, int BN, int WM, int WN>
@@ -1571,7 +1444,8 @@ void launch_plan(const Plan& p, const GemmArgs& a) {
             launch_wide_t<F, 128, 256, 4>(a);
             break;
         case kLds:
-            launch_lds_t<F, 128, 1>(p, a);
+            if (p.bm == 256) launch_lds_t<F, 256, 2>(p, a);
+            else launch_lds_t<F, 128, 1>(p, a);
             break;
         case kTile:
             if (p.bn == 256) launch_tile_t<F, 128, 256, 2, 4>(p, a);

@@ -82,3 +82,25 @@ def test_stored_traffic_only_while_sources_match(tmp_path, monkeypatch):
 def test_more_than_one_gpu_is_refused(capsys):
     assert bench.main(["--gpus", "2"]) == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_counter_summary_table(tmp_path, monkeypatch):
+    """Medians per kernel and counter over the dispatches, one pass per
+    directory, in a markdown table under profiles/ (redirected here)."""
+    d1, d2 = str(tmp_path / "a"), str(tmp_path / "b")
+    _write_counters(d1, "SQ_WAVES", [(PC, 4096.0), (PC, 4096.0), (QACT, 256.0), (COPY, 1.0)])
+    _write_counters(d2, "TCC_HIT_sum", [(PC, 10.0), (PC, 30.0), (PC, 20.0), (GEMM, 7.0)])
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    wl = workloads.WORKLOADS["llama3_8b_qkv_decode"]
+    args = bench.parse_args(["--workload", wl.name, "--counter-summary", d1, d2])
+    assert bench.counter_summary(args, wl, wl.layers[0]) == 0
+    text = (tmp_path / "profiles" / f"counters_{wl.name}_{wl.layers[0].name}.md").read_text()
+    rows = {l.split("|")[1].strip(): [c.strip() for c in l.split("|")[2:-1]]
+            for l in text.splitlines() if l.startswith("| SQ_") or l.startswith("| TCC_")}
+    head = [l for l in text.splitlines() if l.startswith("| counter")][0]
+    cols = [c.strip().strip("`") for c in head.split("|")[2:-1]]
+    assert "__amd_rocclr_copyBuffer" not in cols and len(cols) == 3
+    pc = cols.index("k_gemm_stream<1, 2, 3, 1, 16>")
+    assert rows["SQ_WAVES"][pc] == "4096" and rows["TCC_HIT_sum"][pc] == "20"
+    assert rows["SQ_WAVES"][cols.index("k_gemm_lds<0, 128, 1>")] == ""
+    assert "--pmc SQ_WAVES" in text and "--pmc TCC_HIT_sum" in text
