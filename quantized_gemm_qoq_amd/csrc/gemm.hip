@@ -1303,7 +1303,9 @@ Plan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, bool have_ws) {
         // wide kernel when they fill one to four rounds of the compute units
         // (measured 4-7% faster there; equal beyond)
         const int64_t nb256 = ((M + 255) / 256) * ((N + 255) / 256);
-        if (p.kind == kWide && nb256 >= kCUs && nb256 <= 4 * kCUs) {
+        // (INT8 weights excepted: three stages of their 256 x 256 blocks
+        // would not fit the LDS)
+        if (p.kind == kWide && fmt != kFmtW8 && nb256 >= kCUs && nb256 <= 4 * kCUs) {
             p.kind = kLds;
             p.bm = 256;
             p.group_m = 8;
@@ -1444,8 +1446,13 @@ void launch_plan(const Plan& p, const GemmArgs& a) {
             launch_wide_t<F, 128, 256, 4>(a);
             break;
         case kLds:
-            if (p.bm == 256) launch_lds_t<F, 256, 2>(p, a);
-            else launch_lds_t<F, 128, 1>(p, a);
+            if constexpr (F != kFmtW8) {
+                if (p.bm == 256) {
+                    launch_lds_t<F, 256, 2>(p, a);
+                    break;
+                }
+            }
+            launch_lds_t<F, 128, 1>(p, a);
             break;
         case kTile:
             if (p.bn == 256) launch_tile_t<F, 128, 256, 2, 4>(p, a);
