@@ -709,19 +709,20 @@ __global__ __launch_bounds__(WN * 64, 2) void k_gemm_wide(
 }
 
 // ---------------------------------------------------------------------------
-// LDS-pipelined kernel (large M). One workgroup of 8 waves per compute unit
-// owns a BM x 256 block; wave (wm, wn) computes 128 rows x 256/WN channels
-// (8 row tiles x TN channel tiles), so every weight tile is unpacked by WM
+// LDS-pipelined kernel (M > 64). A workgroup of kW waves owns a BM x BN block
+// (one 8-wave workgroup of 128 x 256, or two 4-wave workgroups of 128 x 128,
+// per compute unit); wave (wm, wn) computes BM/WM rows x BN/WN channels (TM
+// row tiles x TN channel tiles), so every weight tile is unpacked by WM
 // waves. Both operands reach LDS by direct buffer-to-LDS loads (no staging
-// registers), three groups deep: the loads of group g+2 are issued at the
+// registers), NS groups deep: the loads of group g+NS-1 are issued at the
 // start of step g into the buffer that step g-1 has just finished reading, and
 // step g waits only for its own group's loads (the load counter is in order,
-// so the wait leaves the next group's loads in flight), then one barrier
-// publishes the group to all waves. The three buffers are separate arrays
-// named by fixed code (three steps per loop iteration), so that the compiler
-// can tell the loads into one buffer from the reads of another. Small grids
-// split K over S copies of the block grid; each copy writes its exact INT32
-// partial sums and the split-K reduction kernel finishes them.
+// so the wait leaves the next groups' loads in flight), then one barrier
+// publishes the group to all waves. The buffers are separate arrays named by
+// fixed code (NS steps per loop iteration), so that the compiler can tell the
+// loads into one buffer from the reads of another. Small grids split K over S
+// copies of the block grid; each copy writes its exact INT32 partial sums and
+// the split-K reduction kernel finishes them.
 template <int F, int TM, int TN>
 __device__ __forceinline__ void lds_compute(int32x4 (&acc)[TM][TN], const u32x4* la,
                                             const u32x4* lb, const uint8_t* lp) {
@@ -776,13 +777,13 @@ __device__ __forceinline__ void lds_compute(int32x4 (&acc)[TM][TN], const u32x4*
 
 #define QOQ_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
-template <int F, int BM, int WM>
-__global__ __launch_bounds__(512, 1) void k_gemm_lds(
+template <int F, int BM, int WM, int BN, int kW, int NS>
+__global__ __launch_bounds__(kW * 64, 8 / kW) void k_gemm_lds(
     const int8_t* __restrict__ xq, const uint16_t* __restrict__ s_x,
     const int32_t* __restrict__ rowsum, const uint8_t* __restrict__ blob,
     const uint16_t* __restrict__ s_c, int M, int N, int K, uint16_t* __restrict__ y,
     int32_t* __restrict__ acc_out, int group_m, int S, int32_t* __restrict__ part) {
-    constexpr int kThr = 512, kW = 8, BN = 256;
+    constexpr int kThr = kW * 64;
     constexpr int WN = kW / WM;
     constexpr int TM = BM / 16 / WM, TN = BN / WN / 16;
     constexpr bool kG128 = Fmt<F>::kG128;
@@ -794,15 +795,19 @@ __global__ __launch_bounds__(512, 1) void k_gemm_lds(
     constexpr int kADma = kAVec / kThr;          // loads per wave per group
     constexpr int kBDma = kBVec / kThr;
     static_assert(kAVec % kThr == 0 && kBVec % kThr == 0, "loads must divide evenly");
-    static_assert(3 * kStageVec * 16 <= 160 * 1024, "three stages must fit the LDS");
-    // Wait for all but the next group's loads (wave 0's parameter load of the
-    // next group may be waited for too), and for this wave's LDS reads.
-    constexpr int kD = kADma + kBDma;
+    static_assert(NS == 3 || NS == 4, "three or four stages");
+    static_assert(NS * kStageVec * 16 * (8 / kW) <= 160 * 1024,
+                  "the stages of every resident workgroup must fit the LDS");
+    // Wait for all but the next NS-2 groups' loads (wave 0's parameter loads
+    // of those may be waited for too), and for this wave's LDS reads.
+    constexpr int kD = (kADma + kBDma) * (NS - 2);
+    static_assert(kD < 64, "the load counter holds 6 bits");
     constexpr int kWaitStep = (kD & 15) | ((kD >> 4) << 14) | (7 << 4);  // vmcnt(kD) lgkmcnt(0)
     constexpr int kWaitAll = (7 << 4);                                   // vmcnt(0) lgkmcnt(0)
     __shared__ u32x4 st0[kStageVec];
     __shared__ u32x4 st1[kStageVec];
     __shared__ u32x4 st2[kStageVec];
+    __shared__ u32x4 st3[NS > 3 ? kStageVec : 1];
 
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -886,12 +891,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm_lds(
     const int lp = (kAVec + kBVec) * 16 + (wn * TN) * 16 + c;  // byte index
 
     // Step g: wait for group g, publish it, refill the buffer step g-1 read
-    // with group g+2 (clamped at the end: those loads are never read), run g.
+    // with group g+NS-1 (clamped at the end: those loads are never read), run
+    // g.
     auto step = [&](const u32x4* cur, u32x4* refill, int g) {
         __builtin_amdgcn_s_waitcnt(kWaitStep);
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        issue(refill, g0 + min(g + 2, Gc - 1));
+        issue(refill, g0 + min(g + NS - 1, Gc - 1));
         __builtin_amdgcn_sched_barrier(0);
         lds_compute<F, TM, TN>(acc, cur + la, cur + lb, reinterpret_cast<const uint8_t*>(cur) + lp);
         __builtin_amdgcn_sched_barrier(0);
@@ -900,30 +906,46 @@ __global__ __launch_bounds__(512, 1) void k_gemm_lds(
     issue(st0, g0);
     issue(st1, g0 + min(1, Gc - 1));
     int h = 0;
-    for (; h + 2 < Gc; h += 3) {
-        step(st0, st2, h);
-        step(st1, st0, h + 1);
-        step(st2, st1, h + 2);
+    if constexpr (NS == 3) {
+        for (; h + 2 < Gc; h += 3) {
+            step(st0, st2, h);
+            step(st1, st0, h + 1);
+            step(st2, st1, h + 2);
+        }
+        if (h < Gc) step(st0, st2, h);
+        if (h + 1 < Gc) step(st1, st0, h + 1);
+    } else {
+        issue(st2, g0 + min(2, Gc - 1));
+        for (; h + 3 < Gc; h += 4) {
+            step(st0, st3, h);
+            step(st1, st0, h + 1);
+            step(st2, st1, h + 2);
+            step(st3, st2, h + 3);
+        }
+        if (h < Gc) step(st0, st3, h);
+        if (h + 1 < Gc) step(st1, st0, h + 1);
+        if (h + 2 < Gc) step(st2, st1, h + 2);
     }
-    if (h < Gc) step(st0, st2, h);
-    if (h + 1 < Gc) step(st1, st0, h + 1);
     // No load may still be writing this workgroup's LDS when it exits.
     __builtin_amdgcn_s_waitcnt(kWaitAll);
 
-    // Epilogue through LDS (buffer 0, free once every wave's loads have landed
-    // and every wave is past its last group): with S > 1 the raw partial sums
-    // (the reduction kernel adds them and applies the zero-point compensation
-    // and the rescale once), else the outputs.
-    static_assert(kW * 2 * 16 * (TN * 32 + 16) <= kStageVec * 16 && kW * 16 * TN * 64 <= kStageVec * 16,
-                  "epilogue regions must fit buffer 0");
+    // Epilogue through LDS (buffers 0 and 1, half the waves in each, free once
+    // every wave's loads have landed and every wave is past its last group):
+    // with S > 1 the raw partial sums (the reduction kernel adds them and
+    // applies the zero-point compensation and the rescale once), else the
+    // outputs.
+    static_assert((kW / 2) * 2 * 16 * (TN * 32 + 16) <= kStageVec * 16 &&
+                      (kW / 2) * 16 * TN * 64 <= kStageVec * 16,
+                  "epilogue regions must fit two buffers");
     __syncthreads();
+    uint8_t* half = reinterpret_cast<uint8_t*>(wave < kW / 2 ? st0 : st1);
+    const int slot = wave % (kW / 2);
     const int m0 = bm * BM + wm * TM * 16, n0 = (bn * (BN / 16) + wn * TN) * 16;
     if (part)
-        staged_partials<TM, TN>(acc, reinterpret_cast<uint8_t*>(st0) + wave * (16 * TN * 64), m0, n0, M,
-                                N, part + (size_t)split * M * N);
+        staged_partials<TM, TN>(acc, half + slot * (16 * TN * 64), m0, n0, M, N, part + (size_t)split * M * N);
     else
-        staged_epilogue<F, TM, TN>(acc, reinterpret_cast<uint8_t*>(st0) + wave * (2 * 16 * (TN * 32 + 16)),
-                                   m0, n0, M, N, s_x, rowsum, s_c, blob + code_bytes, y, acc_out);
+        staged_epilogue<F, TM, TN>(acc, half + slot * (2 * 16 * (TN * 32 + 16)), m0, n0, M, N, s_x, rowsum,
+                                   s_c, blob + code_bytes, y, acc_out);
 }
 #undef QOQ_LDS_PTR
 
@@ -1225,11 +1247,10 @@ struct Plan {
     int mb = 0, nt = 0, r = 2, w = 8;  // stream kernel: row tiles, channel tiles, ring depth, waves,
     int mgrid = 1;                     //   workgroups along M
     int pl = 0;                        //   and g128 parameter loads per wave (0: one per tile and group)
-    int bn = 256;                      // 16-row-wave tiled kernel: 128 x bn blocks
+    int bn = 256;                      // 16-row-wave tiled and LDS-pipelined kernels: 128 x bn blocks
     int s = 1;                         //   and its K splits (partial sums in the workspace)
     int64_t ws_bytes = 0;
     int group_m = 4;                   // wide and LDS-pipelined kernels: block rows per XCD raster group
-    int bm = 128;                      // LDS-pipelined kernel: rows per block
     int64_t nblk = 0;
 };
 
@@ -1254,11 +1275,15 @@ bool fits_buffer_offsets(int fmt, int64_t M, int64_t N, int64_t K) {
 //       workgroup per compute unit; below 128 blocks, with a workspace, split
 //       over K into min(8, 256 / nb128) ranges (the split sums are added by
 //       the reduction kernel); without one, M >= 512 runs unsplit and
-//       M < 512 takes the 16-row-wave tiled kernel;
+//       M < 512 takes the 16-row-wave tiled kernel; for 4-bit weights with
+//       M < 512 and K <= 16384, 128 x 128 blocks of two 4-wave workgroups
+//       per compute unit instead, split in powers of two;
 //     nb128 > 256, M >= 512: the wide-wave tiled kernel, two 4-wave
 //       workgroups of 128 x 256 per compute unit (256-row blocks of the
-//       LDS-pipelined kernel were within 5% of it either way, depending on
-//       the data); M < 512: the LDS-pipelined kernel with 128-row blocks.
+//       LDS-pipelined kernel were 3-15% slower on the Llama-3-8B o_proj at
+//       M = 4096 and the Qwen1.5-72B qkv at M = 1024, and 2-3% faster on the
+//       Qwen1.5-72B gate_up at M = 1024); M < 512: the LDS-pipelined kernel
+//       with 128-row blocks.
 // Shapes whose offsets do not fit the buffer-load kernels take the reference
 // kernel (M <= 64) or the 16-row-wave tiled kernel, split over K (M > 64).
 Plan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, bool have_ws) {
@@ -1298,20 +1323,21 @@ Plan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, bool have_ws) {
         // they fill about one round; with more blocks, the wide kernel's two
         // 4-wave workgroups per CU.
         p.kind = nb128 > kCUs && M >= 512 ? kWide : kLds;
-        // 256-row blocks of the LDS-pipelined kernel (two rows of four 128 x
-        // 64 waves; each weight tile loaded once for 256 rows) in place of the
-        // wide kernel when they fill one to four rounds of the compute units
-        // (measured 4-7% faster there; equal beyond)
-        const int64_t nb256 = ((M + 255) / 256) * ((N + 255) / 256);
-        // (INT8 weights excepted: three stages of their 256 x 256 blocks
-        // would not fit the LDS)
-        if (p.kind == kWide && fmt != kFmtW8 && nb256 >= kCUs && nb256 <= 4 * kCUs) {
-            p.kind = kLds;
-            p.bm = 256;
-            p.group_m = 8;
-        }
-        if (p.kind == kLds && nb128 < kCUs / 2)
+        if (p.kind == kLds && M < 512 && K <= 16384 && fmt != kFmtW8) {
+            // Below 512 rows, 4-bit weights, K <= 16384: 128 x 128 blocks, two
+            // 4-wave workgroups per CU, split over K in the smallest power of
+            // two (at most 8, at least two groups per split) that gives one
+            // round of workgroups. Against 128 x 256 blocks of 8 waves this
+            // halves the split count and so the partial-sum traffic (Qwen1.5-
+            // 72B o_proj at M = 128: 6-12% faster, Llama-3-8B gate_up and down
+            // at M = 256: 5-8%); with longer K (Qwen1.5-72B down, K = 24576)
+            // the partial sums weigh less and 8-wave blocks were 2-10% faster.
+            p.bn = 128;
+            const int64_t nb = ((M + 127) / 128) * ((N + 127) / 128);
+            while (p.s < 8 && nb * p.s < kCUs && 2 * p.s <= K / kGroup / 2) p.s *= 2;
+        } else if (p.kind == kLds && nb128 < kCUs / 2) {
             p.s = (int)std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(8, kCUs / nb128), K / kGroup / 2));
+        }
     } else {
         p.kind = kTile;
         const int64_t gm128 = (M + 127) / 128, gn256 = (N + 255) / 256, gn128 = (N + 127) / 128;
@@ -1415,11 +1441,11 @@ void launch_wide_t(const GemmArgs& a) {
                        a.group_m);
 }
 
-template <int F, int BM, int WM>
+template <int F, int BM, int WM, int BN = 256, int kW = 8, int NS = 3>
 void launch_lds_t(const Plan& p, const GemmArgs& a) {
-    const unsigned blocks = (unsigned)(((a.M + BM - 1) / BM) * ((a.N + 255) / 256) * p.s);
+    const unsigned blocks = (unsigned)(((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * p.s);
     int32_t* part = p.s > 1 ? a.part : nullptr;
-    hipLaunchKernelGGL((k_gemm_lds<F, BM, WM>), dim3(blocks), dim3(512), 0, a.stream, a.xq, a.s_x,
+    hipLaunchKernelGGL((k_gemm_lds<F, BM, WM, BN, kW, NS>), dim3(blocks), dim3(kW * 64), 0, a.stream, a.xq, a.s_x,
                        a.rowsum, a.blob, a.s_c, a.M, a.N, a.K, a.y, a.acc_out, a.group_m, p.s, part);
     if (part) {
         const int64_t quads = (int64_t)a.M * a.N / 4;
@@ -1447,8 +1473,12 @@ void launch_plan(const Plan& p, const GemmArgs& a) {
             break;
         case kLds:
             if constexpr (F != kFmtW8) {
-                if (p.bm == 256) {
-                    launch_lds_t<F, 256, 2>(p, a);
+                // 128 x 128 blocks: 128 x 32 waves for g128 (each weight tile
+                // unpacked once), 64 x 64 waves for per-channel codes (no
+                // unpack to repeat, half the activation reads from LDS)
+                if (p.bn == 128) {
+                    if (F == kFmtPC) launch_lds_t<F, 128, 2, 128, 4>(p, a);
+                    else launch_lds_t<F, 128, 1, 128, 4>(p, a);
                     break;
                 }
             }

@@ -128,8 +128,8 @@ GEMM_SHAPES = [
     (520, 16, 128), (1024, 48, 256),
     # the wide kernel: too many blocks for one round, ragged rows and channels
     (1024, 8208, 128 * 13), (640, 16400, 128 * 5),
-    # 256-row blocks of the LDS-pipelined kernel (one to four rounds of them):
-    # a ragged last block of rows, of channels
+    # ... with a ragged last block of rows, of channels, at 2 to 3 rounds of
+    # blocks
     (520, 32784, 128 * 3), (1100, 16384, 128 * 2),
 ]
 
