@@ -858,6 +858,32 @@ def format_compare(args, wl, layer):
                                    "gemm_TOPS": round(2 * M * N * K / v_us / 1e6, 1)}
         del sets
         torch.cuda.empty_cache()
+        # ... and its FP8 GEMM (torch._scaled_mm, e4m3 operands, unit scales,
+        # BF16 out), whose dense peak on this chip equals the INT8 one.
+        try:
+            per = M * K + N * K + 2 * M * N
+            R = max(2, math.ceil(args.rotate_mib * 2**20 / per))
+            L = max(R, args.kernel_launches // R * R)
+            a8 = (torch.randn((M, K), generator=g) * 0.5).to(dev).to(torch.float8_e4m3fn)
+            b8 = (torch.randn((N, K), generator=g) * 0.5).to(dev).to(torch.float8_e4m3fn)
+            one = torch.ones((), device=dev)
+            sets = [(a8.clone(), b8.clone(), torch.empty((M, N), dtype=torch.bfloat16, device=dev))
+                    for _ in range(R)]
+
+            def fp8(st):
+                torch._scaled_mm(st[0], st[1].t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16,
+                                 out=st[2])
+
+            for st in sets[:2]:
+                fp8(st)
+            torch.cuda.synchronize()
+            f_us = avg_us([lambda st=st: fp8(st) for st in sets], L)
+            res["vendor_fp8_gemm"] = {"gemm_us": round(f_us, 3),
+                                      "gemm_TFLOPS": round(2 * M * N * K / f_us / 1e6, 1)}
+            del sets
+        except (RuntimeError, TypeError) as e:  # no FP8 GEMM in this build of the vendor library
+            res["vendor_fp8_gemm"] = {"error": str(e)[:200]}
+        torch.cuda.empty_cache()
     return res
 
 
