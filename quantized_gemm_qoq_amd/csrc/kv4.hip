@@ -85,60 +85,117 @@ __global__ __launch_bounds__(kSmoothWaves * kWave) void k_kv4_smooth_scales(
 }
 
 // ---------------------------------------------------------------------------
-// Append T tokens at positions t0 .. t0+T-1: one wave per (b, t, h) vector of
-// the keys and one of the values; lane l handles channels 2l and 2l + 1.
-__device__ __forceinline__ void kv4_quant_pair(float x0, float x1, int& c0, int& c1,
-                                               uint16_t& sbits, int& zz) {
-    const float mn = wave_min_f(fminf(0.0f, fminf(x0, x1)));
-    const float mx = wave_max_f(fmaxf(0.0f, fmaxf(x0, x1)));
+// Append T tokens at positions t0 .. t0+T-1.
+//
+// Quantization of one key or value vector held by a row of 16 lanes, eight
+// channels per lane (8g .. 8g+7 in lane g of the row): the range includes 0,
+// s = f16((max - min) / 15), z = clamp(rne(-min / s), 0, 15), codes
+// clamp(rne(x / s) + z, 0, 15); returns the lane's four code bytes, byte p
+// holding channel 8g + 2p in its low and 8g + 2p + 1 in its high nibble.
+__device__ __forceinline__ uint32_t kv4_quant_row8(const float (&x)[8], uint16_t& sbits, int& zz) {
+    float mn = 0.0f, mx = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        mn = fminf(mn, x[e]);
+        mx = fmaxf(mx, x[e]);
+    }
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) {
+        mn = fminf(mn, __shfl_xor(mn, o, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, o, 16));
+    }
     sbits = f2h((mx - mn) / 15.0f);
     const float sf = h2f(sbits);
     zz = 0;
-    c0 = c1 = 0;
+    uint32_t w = 0;
     if (sf != 0.0f) {
         zz = (int)fminf(fmaxf(rintf(-mn / sf), 0.0f), 15.0f);
-        c0 = min(15, max(0, (int)rintf(x0 / sf) + zz));
-        c1 = min(15, max(0, (int)rintf(x1 / sf) + zz));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int c = min(15, max(0, (int)rintf(x[e] / sf) + zz));
+            w |= (uint32_t)c << (4 * e);
+        }
     }
+    return w;
 }
 
+// One wave per (b, h, 16-token block of the cache) that the appended tokens
+// touch, in four steps of four tokens: lane l takes token 4q + l/16 of step q
+// and channels 8(l%16) .. +7, one 16-byte load per tensor, so each load
+// instruction moves 1 KB and the per-token reductions stay inside a row of
+// 16 lanes. Key codes leave as 4 bytes per lane (a token's 64-byte row per
+// row of lanes); value codes are gathered in a 1 KB LDS slice of the wave in
+// the value layout (channel pair major, 16 tokens per pair) and leave as one
+// 16-byte slot per lane. A block that the append covers only in part keeps
+// its other tokens' value codes (its slots are read into LDS first).
 __global__ __launch_bounds__(kKvThreads) void k_kv4_append(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ lambda, int B, int T, int H, int Tcap, int t0,
+    const uint16_t* __restrict__ lambda, int B, int T, int H, int Tcap, int t0, int blk0, int nblk,
     uint8_t* __restrict__ kq, uint16_t* __restrict__ ks, uint8_t* __restrict__ kz,
     uint8_t* __restrict__ vq, uint16_t* __restrict__ vs, uint8_t* __restrict__ vz) {
+    __shared__ u32x4 vt[kKvThreads / kWave][kWave];
     const int lane = threadIdx.x % kWave;
-    const int64_t vec = (int64_t)blockIdx.x * (kKvThreads / kWave) + threadIdx.x / kWave;
-    const int64_t total = (int64_t)B * T * H;
-    if (vec >= total) return;
-    const int h = (int)(vec % H);
-    const int t = (int)((vec / H) % T);
-    const int b = (int)(vec / ((int64_t)H * T));
-    const size_t src = (size_t)vec * kD + 2 * lane;  // [B][T][H][d] is vec-major
-    const int tc = t0 + t;
-    const size_t row = ((size_t)b * H + h) * Tcap + tc;
+    const int wv = threadIdx.x / kWave;
+    const int64_t item = (int64_t)blockIdx.x * (kKvThreads / kWave) + wv;
+    if (item >= (int64_t)B * H * nblk) return;  // the whole wave
+    const int cb = blk0 + (int)(item % nblk);
+    const int h = (int)((item / nblk) % H);
+    const int b = (int)(item / ((int64_t)nblk * H));
+    const int lo = max(16 * cb, t0), hi = min(16 * cb + 16, t0 + T);  // appended tokens of the block
+    const size_t row0 = ((size_t)b * H + h) * Tcap + 16 * cb;        // cache row of the block's token 0
+    const int g = lane % 16, r = lane / 16;
 
-    // keys, smoothed
-    const uint32_t kw = *reinterpret_cast<const uint32_t*>(k + src);
-    const uint32_t lw = *reinterpret_cast<const uint32_t*>(lambda + (size_t)h * kD + 2 * lane);
-    int c0, c1, zz;
-    uint16_t sb;
-    kv4_quant_pair(h2f(kw & 0xFFFFu) / h2f(lw & 0xFFFFu), h2f(kw >> 16) / h2f(lw >> 16), c0, c1,
-                   sb, zz);
-    kq[row * 64 + lane] = (uint8_t)(c0 | (c1 << 4));
-    if (lane == 0) {
-        ks[row] = sb;
-        kz[row] = (uint8_t)zz;
+    const u32x4 lw = *reinterpret_cast<const u32x4*>(lambda + (size_t)h * kD + 8 * g);
+    u32x4 kin[4], vin[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int t = min(max(16 * cb + 4 * q + r, lo), hi - 1) - t0;  // clamped: outside tokens unused
+        const size_t src = (((size_t)b * T + t) * H + h) * kD + 8 * g;  // [B][T][H][d]
+        kin[q] = *reinterpret_cast<const u32x4*>(k + src);
+        vin[q] = *reinterpret_cast<const u32x4*>(v + src);
     }
-    // values
-    const uint32_t vw = *reinterpret_cast<const uint32_t*>(v + src);
-    kv4_quant_pair(h2f(vw & 0xFFFFu), h2f(vw >> 16), c0, c1, sb, zz);
-    const size_t blk = ((size_t)b * H + h) * (Tcap / 16) + tc / 16;
-    vq[blk * 1024 + lane * 16 + tc % 16] = (uint8_t)(c0 | (c1 << 4));
-    if (lane == 0) {
-        vs[row] = sb;
-        vz[row] = (uint8_t)zz;
+    const size_t blk = ((size_t)b * H + h) * (Tcap / 16) + cb;
+    u32x4* vslot = reinterpret_cast<u32x4*>(vq + blk * 1024) + lane;  // channel pair `lane`, 16 tokens
+    uint8_t* vtb = reinterpret_cast<uint8_t*>(vt[wv]);
+    if (lo > 16 * cb || hi < 16 * cb + 16) vt[wv][lane] = *vslot;
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int i = 4 * q + r;
+        const bool in = 16 * cb + i >= lo && 16 * cb + i < hi;
+        float x[8];
+        uint16_t sb;
+        int zz;
+        // keys, smoothed
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t kw = kin[q][e / 2] >> (16 * (e % 2)), lwe = lw[e / 2] >> (16 * (e % 2));
+            x[e] = h2f(kw & 0xFFFFu) / h2f(lwe & 0xFFFFu);
+        }
+        uint32_t w = kv4_quant_row8(x, sb, zz);  // byte p: channels 8g + 2p (low), 8g + 2p + 1
+        if (in) {
+            *reinterpret_cast<uint32_t*>(kq + (row0 + i) * 64 + 4 * g) = w;
+            if (g == 0) {
+                ks[row0 + i] = sb;
+                kz[row0 + i] = (uint8_t)zz;
+            }
+        }
+        // values
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = h2f((vin[q][e / 2] >> (16 * (e % 2))) & 0xFFFFu);
+        w = kv4_quant_row8(x, sb, zz);
+        if (in) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+                vtb[(4 * g + p) * 16 + i] = (uint8_t)(w >> (8 * p));
+            if (g == 0) {
+                vs[row0 + i] = sb;
+                vz[row0 + i] = (uint8_t)zz;
+            }
+        }
     }
+    __builtin_amdgcn_wave_barrier();
+    *vslot = vt[wv][lane];
 }
 
 // ---------------------------------------------------------------------------
@@ -611,10 +668,12 @@ void launch_kv4_smooth_scales(const uint16_t* k, int64_t T, int64_t H, uint16_t*
 void launch_kv4_append(const uint16_t* k, const uint16_t* v, const uint16_t* lambda, int64_t B,
                        int64_t T, int64_t H, int64_t Tcap, int64_t t0, uint8_t* kq, uint16_t* ks,
                        uint8_t* kz, uint8_t* vq, uint16_t* vs, uint8_t* vz, hipStream_t stream) {
-    const int64_t vecs = B * T * H;
-    hipLaunchKernelGGL(k_kv4_append, dim3(blocks_of(vecs, kKvThreads / kWave)), dim3(kKvThreads), 0,
-                       stream, k, v, lambda, (int)B, (int)T, (int)H, (int)Tcap, (int)t0, kq, ks, kz,
-                       vq, vs, vz);
+    // the 16-token cache blocks the tokens t0 .. t0+T-1 fall in
+    const int64_t blk0 = t0 / 16, nblk = (t0 + T - 1) / 16 - blk0 + 1;
+    const int64_t items = B * H * nblk;
+    hipLaunchKernelGGL(k_kv4_append, dim3(blocks_of(items, kKvThreads / kWave)), dim3(kKvThreads), 0,
+                       stream, k, v, lambda, (int)B, (int)T, (int)H, (int)Tcap, (int)t0, (int)blk0,
+                       (int)nblk, kq, ks, kz, vq, vs, vz);
 }
 
 // Chunk length: the sequence is cut into n = ceil(256 / (B H)) chunks (at
