@@ -124,6 +124,8 @@ GEMM_SHAPES = [
     (9, 32, 128 * 21), (30, 48, 128 * 67), (48, 64, 128 * 70),
     # split K over 6 uneven group ranges (13 groups), ragged rows and channels
     (200, 272, 128 * 13),
+    # 128 x 128 blocks, two workgroups per CU, K split 8 ways (33 groups)
+    (130, 1040, 128 * 33),
     # LDS-pipelined kernel, 128-row blocks: group counts 0, 1 and 2 past a
     # multiple of its three-buffer loop, ragged rows and channels
     (600, 528, 128 * 9), (700, 400, 128 * 10), (200, 16400, 128 * 3),
