@@ -137,6 +137,26 @@ def test_workspace_bytes(lib):
     assert f(0, 64, 6144, 4096) % 16 == 0
 
 
+def test_middle_m_split_plans(lib):
+    """The K splits the plan picks for the middle-M benchmark layers, seen
+    through the workspace they need (S * M * N INT32 partial sums): 128 x 128
+    blocks of two workgroups per CU split in the smallest power of two that
+    fills a round (4-bit weights, M < 512, K <= 16384), else 128 x 256 blocks
+    split up to 8 ways."""
+    f, w8 = lib.qoq_gemm_workspace_bytes, lib.qoq_w8a8_gemm_workspace_bytes
+    part = lambda S, M, N: S * M * N * 4
+    for mode in (0, 1):
+        assert f(mode, 128, 8192, 8192) == part(4, 128, 8192)      # Qwen1.5-72B o_proj: 64 blocks
+        assert f(mode, 128, 24576, 8192) == part(2, 128, 24576)    # qkv: 192 blocks
+        assert f(mode, 128, 49152, 8192) == 0                      # gate_up: 384 blocks, no split
+        assert f(mode, 128, 8192, 24576) == part(8, 128, 8192)     # down, K > 16384: 32 wide blocks
+        assert f(mode, 256, 4096, 14336) == part(4, 256, 4096)     # Llama-3-8B down: 64 blocks
+        assert f(mode, 256, 28672, 4096) == 0                      # Llama-3-8B gate_up: 448 blocks
+    assert w8(128, 8192, 8192) == part(8, 128, 8192)               # INT8 weights: 128 x 256 blocks
+    assert f(0, 130, 1040, 128 * 33) == part(8, 130, 1040)         # 18 blocks: 8 splits of 33 groups
+    assert f(0, 200, 272, 128 * 13) == part(4, 200, 272)           # 13 groups: at most 6 splits -> 4
+
+
 def test_w8a8_validation(lib):
     assert lib.qoq_w8a8_packed_bytes(16, 128) == 16 * 128
     assert lib.qoq_w8a8_packed_bytes(15, 128) == -1

@@ -122,7 +122,8 @@ GEMM_SHAPES = [
     (129, 32, 640), (257, 80, 128), (512, 512, 1024), (520, 272, 640), (3, 16, 132096),
     # streaming-kernel ring: main loop plus a leftover group, for 1, 2 and 4 row blocks
     (9, 32, 128 * 21), (30, 48, 128 * 67), (48, 64, 128 * 70),
-    # split K over 6 uneven group ranges (13 groups), ragged rows and channels
+    # split K over 4 uneven group ranges (13 groups) on 128 x 128 blocks,
+    # ragged rows and channels
     (200, 272, 128 * 13),
     # 128 x 128 blocks, two workgroups per CU, K split 8 ways (33 groups)
     (130, 1040, 128 * 33),
