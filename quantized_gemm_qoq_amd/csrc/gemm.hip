@@ -714,13 +714,13 @@ __global__ __launch_bounds__(WN * 64, 2) void k_gemm_wide(
 // per compute unit); wave (wm, wn) computes BM/WM rows x BN/WN channels (TM
 // row tiles x TN channel tiles), so every weight tile is unpacked by WM
 // waves. Both operands reach LDS by direct buffer-to-LDS loads (no staging
-// registers), NS groups deep: the loads of group g+NS-1 are issued at the
+// registers), three groups deep: the loads of group g+2 are issued at the
 // start of step g into the buffer that step g-1 has just finished reading, and
 // step g waits only for its own group's loads (the load counter is in order,
-// so the wait leaves the next groups' loads in flight), then one barrier
-// publishes the group to all waves. The buffers are separate arrays named by
-// fixed code (NS steps per loop iteration), so that the compiler can tell the
-// loads into one buffer from the reads of another. Small grids split K over S
+// so the wait leaves the next group's loads in flight), then one barrier
+// publishes the group to all waves. The three buffers are separate arrays
+// named by fixed code (three steps per loop iteration), so that the compiler
+// can tell the loads into one buffer from the reads of another. Small grids split K over S
 // copies of the block grid; each copy writes its exact INT32 partial sums and
 // the split-K reduction kernel finishes them.
 template <int F, int TM, int TN>
@@ -777,7 +777,7 @@ __device__ __forceinline__ void lds_compute(int32x4 (&acc)[TM][TN], const u32x4*
 
 #define QOQ_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
-template <int F, int BM, int WM, int BN, int kW, int NS>
+template <int F, int BM, int WM, int BN, int kW>
 __global__ __launch_bounds__(kW * 64, 8 / kW) void k_gemm_lds(
     const int8_t* __restrict__ xq, const uint16_t* __restrict__ s_x,
     const int32_t* __restrict__ rowsum, const uint8_t* __restrict__ blob,
@@ -795,19 +795,17 @@ __global__ __launch_bounds__(kW * 64, 8 / kW) void k_gemm_lds(
     constexpr int kADma = kAVec / kThr;          // loads per wave per group
     constexpr int kBDma = kBVec / kThr;
     static_assert(kAVec % kThr == 0 && kBVec % kThr == 0, "loads must divide evenly");
-    static_assert(NS == 3 || NS == 4, "three or four stages");
-    static_assert(NS * kStageVec * 16 * (8 / kW) <= 160 * 1024,
-                  "the stages of every resident workgroup must fit the LDS");
-    // Wait for all but the next NS-2 groups' loads (wave 0's parameter loads
-    // of those may be waited for too), and for this wave's LDS reads.
-    constexpr int kD = (kADma + kBDma) * (NS - 2);
+    static_assert(3 * kStageVec * 16 * (8 / kW) <= 160 * 1024,
+                  "three stages of every resident workgroup must fit the LDS");
+    // Wait for all but the next group's loads (wave 0's parameter load of the
+    // next group may be waited for too), and for this wave's LDS reads.
+    constexpr int kD = kADma + kBDma;
     static_assert(kD < 64, "the load counter holds 6 bits");
     constexpr int kWaitStep = (kD & 15) | ((kD >> 4) << 14) | (7 << 4);  // vmcnt(kD) lgkmcnt(0)
     constexpr int kWaitAll = (7 << 4);                                   // vmcnt(0) lgkmcnt(0)
     __shared__ u32x4 st0[kStageVec];
     __shared__ u32x4 st1[kStageVec];
     __shared__ u32x4 st2[kStageVec];
-    __shared__ u32x4 st3[NS > 3 ? kStageVec : 1];
 
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -891,13 +889,12 @@ __global__ __launch_bounds__(kW * 64, 8 / kW) void k_gemm_lds(
     const int lp = (kAVec + kBVec) * 16 + (wn * TN) * 16 + c;  // byte index
 
     // Step g: wait for group g, publish it, refill the buffer step g-1 read
-    // with group g+NS-1 (clamped at the end: those loads are never read), run
-    // g.
+    // with group g+2 (clamped at the end: those loads are never read), run g.
     auto step = [&](const u32x4* cur, u32x4* refill, int g) {
         __builtin_amdgcn_s_waitcnt(kWaitStep);
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        issue(refill, g0 + min(g + NS - 1, Gc - 1));
+        issue(refill, g0 + min(g + 2, Gc - 1));
         __builtin_amdgcn_sched_barrier(0);
         lds_compute<F, TM, TN>(acc, cur + la, cur + lb, reinterpret_cast<const uint8_t*>(cur) + lp);
         __builtin_amdgcn_sched_barrier(0);
@@ -906,26 +903,13 @@ __global__ __launch_bounds__(kW * 64, 8 / kW) void k_gemm_lds(
     issue(st0, g0);
     issue(st1, g0 + min(1, Gc - 1));
     int h = 0;
-    if constexpr (NS == 3) {
-        for (; h + 2 < Gc; h += 3) {
-            step(st0, st2, h);
-            step(st1, st0, h + 1);
-            step(st2, st1, h + 2);
-        }
-        if (h < Gc) step(st0, st2, h);
-        if (h + 1 < Gc) step(st1, st0, h + 1);
-    } else {
-        issue(st2, g0 + min(2, Gc - 1));
-        for (; h + 3 < Gc; h += 4) {
-            step(st0, st3, h);
-            step(st1, st0, h + 1);
-            step(st2, st1, h + 2);
-            step(st3, st2, h + 3);
-        }
-        if (h < Gc) step(st0, st3, h);
-        if (h + 1 < Gc) step(st1, st0, h + 1);
-        if (h + 2 < Gc) step(st2, st1, h + 2);
+    for (; h + 2 < Gc; h += 3) {
+        step(st0, st2, h);
+        step(st1, st0, h + 1);
+        step(st2, st1, h + 2);
     }
+    if (h < Gc) step(st0, st2, h);
+    if (h + 1 < Gc) step(st1, st0, h + 1);
     // No load may still be writing this workgroup's LDS when it exits.
     __builtin_amdgcn_s_waitcnt(kWaitAll);
 
@@ -1441,11 +1425,11 @@ void launch_wide_t(const GemmArgs& a) {
                        a.group_m);
 }
 
-template <int F, int BM, int WM, int BN = 256, int kW = 8, int NS = 3>
+template <int F, int BM, int WM, int BN = 256, int kW = 8>
 void launch_lds_t(const Plan& p, const GemmArgs& a) {
     const unsigned blocks = (unsigned)(((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * p.s);
     int32_t* part = p.s > 1 ? a.part : nullptr;
-    hipLaunchKernelGGL((k_gemm_lds<F, BM, WM, BN, kW, NS>), dim3(blocks), dim3(kW * 64), 0, a.stream, a.xq, a.s_x,
+    hipLaunchKernelGGL((k_gemm_lds<F, BM, WM, BN, kW>), dim3(blocks), dim3(kW * 64), 0, a.stream, a.xq, a.s_x,
                        a.rowsum, a.blob, a.s_c, a.M, a.N, a.K, a.y, a.acc_out, a.group_m, p.s, part);
     if (part) {
         const int64_t quads = (int64_t)a.M * a.N / 4;
