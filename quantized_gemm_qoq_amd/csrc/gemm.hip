@@ -934,6 +934,411 @@ __global__ __launch_bounds__(kW * 64, 8 / kW) void k_gemm_lds(
 #undef QOQ_LDS_PTR
 
 // ---------------------------------------------------------------------------
+// Large-block persistent kernel (many 256 x 256 blocks). One 4-wave workgroup
+// per CU, one wave per SIMD; wave w computes all 256 rows of the block for 64
+// channels (16 x 4 accumulator tiles = all 256 AccVGPRs), so each weight tile
+// is unpacked once per 16 matrix-core operations (half the unpack per
+// operation of the 128-row waves) and a block moves 48 KB from L2 per group
+// for 65536 outputs instead of 32 KB for 32768.
+//   - Operands: A by direct buffer-to-LDS loads into four 32 KB stages; B (and
+//     the g128 parameter bytes) straight into four named register sets. The
+//     loads of group g+3 are issued during group g, so three groups are in
+//     flight behind the one being computed.
+//   - The weights are the first matrix-core operand, so an accumulator lane
+//     holds four consecutive channels of one row (c[n][m] = sum_k w[n,k]
+//     x[m,k]); the epilogue stores them as one 8-byte piece per (row tile,
+//     channel tile) without an LDS round trip.
+//   - Each k-step (64 of a group's 128 inputs) is 16 sub-blocks fenced against
+//     the scheduler: the LDS read of activation fragment a+3 (the last three
+//     read the next k-step's first fragments), one load of a later group, the
+//     four operations of fragment a, and one register of the next k-step's B
+//     operands. One barrier per group, between its k-steps, publishes group
+//     g+1 and frees the stage of group g-1.
+//   - Persistent: with more blocks than CUs, each workgroup walks the blocks of
+//     its XCD's contiguous share of the raster, and the pipeline runs through
+//     block boundaries (the next block's first groups load during the
+//     epilogue). The group count must be a multiple of four (the named stages).
+//   - The matrix-core operations are inline asm on accumulators tied to their
+//     AccVGPRs: with the builtin, blocks that hold two operations on one
+//     accumulator make the register allocator move accumulators through VGPRs.
+//     Their hazards are handled here: each operation starts with s_nop 1 (two
+//     wait states after a VALU write of an operand register: what the compiler
+//     inserts for the builtin on this chip), and 16 wait states separate the
+//     last operation from the epilogue's AccVGPR reads (the compiler inserts 8
+//     for a VALU read of a 16x16x64 result).
+__device__ __forceinline__ void mfma_tied(int32x4& c, int32x4 x, int32x4 w) {
+    asm volatile("s_nop 1\n\tv_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(c) : "v"(w), "v"(x));
+}
+
+// Register R (0..3) of the k-step KS B operand of a lane from its loaded
+// weight vectors.
+template <int F, int KS, int R>
+__device__ __forceinline__ int big_breg(const u32x4 (&p)[Fmt<F>::kVec], uint32_t gw) {
+    if constexpr (F == kFmtW8) {
+        const u32x4 v = p[KS];
+        return (int)(R == 0 ? v.x : R == 1 ? v.y : R == 2 ? v.z : v.w);
+    } else {
+        const uint32_t w = R < 2 ? (KS ? p[0].z : p[0].x) : (KS ? p[0].w : p[0].y);
+        uint32_t a = (R & 1) ? (w >> 4) & 0x0F0F0F0Fu : w & 0x0F0F0F0Fu;
+        if (F == kFmtG128) a = unpack4_g128w(a, gw);
+        return (int)a;
+    }
+}
+
+// One k-step of a wave: 16 sub-blocks (see above). af holds activation
+// fragments 0..2 of this k-step on entry and of the next one on exit; bcur
+// this k-step's B operands on entry and the next one's (built from bsrc with
+// gwsrc, k-step KSN) on exit. hook(a) adds work to sub-block a.
+template <int F, int KSN, typename Hook>
+__device__ __forceinline__ void big_kstep(int32x4 (&acc)[16][4], u32x4 (&af)[4], int32x4 (&bcur)[4],
+                                          const u32x4* lcur, const u32x4* lnext,
+                                          const u32x4 (&bsrc)[4][Fmt<F>::kVec], const uint32_t (&gwsrc)[4],
+                                          Hook&& hook) {
+    int32x4 bn[4];
+#pragma unroll
+    for (int a = 0; a < 16; ++a) {
+        const int na = a + 3;
+        af[na % 4] = na < 16 ? lcur[na * 128] : lnext[(na - 16) * 128];
+        hook(a);
+        const int32x4 xa = __builtin_bit_cast(int32x4, af[a % 4]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mfma_tied(acc[a][i], xa, bcur[i]);
+        const int t = a / 4;
+        int r;
+        switch (a % 4) {
+            case 0: r = big_breg<F, KSN, 0>(bsrc[t], gwsrc[t]); break;
+            case 1: r = big_breg<F, KSN, 1>(bsrc[t], gwsrc[t]); break;
+            case 2: r = big_breg<F, KSN, 2>(bsrc[t], gwsrc[t]); break;
+            default: r = big_breg<F, KSN, 3>(bsrc[t], gwsrc[t]); break;
+        }
+        // keeps the unpack in this sub-block (earlier passes would otherwise
+        // sink it to the end of the k-step)
+        asm volatile("" : "+v"(r));
+        bn[t][a % 4] = r;
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bcur[i] = bn[i];
+}
+
+#define QOQ_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+template <int F, bool kAccOut>
+__global__ __launch_bounds__(256, 1) void k_gemm_big(
+    const int8_t* __restrict__ xq, const uint16_t* __restrict__ s_x,
+    const int32_t* __restrict__ rowsum, const uint8_t* __restrict__ blob,
+    const uint16_t* __restrict__ s_c, int M, int N, int K, uint16_t* __restrict__ y,
+    int32_t* __restrict__ acc_out, int group_m) {
+    constexpr int NS = 4, BM = 256, BN = 256, kW = 4, TN = 4;
+    constexpr bool kG128 = Fmt<F>::kG128;
+    constexpr bool kZp = Fmt<F>::kZp;
+    constexpr int kV = Fmt<F>::kVec;
+    constexpr int kAVec = BM * 128 / 16;  // 16-byte vectors of A per group (32 KB)
+    constexpr int kADma = kAVec / (kW * 64);
+    constexpr int kD = kADma + 4 * kV + (kG128 ? 4 : 0);  // loads per wave per group
+    static_assert(2 * kD < 64, "the load counter holds 6 bits");
+    constexpr int kWaitMid = (kD & 15) | ((kD >> 4) << 14) | (7 << 4);              // vmcnt(kD) lgkmcnt(0)
+    constexpr int kWaitPro = ((2 * kD) & 15) | (((2 * kD) >> 4) << 14) | (7 << 4);  // vmcnt(2 kD) lgkmcnt(0)
+    constexpr int kWaitAll = (7 << 4);
+    __shared__ u32x4 st0[kAVec];
+    __shared__ u32x4 st1[kAVec];
+    __shared__ u32x4 st2[kAVec];
+    __shared__ u32x4 st3[kAVec];
+    __shared__ u32x4 ep[kW * 512];  // 8 KB per wave: the epilogue's scales
+    auto stage = [&](auto jc) __attribute__((always_inline)) -> u32x4* {
+        constexpr int J = decltype(jc)::value % NS;
+        if constexpr (J == 0) return st0;
+        else if constexpr (J == 1) return st1;
+        else if constexpr (J == 2) return st2;
+        else return st3;
+    };
+
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int c = lane % 16;
+    const int G = K / kGroup;
+    const int U = (M + 15) / 16;
+    const int tiles = N / 16;
+    const int grid_m = (M + BM - 1) / BM, grid_n = (N + BN - 1) / BN;
+    const int T = grid_m * grid_n;
+
+    // The blocks of this workgroup. With more blocks than workgroups, XCD x
+    // owns the contiguous range [xT/8, (x+1)T/8) of the raster (workgroups are
+    // dealt to the XCDs round-robin) and deals it to its workgroups in turn;
+    // otherwise each workgroup takes one block.
+    int t_first, t_step, n_my;
+    if (T > (int)gridDim.x) {
+        const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8, slots = gridDim.x / 8;
+        const int lo = xcd * T / 8, hi = (xcd + 1) * T / 8;
+        t_first = lo + slot;
+        t_step = slots;
+        n_my = t_first < hi ? (hi - t_first + slots - 1) / slots : 0;
+    } else {
+        int pid = blockIdx.x;
+        if (T % 8 == 0) pid = (pid % 8) * (T / 8) + pid / 8;
+        t_first = pid;
+        t_step = 0;
+        n_my = 1;
+    }
+    // Raster: groups of group_m block rows, column by column.
+    auto block_of = [&](int k, int& bm, int& bn) __attribute__((always_inline)) {
+        const int t = t_first + k * t_step;
+        const int per_group = group_m * grid_n;
+        const int first_m = (t / per_group) * group_m;
+        const int gsz = min(grid_m - first_m, group_m);
+        bm = first_m + (t % per_group) % gsz;
+        bn = (t % per_group) / gsz;
+    };
+
+    const size_t code_bytes = code_bytes_of(F, N, K);
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)xq, (short)0, (int)((uint32_t)G * (uint32_t)U * 2048u), kBufferConfig);
+    const __amdgpu_buffer_rsrc_t rb =
+        __builtin_amdgcn_make_buffer_rsrc((void*)blob, (short)0, (int)(uint32_t)code_bytes, kBufferConfig);
+    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(blob + code_bytes), (short)0, (int)(uint32_t)(kG128 ? N * G : N), kBufferConfig);
+    const __amdgpu_buffer_rsrc_t rsx = __builtin_amdgcn_make_buffer_rsrc((void*)s_x, (short)0, 2 * M, kBufferConfig);
+    const __amdgpu_buffer_rsrc_t rrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)rowsum, (short)0, kZp ? 4 * M : 0, kBufferConfig);
+    const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc((void*)s_c, (short)0, 2 * N, kBufferConfig);
+    const __amdgpu_buffer_rsrc_t rz =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(blob + code_bytes), (short)0, kZp ? N : 0, kBufferConfig);
+    const __amdgpu_buffer_rsrc_t ry =
+        __builtin_amdgcn_make_buffer_rsrc((void*)y, (short)0, (int)((uint32_t)M * (uint32_t)N * 2u), kBufferConfig);
+
+    // Load offsets: a per-lane constant part and a per-block scalar part. DMA
+    // load v of this wave moves vector (4v + wave) * 64 + lane of the group's
+    // A run, i.e. row tile u0 + (4v + wave) / 2 (clamped) and half (4v + wave)
+    // % 2; row tiles past the last are clamped and their rows never stored.
+    const uint32_t va = (uint32_t)(((wave & 1) * 64 + lane) * 16);
+    const uint32_t vb = (uint32_t)lane * 16u;
+    const uint32_t vp = (uint32_t)c;
+    const uint32_t a_step = (uint32_t)U * 2048u;
+    uint32_t oa[kADma], ob[4], op[4];
+    auto load_offsets = [&](int k) __attribute__((always_inline)) {
+        int bm, bn;
+        block_of(k, bm, bn);
+        const int u0 = bm * (BM / 16);
+#pragma unroll
+        for (int v = 0; v < kADma; ++v) oa[v] = (uint32_t)min(u0 + ((v * kW + wave) >> 1), U - 1) * 2048u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t t = (uint32_t)min(bn * (BN / 16) + wave * TN + i, tiles - 1);
+            ob[i] = t * (uint32_t)G * 64u * kV * 16u;
+            op[i] = t * (uint32_t)G * 16u;
+        }
+    };
+    uint32_t sa[kADma], sb[4], sp[4];  // scalar offsets of the next refill
+    auto refill_offsets = [&](int gl) __attribute__((always_inline)) {
+#pragma unroll
+        for (int v = 0; v < kADma; ++v) sa[v] = oa[v] + (uint32_t)gl * a_step;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sb[i] = ob[i] + (uint32_t)gl * (uint32_t)kV * 1024u;
+            sp[i] = op[i] + (uint32_t)gl * 16u;
+        }
+    };
+
+    u32x4 bq[NS][4][kV];
+    uint32_t pq[NS][4];
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pq[j][i] = 0;
+    // Load a (0..15) of a group into stage st / register set j: 8 DMA loads of
+    // A, then the 4 (8 for INT8 weights) B loads, then the 4 parameter bytes.
+    auto load_one = [&](u32x4* st, int j, int a) __attribute__((always_inline)) {
+        if (a < kADma) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, QOQ_LDS_PTR(st + (a * kW + wave) * 64), 16, (int)va,
+                                                     (int)sa[a], 0, 0);
+        } else if (a < kADma + 4) {
+            const int i = a - kADma;
+#pragma unroll
+            for (int v = 0; v < kV; ++v)
+                bq[j][i][v] = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)vb, (int)(sb[i] + v * 1024u), 0);
+        } else if (kG128 && a < kADma + 8) {
+            const int i = a - kADma - 4;
+            pq[j][i] = __builtin_amdgcn_raw_buffer_load_b8(rp, (int)vp, (int)sp[i], 0);
+        }
+    };
+
+    int32x4 acc[16][TN];
+#pragma unroll
+    for (int a = 0; a < 16; ++a)
+#pragma unroll
+        for (int b = 0; b < TN; ++b) acc[a][b] = int32x4{0, 0, 0, 0};
+
+    uint32_t gw[4], gwn[4];
+    u32x4 af[4];
+    int32x4 bcur[4];
+    int kl = 0;  // block of the load stream
+    // Epilogue scales of the block being computed: s_x and rowsum of 4 of its
+    // rows, s_c and zero of 4 consecutive channels per channel tile.
+    uint32_t sxw0 = 0, sxw1 = 0, zw[TN];
+    uint2 scw[TN];
+    u32x4 rsv = {0, 0, 0, 0};
+    int m0 = 0, n0 = 0;
+    uint8_t* rows = reinterpret_cast<uint8_t*>(ep) + wave * 8192;  // 256 s_x, 256 rowsum, 64 s_c, 64 z
+
+    // Group g (of the block being computed) in stage/set J, g+1 in J+1; the
+    // loads of stream position g+3 (the next block's groups when g+3 >= G)
+    // refill J-1, which every wave finished with before this group's barrier.
+    auto group = [&](auto jc, int g) __attribute__((always_inline)) {
+        constexpr int J = decltype(jc)::value % NS;
+        constexpr int JN = (J + 1) % NS, JR = (J + NS - 1) % NS;
+        const u32x4* cur = stage(std::integral_constant<int, J>{});
+        const u32x4* nxt = stage(std::integral_constant<int, JN>{});
+        u32x4* ref = stage(std::integral_constant<int, JR>{});
+        // k-step 0 hooks: the next group's g128 words; the scalar offsets of
+        // this group's refill (moving the load stream to the next block when
+        // it gets there); this block's epilogue scales in its first group.
+        auto hook0 = [&](int a) __attribute__((always_inline)) {
+            if (kG128 && a % 4 == 2) {
+                uint32_t w = group_word(pq[JN][a / 4] & 0xFFu);
+                asm volatile("" : "+v"(w));
+                gwn[a / 4] = w;
+            }
+            if (a == 5) {
+                int gl = g + 3;
+                if (gl >= G) {
+                    gl -= G;
+                    if (gl == 0 && kl + 1 < n_my) load_offsets(++kl);
+                }
+                refill_offsets(gl);
+#pragma unroll
+                for (int v = 0; v < kADma; ++v) asm volatile("" : "+s"(sa[v]));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) asm volatile("" : "+s"(sb[i]), "+s"(sp[i]));
+            }
+            if (a == 9 && g == 0) {
+                sxw0 = __builtin_amdgcn_raw_buffer_load_b32(rsx, (m0 + 4 * lane) * 2, 0, 0);
+                sxw1 = __builtin_amdgcn_raw_buffer_load_b32(rsx, (m0 + 4 * lane) * 2 + 4, 0, 0);
+                if (kZp) rsv = __builtin_amdgcn_raw_buffer_load_b128(rrs, (m0 + 4 * lane) * 4, 0, 0);
+#pragma unroll
+                for (int i = 0; i < TN; ++i) {
+                    const int nq = n0 + 16 * i + 4 * (lane / 16);
+                    const auto v2 = __builtin_amdgcn_raw_buffer_load_b64(rsc, nq * 2, 0, 0);
+                    scw[i] = make_uint2(v2[0], v2[1]);
+                    zw[i] = kZp ? __builtin_amdgcn_raw_buffer_load_b32(rz, nq, 0, 0) : 0u;
+                }
+            }
+        };
+        big_kstep<F, 1>(acc, af, bcur, cur + lane, cur + lane + 64, bq[J], gw, hook0);
+        __builtin_amdgcn_s_waitcnt(kWaitMid);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        auto issue_one = [&](int a) __attribute__((always_inline)) { load_one(ref, JR, a); };
+        big_kstep<F, 0>(acc, af, bcur, cur + lane + 64, nxt + lane, bq[JN], gwn, issue_one);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gw[i] = gwn[i];
+    };
+
+    // Prologue: groups 0..2 of the first block in flight, wait for group 0.
+    load_offsets(0);
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j) {
+        u32x4* st = j == 0 ? st0 : j == 1 ? st1 : st2;
+        refill_offsets(j);
+#pragma unroll
+        for (int a = 0; a < 16; ++a) load_one(st, j, a);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitPro);
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gw[i] = kG128 ? group_word(pq[0][i] & 0xFFu) : 0u;
+    af[0] = st0[lane];
+    af[1] = st0[lane + 128];
+    af[2] = st0[lane + 256];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bcur[i] = b_operand<F, 0>(bq[0][i], gw[i]);
+
+    const int jq = lane / 16;
+    for (int k = 0; k < n_my; ++k) {
+        int bm, bn;
+        block_of(k, bm, bn);
+        m0 = bm * BM;
+        n0 = (bn * (BN / 16) + wave * TN) * 16;
+        for (int h = 0; h < G; h += NS) {
+            group(std::integral_constant<int, 0>{}, h);
+            group(std::integral_constant<int, 1>{}, h + 1);
+            group(std::integral_constant<int, 2>{}, h + 2);
+            group(std::integral_constant<int, 3>{}, h + 3);
+        }
+        // Epilogue. 16 wait states after the last matrix-core operation, and
+        // every accumulator passed through an empty asm so that no read moves
+        // above them. Lane (c, jq) holds rows m0 + 16a + c, channels n0 + 16i +
+        // 4jq .. +3. The scales go through the wave's LDS region; each (row
+        // tile, channel tile) leaves as one store, and stores outside the
+        // output get an out-of-range offset (no branches).
+        asm volatile("s_nop 7\n\ts_nop 7");
+#pragma unroll
+        for (int a = 0; a < 16; ++a)
+#pragma unroll
+            for (int b = 0; b < TN; ++b) asm volatile("" : "+a"(acc[a][b]));
+        *reinterpret_cast<uint2*>(rows + lane * 8) = make_uint2(sxw0, sxw1);
+        if (kZp) *reinterpret_cast<u32x4*>(rows + 512 + lane * 16) = rsv;
+#pragma unroll
+        for (int i = 0; i < TN; ++i) {
+            *reinterpret_cast<uint2*>(rows + 1536 + (16 * i + 4 * jq) * 2) = scw[i];
+            if (kZp) *reinterpret_cast<uint32_t*>(rows + 1664 + 16 * i + 4 * jq) = zw[i];
+        }
+        if constexpr (kAccOut) {
+            const __amdgpu_buffer_rsrc_t racc = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)acc_out, (short)0, (int)((uint32_t)M * (uint32_t)N * 4u), kBufferConfig);
+#pragma unroll
+            for (int a = 0; a < 16; ++a) {
+                const int m = m0 + 16 * a + c;
+                const int rs = kZp ? *reinterpret_cast<const int*>(rows + 512 + (16 * a + c) * 4) : 0;
+#pragma unroll
+                for (int i = 0; i < TN; ++i) {
+                    const int n = n0 + 16 * i + 4 * jq;
+                    const uint32_t zz = kZp ? *reinterpret_cast<const uint32_t*>(rows + 1664 + 16 * i + 4 * jq) : 0u;
+                    u32x4 r;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        r[v] = (uint32_t)(acc[a][i][v] - (kZp ? (int)((zz >> (8 * v)) & 0xFFu) * rs : 0));
+                    const uint32_t off = (m < M && n < N) ? ((uint32_t)m * (uint32_t)N + (uint32_t)n) * 4u : 0x80000000u;
+                    __builtin_amdgcn_raw_buffer_store_b128(r, racc, (int)off, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int a = 0; a < 16; ++a) {
+            const int m = m0 + 16 * a + c;
+            const float sx = h2f(*reinterpret_cast<const uint16_t*>(rows + (16 * a + c) * 2));
+            const int rs = kZp ? *reinterpret_cast<const int*>(rows + 512 + (16 * a + c) * 4) : 0;
+#pragma unroll
+            for (int i = 0; i < TN; ++i) {
+                const int n = n0 + 16 * i + 4 * jq;
+                const uint2 scq = *reinterpret_cast<const uint2*>(rows + 1536 + (16 * i + 4 * jq) * 2);
+                const uint32_t zz = kZp ? *reinterpret_cast<const uint32_t*>(rows + 1664 + 16 * i + 4 * jq) : 0u;
+                uint32_t h[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    int r = acc[a][i][v];
+                    if (kZp) r -= (int)((zz >> (8 * v)) & 0xFFu) * rs;
+                    h[v] = output_value(r, sx, h2f(((v < 2 ? scq.x : scq.y) >> (16 * (v & 1))) & 0xFFFFu));
+                }
+                typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                const uint32_t off = (m < M && n < N) ? ((uint32_t)m * (uint32_t)N + (uint32_t)n) * 2u : 0x80000000u;
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)}, ry, (int)off,
+                                                      0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int a = 0; a < 16; ++a)
+#pragma unroll
+            for (int b = 0; b < TN; ++b) acc[a][b] = int32x4{0, 0, 0, 0};
+    }
+    // No load may still be writing this workgroup's LDS when it exits.
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
+}
+#undef QOQ_LDS_PTR
+
+// ---------------------------------------------------------------------------
 // Pipelined decode kernel (M <= 64): weight streaming at HBM rate.
 //
 // A workgroup of W waves owns NT 16-channel tiles and the whole K; wave w takes
@@ -1224,7 +1629,7 @@ __global__ __launch_bounds__(W * 64) void k_gemm_stream(
 
 constexpr int kCUs = 256;
 
-enum Kind { kSimple = 0, kTile = 2, kWide = 3, kStream = 4, kLds = 5 };
+enum Kind { kSimple = 0, kTile = 2, kWide = 3, kStream = 4, kLds = 5, kBig = 6 };
 
 struct Plan {
     int kind = kSimple;
@@ -1267,7 +1672,13 @@ bool fits_buffer_offsets(int fmt, int64_t M, int64_t N, int64_t K) {
 //       LDS-pipelined kernel were 3-15% slower on the Llama-3-8B o_proj at
 //       M = 4096 and the Qwen1.5-72B qkv at M = 1024, and 2-3% faster on the
 //       Qwen1.5-72B gate_up at M = 1024); M < 512: the LDS-pipelined kernel
-//       with 128-row blocks.
+//       with 128-row blocks;
+//     256 x 256 blocks in whole rounds of the compute units, with the group
+//       count a multiple of 4: the large-block persistent kernel (against
+//       the wide kernel: Llama-3-8B gate_up at M = 4096 4% faster in g128,
+//       10% per-channel, 4% INT8 weights; o_proj and down at M = 4096 7-11%).
+//       With a partial last round (Qwen1.5-72B qkv at M = 1024: 1.5 rounds)
+//       it was 5% slower, and below one round it would leave CUs idle.
 // Shapes whose offsets do not fit the buffer-load kernels take the reference
 // kernel (M <= 64) or the 16-row-wave tiled kernel, split over K (M > 64).
 Plan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, bool have_ws) {
@@ -1307,6 +1718,13 @@ Plan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, bool have_ws) {
         // they fill about one round; with more blocks, the wide kernel's two
         // 4-wave workgroups per CU.
         p.kind = nb128 > kCUs && M >= 512 ? kWide : kLds;
+        // Whole rounds of 256 x 256 blocks (at least one) with the group count
+        // a multiple of four: the large-block persistent kernel.
+        const int64_t nb256 = ((M + 255) / 256) * ((N + 255) / 256);
+        if (nb256 >= kCUs && nb256 % kCUs == 0 && (K / kGroup) % 4 == 0 && M * N * 2 < (int64_t(1) << 31)) {
+            p.kind = kBig;
+            p.group_m = 8;
+        }
         if (p.kind == kLds && M < 512 && K <= 16384 && fmt != kFmtW8) {
             // Below 512 rows, 4-bit weights, K <= 16384: 128 x 128 blocks, two
             // 4-wave workgroups per CU, split over K in the smallest power of
@@ -1440,6 +1858,18 @@ void launch_lds_t(const Plan& p, const GemmArgs& a) {
 }
 
 template <int F>
+void launch_big(const GemmArgs& a) {
+    const int64_t T = (int64_t)((a.M + 255) / 256) * ((a.N + 255) / 256);
+    const unsigned blocks = (unsigned)std::min<int64_t>(T, kCUs);
+    if (a.acc_out)
+        hipLaunchKernelGGL((k_gemm_big<F, true>), dim3(blocks), dim3(256), 0, a.stream, a.xq, a.s_x, a.rowsum,
+                           a.blob, a.s_c, a.M, a.N, a.K, a.y, a.acc_out, a.group_m);
+    else
+        hipLaunchKernelGGL((k_gemm_big<F, false>), dim3(blocks), dim3(256), 0, a.stream, a.xq, a.s_x, a.rowsum,
+                           a.blob, a.s_c, a.M, a.N, a.K, a.y, a.acc_out, a.group_m);
+}
+
+template <int F>
 void launch_simple(const GemmArgs& a) {
     const dim3 grid((unsigned)((a.N / 16 + 3) / 4), (unsigned)((a.M + 63) / 64));
     hipLaunchKernelGGL(k_gemm_simple<F>, grid, dim3(kThreads), 0, a.stream, a.xq, a.s_x,
@@ -1454,6 +1884,16 @@ void launch_plan(const Plan& p, const GemmArgs& a) {
             break;
         case kWide:
             launch_wide_t<F, 128, 256, 4>(a);
+            break;
+        case kBig:
+            // the INT32 sums' buffer offsets must fit too; else the wide kernel
+            if (a.acc_out && (int64_t)a.M * a.N * 4 >= (int64_t(1) << 31)) {
+                const GemmArgs w{a.part, a.xq, a.s_x, a.rowsum, a.blob, a.s_c, a.M, a.N, a.K, a.y, a.acc_out,
+                                 a.stream, 4};
+                launch_wide_t<F, 128, 256, 4>(w);
+            } else {
+                launch_big<F>(a);
+            }
             break;
         case kLds:
             if constexpr (F != kFmtW8) {

@@ -137,6 +137,10 @@ GEMM_SHAPES = [
     # ... with a ragged last block of rows, of channels, at 2 to 3 rounds of
     # blocks
     (520, 32784, 128 * 3), (1100, 16384, 128 * 2),
+    # the large-block persistent kernel: one round of 256 x 256 blocks with
+    # ragged rows and channels; two rounds (each workgroup crosses a block
+    # boundary every 4 groups); 12 groups
+    (4000, 4000, 128 * 8), (4000, 8000, 128 * 4), (2048, 8192, 128 * 12),
 ]
 
 
