@@ -82,7 +82,7 @@ WORKLOADS: Dict[str, Workload] = {
          Layer("llama3_8b_down_m256", M=256, K=14336, N=4096, seed=3001, x_kind="silu_mul"))),
     "llama3_8b_prefill": Workload(
         "llama3_8b_prefill", "Llama-3-8B prefill, M=4096: o_proj K=4096 N=4096, gate_up K=4096 N=28672",
-        ("g128",),
+        ("g128", "per_channel"),
         # 1% of the 4096 activation channels (41) carry x20 values.
         (Layer("llama3_8b_o_proj_m4096", M=4096, K=4096, N=4096, seed=4000,
                x_outliers=41, x_outlier_scale=20.0),
