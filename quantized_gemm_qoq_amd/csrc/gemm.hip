@@ -961,34 +961,27 @@ __global__ __launch_bounds__(kW * 64, 8 / kW) void k_gemm_lds(
 //   - The matrix-core operations are inline asm on accumulators tied to their
 //     AccVGPRs: with the builtin, blocks that hold two operations on one
 //     accumulator make the register allocator move accumulators through VGPRs.
-//     Their hazards are handled here: each operation starts with s_nop 1 (two
-//     wait states after a VALU write of an operand register: what the compiler
-//     inserts for the builtin on this chip), and 16 wait states separate the
-//     last operation from the epilogue's AccVGPR reads (the compiler inserts 8
-//     for a VALU read of a 16x16x64 result).
+//     No wait states precede them: every VGPR they read is written by a VALU
+//     at least two instructions earlier (B operands are built one k-step ahead,
+//     activation fragments come from LDS reads), which a CPU test checks on
+//     the generated assembly. A wait state after a VALU is costly here: the
+//     s_nop waits for the VALU, so the operation after it issues late. 16 wait
+//     states separate the last operation from the epilogue's AccVGPR reads (the
+//     compiler inserts 8 for a VALU read of a 16x16x64 result).
+//   - The B unpack is spread one VALU instruction per matrix-core operation
+//     (a VALU beside an operation in flight is free; several in a row are
+//     not); the g128 steps are asm so that the compiler's inline-asm hazard
+//     padding does not put an s_nop after a VALU.
 __device__ __forceinline__ void mfma_tied(int32x4& c, int32x4 x, int32x4 w) {
-    asm volatile("s_nop 1\n\tv_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(c) : "v"(w), "v"(x));
+    asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(c) : "v"(w), "v"(x));
 }
 
-// Register R (0..3) of the k-step KS B operand of a lane from its loaded
-// weight vectors.
-template <int F, int KS, int R>
-__device__ __forceinline__ int big_breg(const u32x4 (&p)[Fmt<F>::kVec], uint32_t gw) {
-    if constexpr (F == kFmtW8) {
-        const u32x4 v = p[KS];
-        return (int)(R == 0 ? v.x : R == 1 ? v.y : R == 2 ? v.z : v.w);
-    } else {
-        const uint32_t w = R < 2 ? (KS ? p[0].z : p[0].x) : (KS ? p[0].w : p[0].y);
-        uint32_t a = (R & 1) ? (w >> 4) & 0x0F0F0F0Fu : w & 0x0F0F0F0Fu;
-        if (F == kFmtG128) a = unpack4_g128w(a, gw);
-        return (int)a;
-    }
-}
-
-// One k-step of a wave: 16 sub-blocks (see above). af holds activation
-// fragments 0..2 of this k-step on entry and of the next one on exit; bcur
-// this k-step's B operands on entry and the next one's (built from bsrc with
-// gwsrc, k-step KSN) on exit. hook(a) adds work to sub-block a.
+// One k-step of a wave: 16 sub-blocks (see above), each of four fenced
+// phases (one matrix-core operation each). af holds activation fragments
+// 0..2 of this k-step on entry and of the next one on exit; bcur this k-step's
+// B operands on entry and the next one's (built from bsrc with gwsrc, k-step
+// KSN) on exit: register R of tile t is built in sub-block 4t + R, one step
+// per phase. hook(a, phase) adds work to phase `phase` of sub-block a.
 template <int F, int KSN, typename Hook>
 __device__ __forceinline__ void big_kstep(int32x4 (&acc)[16][4], u32x4 (&af)[4], int32x4 (&bcur)[4],
                                           const u32x4* lcur, const u32x4* lnext,
@@ -997,24 +990,39 @@ __device__ __forceinline__ void big_kstep(int32x4 (&acc)[16][4], u32x4 (&af)[4],
     int32x4 bn[4];
 #pragma unroll
     for (int a = 0; a < 16; ++a) {
+        const int t = a / 4, R = a % 4;
         const int na = a + 3;
         af[na % 4] = na < 16 ? lcur[na * 128] : lnext[(na - 16) * 128];
-        hook(a);
+        hook(a, 0);
         const int32x4 xa = __builtin_bit_cast(int32x4, af[a % 4]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mfma_tied(acc[a][i], xa, bcur[i]);
-        const int t = a / 4;
-        int r;
-        switch (a % 4) {
-            case 0: r = big_breg<F, KSN, 0>(bsrc[t], gwsrc[t]); break;
-            case 1: r = big_breg<F, KSN, 1>(bsrc[t], gwsrc[t]); break;
-            case 2: r = big_breg<F, KSN, 2>(bsrc[t], gwsrc[t]); break;
-            default: r = big_breg<F, KSN, 3>(bsrc[t], gwsrc[t]); break;
+        uint32_t x;
+        if constexpr (F == kFmtW8) {
+            x = bsrc[t][KSN][R];
+        } else {
+            const uint32_t w = R < 2 ? (KSN ? bsrc[t][0].z : bsrc[t][0].x) : (KSN ? bsrc[t][0].w : bsrc[t][0].y);
+            x = (R & 1) ? (w >> 4) : (w & 0x0F0F0F0Fu);
         }
-        // keeps the unpack in this sub-block (earlier passes would otherwise
-        // sink it to the end of the k-step)
-        asm volatile("" : "+v"(r));
-        bn[t][a % 4] = r;
+        // the pins keep each step in its phase (earlier passes would
+        // otherwise sink the unpack to the end of the k-step)
+        asm volatile("" : "+v"(x));
+        mfma_tied(acc[a][0], xa, bcur[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (F != kFmtW8) {
+            if (R & 1) x &= 0x0F0F0F0Fu;
+            asm volatile("" : "+v"(x));
+        }
+        hook(a, 1);
+        mfma_tied(acc[a][1], xa, bcur[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (F == kFmtG128)  // q * s + (128 - z s) per byte (see unpack4_g128w)
+            asm volatile("v_pk_mad_u16 %0, %0, %1, %1 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "+v"(x) : "v"(gwsrc[t]));
+        hook(a, 2);
+        mfma_tied(acc[a][2], xa, bcur[2]);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (F == kFmtG128) asm volatile("v_xor_b32 %0, 0x80808080, %0" : "+v"(x));
+        hook(a, 3);
+        mfma_tied(acc[a][3], xa, bcur[3]);
+        bn[t][R] = (int)x;
         __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -1112,7 +1120,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(
     // % 2; row tiles past the last are clamped and their rows never stored.
     const uint32_t va = (uint32_t)(((wave & 1) * 64 + lane) * 16);
     const uint32_t vb = (uint32_t)lane * 16u;
-    const uint32_t vp = (uint32_t)c;
+    // g128 parameter bytes arrive as the aligned dword that holds the lane's
+    // byte (a byte load's narrowed loop copies would wait on recent loads)
+    const uint32_t vp = (uint32_t)(c & ~3), psh = 8u * (uint32_t)(c & 3);
     const uint32_t a_step = (uint32_t)U * 2048u;
     uint32_t oa[kADma], ob[4], op[4];
     auto load_offsets = [&](int k) __attribute__((always_inline)) {
@@ -1145,20 +1155,22 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(
     for (int j = 0; j < NS; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) pq[j][i] = 0;
-    // Load a (0..15) of a group into stage st / register set j: 8 DMA loads of
-    // A, then the 4 (8 for INT8 weights) B loads, then the 4 parameter bytes.
+    // Load a (0..15) of a group into stage st / register set j: for g128 the 4
+    // parameter dwords first (the oldest loads of the group, so that the word
+    // computation one group ahead waits on them alone), then 8 DMA loads of A,
+    // then the 4 (8 for INT8 weights) B loads.
     auto load_one = [&](u32x4* st, int j, int a) __attribute__((always_inline)) {
-        if (a < kADma) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, QOQ_LDS_PTR(st + (a * kW + wave) * 64), 16, (int)va,
-                                                     (int)sa[a], 0, 0);
-        } else if (a < kADma + 4) {
-            const int i = a - kADma;
+        const int ap = kG128 ? a - 4 : a;
+        if (kG128 && a < 4) {
+            pq[j][a] = __builtin_amdgcn_raw_buffer_load_b32(rp, (int)vp, (int)sp[a], 0);
+        } else if (ap < kADma) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, QOQ_LDS_PTR(st + (ap * kW + wave) * 64), 16, (int)va,
+                                                     (int)sa[ap], 0, 0);
+        } else if (ap < kADma + 4) {
+            const int i = ap - kADma;
 #pragma unroll
             for (int v = 0; v < kV; ++v)
                 bq[j][i][v] = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)vb, (int)(sb[i] + v * 1024u), 0);
-        } else if (kG128 && a < kADma + 8) {
-            const int i = a - kADma - 4;
-            pq[j][i] = __builtin_amdgcn_raw_buffer_load_b8(rp, (int)vp, (int)sp[i], 0);
         }
     };
 
@@ -1168,7 +1180,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(
 #pragma unroll
         for (int b = 0; b < TN; ++b) acc[a][b] = int32x4{0, 0, 0, 0};
 
-    uint32_t gw[4], gwn[4];
+    uint32_t gw[4], gwn[4], gts[4], gte[4];
     u32x4 af[4];
     int32x4 bcur[4];
     int kl = 0;  // block of the load stream
@@ -1189,16 +1201,30 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(
         const u32x4* cur = stage(std::integral_constant<int, J>{});
         const u32x4* nxt = stage(std::integral_constant<int, JN>{});
         u32x4* ref = stage(std::integral_constant<int, JR>{});
-        // k-step 0 hooks: the next group's g128 words; the scalar offsets of
-        // this group's refill (moving the load stream to the next block when
-        // it gets there); this block's epilogue scales in its first group.
-        auto hook0 = [&](int a) __attribute__((always_inline)) {
-            if (kG128 && a % 4 == 2) {
-                uint32_t w = group_word(pq[JN][a / 4] & 0xFFu);
-                asm volatile("" : "+v"(w));
-                gwn[a / 4] = w;
+        // k-step 0 hooks: the next group's g128 words, one step per phase in
+        // sub-blocks 4t+1 and 4t+2 (the value of group_word: s | ((0x8080 -
+        // 257 z s) << 16) with s = hi + 1, z = lo of the byte); the scalar
+        // offsets of this group's refill (moving the load stream to the next
+        // block when it gets there); this block's epilogue scales in its
+        // first group.
+        auto hook0 = [&](int a, int ph) __attribute__((always_inline)) {
+            if constexpr (kG128) {
+                const int t = a / 4;
+                if (a % 4 == 1 && (ph == 0 || ph == 2)) {
+                    gts[t] = ph == 0 ? __builtin_amdgcn_ubfe(pq[JN][t], psh + 4, 4) : gts[t] + 1u;
+                    asm volatile("" : "+v"(gts[t]));
+                }
+                if ((a % 4 == 1 && (ph == 1 || ph == 3)) || (a % 4 == 2 && ph < 2)) {
+                    if (a % 4 == 1) gte[t] = ph == 1 ? __builtin_amdgcn_ubfe(pq[JN][t], psh, 4) : __umul24(gte[t], gts[t]);
+                    else gte[t] = ph == 0 ? (gte[t] << 8) + gte[t] : 0x8080u - gte[t];
+                    asm volatile("" : "+v"(gte[t]));
+                }
+                if (a % 4 == 2 && ph == 2) {
+                    gwn[t] = (gte[t] << 16) | gts[t];
+                    asm volatile("" : "+v"(gwn[t]));
+                }
             }
-            if (a == 5) {
+            if (a == 5 && ph == 0) {
                 int gl = g + 3;
                 if (gl >= G) {
                     gl -= G;
@@ -1210,7 +1236,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(
 #pragma unroll
                 for (int i = 0; i < 4; ++i) asm volatile("" : "+s"(sb[i]), "+s"(sp[i]));
             }
-            if (a == 9 && g == 0) {
+            if (a == 9 && ph == 0 && g == 0) {
                 sxw0 = __builtin_amdgcn_raw_buffer_load_b32(rsx, (m0 + 4 * lane) * 2, 0, 0);
                 sxw1 = __builtin_amdgcn_raw_buffer_load_b32(rsx, (m0 + 4 * lane) * 2 + 4, 0, 0);
                 if (kZp) rsv = __builtin_amdgcn_raw_buffer_load_b128(rrs, (m0 + 4 * lane) * 4, 0, 0);
@@ -1227,13 +1253,21 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(
         __builtin_amdgcn_s_waitcnt(kWaitMid);
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        auto issue_one = [&](int a) __attribute__((always_inline)) { load_one(ref, JR, a); };
+        auto issue_one = [&](int a, int ph) __attribute__((always_inline)) {
+            if (ph == 0) load_one(ref, JR, a);
+        };
         big_kstep<F, 0>(acc, af, bcur, cur + lane + 64, nxt + lane, bq[JN], gwn, issue_one);
 #pragma unroll
         for (int i = 0; i < 4; ++i) gw[i] = gwn[i];
     };
 
     // Prologue: groups 0..2 of the first block in flight, wait for group 0.
+    // (Without blocks, return before any load; with blocks, the block loop
+    // needs no guard, which would otherwise pull the prologue's B loads past
+    // its DMA loads and leave the wait counts at the group loop's head
+    // assuming the wrong order.)
+    if (n_my == 0) return;
+    __builtin_assume(n_my > 0);
     load_offsets(0);
 #pragma unroll
     for (int j = 0; j < NS - 1; ++j) {
@@ -1246,7 +1280,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(
     __builtin_amdgcn_s_waitcnt(kWaitPro);
     __builtin_amdgcn_s_barrier();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) gw[i] = kG128 ? group_word(pq[0][i] & 0xFFu) : 0u;
+    for (int i = 0; i < 4; ++i) gw[i] = kG128 ? group_word(__builtin_amdgcn_ubfe(pq[0][i], psh, 8)) : 0u;
     af[0] = st0[lane];
     af[1] = st0[lane + 128];
     af[2] = st0[lane + 256];
@@ -1264,6 +1298,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(
             group(std::integral_constant<int, 1>{}, h + 1);
             group(std::integral_constant<int, 2>{}, h + 2);
             group(std::integral_constant<int, 3>{}, h + 3);
+            // The register allocator may place AccVGPR copies on this loop's
+            // edges, and it does not know that the asm above wrote them: give
+            // every such copy the wait states a matrix-core result needs.
+            asm volatile("s_nop 7\n\ts_nop 7");
         }
         // Epilogue. 16 wait states after the last matrix-core operation, and
         // every accumulator passed through an empty asm so that no read moves
