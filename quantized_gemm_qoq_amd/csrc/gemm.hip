@@ -1306,9 +1306,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(
         // Epilogue. 16 wait states after the last matrix-core operation, and
         // every accumulator passed through an empty asm so that no read moves
         // above them. Lane (c, jq) holds rows m0 + 16a + c, channels n0 + 16i +
-        // 4jq .. +3. The scales go through the wave's LDS region; each (row
-        // tile, channel tile) leaves as one store, and stores outside the
-        // output get an out-of-range offset (no branches).
+        // 4jq .. +3. The scales go through the wave's LDS region. Two lane
+        // swaps per register turn the four-channel pieces of a tile pair into
+        // eight consecutive channels per lane, so each (row tile, tile pair)
+        // leaves as one 16-byte store per lane (16 rows x 64 bytes; 8-byte
+        // stores of 16 rows x 32 bytes drained at about 4 TB/s, these at 6.5).
+        // Stores outside the output get an out-of-range offset (no branches).
         asm volatile("s_nop 7\n\ts_nop 7");
 #pragma unroll
         for (int a = 0; a < 16; ++a)
@@ -1347,9 +1350,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(
             const int m = m0 + 16 * a + c;
             const float sx = h2f(*reinterpret_cast<const uint16_t*>(rows + (16 * a + c) * 2));
             const int rs = kZp ? *reinterpret_cast<const int*>(rows + 512 + (16 * a + c) * 4) : 0;
+            uint32_t d[TN][2];  // FP16 pairs: channels 4jq, 4jq+1 and 4jq+2, 4jq+3 of tile i
 #pragma unroll
             for (int i = 0; i < TN; ++i) {
-                const int n = n0 + 16 * i + 4 * jq;
                 const uint2 scq = *reinterpret_cast<const uint2*>(rows + 1536 + (16 * i + 4 * jq) * 2);
                 const uint32_t zz = kZp ? *reinterpret_cast<const uint32_t*>(rows + 1664 + 16 * i + 4 * jq) : 0u;
                 uint32_t h[4];
@@ -1359,10 +1362,26 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(
                     if (kZp) r -= (int)((zz >> (8 * v)) & 0xFFu) * rs;
                     h[v] = output_value(r, sx, h2f(((v < 2 ? scq.x : scq.y) >> (16 * (v & 1))) & 0xFFFFu));
                 }
-                typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                d[i][0] = h[0] | (h[1] << 16);
+                d[i][1] = h[2] | (h[3] << 16);
+            }
+#pragma unroll
+            for (int p = 0; p < TN; p += 2) {
+                // Rows of 16 lanes (jq) hold quads 0..3 of tiles p (X) and p+1
+                // (Y). The 32-lane swap gives [Xq0 Xq1 Yq0 Yq1] / [Xq2 Xq3 Yq2
+                // Yq3], the 16-lane swap [Xq0 Xq2 Yq0 Yq2] / [Xq1 Xq3 Yq1 Yq3]:
+                // row jq then holds channels 8jq .. 8jq+7 of the pair.
+                u32x4 o;
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const auto h32 = __builtin_amdgcn_permlane32_swap(d[p][k], d[p + 1][k], false, false);
+                    const auto h16 = __builtin_amdgcn_permlane16_swap(h32[0], h32[1], false, false);
+                    o[k] = h16[0];
+                    o[2 + k] = h16[1];
+                }
+                const int n = n0 + 16 * p + 8 * jq;
                 const uint32_t off = (m < M && n < N) ? ((uint32_t)m * (uint32_t)N + (uint32_t)n) * 2u : 0x80000000u;
-                __builtin_amdgcn_raw_buffer_store_b64(u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)}, ry, (int)off,
-                                                      0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(o, ry, (int)off, 0, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
