@@ -93,6 +93,9 @@ def _functions(asm_text):
         m = re.match(r"^([.\w$]+):$", line)
         if m:
             lab = m.group(1)
+            if lab.startswith(".Lfunc_end"):
+                cur = None  # the function's code ends here (it may hold several s_endpgm)
+                continue
             if not lab.startswith("."):
                 name = lab
                 cur = funcs.setdefault(name, [])
@@ -101,8 +104,6 @@ def _functions(asm_text):
             continue
         if cur is not None:
             cur.append(_Insn(ln, line))
-            if line.startswith("s_endpgm"):
-                cur = None
     return funcs
 
 

@@ -94,3 +94,19 @@ k:
 """
     n, problems = asm_hazards.check(text, "k")
     assert len(problems) == 1 and "0 wait states" in problems[0]
+
+
+def test_checker_reads_past_an_early_endpgm():
+    # an early-exit path ends in s_endpgm before the rest of the function
+    text = """\
+k:
+\ts_cbranch_scc1 .LBB0_9
+\ts_endpgm
+.LBB0_9:
+\tv_mfma_i32_16x16x64_i8 a[0:3], v[4:7], v[0:3], a[0:3]
+\tv_accvgpr_read_b32 v20, a1
+\ts_endpgm
+.Lfunc_end0:
+"""
+    n, problems = asm_hazards.check(text, "k")
+    assert n == 1 and len(problems) == 1 and "0 wait states" in problems[0]
