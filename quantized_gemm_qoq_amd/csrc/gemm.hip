@@ -1730,12 +1730,11 @@ bool fits_buffer_offsets(int fmt, int64_t M, int64_t N, int64_t K) {
 //       M = 4096 and the Qwen1.5-72B qkv at M = 1024, and 2-3% faster on the
 //       Qwen1.5-72B gate_up at M = 1024); M < 512: the LDS-pipelined kernel
 //       with 128-row blocks;
-//     256 x 256 blocks in whole rounds of the compute units, with the group
+//     at least one round of 256 x 256 blocks (whole or not), with the group
 //       count a multiple of 4: the large-block persistent kernel (against
-//       the wide kernel: Llama-3-8B gate_up at M = 4096 4% faster in g128,
-//       10% per-channel, 4% INT8 weights; o_proj and down at M = 4096 7-11%).
-//       With a partial last round (Qwen1.5-72B qkv at M = 1024: 1.5 rounds)
-//       it was 5% slower, and below one round it would leave CUs idle.
+//       the wide kernel: Llama-3-8B gate_up at M = 4096 15% faster in g128;
+//       Qwen1.5-72B qkv at M = 1024, 1.5 rounds, 11%). Below one round it
+//       would leave CUs idle.
 // Shapes whose offsets do not fit the buffer-load kernels take the reference
 // kernel (M <= 64) or the 16-row-wave tiled kernel, split over K (M > 64).
 Plan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, bool have_ws) {
@@ -1775,10 +1774,12 @@ Plan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, bool have_ws) {
         // they fill about one round; with more blocks, the wide kernel's two
         // 4-wave workgroups per CU.
         p.kind = nb128 > kCUs && M >= 512 ? kWide : kLds;
-        // Whole rounds of 256 x 256 blocks (at least one) with the group count
-        // a multiple of four: the large-block persistent kernel.
+        // At least one round of 256 x 256 blocks with the group count a
+        // multiple of four: the large-block persistent kernel (also with a
+        // partial last round: Qwen1.5-72B qkv at M = 1024, 1.5 rounds, ran
+        // 11% faster on it than on the wide kernel).
         const int64_t nb256 = ((M + 255) / 256) * ((N + 255) / 256);
-        if (nb256 >= kCUs && nb256 % kCUs == 0 && (K / kGroup) % 4 == 0 && M * N * 2 < (int64_t(1) << 31)) {
+        if (nb256 >= kCUs && (K / kGroup) % 4 == 0 && M * N * 2 < (int64_t(1) << 31)) {
             p.kind = kBig;
             p.group_m = 8;
         }

@@ -141,6 +141,8 @@ GEMM_SHAPES = [
     # ragged rows and channels; two rounds (each workgroup crosses a block
     # boundary every 4 groups); 12 groups
     (4000, 4000, 128 * 8), (4000, 8000, 128 * 4), (2048, 8192, 128 * 12),
+    # ... with a partial last round (384 blocks: half the workgroups take two)
+    (1000, 24560, 128 * 4),
 ]
 
 

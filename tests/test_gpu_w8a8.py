@@ -89,8 +89,8 @@ GEMM_SHAPES = [
     (9, 32, 128 * 21), (30, 48, 128 * 67), (48, 64, 128 * 70),
     (200, 272, 128 * 13),
     (600, 528, 128 * 9), (700, 400, 128 * 10), (200, 16400, 128 * 3), (1024, 8208, 128 * 13),
-    # the large-block persistent kernel: one and two rounds of 256 x 256 blocks
-    (4000, 4000, 128 * 8), (4000, 8000, 128 * 4),
+    # the large-block persistent kernel: one, two and 1.5 rounds of 256 x 256 blocks
+    (4000, 4000, 128 * 8), (4000, 8000, 128 * 4), (1000, 24560, 128 * 4),
 ]
 
 
