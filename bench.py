@@ -74,6 +74,11 @@ def parse_args(argv=None):
                    help="instead of the one-line result: time KV4 decode attention (4-bit "
                         "cache, SmoothAttention) at the serving shapes next to torch's FP16 "
                         "attention on an FP16 cache of the same shape")
+    p.add_argument("--read-probe", action="store_true",
+                   help="instead of the one-line result: time plain device-to-device copies "
+                        "that move the decode layer's algorithmic bytes (and larger sizes) "
+                        "from cold HBM, replayed from a graph like the GEMMs: what one launch "
+                        "of that size reaches on this chip")
     p.add_argument("--no-large-m", action="store_true",
                    help="leave the large-M half (Llama-3-8B prefill gate_up, M=4096) out of the "
                         "default run's line")
@@ -507,6 +512,8 @@ def main(argv=None) -> int:
                         return out
                     print(json.dumps(out), flush=True)
         return 0
+    if args.read_probe:
+        return read_probe(args, wl, layer)
     if args.formats:
         todo = [(w, l) for w in (workloads.WORKLOADS.values() if args.all_layers else [wl])
                 for l in w.layers if args.all_layers or args.layer in (None, l.name)]
@@ -751,6 +758,48 @@ def rmsnorm_compare(args, layer, eps=1e-5):
 
 
 FORMATS = ("w4a8_g128", "w4a8_per_channel", "w8a8", "w4a16_g128")
+
+
+def read_probe(args, wl, layer):
+    """Copies that move as many bytes as one GEMM launch of the layer (and
+    larger ones), over rotating source and destination buffers (cold HBM),
+    replayed from a graph and timed with HIP events like the GEMMs. A copy
+    of S bytes reads S and writes S; one line per size with the bytes moved
+    per launch, the time and the rate."""
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 3
+    dev = torch.device("cuda:0")
+    layer_bytes = max(gemm_bytes(m, layer.M, layer.N, layer.K) for m in (0, 1))
+    for moved in (layer_bytes, 2 * layer_bytes, 100 * 2**20, 400 * 2**20):
+        size = (moved // 2 + 255) // 256 * 256
+        R = max(2, math.ceil(args.rotate_mib * 2**20 / (2 * size)))
+        src = [torch.empty(size, dtype=torch.uint8, device=dev).fill_(i % 251) for i in range(R)]
+        dst = [torch.empty(size, dtype=torch.uint8, device=dev) for _ in range(R)]
+        L = max(R, args.kernel_launches // R * R)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(L):
+                dst[i % R].copy_(src[i % R])
+        g.replay()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / L
+        print(json.dumps({"probe": "device copy", "layer": layer.name, "bytes_moved": 2 * size,
+                          "copy_bytes": size, "rotating_copies": R, "launches": L,
+                          "avg_us": round(us, 3), "GB/s": round(2 * size / us / 1e3, 1),
+                          "frac_of_8TBps": round(2 * size / us / 1e3 / 8000, 3)}), flush=True)
+        del src, dst, g
+        torch.cuda.empty_cache()
+    return 0
 
 
 def format_compare(args, wl, layer):
