@@ -1716,7 +1716,14 @@ bool fits_buffer_offsets(int fmt, int64_t M, int64_t N, int64_t K) {
 //     fewer groups each beat a deeper ring, which would not fit the registers
 //     of 16 waves); for 33..64 rows two 32-row workgroups per band of three
 //     channel tiles.
-//   M > 64, counting 128 x 256 blocks (nb128):
+//   64 < M <= 256, K <= 16384, 4-bit weights, when 64-row workgroups over
+//     bands of four channel tiles make between 3/4 and one round of the
+//     compute units: the streaming kernel with 8 waves that each load one
+//     group at a time (Qwen1.5-72B o_proj at M = 128 22-25% faster and
+//     Llama-3-8B down at M = 256 16% faster than the split LDS-pipelined
+//     plan, with no partial sums; with more workgroups (qkv and gate_up) the
+//     activation re-reads made it 10-60% slower, and at K = 24576 it tied);
+//   M > 64 otherwise, counting 128 x 256 blocks (nb128):
 //     nb128 <= 256: the LDS-pipelined kernel with 128-row blocks, one 8-wave
 //       workgroup per compute unit; below 128 blocks, with a workspace, split
 //       over K into min(8, 256 / nb128) ranges (the split sums are added by
@@ -1737,6 +1744,10 @@ bool fits_buffer_offsets(int fmt, int64_t M, int64_t N, int64_t K) {
 //       would leave CUs idle.
 // Shapes whose offsets do not fit the buffer-load kernels take the reference
 // kernel (M <= 64) or the 16-row-wave tiled kernel, split over K (M > 64).
+// Workgroups of the streaming kernel with 64-row blocks and bands of four
+// channel tiles.
+int64_t stream64_grid(int64_t M, int64_t N) { return ((M + 63) / 64) * ((N / 16 + 3) / 4); }
+
 Plan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, bool have_ws) {
     Plan p;
     const int64_t tiles = N / 16;
@@ -1767,6 +1778,15 @@ Plan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, bool have_ws) {
                 p.w = 2 * ((tiles + 2) / 3) <= kCUs ? 16 : 8;
             }
         }
+    } else if (fits && M <= 256 && K <= 16384 && fmt != kFmtW8 &&
+               4 * stream64_grid(M, N) >= 3 * kCUs && stream64_grid(M, N) <= kCUs) {
+        // 64-row workgroups of the streaming kernel over bands of four
+        // channel tiles, when they make between 3/4 and one round
+        p.kind = kStream;
+        p.mb = 4;
+        p.nt = 4;
+        p.r = 1;
+        p.w = 8;
     } else if (fits && (M >= 512 || nb128 >= kCUs / 2 || have_ws)) {
         // 128 x 256 blocks that fill at most one round of the compute units
         // run as one 8-wave workgroup per CU (two waves per SIMD even then),
@@ -1874,6 +1894,12 @@ void launch_stream_nt(const Plan& p, const GemmArgs& a) {
 
 template <int F>
 void launch_stream(const Plan& p, const GemmArgs& a) {
+    if constexpr (F != kFmtW8) {
+        if (p.mb == 4) {
+            launch_stream_pl<F, 4, 4, 1, 8>(p, a);
+            return;
+        }
+    }
     if (p.mb == 1) launch_stream_nt<F, 1>(p, a);
     else launch_stream_nt<F, 2>(p, a);
 }

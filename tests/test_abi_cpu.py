@@ -139,19 +139,24 @@ def test_workspace_bytes(lib):
 
 def test_middle_m_split_plans(lib):
     """The K splits the plan picks for the middle-M benchmark layers, seen
-    through the workspace they need (S * M * N INT32 partial sums): 128 x 128
-    blocks of two workgroups per CU split in the smallest power of two that
-    fills a round (4-bit weights, M < 512, K <= 16384), else 128 x 256 blocks
-    split up to 8 ways."""
+    through the workspace they need (S * M * N INT32 partial sums): none where
+    64-row streaming workgroups make 3/4 to one round (4-bit weights,
+    M <= 256, K <= 16384); else 128 x 128 blocks of two workgroups per CU
+    split in the smallest power of two that fills a round (4-bit weights,
+    M < 512, K <= 16384), else 128 x 256 blocks split up to 8 ways."""
     f, w8 = lib.qoq_gemm_workspace_bytes, lib.qoq_w8a8_gemm_workspace_bytes
     part = lambda S, M, N: S * M * N * 4
     for mode in (0, 1):
-        assert f(mode, 128, 8192, 8192) == part(4, 128, 8192)      # Qwen1.5-72B o_proj: 64 blocks
+        assert f(mode, 128, 8192, 8192) == 0                       # Qwen1.5-72B o_proj: 256 streams
+        assert f(mode, 128, 4096, 8192) == part(8, 128, 4096)      # 128 streams: 32 blocks, 8 splits
         assert f(mode, 128, 24576, 8192) == part(2, 128, 24576)    # qkv: 192 blocks
         assert f(mode, 128, 49152, 8192) == 0                      # gate_up: 384 blocks, no split
         assert f(mode, 128, 8192, 24576) == part(8, 128, 8192)     # down, K > 16384: 32 wide blocks
-        assert f(mode, 256, 4096, 14336) == part(4, 256, 4096)     # Llama-3-8B down: 64 blocks
+        assert f(mode, 256, 4096, 14336) == 0                      # Llama-3-8B down: 256 streams
+        assert f(mode, 256, 4096, 24576) == part(8, 256, 4096)     # K > 16384: 32 wide blocks, 8 splits
         assert f(mode, 256, 28672, 4096) == 0                      # Llama-3-8B gate_up: 448 blocks
+    for mode in (0, 1):  # the GPU parity shapes of the 64-row streaming plan need no workspace
+        assert f(mode, 72, 6144, 640) == f(mode, 256, 4080, 128 * 9) == f(mode, 129, 4096, 384) == 0
     assert w8(128, 8192, 8192) == part(8, 128, 8192)               # INT8 weights: 128 x 256 blocks
     assert f(0, 130, 1040, 128 * 33) == part(8, 130, 1040)         # 18 blocks: 8 splits of 33 groups
     assert f(0, 200, 272, 128 * 13) == part(4, 200, 272)           # 13 groups: at most 6 splits -> 4

@@ -48,9 +48,10 @@ def _f16(shape, seed, scale):
     return workloads.random_fp16(shape, seed, scale).to(DEV)
 
 
-# (M, K, N) reaching: stream (M <= 64), tiled without workspace, LDS-pipelined
-# split-K with workspace, LDS-pipelined unsplit, wide.
-GEMM_CASES = [(1, 256, 48), (17, 384, 272), (33, 640, 16), (63, 256, 528),
+# (M, K, N) reaching: stream (M <= 64, and 64-row workgroups at 72 rows),
+# tiled without workspace, LDS-pipelined split-K with workspace, LDS-pipelined
+# unsplit, wide.
+GEMM_CASES = [(1, 256, 48), (17, 384, 272), (33, 640, 16), (63, 256, 528), (72, 640, 6144),
               (65, 512, 272), (130, 1024, 144), (200, 1664, 272), (257, 256, 48),
               (600, 1152, 528), (640, 640, 16400)]
 

@@ -109,7 +109,7 @@ def test_captured_split_call_survives_workspace_growth():
     still replays correctly after a later call on the same stream needed a
     larger workspace: the smaller one stays allocated, so tensors allocated
     afterwards neither receive the replay's partial sums nor feed it."""
-    small, large = (200, 1664, 272), (128, 8192, 8192)  # (M, K, N)
+    small, large = (200, 1664, 272), (128, 8192, 24576)  # (M, K, N)
     need_small = qoq.qoq_gemm_workspace_bytes("g128", small[0], small[2], small[1])
     assert 0 < need_small < qoq.qoq_gemm_workspace_bytes("g128", large[0], large[2], large[1])
     s = torch.cuda.Stream()

@@ -122,6 +122,11 @@ GEMM_SHAPES = [
     (129, 32, 640), (257, 80, 128), (512, 512, 1024), (520, 272, 640), (3, 16, 132096),
     # streaming-kernel ring: main loop plus a leftover group, for 1, 2 and 4 row blocks
     (9, 32, 128 * 21), (30, 48, 128 * 67), (48, 64, 128 * 70),
+    # streaming kernel with 64-row workgroups over bands of four channel
+    # tiles (between 3/4 and one round): fewer groups than waves and a ragged
+    # row block; a ragged last band and 9 groups over 8 waves; a last row
+    # block of one row
+    (72, 6144, 640), (256, 4080, 128 * 9), (129, 4096, 128 * 3),
     # split K over 4 uneven group ranges (13 groups) on 128 x 128 blocks,
     # ragged rows and channels
     (200, 272, 128 * 13),

@@ -35,7 +35,7 @@ def _noalloc(mode, pw, xq, s_x, rowsum, M, N, K, y, acc):
 
 
 # (first call, second smaller call): split-K plans (scratch used) and plans without.
-PAIRS = [((128, 8192, 8192), (200, 1664, 272)),   # 32 MiB of partial sums, then a small split
+PAIRS = [((128, 24576, 8192), (200, 1664, 272)),  # 32 MiB of partial sums, then a small split
          ((256, 4096, 2048), (130, 1024, 144)),
          ((64, 4096, 6144), (17, 384, 272)),       # decode plans: no scratch
          ((600, 1152, 528), (65, 512, 272))]
