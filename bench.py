@@ -79,6 +79,9 @@ def parse_args(argv=None):
                         "that move the decode layer's algorithmic bytes (and larger sizes) "
                         "from cold HBM, replayed from a graph like the GEMMs: what one launch "
                         "of that size reaches on this chip")
+    p.add_argument("--k-sweep", action="store_true",
+                   help="time the layer's GEMMs at K = 128 .. the layer's K (same M and N, same "
+                        "seeds) and fit time = fixed + per-K cost; no CPU baseline")
     p.add_argument("--no-large-m", action="store_true",
                    help="leave the large-M half (Llama-3-8B prefill gate_up, M=4096) out of the "
                         "default run's line")
@@ -514,6 +517,8 @@ def main(argv=None) -> int:
         return 0
     if args.read_probe:
         return read_probe(args, wl, layer)
+    if args.k_sweep:
+        return k_sweep(args, wl, layer)
     if args.formats:
         todo = [(w, l) for w in (workloads.WORKLOADS.values() if args.all_layers else [wl])
                 for l in w.layers if args.all_layers or args.layer in (None, l.name)]
@@ -758,6 +763,47 @@ def rmsnorm_compare(args, layer, eps=1e-5):
 
 
 FORMATS = ("w4a8_g128", "w4a8_per_channel", "w8a8", "w4a16_g128")
+
+
+def k_sweep(args, wl, layer):
+    """The layer's GEMMs at K = 128, 256, ... up to its own K (same M, N and
+    seeds), timed like the default run, one line per K; then, per GEMM, the
+    least-squares line time = fixed + slope * K. The intercept is what a
+    launch of this M and N costs before its time grows with the streamed
+    bytes; the slope gives the rate at which the K-dependent bytes (codes,
+    group parameters and activations) stream."""
+    import dataclasses
+
+    args.cpu_seconds = 0
+    ks, times = [], {}
+    K = 128
+    while K <= layer.K:
+        sub = dataclasses.replace(layer, name=f"{layer.name}_k{K}", K=K)
+        out = run_layer(args, wl, sub)
+        if isinstance(out, int):
+            return out
+        ks.append(K)
+        line = {"probe": "k sweep", "layer": layer.name, "M": layer.M, "N": layer.N, "K": K}
+        for name, v in out["kernels"].items():
+            times.setdefault(name, []).append(v["avg_us"])
+            line[name + "_us"] = v["avg_us"]
+        print(json.dumps(line), flush=True)
+        K *= 2
+    n = len(ks)
+    mk = sum(ks) / n
+    for name, ts in times.items():
+        mt = sum(ts) / n
+        slope = sum((k - mk) * (t - mt) for k, t in zip(ks, ts)) / sum((k - mk) ** 2 for k in ks)
+        fixed = mt - slope * mk
+        fit = {"probe": "k sweep fit", "layer": layer.name, "kernel": name,
+               "fixed_us": round(fixed, 3), "us_per_1024_k": round(slope * 1024, 3)}
+        if name.startswith("w4a8_gemm"):
+            mode = 0 if name.endswith("g128") else 1
+            per_k = (gemm_bytes(mode, layer.M, layer.N, 2 * 128) -
+                     gemm_bytes(mode, layer.M, layer.N, 128)) / 128  # bytes per unit of K
+            fit["streamed_GB/s"] = round(per_k / slope / 1e3, 1)
+        print(json.dumps(fit), flush=True)
+    return 0
 
 
 def read_probe(args, wl, layer):
