@@ -769,14 +769,16 @@ def k_sweep(args, wl, layer):
     """The layer's GEMMs at K = 128, 256, ... up to its own K (same M, N and
     seeds), timed like the default run, one line per K; then, per GEMM, the
     least-squares line time = fixed + slope * K. The intercept is what a
-    launch of this M and N costs before its time grows with the streamed
-    bytes; the slope gives the rate at which the K-dependent bytes (codes,
-    group parameters and activations) stream."""
+    launch of this M and N costs before its time grows with K; the slope
+    gives the rate at which the K-dependent bytes (codes, group parameters
+    and activations) stream, and, above the ridge (M > 162), the rate of the
+    K-dependent matrix work. Above the ridge the sweep starts at K = 512, the
+    smallest K the large-block kernel takes, so that one kernel spans it."""
     import dataclasses
 
     args.cpu_seconds = 0
     ks, times = [], {}
-    K = 128
+    K = 512 if layer.M > 162 else 128
     while K <= layer.K:
         sub = dataclasses.replace(layer, name=f"{layer.name}_k{K}", K=K)
         out = run_layer(args, wl, sub)
@@ -802,6 +804,7 @@ def k_sweep(args, wl, layer):
             per_k = (gemm_bytes(mode, layer.M, layer.N, 2 * 128) -
                      gemm_bytes(mode, layer.M, layer.N, 128)) / 128  # bytes per unit of K
             fit["streamed_GB/s"] = round(per_k / slope / 1e3, 1)
+            fit["k_work_TOPS"] = round(2 * layer.M * layer.N / slope / 1e6, 1)
         print(json.dumps(fit), flush=True)
     return 0
 

@@ -70,6 +70,18 @@ __device__ __forceinline__ uint16_t output_value(int r, float sx, float sc) {
     return f2h(v);
 }
 
+// Two outputs of one row, (f32(r)·sx)·sc each, rounded to FP16 and packed
+// (low half: r0) by one conversion instruction.
+__device__ __forceinline__ uint32_t output_pair(int r0, int r1, float sx, float sc0, float sc1) {
+    float v0 = ((float)r0 * sx) * sc0;
+    float v1 = ((float)r1 * sx) * sc1;
+    asm("" : "+v"(v0));
+    asm("" : "+v"(v1));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){v0, v1}, f16x2));
+}
+
 // Epilogue for one lane's four accumulator rows of one channel.
 template <int F>
 __device__ __forceinline__ void store_outputs(int32x4 a, int m_first, int n, int M, int N,
@@ -1345,6 +1357,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+        // The lane's 4 TN channel scales as fp32, once per block (converting
+        // them per row tile was a sixth of the epilogue's instructions).
+        float scf[TN][4];
+#pragma unroll
+        for (int i = 0; i < TN; ++i) {
+            const uint2 scq = *reinterpret_cast<const uint2*>(rows + 1536 + (16 * i + 4 * jq) * 2);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) scf[i][v] = h2f(((v < 2 ? scq.x : scq.y) >> (16 * (v & 1))) & 0xFFFFu);
+        }
 #pragma unroll
         for (int a = 0; a < 16; ++a) {
             const int m = m0 + 16 * a + c;
@@ -1353,17 +1374,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(
             uint32_t d[TN][2];  // FP16 pairs: channels 4jq, 4jq+1 and 4jq+2, 4jq+3 of tile i
 #pragma unroll
             for (int i = 0; i < TN; ++i) {
-                const uint2 scq = *reinterpret_cast<const uint2*>(rows + 1536 + (16 * i + 4 * jq) * 2);
                 const uint32_t zz = kZp ? *reinterpret_cast<const uint32_t*>(rows + 1664 + 16 * i + 4 * jq) : 0u;
-                uint32_t h[4];
+                int r[4];
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    int r = acc[a][i][v];
-                    if (kZp) r -= (int)((zz >> (8 * v)) & 0xFFu) * rs;
-                    h[v] = output_value(r, sx, h2f(((v < 2 ? scq.x : scq.y) >> (16 * (v & 1))) & 0xFFFFu));
+                    r[v] = acc[a][i][v];
+                    if (kZp) r[v] -= (int)((zz >> (8 * v)) & 0xFFu) * rs;
                 }
-                d[i][0] = h[0] | (h[1] << 16);
-                d[i][1] = h[2] | (h[3] << 16);
+                d[i][0] = output_pair(r[0], r[1], sx, scf[i][0], scf[i][1]);
+                d[i][1] = output_pair(r[2], r[3], sx, scf[i][2], scf[i][3]);
             }
 #pragma unroll
             for (int p = 0; p < TN; p += 2) {
