@@ -765,6 +765,19 @@ def rmsnorm_compare(args, layer, eps=1e-5):
 FORMATS = ("w4a8_g128", "w4a8_per_channel", "w8a8", "w4a16_g128")
 
 
+def fit_line(xs, ys):
+    """Least-squares line y = a + b x through the points; returns (a, b)."""
+    n = len(xs)
+    if n < 2 or len(ys) != n:
+        raise ValueError("a line needs at least two points")
+    mx, my = sum(xs) / n, sum(ys) / n
+    sxx = sum((x - mx) ** 2 for x in xs)
+    if sxx == 0:
+        raise ValueError("a line needs two distinct x values")
+    b = sum((x - mx) * (y - my) for x, y in zip(xs, ys)) / sxx
+    return my - b * mx, b
+
+
 def k_sweep(args, wl, layer):
     """The layer's GEMMs at K = 128, 256, ... up to its own K (same M, N and
     seeds), timed like the default run, one line per K; then, per GEMM, the
@@ -791,12 +804,8 @@ def k_sweep(args, wl, layer):
             line[name + "_us"] = v["avg_us"]
         print(json.dumps(line), flush=True)
         K *= 2
-    n = len(ks)
-    mk = sum(ks) / n
     for name, ts in times.items():
-        mt = sum(ts) / n
-        slope = sum((k - mk) * (t - mt) for k, t in zip(ks, ts)) / sum((k - mk) ** 2 for k in ks)
-        fixed = mt - slope * mk
+        fixed, slope = fit_line(ks, ts)
         fit = {"probe": "k sweep fit", "layer": layer.name, "kernel": name,
                "fixed_us": round(fixed, 3), "us_per_1024_k": round(slope * 1024, 3)}
         if name.startswith("w4a8_gemm"):

@@ -104,3 +104,17 @@ def test_counter_summary_table(tmp_path, monkeypatch):
     assert rows["SQ_WAVES"][pc] == "4096" and rows["TCC_HIT_sum"][pc] == "20"
     assert rows["SQ_WAVES"][cols.index("k_gemm_lds<0, 128, 1>")] == ""
     assert "--pmc SQ_WAVES" in text and "--pmc TCC_HIT_sum" in text
+
+
+def test_fit_line_recovers_fixed_cost_and_slope():
+    """The K sweep's line fit: exact on points of a line, least squares
+    (mean residual zero) on noisy ones, and an error without two distinct K."""
+    ks = [128, 256, 512, 1024, 2048, 4096]
+    a, b = bench.fit_line(ks, [4.0 + 0.001 * k for k in ks])
+    assert abs(a - 4.0) < 1e-12 and abs(b - 0.001) < 1e-15
+    ys = [4.0 + 0.001 * k + (0.05 if i % 2 else -0.05) for i, k in enumerate(ks)]
+    a, b = bench.fit_line(ks, ys)
+    assert abs(sum(y - (a + b * k) for k, y in zip(ks, ys))) < 1e-9
+    for bad in ([1], [512, 512]):
+        with pytest.raises(ValueError):
+            bench.fit_line(bad, [1.0] * len(bad))
