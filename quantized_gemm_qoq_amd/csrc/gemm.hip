@@ -1305,7 +1305,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(
         block_of(k, bm, bn);
         m0 = bm * BM;
         n0 = (bn * (BN / 16) + wave * TN) * 16;
-        for (int h = 0; h < G; h += NS) {
+        // G is a positive multiple of NS (the plan's condition), so the loop
+        // runs at least once: without a zero-trip path to the epilogue the
+        // accumulators are zeroed once per block and reach the epilogue in
+        // the registers the loop left them in.
+        int h = 0;
+        do {
             group(std::integral_constant<int, 0>{}, h);
             group(std::integral_constant<int, 1>{}, h + 1);
             group(std::integral_constant<int, 2>{}, h + 2);
@@ -1314,7 +1319,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(
             // edges, and it does not know that the asm above wrote them: give
             // every such copy the wait states a matrix-core result needs.
             asm volatile("s_nop 7\n\ts_nop 7");
-        }
+            h += NS;
+        } while (h < G);
         // Epilogue. 16 wait states after the last matrix-core operation, and
         // every accumulator passed through an empty asm so that no read moves
         // above them. Lane (c, jq) holds rows m0 + 16a + c, channels n0 + 16i +
